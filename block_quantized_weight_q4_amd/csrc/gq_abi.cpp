@@ -1,0 +1,150 @@
+// gq_abi.cpp -- the extern "C" boundary: argument validation (before any HIP
+// call), dispatch to the kernel launchers, status codes.  See include/gq.h.
+#include "../../include/gq.h"
+
+#include <hip/hip_runtime.h>
+
+#include "gq_internal.h"
+
+namespace {
+
+bool known_type(int t) { return t == GQ_Q4_0 || t == GQ_Q4_K || t == GQ_Q6_K; }
+
+int qk_of(int t) { return t == GQ_Q4_0 ? 32 : 256; }
+int bytes_of(int t) { return t == GQ_Q4_0 ? 18 : (t == GQ_Q4_K ? 144 : 210); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+gq_status from_hip(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_LAUNCH; }
+
+// Largest element count any single launch handles (keeps 32-bit grid sizes
+// and 64-bit byte offsets far from overflow).
+constexpr int64_t MAX_ELEMS = (int64_t)1 << 40;
+
+}  // namespace
+
+extern "C" {
+
+int gq_abi_version(void) { return GQ_ABI_VERSION; }
+
+const char* gq_status_str(gq_status s) {
+    switch (s) {
+    case GQ_OK: return "ok";
+    case GQ_ERR_TYPE: return "unknown block type";
+    case GQ_ERR_DTYPE: return "unsupported element type";
+    case GQ_ERR_SHAPE: return "invalid shape";
+    case GQ_ERR_NULL: return "null pointer";
+    case GQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case GQ_ERR_UNSUPPORTED: return "unsupported combination";
+    case GQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case GQ_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+gq_status gq_block_info(gq_type t, int32_t* elems, int32_t* bytes) {
+    if (!known_type(t)) return GQ_ERR_TYPE;
+    if (!elems || !bytes) return GQ_ERR_NULL;
+    *elems = qk_of(t);
+    *bytes = bytes_of(t);
+    return GQ_OK;
+}
+
+gq_status gq_dequant(gq_type t, const void* blocks, int64_t n_blocks, void* out, gq_dtype out_dtype,
+                     hipStream_t stream) {
+    if (!known_type(t)) return GQ_ERR_TYPE;
+    if (out_dtype != GQ_F32 && out_dtype != GQ_BF16 && out_dtype != GQ_F16) return GQ_ERR_DTYPE;
+    if (n_blocks < 0 || n_blocks * qk_of(t) > MAX_ELEMS) return GQ_ERR_SHAPE;
+    if (n_blocks == 0) return GQ_OK;
+    if (!blocks || !out) return GQ_ERR_NULL;
+    if (!aligned16(blocks) || !aligned16(out)) return GQ_ERR_ALIGN;
+    try {
+        return from_hip(gqk_dequant(t, blocks, n_blocks, out, out_dtype, stream));
+    } catch (...) {
+        return GQ_ERR_LAUNCH;
+    }
+}
+
+gq_status gq_matvec(gq_type t, const void* W, int64_t N, int64_t K, const void* x, gq_dtype x_dtype,
+                    int32_t batch, float* y, hipStream_t stream) {
+    if (!known_type(t)) return GQ_ERR_TYPE;
+    if (x_dtype != GQ_F32 && x_dtype != GQ_BF16) return GQ_ERR_DTYPE;
+    if (N < 0 || K < 0 || K % qk_of(t) != 0 || batch < 1) return GQ_ERR_SHAPE;
+    if (N > MAX_ELEMS || K > MAX_ELEMS || (K > 0 && N > MAX_ELEMS / K)) return GQ_ERR_SHAPE;
+    if (batch > 8) return GQ_ERR_UNSUPPORTED;
+    if (N == 0) return GQ_OK;
+    if (!y || (K > 0 && (!W || !x))) return GQ_ERR_NULL;
+    if (!aligned16(y) || (K > 0 && (!aligned16(W) || !aligned16(x)))) return GQ_ERR_ALIGN;
+    try {
+        return from_hip(gqk_matvec(t, W, N, K, x, x_dtype, batch, y, stream));
+    } catch (...) {
+        return GQ_ERR_LAUNCH;
+    }
+}
+
+gq_status gq_matvec_id_workspace(int32_t n_experts, int32_t n_tokens, int32_t top_k, int64_t N, size_t* bytes) {
+    if (!bytes) return GQ_ERR_NULL;
+    if (n_experts < 1 || n_tokens < 0 || top_k < 1 || top_k > n_experts || N < 0 ||
+        (int64_t)n_tokens * top_k > 4096)
+        return GQ_ERR_SHAPE;
+    *bytes = gqk_matvec_id_ws_bytes(n_experts, n_tokens, top_k, N);
+    return GQ_OK;
+}
+
+gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_t N, int64_t K,
+                       const int32_t* ids, int32_t n_tokens, int32_t top_k, const void* x, gq_dtype x_dtype,
+                       int32_t x_per_slot, const float* route_w, float* y, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    if (!known_type(t)) return GQ_ERR_TYPE;
+    if (x_dtype != GQ_F32 && x_dtype != GQ_BF16) return GQ_ERR_DTYPE;
+    if (n_experts < 1 || n_tokens < 0 || top_k < 1 || top_k > n_experts || N < 0 || K < 0 ||
+        K % qk_of(t) != 0 || (x_per_slot != 0 && x_per_slot != 1) || (int64_t)n_tokens * top_k > 4096)
+        return GQ_ERR_SHAPE;
+    if (N > MAX_ELEMS || K > MAX_ELEMS || (K > 0 && N > MAX_ELEMS / K) ||
+        (K > 0 && N > 0 && (int64_t)n_experts > MAX_ELEMS / (N * K)))
+        return GQ_ERR_SHAPE;
+    if (n_tokens == 0 || N == 0) return GQ_OK;
+    if (!ids || !y || !ws || (K > 0 && (!experts || !x))) return GQ_ERR_NULL;
+    if (!aligned16(ids) || !aligned16(y) || !aligned16(ws) || (route_w && !aligned16(route_w)) ||
+        (K > 0 && (!aligned16(experts) || !aligned16(x))))
+        return GQ_ERR_ALIGN;
+    if (ws_bytes < gqk_matvec_id_ws_bytes(n_experts, n_tokens, top_k, N)) return GQ_ERR_WORKSPACE;
+    try {
+        return from_hip(gqk_matvec_id(t, experts, n_experts, N, K, ids, n_tokens, top_k, x, x_dtype, x_per_slot,
+                                      route_w, y, ws, stream));
+    } catch (...) {
+        return GQ_ERR_LAUNCH;
+    }
+}
+
+gq_status gq_matvec_id_check(const void* ws, hipStream_t stream, int32_t* n_bad_ids) {
+    if (!ws || !n_bad_ids) return GQ_ERR_NULL;
+    if (!aligned16(ws)) return GQ_ERR_ALIGN;
+    try {
+        return from_hip(gqk_matvec_id_bad_count(ws, stream, n_bad_ids));
+    } catch (...) {
+        return GQ_ERR_LAUNCH;
+    }
+}
+
+gq_status gq_matmul(gq_type t, const void* W, int64_t N, int64_t K, const void* X, gq_dtype x_dtype, int64_t M,
+                    int64_t ldx, float* Y, int64_t ldy, hipStream_t stream) {
+    if (!known_type(t)) return GQ_ERR_TYPE;
+    if (x_dtype != GQ_F32 && x_dtype != GQ_BF16) return GQ_ERR_DTYPE;
+    if (N < 0 || K < 0 || M < 0 || K % qk_of(t) != 0 || ldx < K || ldy < N) return GQ_ERR_SHAPE;
+    if (N > MAX_ELEMS || K > MAX_ELEMS || M > MAX_ELEMS || (M > 0 && ldx > MAX_ELEMS / M) ||
+        (M > 0 && ldy > MAX_ELEMS / M) || (K > 0 && N > MAX_ELEMS / K))
+        return GQ_ERR_SHAPE;
+    if (t != GQ_Q4_K || x_dtype != GQ_BF16) return GQ_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return GQ_OK;
+    if (!Y || (K > 0 && (!W || !X))) return GQ_ERR_NULL;
+    if (!aligned16(Y) || (K > 0 && (!aligned16(W) || !aligned16(X)))) return GQ_ERR_ALIGN;
+    if ((ldx * 2) % 16 != 0 || (ldy * 4) % 16 != 0) return GQ_ERR_ALIGN;
+    try {
+        return from_hip(gqk_matmul(t, W, N, K, X, x_dtype, M, ldx, Y, ldy, stream));
+    } catch (...) {
+        return GQ_ERR_LAUNCH;
+    }
+}
+
+}  // extern "C"

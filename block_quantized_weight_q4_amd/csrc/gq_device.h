@@ -1,0 +1,82 @@
+// gq_device.h -- device-side helpers shared by the gfx950 kernels of the
+// library (HIP, wave64).  Nothing here is used by the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqd {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Block geometry (weights per block, bytes per block) of the three formats.
+enum { T_Q4_0 = 1, T_Q4_K = 2, T_Q6_K = 3 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+// fp16 pair (1024, 1024): OR-ing a small integer n into the low mantissa bits
+// of each half gives the fp16 value 1024 + n exactly (the exponent field of
+// 1024 leaves the ten mantissa bits free and their weight is one).
+constexpr uint32_t MAGIC = 0x64006400u;
+
+// Loads that may be only 2-byte aligned (Q4_0 and Q6_K blocks are 18 and 210
+// bytes long).  gfx9 global memory instructions accept unaligned addresses.
+__device__ __forceinline__ u32x4 ld16u(const uint8_t* p) {
+    u32x4 v;
+    __builtin_memcpy(&v, p, 16);
+    return v;
+}
+__device__ __forceinline__ u32x2 ld8u(const uint8_t* p) {
+    u32x2 v;
+    __builtin_memcpy(&v, p, 8);
+    return v;
+}
+__device__ __forceinline__ uint32_t ld4u(const uint8_t* p) {
+    uint32_t v;
+    __builtin_memcpy(&v, p, 4);
+    return v;
+}
+__device__ __forceinline__ uint16_t ld2(const uint8_t* p) {
+    uint16_t v;
+    __builtin_memcpy(&v, p, 2);
+    return v;
+}
+__device__ __forceinline__ u32x4 ld16a(const uint8_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// D = a.lo*b.lo + a.hi*b.hi + c (fp16 pairs, fp32 accumulate).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c, false);
+}
+
+// Two fp32 -> fp16 (round to nearest even), packed lo | hi << 16.
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+    half2v h = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// fp32 -> fp16, round to nearest even.  The empty asm keeps f an fp32 value in
+// a register: otherwise the compiler may fold a preceding multiply and this
+// rounding into one v_fma_mixlo_f16 with a +0 addend, which turns a -0 product
+// into +0.
+__device__ __forceinline__ uint16_t f2h(float f) {
+    __asm__ volatile("" : "+v"(f));
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float bf2f(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+__device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8 * i)) & 0xffu; }
+
+}  // namespace gqd

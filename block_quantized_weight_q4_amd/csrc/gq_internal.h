@@ -1,0 +1,23 @@
+// gq_internal.h -- launchers behind the C ABI (host side of the kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// All launchers assume their arguments were validated by the ABI layer.
+hipError_t gqk_dequant(int type, const void* blocks, int64_t n_blocks, void* out, int out_dtype,
+                       hipStream_t s);
+
+hipError_t gqk_matvec(int type, const void* W, int64_t N, int64_t K, const void* x, int x_dtype,
+                      int batch, float* y, hipStream_t s);
+
+// Routed experts.  Workspace layout is private to gq_matvec_id.hip.
+size_t gqk_matvec_id_ws_bytes(int n_experts, int n_tokens, int top_k, int64_t N);
+hipError_t gqk_matvec_id(int type, const void* experts, int n_experts, int64_t N, int64_t K,
+                         const int32_t* ids, int n_tokens, int top_k, const void* x, int x_dtype,
+                         int x_per_slot, const float* route_w, float* y, void* ws, hipStream_t s);
+hipError_t gqk_matvec_id_bad_count(const void* ws, hipStream_t s, int32_t* n_bad);
+
+hipError_t gqk_matmul(int type, const void* W, int64_t N, int64_t K, const void* X, int x_dtype,
+                      int64_t M, int64_t ldx, float* Y, int64_t ldy, hipStream_t s);

@@ -1,0 +1,158 @@
+/*
+ * gq.h -- C ABI of the block-quantized weight product library (gfx950).
+ *
+ * The library computes products against weights kept in their packed ggml
+ * block form, the operation that "GGUF in transformers" (Hugging Face blog)
+ * describes in section "Reusing ggml's Metal kernels", kernel table, row
+ * "ggml-quantization": matrix operations that read the packed quantized
+ * weights directly -- including only the selected experts of an MoE model --
+ * instead of expanding the whole weight matrix before each decode step.  The
+ * same section notes that such a kernel works on tensors and does not need the
+ * model to come from a GGUF file; this ABI therefore takes plain device
+ * pointers.  The section "What is the GGUF file format?" names the block
+ * formats (Q4_K_M mixes Q4_K with Q6_K tensors); the page "Show HN: Gemma 4
+ * 26B-A4B at up to 100+ tokens/s on a 16 GB Mac" (Architecture section) uses
+ * the same product for routed 4-bit experts, and its prefill step, where the
+ * GPU expands 4-bit experts to fp16 for a matrix engine, motivates the
+ * dequantise-then-matrix-core prefill path.
+ *
+ * Block formats (public ggml layout; byte offsets inside one block):
+ *   GQ_Q4_0:  32 weights, 18 B.  fp16 d @0; 16 quant bytes @2.  Weight j < 16 is
+ *             the low nibble of quant byte j, weight j >= 16 the high nibble of
+ *             byte j-16.  w = d * (q - 8).
+ *   GQ_Q4_K: 256 weights, 144 B.  fp16 d @0, fp16 dmin @2, 12 bytes of eight
+ *             6-bit (scale, min) pairs @4, 128 quant bytes @16.  Weight i:
+ *             chunk c = i/64 uses quant bytes 32c..32c+31; i%64 < 32 is the low
+ *             nibble (sub-block 2c), otherwise the high nibble (sub-block 2c+1).
+ *             w = (d * sc) * q - dmin * m.
+ *   GQ_Q6_K: 256 weights, 210 B.  128 B low 4-bit parts @0, 64 B high 2-bit
+ *             parts @128, 16 int8 scales @192 (one per 16 weights), fp16 d @208.
+ *             w = (d * sc) * (q - 32), q in 0..63.
+ *
+ * Matrix layout: a matrix with N output rows and K inputs is N rows of K/QK
+ * consecutive blocks each (QK = 32 or 256), rows back to back with no padding.
+ * Activations are row-major [batch][K] (fp32 or bf16); outputs row-major fp32.
+ *
+ * Conventions shared by every call:
+ *  - Every pointer argument except host out-parameters is a DEVICE pointer owned
+ *    by the caller; the library never frees or retains it.  Device pointers must
+ *    be 16-byte aligned (rows inside a matrix need not be).
+ *  - Calls are asynchronous: they enqueue work on `stream` (0 = the default
+ *    stream) and return.  Only gq_matvec_id_check waits for the device.
+ *  - All arguments are validated on the host before any HIP call.  On an error
+ *    nothing is launched and no output is written.
+ *  - No C++ exception crosses this boundary.  Launch failures return
+ *    GQ_ERR_LAUNCH.
+ *  - Calls are re-entrant; the library keeps no mutable global state.
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQ_ABI_VERSION 1
+
+typedef enum { GQ_Q4_0 = 1, GQ_Q4_K = 2, GQ_Q6_K = 3 } gq_type;
+
+typedef enum { GQ_F32 = 0, GQ_BF16 = 1, GQ_F16 = 2 } gq_dtype;
+
+typedef enum {
+    GQ_OK = 0,
+    GQ_ERR_TYPE = 1,        /* unknown block type */
+    GQ_ERR_DTYPE = 2,       /* unsupported activation / output element type */
+    GQ_ERR_SHAPE = 3,       /* negative size, K not a whole number of blocks, batch/top_k out of range */
+    GQ_ERR_NULL = 4,        /* required pointer is NULL */
+    GQ_ERR_ALIGN = 5,       /* device pointer not 16-byte aligned */
+    GQ_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+    GQ_ERR_WORKSPACE = 7,   /* workspace missing or too small */
+    GQ_ERR_LAUNCH = 8       /* the HIP runtime refused a launch */
+} gq_status;
+
+/* ABI version of the loaded library (GQ_ABI_VERSION at build time). */
+int gq_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* gq_status_str(gq_status s);
+
+/* Host only.  Weights per block and bytes per block of type t
+ * (32/18, 256/144, 256/210).  GQ_ERR_TYPE for an unknown t, GQ_ERR_NULL for a
+ * NULL out-parameter. */
+gq_status gq_block_info(gq_type t, int32_t* elems, int32_t* bytes);
+
+/* Dequantise n_blocks consecutive blocks of type t into out[0 .. n_blocks*QK).
+ * The operation is the dequantising fallback that "GGUF in transformers"
+ * mentions twice: when no packed kernel is available, and as
+ * GgufConfig(dequantize=True) for fine-tuning (section "transformers and
+ * llama.cpp").
+ *   out_dtype GQ_F32: bit-exact fp32 weights, each formula evaluated with fp32
+ *     factors left to right (the only rounding is Q4_K's final subtraction).
+ *   GQ_BF16 / GQ_F16: that fp32 value rounded to nearest even.
+ * n_blocks == 0 is a no-op.  blocks and out must be 16-byte aligned. */
+gq_status gq_dequant(gq_type t, const void* blocks, int64_t n_blocks, void* out,
+                     gq_dtype out_dtype, hipStream_t stream);
+
+/* Decode matrix-vector product for a small batch:
+ *   y[b][n] = sum_k w[n][k] * x[b][k],  0 <= b < batch, 0 <= n < N.
+ * W: packed [N][K/QK] blocks of type t.  x: [batch][K] of x_dtype (GQ_F32 or
+ * GQ_BF16).  y: [batch][N] fp32.  1 <= batch <= 8 (GQ_ERR_UNSUPPORTED above).
+ * K must be a multiple of QK.  N == 0 is a no-op; K == 0 writes zeros.
+ * Accuracy: every y element is within 1e-3 * sum_k |w[n][k] * x[b][k]| of the
+ * exact product (fp32 accumulation of per-sub-block partial sums; activations
+ * enter the dot instructions as fp16 after an exact power-of-two scaling per
+ * 32 inputs). */
+gq_status gq_matvec(gq_type t, const void* W, int64_t N, int64_t K, const void* x,
+                    gq_dtype x_dtype, int32_t batch, float* y, hipStream_t stream);
+
+/* Workspace bytes needed by gq_matvec_id for these sizes (host only). */
+gq_status gq_matvec_id_workspace(int32_t n_experts, int32_t n_tokens, int32_t top_k, int64_t N,
+                                 size_t* bytes);
+
+/* Routed-expert product: only the experts chosen for each token are read
+ * (ggml-quantization row of the kernel table in "GGUF in transformers").
+ * experts: packed [n_experts][N][K/QK] blocks; ids: [n_tokens][top_k] int32
+ * expert ids (device).  x: [n_tokens][K] when x_per_slot == 0 (all slots of a
+ * token read the token's vector, as gate/up projections do), or
+ * [n_tokens][top_k][K] when x_per_slot == 1 (each slot its own vector, as for
+ * a down projection).
+ *   route_w == NULL: y is [n_tokens][top_k][N],
+ *       y[t][j][n] = sum_k w_{ids[t][j]}[n][k] * x_{t,j}[k].
+ *   route_w != NULL (fp32 [n_tokens][top_k], device): y is [n_tokens][N],
+ *       y[t][n] = sum_j route_w[t][j] * (sum_k w_{ids[t][j]}[n][k] * x_{t,j}[k]),
+ *       summed over j in increasing order.
+ * Each distinct expert's rows are read once for all the (token, slot) pairs
+ * routed to it.  ws: device workspace of at least gq_matvec_id_workspace
+ * bytes; its contents need no initialisation.  An id outside [0, n_experts)
+ * makes its slot contribute zero and is counted in ws (see
+ * gq_matvec_id_check).  1 <= top_k <= n_experts, n_tokens * top_k <= 4096,
+ * x_dtype GQ_F32 or GQ_BF16.  Accuracy as gq_matvec (for route_w != NULL the
+ * bound is 1e-3 * sum_j |route_w[t][j]| * sum_k |w * x|). */
+gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_t N, int64_t K,
+                       const int32_t* ids, int32_t n_tokens, int32_t top_k, const void* x,
+                       gq_dtype x_dtype, int32_t x_per_slot, const float* route_w, float* y,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Waits for `stream`, then reports how many ids of the last gq_matvec_id call
+ * that used `ws` were outside [0, n_experts). */
+gq_status gq_matvec_id_check(const void* ws, hipStream_t stream, int32_t* n_bad_ids);
+
+/* Prefill product Y[m][n] = sum_k X[m][k] * w[n][k] for 0 <= m < M, 0 <= n < N.
+ * X: [M][ldx] of x_dtype (row stride ldx >= K elements); Y: [M][ldy] fp32
+ * (ldy >= N).  Weight tiles are dequantised to bf16 in LDS and multiplied on
+ * the matrix cores with fp32 accumulation.  This build implements t = GQ_Q4_K
+ * with x_dtype = GQ_BF16 (other combinations: GQ_ERR_UNSUPPORTED).  K must be a
+ * multiple of 256; M == 0 or N == 0 is a no-op. */
+gq_status gq_matmul(gq_type t, const void* W, int64_t N, int64_t K, const void* X,
+                    gq_dtype x_dtype, int64_t M, int64_t ldx, float* Y, int64_t ldy,
+                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQ_H */

@@ -24,3 +24,14 @@ def orc():
     from oracle import oracle as o
     o.lib()
     return o
+
+
+@pytest.fixture(scope="session")
+def gq_lib_path():
+    """Path of libgq.so; built here (hipcc cross-compiles for gfx950 without a
+    GPU) if it is missing."""
+    path = os.path.join(ROOT, "block_quantized_weight_q4_amd", "libgq.so")
+    if not os.path.exists(path):
+        from block_quantized_weight_q4_amd import build
+        build.build()
+    return path

@@ -1,0 +1,162 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/gq.h declares, and rejects invalid arguments on the host -- before any
+HIP call -- with the documented status codes.  No call here launches work:
+every call either fails validation or is a documented no-op."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+GQ_OK, GQ_ERR_TYPE, GQ_ERR_DTYPE, GQ_ERR_SHAPE, GQ_ERR_NULL, GQ_ERR_ALIGN, GQ_ERR_UNSUPPORTED, \
+    GQ_ERR_WORKSPACE, GQ_ERR_LAUNCH = range(9)
+
+A = 0x10000  # fake, 16-byte aligned "device" address: never dereferenced
+MIS = 0x10008  # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib(gq_lib_path):
+    L = ctypes.CDLL(gq_lib_path)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.gq_status_str.restype = ctypes.c_char_p
+    L.gq_dequant.argtypes = [ctypes.c_int, P, I64, P, ctypes.c_int, P]
+    L.gq_matvec.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I32, P, P]
+    L.gq_matvec_id_workspace.argtypes = [I32, I32, I32, I64, ctypes.POINTER(SZ)]
+    L.gq_matvec_id.argtypes = [ctypes.c_int, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, I32, P, P, P, SZ, P]
+    L.gq_matvec_id_check.argtypes = [P, P, ctypes.POINTER(I32)]
+    L.gq_matmul.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I64, I64, P, I64, P]
+    L.gq_block_info.argtypes = [ctypes.c_int, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+    return L
+
+
+def declared_functions() -> list[str]:
+    text = open(os.path.join(ROOT, "include", "gq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gq_abi_version() == 1
+    for s in range(9):
+        assert lib.gq_status_str(s)
+    assert lib.gq_status_str(GQ_OK) == b"ok"
+
+
+def test_block_info(lib):
+    e, b = ctypes.c_int32(), ctypes.c_int32()
+    for t, want in ((1, (32, 18)), (2, (256, 144)), (3, (256, 210))):
+        assert lib.gq_block_info(t, ctypes.byref(e), ctypes.byref(b)) == GQ_OK
+        assert (e.value, b.value) == want
+    assert lib.gq_block_info(4, ctypes.byref(e), ctypes.byref(b)) == GQ_ERR_TYPE
+    assert lib.gq_block_info(0, ctypes.byref(e), ctypes.byref(b)) == GQ_ERR_TYPE
+    assert lib.gq_block_info(2, None, ctypes.byref(b)) == GQ_ERR_NULL
+
+
+def test_dequant_validation(lib):
+    assert lib.gq_dequant(7, A, 4, A, 0, None) == GQ_ERR_TYPE
+    assert lib.gq_dequant(2, A, 4, A, 5, None) == GQ_ERR_DTYPE
+    assert lib.gq_dequant(2, A, -1, A, 0, None) == GQ_ERR_SHAPE
+    assert lib.gq_dequant(2, None, 4, A, 0, None) == GQ_ERR_NULL
+    assert lib.gq_dequant(2, A, 4, None, 0, None) == GQ_ERR_NULL
+    assert lib.gq_dequant(2, MIS, 4, A, 0, None) == GQ_ERR_ALIGN
+    assert lib.gq_dequant(2, A, 4, MIS, 0, None) == GQ_ERR_ALIGN
+    assert lib.gq_dequant(2, None, 0, None, 0, None) == GQ_OK  # empty: no-op
+
+
+def test_matvec_validation(lib):
+    mv = lib.gq_matvec
+    assert mv(0, A, 8, 256, A, 0, 1, A, None) == GQ_ERR_TYPE
+    assert mv(2, A, 8, 256, A, 2, 1, A, None) == GQ_ERR_DTYPE  # fp16 activations not offered
+    assert mv(2, A, 8, 100, A, 0, 1, A, None) == GQ_ERR_SHAPE  # K not whole blocks
+    assert mv(1, A, 8, 48, A, 0, 1, A, None) == GQ_ERR_SHAPE
+    assert mv(2, A, -1, 256, A, 0, 1, A, None) == GQ_ERR_SHAPE
+    assert mv(2, A, 8, -256, A, 0, 1, A, None) == GQ_ERR_SHAPE
+    assert mv(2, A, 8, 256, A, 0, 0, A, None) == GQ_ERR_SHAPE
+    assert mv(2, A, 8, 256, A, 0, 9, A, None) == GQ_ERR_UNSUPPORTED
+    assert mv(2, None, 8, 256, A, 0, 1, A, None) == GQ_ERR_NULL
+    assert mv(2, A, 8, 256, None, 0, 1, A, None) == GQ_ERR_NULL
+    assert mv(2, A, 8, 256, A, 0, 1, None, None) == GQ_ERR_NULL
+    assert mv(2, MIS, 8, 256, A, 0, 1, A, None) == GQ_ERR_ALIGN
+    assert mv(2, A, 8, 256, MIS, 0, 1, A, None) == GQ_ERR_ALIGN
+    assert mv(2, A, 8, 256, A, 0, 1, MIS, None) == GQ_ERR_ALIGN
+    assert mv(2, A, 0, 256, A, 0, 1, A, None) == GQ_OK  # N == 0: no-op
+    assert mv(3, A, 1 << 41, 256, A, 0, 1, A, None) == GQ_ERR_SHAPE  # size guard
+
+
+def test_matvec_id_validation(lib):
+    sz = ctypes.c_size_t()
+    assert lib.gq_matvec_id_workspace(128, 8, 8, 2816, ctypes.byref(sz)) == GQ_OK
+    need = sz.value
+    assert need > 0
+    assert lib.gq_matvec_id_workspace(4, 8, 8, 64, ctypes.byref(sz)) == GQ_ERR_SHAPE  # top_k > experts
+    assert lib.gq_matvec_id_workspace(128, 1000, 8, 64, ctypes.byref(sz)) == GQ_ERR_SHAPE  # > 4096 slots
+    assert lib.gq_matvec_id_workspace(128, 8, 8, 64, None) == GQ_ERR_NULL
+    f = lib.gq_matvec_id
+    args = [1, A, 128, 704, 2816, A, 8, 8, A, 0, 0, None, A, A, need, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["t", "ex", "E", "N", "K", "ids", "T", "k", "x", "xd", "per", "rw", "y", "ws", "wsb", "s"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(t=5) == GQ_ERR_TYPE
+    assert call(xd=2) == GQ_ERR_DTYPE
+    assert call(K=2817) == GQ_ERR_SHAPE
+    assert call(k=129) == GQ_ERR_SHAPE
+    assert call(E=0) == GQ_ERR_SHAPE
+    assert call(per=2) == GQ_ERR_SHAPE
+    assert call(T=600) == GQ_ERR_SHAPE
+    assert call(ids=None) == GQ_ERR_NULL
+    assert call(ws=None) == GQ_ERR_NULL
+    assert call(y=MIS) == GQ_ERR_ALIGN
+    assert call(rw=MIS) == GQ_ERR_ALIGN
+    assert call(wsb=need - 1) == GQ_ERR_WORKSPACE
+    assert call(T=0) == GQ_OK  # no tokens: no-op
+    n = ctypes.c_int32()
+    assert lib.gq_matvec_id_check(None, None, ctypes.byref(n)) == GQ_ERR_NULL
+    assert lib.gq_matvec_id_check(MIS, None, ctypes.byref(n)) == GQ_ERR_ALIGN
+
+
+def test_matmul_validation(lib):
+    mm = lib.gq_matmul
+    assert mm(9, A, 64, 256, A, 1, 16, 256, A, 64, None) == GQ_ERR_TYPE
+    assert mm(2, A, 64, 256, A, 2, 16, 256, A, 64, None) == GQ_ERR_DTYPE
+    assert mm(2, A, 64, 300, A, 1, 16, 300, A, 64, None) == GQ_ERR_SHAPE
+    assert mm(2, A, 64, 256, A, 1, 16, 255, A, 64, None) == GQ_ERR_SHAPE  # ldx < K
+    assert mm(2, A, 64, 256, A, 1, 16, 256, A, 63, None) == GQ_ERR_SHAPE  # ldy < N
+    assert mm(2, A, 64, 256, A, 1, -1, 256, A, 64, None) == GQ_ERR_SHAPE
+    assert mm(1, A, 64, 256, A, 1, 16, 256, A, 64, None) == GQ_ERR_UNSUPPORTED
+    assert mm(2, A, 64, 256, A, 0, 16, 256, A, 64, None) == GQ_ERR_UNSUPPORTED
+    assert mm(2, None, 64, 256, A, 1, 16, 256, A, 64, None) == GQ_ERR_NULL
+    assert mm(2, A, 64, 256, A, 1, 16, 256, MIS, 64, None) == GQ_ERR_ALIGN
+    assert mm(2, A, 64, 256, A, 1, 16, 260, A, 64, None) == GQ_ERR_ALIGN  # row stride breaks alignment
+    assert mm(2, A, 64, 256, A, 1, 0, 256, A, 64, None) == GQ_OK  # M == 0: no-op
+
+
+def test_binding_refuses_without_library(tmp_path, monkeypatch):
+    """The Python binding has no fallback: with the library gone it raises."""
+    import importlib.util
+    import shutil
+    pkg = os.path.join(ROOT, "block_quantized_weight_q4_amd")
+    fake = tmp_path / "block_quantized_weight_q4_amd"
+    fake.mkdir()
+    for f in ("__init__.py", "_binding.py"):
+        shutil.copy(os.path.join(pkg, f), fake / f)
+    spec = importlib.util.spec_from_file_location("fakepkg._binding", fake / "_binding.py")
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError, match="libgq.so is not built"):
+        spec.loader.exec_module(mod)
