@@ -85,7 +85,7 @@ gq_status gq_matvec(gq_type t, const void* W, int64_t N, int64_t K, const void* 
 gq_status gq_matvec_id_workspace(int32_t n_experts, int32_t n_tokens, int32_t top_k, int64_t N, size_t* bytes) {
     if (!bytes) return GQ_ERR_NULL;
     if (n_experts < 1 || n_tokens < 0 || top_k < 1 || top_k > n_experts || N < 0 ||
-        (int64_t)n_tokens * top_k > 4096)
+        (int64_t)n_tokens * top_k > 1024)
         return GQ_ERR_SHAPE;
     *bytes = gqk_matvec_id_ws_bytes(n_experts, n_tokens, top_k, N);
     return GQ_OK;
@@ -98,7 +98,7 @@ gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_
     if (!known_type(t)) return GQ_ERR_TYPE;
     if (x_dtype != GQ_F32 && x_dtype != GQ_BF16) return GQ_ERR_DTYPE;
     if (n_experts < 1 || n_tokens < 0 || top_k < 1 || top_k > n_experts || N < 0 || K < 0 ||
-        K % qk_of(t) != 0 || (x_per_slot != 0 && x_per_slot != 1) || (int64_t)n_tokens * top_k > 4096)
+        K % qk_of(t) != 0 || (x_per_slot != 0 && x_per_slot != 1) || (int64_t)n_tokens * top_k > 1024)
         return GQ_ERR_SHAPE;
     if (N > MAX_ELEMS || K > MAX_ELEMS || (K > 0 && N > MAX_ELEMS / K) ||
         (K > 0 && N > 0 && (int64_t)n_experts > MAX_ELEMS / (N * K)))

@@ -503,7 +503,134 @@ __device__ __forceinline__ void reduce_group(float acc[R][BMAX], int LPR) {
             for (int off = LPR >> 1; off > 0; off >>= 1) acc[i][b] += __shfl_xor(acc[i][b], off);
 }
 
+// Output rows of the vectors: y_b[n] = p[b][n].  Wave-uniform.
+struct YDst {
+    float* p[8];
+};
+
+// The whole decode product for one workgroup: rows [rowA, rowA + waves*R*SR)
+// of the packed matrix W (N rows, K inputs) against nb <= BMAX staged vectors.
+template <int TYPE, int XT, int BMAX, int R, int D>
+__device__ __forceinline__ void gemv_workgroup(const uint8_t* __restrict__ W, int64_t N, int64_t K, int64_t rowA,
+                                               const XSrc& xs, int nb, const YDst& yd, int LPR, int tile_units,
+                                               uint8_t* lds) {
+    using F = Fmt<TYPE>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int SR = 64 / LPR;
+    const int s = lane / LPR, v = lane - s * LPR;
+    const int64_t row_bytes = (K / F::QK) * F::BB;
+    const int64_t row0 = rowA + (int64_t)wave * R * SR + s;
+
+    const uint8_t* rowp[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        int64_t r = row0 + (int64_t)i * SR;
+        rowp[i] = W + (r < N ? r : N - 1) * row_bytes;
+    }
+    float acc[R][BMAX];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < BMAX; ++b) acc[i][b] = 0.f;
+
+    const int64_t units = K / F::UW;
+    for (int64_t u0 = 0; u0 < units; u0 += tile_units) {
+        int U = (int)((units - u0) < tile_units ? (units - u0) : tile_units);
+        TileLds<F> L;
+        L.carve(lds, U, nb);
+        // activation loads first, then the first D units of weights, so the
+        // staging arithmetic overlaps the weight stream
+        XRaw<XT> xin;
+        stage_issue<F, XT>(xs, u0 * F::UW, L, xin);
+        __builtin_amdgcn_sched_barrier(0);
+        typename F::Raw ring[D][R];
+        prefetch_ring<F, R, D>(rowp, (int)u0, v, LPR, U, ring);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_finish<F, XT>(xs, u0 * F::UW, L, xin);
+        compute_tile<F, BMAX, R, D>(L, rowp, (int)u0, v, LPR, ring, acc);
+        lds_barrier();
+    }
+    reduce_group<BMAX, R>(acc, LPR);
+    if (v == 0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            int64_t r = row0 + (int64_t)i * SR;
+            if (r < N) {
+#pragma unroll
+                for (int b = 0; b < BMAX; ++b)
+                    if (b < nb) yd.p[b][r] = acc[i][b];
+            }
+        }
+    }
+}
+
 // LDS budget per workgroup for staged activations.
 constexpr int LDS_BUDGET = 48 * 1024;
+
+// ------------------------------------------------------ launch plan ----
+
+struct Plan {
+    int LPR, R, WPW, tile_units;
+    int64_t grid;
+    size_t lds;
+};
+
+// Lanes per row (LPR) depends only on K, and every K tile holds a multiple of
+// LPR units, so lane v of a row group always sums units v, v+LPR, v+2LPR, ...
+// in the same order whatever the batch size: each batch column is
+// bit-identical to a batch-1 product of the same vector.  (Rows per lane R and
+// waves per workgroup only decide which lane group owns a row.)
+template <class F>
+inline int lanes_per_row(int64_t units) {
+    // 32 at most: a tile of 32 units for 8 vectors still fits the LDS budget
+    int best = 32;
+    double best_u = -1;
+    for (int lpr = 32; lpr >= 8; lpr >>= 1) {
+        int64_t slots = ((units + lpr - 1) / lpr) * lpr;
+        double util = units ? (double)units / (double)slots : 1.0;
+        if (util >= 0.9) return lpr;
+        if (util > best_u + 1e-9) {
+            best_u = util;
+            best = lpr;
+        }
+    }
+    return best;
+}
+
+template <class F>
+inline Plan plan_for(int64_t N, int64_t K, int nb) {
+    Plan p;
+    int64_t units = K / F::UW;
+    p.LPR = lanes_per_row<F>(units);
+    const int SR = 64 / p.LPR;
+    // K tile: as many units as the LDS budget allows for nb vectors, rounded
+    // down to a multiple of LPR (a multiple of 4 units = whole super-blocks)
+    size_t per_unit = (size_t)16 * (F::NQ + F::NF) * nb;
+    int64_t step = p.LPR;
+    int64_t max_units = (int64_t)(LDS_BUDGET / per_unit) / step * step;
+    if (max_units < step) max_units = step;
+    if (units <= max_units) {
+        p.tile_units = (int)(units > 0 ? units : 1);
+    } else {
+        int64_t n_tiles = (units + max_units - 1) / max_units;
+        int64_t tu = (units + n_tiles - 1) / n_tiles;
+        p.tile_units = (int)((tu + step - 1) / step * step);
+    }
+    // rows per lane group (R = 2 would let one LDS read of an activation serve
+    // two rows, but costs too many registers at present)
+    p.R = 1;
+    // waves per workgroup: the most (least staging per row) that still gives
+    // >= 512 workgroups (two per CU); for small N fewer rows per lane group
+    p.WPW = 1;
+    for (int w = 4; w >= 1; w >>= 1) {
+        if ((N + (int64_t)w * p.R * SR - 1) / ((int64_t)w * p.R * SR) >= 512) {
+            p.WPW = w;
+            break;
+        }
+    }
+    p.grid = (N + (int64_t)p.WPW * p.R * SR - 1) / ((int64_t)p.WPW * p.R * SR);
+    p.lds = per_unit * p.tile_units;
+    return p;
+}
 
 }  // namespace gqd

@@ -129,7 +129,7 @@ gq_status gq_matvec_id_workspace(int32_t n_experts, int32_t n_tokens, int32_t to
  * routed to it.  ws: device workspace of at least gq_matvec_id_workspace
  * bytes; its contents need no initialisation.  An id outside [0, n_experts)
  * makes its slot contribute zero and is counted in ws (see
- * gq_matvec_id_check).  1 <= top_k <= n_experts, n_tokens * top_k <= 4096,
+ * gq_matvec_id_check).  1 <= top_k <= n_experts, n_tokens * top_k <= 1024,
  * x_dtype GQ_F32 or GQ_BF16.  Accuracy as gq_matvec (for route_w != NULL the
  * bound is 1e-3 * sum_j |route_w[t][j]| * sum_k |w * x|). */
 gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_t N, int64_t K,

@@ -97,11 +97,12 @@ def test_matvec_validation(lib):
 
 def test_matvec_id_validation(lib):
     sz = ctypes.c_size_t()
-    assert lib.gq_matvec_id_workspace(128, 8, 8, 2816, ctypes.byref(sz)) == GQ_OK
+    # the workspace is sized for exactly the call below (N = 704)
+    assert lib.gq_matvec_id_workspace(128, 8, 8, 704, ctypes.byref(sz)) == GQ_OK
     need = sz.value
     assert need > 0
     assert lib.gq_matvec_id_workspace(4, 8, 8, 64, ctypes.byref(sz)) == GQ_ERR_SHAPE  # top_k > experts
-    assert lib.gq_matvec_id_workspace(128, 1000, 8, 64, ctypes.byref(sz)) == GQ_ERR_SHAPE  # > 4096 slots
+    assert lib.gq_matvec_id_workspace(128, 129, 8, 64, ctypes.byref(sz)) == GQ_ERR_SHAPE  # > 1024 slots
     assert lib.gq_matvec_id_workspace(128, 8, 8, 64, None) == GQ_ERR_NULL
     f = lib.gq_matvec_id
     args = [1, A, 128, 704, 2816, A, 8, 8, A, 0, 0, None, A, A, need, None]
@@ -119,12 +120,13 @@ def test_matvec_id_validation(lib):
     assert call(k=129) == GQ_ERR_SHAPE
     assert call(E=0) == GQ_ERR_SHAPE
     assert call(per=2) == GQ_ERR_SHAPE
-    assert call(T=600) == GQ_ERR_SHAPE
+    assert call(T=129) == GQ_ERR_SHAPE  # 129 * 8 > 1024 slots
     assert call(ids=None) == GQ_ERR_NULL
     assert call(ws=None) == GQ_ERR_NULL
     assert call(y=MIS) == GQ_ERR_ALIGN
     assert call(rw=MIS) == GQ_ERR_ALIGN
     assert call(wsb=need - 1) == GQ_ERR_WORKSPACE
+    assert call(wsb=0) == GQ_ERR_WORKSPACE
     assert call(T=0) == GQ_OK  # no tokens: no-op
     n = ctypes.c_int32()
     assert lib.gq_matvec_id_check(None, None, ctypes.byref(n)) == GQ_ERR_NULL

@@ -1,0 +1,170 @@
+"""GPU parity of gq_matvec_id (routed experts) against the CPU oracle.
+
+Bars: per-slot outputs within 1e-3 * sum_k |w x|; routing-weighted outputs
+within 1e-3 * sum_j |r_j| * sum_k |w x|; invariants that reduce the routed
+product to gq_matvec bit for bit."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_quantized_weight_q4_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BB = {"q4_0": 18, "q4_k": 144, "q6_k": 210}
+QK = {"q4_0": 32, "q4_k": 256, "q6_k": 256}
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    print("\n[gpu case] %s" % request.node.nodeid, flush=True)
+    sys.stdout.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def gq():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_quantized_weight_q4_amd as g
+    return g
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def check_bound(y, yref, sumabs, what=""):
+    y = np.asarray(y, np.float64)
+    assert np.all(np.isfinite(y)), what
+    err = np.abs(y - yref)
+    bound = 1e-3 * sumabs
+    bad = err > bound
+    assert not bad.any(), "%s: %d elements outside the bound, first %s" % (what, bad.sum(), np.argwhere(bad)[0])
+    pos = bound > 0
+    return float(np.max(err[pos] / bound[pos])) if pos.any() else 0.0
+
+
+def run_id(gq, t, experts_np, E, N, K, ids_np, x_t, per_slot, route_w=None):
+    T, k = ids_np.shape
+    ws = torch.empty(gq.gq_matvec_id_workspace(E, T, k, N), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xAB)  # contents need no initialisation
+    shape = (T, N) if route_w is not None else (T, k, N)
+    y = torch.full(shape, float("nan"), device="cuda")
+    gq.gq_matvec_id(t, dev(experts_np), E, N, K, dev(ids_np), x_t, per_slot, y, ws,
+                    None if route_w is None else dev(route_w))
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), ws
+
+
+def test_moe_workload_gate_up_down(gq, orc):
+    """128 experts, hidden 2816, expert FFN 704 (Q4_0); 8 tokens, top-8 seeded
+    routing with softmax weights on the down projection."""
+    E, H, F, T, k = 128, 2816, 704, 8, 8
+    g = synth.rng(0x67510004, 0)
+    ids, rw = synth.routing(g, T, E, k)
+    print("distinct experts:", len(np.unique(ids)))
+    x = synth.normal_f32(g, (T, H))
+    for name, N, K in (("gate", F, H), ("up", F, H)):
+        ex = synth.weight("q4_0", synth.rng(0x67510004, 1 + (name == "up")), E * N, K)
+        y, ws = run_id(gq, "q4_0", ex, E, N, K, ids, dev(x), False)
+        yref, sa = orc.matvec_id("q4_0", ex, E, N, K, ids, x, False)
+        r = check_bound(y, yref, sa, name)
+        print("%s worst err/bound %.4f" % (name, r))
+        assert gq.gq_matvec_id_check(ws) == 0
+    h = synth.normal_f32(g, (T, k, F))
+    exd = synth.weight("q4_0", synth.rng(0x67510004, 3), E * H, F)
+    y, ws = run_id(gq, "q4_0", exd, E, H, F, ids, dev(h), True, rw)
+    yref, sa = orc.matvec_id("q4_0", exd, E, H, F, ids, h, True, rw)
+    r = check_bound(y, yref, sa, "down")
+    print("down (routed) worst err/bound %.4f" % r)
+
+
+@pytest.mark.parametrize("t", ["q4_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_matvec_id_shapes(gq, orc, t, xdt):
+    g = synth.rng(0x67510004, 10 + ["q4_0", "q4_k", "q6_k"].index(t))
+    for (E, N, K, T, k) in ((5, 37, 512, 3, 2), (16, 130, 1024, 6, 4), (9, 64, 2048, 16, 3)):
+        ex = synth.weight(t, g, E * N, K)
+        ids = g.integers(0, E, (T, k)).astype(np.int32)
+        for per_slot in (False, True):
+            x = synth.normal_f32(g, (T, k, K) if per_slot else (T, K))
+            if xdt == "bf16":
+                bits = synth.bf16_bits(x)
+                x = synth.bf16_to_f32(bits)
+                x_t = dev(bits.view(np.int16)).view(torch.bfloat16)
+            else:
+                x_t = dev(x)
+            y, _ = run_id(gq, t, ex, E, N, K, ids, x_t, per_slot)
+            yref, sa = orc.matvec_id(t, ex, E, N, K, ids, x, per_slot)
+            check_bound(y, yref, sa, "%s E=%d N=%d K=%d per_slot=%s" % (t, E, N, K, per_slot))
+            rw = g.random((T, k)).astype(np.float32)
+            y, _ = run_id(gq, t, ex, E, N, K, ids, x_t, per_slot, rw)
+            yref, sa = orc.matvec_id(t, ex, E, N, K, ids, x, per_slot, rw)
+            check_bound(y, yref, sa, "%s routed" % t)
+
+
+@pytest.mark.parametrize("t", ["q4_0", "q4_k"])
+def test_matvec_id_single_expert_equals_matvec(gq, t):
+    """Every slot routed to one expert (groups of 4 slots, several groups):
+    each output row equals gq_matvec of that expert on the same vector, bit for
+    bit."""
+    g = synth.rng(0x67510004, 20)
+    E, N, K, T, k = 6, 96, 1024, 7, 2
+    ex = synth.weight(t, g, E * N, K)
+    ids = np.full((T, k), 3, np.int32)
+    x = synth.normal_f32(g, (T, K))
+    y, _ = run_id(gq, t, ex, E, N, K, ids, dev(x), False)
+    eb = N * K // QK[t] * BB[t]
+    W3 = dev(ex.reshape(-1)[3 * eb:4 * eb])
+    # gq_matvec with 4 vectors at a time uses the same 4-vector kernel
+    for tok0 in range(0, T, 4):
+        xs = x[tok0:tok0 + 4]
+        yy = torch.empty(xs.shape[0], N, device="cuda")
+        gq.gq_matvec(t, W3, N, K, dev(xs), yy)
+        torch.cuda.synchronize()
+        yy = yy.cpu().numpy()
+        for i in range(xs.shape[0]):
+            for j in range(k):
+                assert np.array_equal(y[tok0 + i, j].view(np.uint32), yy[i].view(np.uint32))
+
+
+def test_matvec_id_bad_ids_counted_and_zero(gq, orc):
+    g = synth.rng(0x67510004, 21)
+    E, N, K, T, k = 8, 40, 512, 4, 3
+    ex = synth.weight("q4_k", g, E * N, K)
+    ids = g.integers(0, E, (T, k)).astype(np.int32)
+    ids[0, 1] = E        # one past the end
+    ids[2, 0] = -1       # negative
+    ids[3, 2] = 1 << 30  # far out
+    x = synth.normal_f32(g, (T, K))
+    y, ws = run_id(gq, "q4_k", ex, E, N, K, ids, dev(x), False)
+    assert gq.gq_matvec_id_check(ws) == 3
+    yref, sa = orc.matvec_id("q4_k", ex, E, N, K, ids, x, False)
+    assert np.all(y[0, 1] == 0) and np.all(y[2, 0] == 0) and np.all(y[3, 2] == 0)
+    check_bound(y, yref, sa, "bad ids")
+    rw = g.random((T, k)).astype(np.float32)
+    y, ws = run_id(gq, "q4_k", ex, E, N, K, ids, dev(x), False, rw)
+    yref, sa = orc.matvec_id("q4_k", ex, E, N, K, ids, x, False, rw)
+    check_bound(y, yref, sa, "bad ids routed")
+    assert gq.gq_matvec_id_check(ws) == 3
+
+
+def test_matvec_id_many_slots_one_expert_and_determinism(gq, orc):
+    """256 slots, heavily skewed routing (most to two experts): long runs split
+    into many groups; repeated calls are bit-identical."""
+    g = synth.rng(0x67510004, 22)
+    E, N, K, T, k = 32, 72, 768, 64, 4
+    ex = synth.weight("q4_k", g, E * N, K)
+    ids = np.where(g.random((T, k)) < 0.7, g.integers(0, 2, (T, k)), g.integers(0, E, (T, k))).astype(np.int32)
+    x = synth.normal_f32(g, (T, K))
+    rw = g.random((T, k)).astype(np.float32)
+    y1, _ = run_id(gq, "q4_k", ex, E, N, K, ids, dev(x), False, rw)
+    y2, _ = run_id(gq, "q4_k", ex, E, N, K, ids, dev(x), False, rw)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    yref, sa = orc.matvec_id("q4_k", ex, E, N, K, ids, x, False, rw)
+    check_bound(y1, yref, sa, "skewed")
