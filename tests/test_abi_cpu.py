@@ -147,6 +147,7 @@ def test_matmul_validation(lib):
     assert mm(2, A, 64, 256, A, 1, 16, 256, MIS, 64, None) == GQ_ERR_ALIGN
     assert mm(2, A, 64, 256, A, 1, 16, 260, A, 64, None) == GQ_ERR_ALIGN  # row stride breaks alignment
     assert mm(2, A, 64, 256, A, 1, 0, 256, A, 64, None) == GQ_OK  # M == 0: no-op
+    assert mm(2, A, 0, 256, A, 1, 16, 256, A, 64, None) == GQ_OK  # N == 0: no-op
 
 
 def test_binding_refuses_without_library(tmp_path, monkeypatch):
