@@ -1,21 +1,22 @@
-"""Benchmark of the packed-weight decode product on one MI355X.
+"""Benchmark of the packed-weight products on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu-baseline]
 
-A step is one decoder layer of Q4_K products at batch 1, hidden 2560:
-q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up 9728x2560, down 2560x9728
-(56,770,560 packed bytes).  q|k|v and gate|up read the same activation vector
-and are issued as one launch each over their row-concatenated weights (rows
-back to back, as a model loader stores them), so a step is four launches:
-qkv, o, gate|up, down.  Weights rotate over >= 1 GiB of distinct copies so every
-step reads HBM, not the 256 MB last-level cache.  Inputs are resident in HBM
-before the timed region.
+The step (the headline workload) is one decoder layer of Q4_K products at
+batch 1, hidden 2560: q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up
+9728x2560, down 2560x9728 -- 56,770,560 packed bytes.  q|k|v and gate|up read
+the same activation vector and are issued as one launch each over their
+row-concatenated weights (a loader stores them that way), so a step is four
+dependent launches: qkv, o, gate|up, down.  Weights rotate over >= 1 GiB of
+distinct copies so each step streams from HBM, not from the 256 MB last-level
+cache; inputs are resident in HBM before the timed region.  The steps are
+captured once in a HIP graph that walks every copy; the timed region replays
+it, bracketed by device synchronisation and HIP events on the launch stream.
 
-Printed: one JSON line with the whole-step packed-weight rate (value, GB/s),
-the dominant kernel's roofline figures (gate|up, timed per launch with HIP
-events on the launch stream) and the CPU oracle timed on the host for the same
-layer.  Extra keys report the unfused seven-launch layer, and every other
-workload shape as context.
+One JSON line: value = packed-weight GB/s of the whole step; roofline = the
+dominant kernel (gate|up, 28,016,640 B per launch) timed over back-to-back
+launches of it alone; cpu_baseline = the CPU oracle on the same layer; plus
+the prefill product's TFLOP/s and the other workloads as context.
 """
 from __future__ import annotations
 
@@ -31,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 METRIC = "packed-weight GB/s (% of HBM peak), Q4_K GEMV batch 1; prefill TFLOP/s"
 ROTATE_BYTES = 1 << 30
 
@@ -38,26 +40,48 @@ DENSE = [("q", 4096, 2560), ("k", 1024, 2560), ("v", 1024, 2560), ("o", 2560, 40
          ("gate", 9728, 2560), ("up", 9728, 2560), ("down", 2560, 9728)]
 
 
-def row_bytes(K: int) -> int:
-    return K // 256 * 144
-
-
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--quick", action="store_true", help="skip the context workloads")
+    ap.add_argument("--quick", action="store_true", help="headline only (no context workloads)")
     return ap.parse_args()
+
+
+class Timer:
+    """Capture a list of launches once in a HIP graph; replay and time it."""
+
+    def __init__(self, torch, fn, stream):
+        self.torch, self.fn, self.stream = torch, fn, stream
+        fn()  # warm the code objects before capture
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, stream=stream):
+            fn()
+        torch.cuda.synchronize()
+
+    def time(self, reps: int, warm: int = 2) -> float:
+        """Mean ms per replay over `reps` replays."""
+        torch = self.torch
+        for _ in range(warm):
+            self.graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for _ in range(reps):
+            self.graph.replay()
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
 
 
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the product is sharded by output rows across GPUs in a larger deployment; "
-              "see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: this build has no multi-GPU path (the products shard by "
+              "output rows across GPUs; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -66,115 +90,95 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    side = torch.cuda.Stream()  # graphs are captured on a non-default stream
+    torch.cuda.set_stream(side)
     stream = torch.cuda.current_stream()
 
-    # ---- weights: one seeded layer, copied to >= 1 GiB of distinct buffers
-    g = synth.rng(0x67510002, 0)
+    def t_(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ------------------------------------------------ headline: dense layer
     mats = {name: synth.weight("q4_k", synth.rng(0x67510002, i), N, K) for i, (name, N, K) in enumerate(DENSE)}
-    qkv = np.concatenate([mats["q"], mats["k"], mats["v"]], axis=0)
-    gu = np.concatenate([mats["gate"], mats["up"]], axis=0)
+    host = {"qkv": np.concatenate([mats["q"], mats["k"], mats["v"]]), "o": mats["o"],
+            "gu": np.concatenate([mats["gate"], mats["up"]]), "down": mats["down"]}
+    shapes = {"qkv": (6144, 2560), "o": (2560, 4096), "gu": (19456, 2560), "down": (2560, 9728)}
     layer_bytes = sum(m.nbytes for m in mats.values())
     n_copies = max(2, -(-ROTATE_BYTES // layer_bytes))
-    host = {"qkv": qkv, "o": mats["o"], "gu": gu, "down": mats["down"]}
-    copies = []
-    for c in range(n_copies):
-        copies.append({k: torch.from_numpy(v).to(dev) for k, v in host.items()})
-    # activations (distinct vectors per launch; resident before timing)
-    xs = {
-        "qkv": torch.from_numpy(synth.normal_f32(g, (1, 2560))).to(dev),
-        "o": torch.from_numpy(synth.normal_f32(g, (1, 4096))).to(dev),
-        "gu": torch.from_numpy(synth.normal_f32(g, (1, 2560))).to(dev),
-        "down": torch.from_numpy(synth.normal_f32(g, (1, 9728))).to(dev),
-    }
-    shapes = {"qkv": (6144, 2560), "o": (2560, 4096), "gu": (19456, 2560), "down": (2560, 9728)}
-    ys = {k: torch.empty(1, n, device=dev) for k, (n, _) in shapes.items()}
+    copies = [{k: t_(v) for k, v in host.items()} for _ in range(n_copies)]
+    g = synth.rng(0x67510002, 100)
+    xs = {k: t_(synth.normal_f32(g, (1, K))) for k, (N, K) in shapes.items()}
+    ys = {k: torch.empty(1, N, device=dev) for k, (N, K) in shapes.items()}
 
-    def step(c):
-        w = copies[c % n_copies]
-        for k in ("qkv", "o", "gu", "down"):
-            n, kk = shapes[k]
-            gq.gq_matvec("q4_k", w[k], n, kk, xs[k], ys[k], stream)
+    def layer_pass():
+        for c in copies:
+            for k in ("qkv", "o", "gu", "down"):
+                n, kk = shapes[k]
+                gq.gq_matvec("q4_k", c[k], n, kk, xs[k], ys[k], stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / args.steps
+    tl = Timer(torch, layer_pass, stream)
+    reps = max(1, args.steps // n_copies)
+    tl.time(max(1, args.warmup // n_copies))
+    ms_pass = tl.time(reps)
+    steps = reps * n_copies
+    ms_step = ms_pass / n_copies
     value = layer_bytes / (ms_step * 1e-3) / 1e9
 
-    # ---- dominant kernel: gate|up, per-launch HIP events on the launch stream
-    gu_bytes = gu.nbytes
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.warmup):
-        gq.gq_matvec("q4_k", copies[i % n_copies]["gu"], 19456, 2560, xs["gu"], ys["gu"], stream)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        a, b = ev[i]
-        a.record(stream)
-        gq.gq_matvec("q4_k", copies[i % n_copies]["gu"], 19456, 2560, xs["gu"], ys["gu"], stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    gu_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # dominant kernel: gate|up alone, back to back over the copies
+    def gu_pass():
+        for c in copies:
+            gq.gq_matvec("q4_k", c["gu"], 19456, 2560, xs["gu"], ys["gu"], stream)
+
+    tg = Timer(torch, gu_pass, stream)
+    gu_ms = tg.time(max(2, reps)) / n_copies
+    gu_bytes = host["gu"].nbytes
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
-
-    # ---- unfused seven-launch layer (context)
-    sep = {name: [torch.from_numpy(m).to(dev) for _ in range(max(2, -(-ROTATE_BYTES // layer_bytes)))]
-           for name, m in mats.items()} if not args.quick else None
-    unfused = None
-    if sep is not None:
-        xk = {2560: xs["qkv"], 4096: xs["o"], 9728: xs["down"]}
-        yk = {name: torch.empty(1, N, device=dev) for name, N, K in DENSE}
-        nc = len(sep["q"])
-
-        def step7(c):
-            for name, N, K in DENSE:
-                gq.gq_matvec("q4_k", sep[name][c % nc], N, K, xk[K], yk[name], stream)
-
-        for i in range(args.warmup):
-            step7(i)
-        torch.cuda.synchronize()
-        t0.record(stream)
-        for i in range(args.steps):
-            step7(i)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        ms7 = t0.elapsed_time(t1) / args.steps
-        unfused = {"ms_per_layer": ms7, "GBps": layer_bytes / (ms7 * 1e-3) / 1e9, "launches": 7}
-        del sep
-    del copies
+    del tl, tg, copies
     torch.cuda.empty_cache()
 
-    # ---- CPU oracle on the host (the same layer, single thread)
+    context = {}
+    # ------------------------------------------------ prefill product
+    M, N5, K5 = 3015, 17408, 5120
+    W5 = t_(synth.weight("q4_k", synth.rng(0x67510005, 0), N5, K5))
+    X5 = t_(synth.bf16_bits(synth.normal_f32(synth.rng(0x67510005, 1), (M, K5))).view(np.int16)).view(torch.bfloat16)
+    Y5 = torch.empty(M, N5, device=dev)
+    tp = Timer(torch, lambda: gq.gq_matmul("q4_k", W5, N5, K5, X5, Y5, stream), stream)
+    ms_mm = tp.time(20)
+    flops = 2.0 * M * N5 * K5
+    prefill = {"workload": "q4_k_prefill_3015x17408x5120_bf16", "ms": round(ms_mm, 4),
+               "TFLOPs": round(flops / (ms_mm * 1e-3) / 1e12, 2),
+               "frac_bf16_dense_peak": round(flops / (ms_mm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+               "tokens_per_s": round(M / (ms_mm * 1e-3), 1)}
+    del tp, W5, X5, Y5
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        context = bench_context(torch, gq, synth, dev, stream, t_)
+
+    # ------------------------------------------------ CPU oracle on the host
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import oracle as orc
         xh = {2560: xs["qkv"].cpu().numpy(), 4096: xs["o"].cpu().numpy(), 9728: xs["down"].cpu().numpy()}
         tc = time.perf_counter()
-        reps = 0
+        nrep = 0
         while True:
             for name, N, K in DENSE:
                 orc.matvec("q4_k", mats[name], N, K, xh[K])
-            reps += 1
-            if time.perf_counter() - tc > 10.0 or reps >= 20:
+            nrep += 1
+            if time.perf_counter() - tc > 10.0 or nrep >= 30:
                 break
-        dt = (time.perf_counter() - tc) / reps
-        cpu = {"value": layer_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": "the full 7-projection Q4_K layer at batch 1, %d repetition(s), single thread "
-                         "(plain C, fp32 dequant + fp64 dot), %.3f s per layer" % (reps, dt)}
+        dt = (time.perf_counter() - tc) / nrep
+        cpu = {"value": round(layer_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "the whole 7-projection Q4_K layer at batch 1 (56,770,560 packed bytes), %d "
+                         "repetition(s) on one host thread (plain C: fp32 dequant + fp64 dot), %.3f s per layer"
+                         % (nrep, dt)}
 
     out = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
@@ -185,21 +189,130 @@ def main():
         "config": {
             "workload": "q4_k_gemv_dense_layer_hidden2560_batch1",
             "layer": "q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up 9728x2560, down 2560x9728 (Q4_K)",
-            "launches_per_step": "qkv (6144x2560), o, gate|up (19456x2560), down",
+            "launches_per_step": "qkv 6144x2560, o, gate|up 19456x2560, down (HIP graph)",
             "batch": 1,
             "packed_bytes_per_step": layer_bytes,
             "weight_copies_rotated": n_copies,
             "activations": "fp32 N(0,1)",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s_equiv": round(value / 2.74, 1),
         "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_matvec Q4_K gate|up 19456x2560 batch 1",
-                     "bytes_per_launch": gu_bytes, "avg_launch_ms": round(gu_ms, 5)},
+                     "kernel": "k_matvec<Q4_K, fp32, 1, 1, 4> gate|up 19456x2560 batch 1",
+                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1e3, 3)},
         "cpu_baseline": cpu,
-        "unfused_layer": unfused,
+        "prefill": prefill,
+        "context": context,
     }
     print(json.dumps(out))
+
+
+def bench_context(torch, gq, synth, dev, stream, t_):
+    """The other workloads, each timed the same way (graph of back-to-back
+    launches over rotated copies)."""
+    res = {}
+
+    def rotated(make, nbytes):
+        return [make() for _ in range(max(2, -(-ROTATE_BYTES // nbytes)))]
+
+    # Q4_0 2048x2048, batch 1
+    w1 = synth.weight("q4_0", synth.rng(0x67510001, 0), 2048, 2048)
+    c1 = [t_(w1) for _ in range(max(2, -(-(256 << 20) // w1.nbytes)))]
+    x1 = t_(synth.normal_f32(synth.rng(0x67510001, 1), (1, 2048)))
+    y1 = torch.empty(1, 2048, device=dev)
+
+    def p1():
+        for c in c1:
+            gq.gq_matvec("q4_0", c, 2048, 2048, x1, y1, stream)
+
+    ms = Timer(torch, p1, stream).time(20) / len(c1)
+    res["q4_0_2048x2048_b1"] = {"us": round(ms * 1e3, 3), "GBps": round(w1.nbytes / (ms * 1e-3) / 1e9, 1)}
+    del c1
+
+    # dense layer at batch 4
+    mats = {name: synth.weight("q4_k", synth.rng(0x67510002, i), N, K) for i, (name, N, K) in enumerate(DENSE)}
+    host = {"qkv": (np.concatenate([mats["q"], mats["k"], mats["v"]]), 6144, 2560), "o": (mats["o"], 2560, 4096),
+            "gu": (np.concatenate([mats["gate"], mats["up"]]), 19456, 2560), "down": (mats["down"], 2560, 9728)}
+    lb = sum(m.nbytes for m in mats.values())
+    cp = [{k: t_(v[0]) for k, v in host.items()} for _ in range(max(2, -(-ROTATE_BYTES // lb)))]
+    x4 = {k: t_(synth.normal_f32(synth.rng(0x67510002, 200), (4, v[2]))) for k, v in host.items()}
+    y4 = {k: torch.empty(4, v[1], device=dev) for k, v in host.items()}
+
+    def p2():
+        for c in cp:
+            for k, v in host.items():
+                gq.gq_matvec("q4_k", c[k], v[1], v[2], x4[k], y4[k], stream)
+
+    ms = Timer(torch, p2, stream).time(5) / len(cp)
+    res["q4_k_dense_layer_b4"] = {"us_per_layer": round(ms * 1e3, 2), "GBps": round(lb / (ms * 1e-3) / 1e9, 1),
+                                  "tokens_per_s_equiv": round(4 * lb / (ms * 1e-3) / 1e9 / 2.74, 1)}
+    del cp
+    torch.cuda.empty_cache()
+
+    # mixed Q4_K / Q6_K layer, hidden 5120, FFN 17408, bf16 activations
+    specs = [("qk", "q4_k", [("q", 5120), ("k", 1024)], 5120), ("v", "q6_k", [("v", 1024)], 5120),
+             ("o", "q4_k", [("o", 5120)], 5120), ("gu", "q4_k", [("gate", 17408), ("up", 17408)], 5120),
+             ("down", "q6_k", [("down", 5120)], 17408)]
+    idx = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6}
+    hw = {}
+    lb3 = 0
+    for name, t, parts, K in specs:
+        arrs = [synth.weight(t, synth.rng(0x67510003, idx[p]), n, K) for p, n in parts]
+        hw[name] = (np.concatenate(arrs), t, sum(n for _, n in parts), K)
+        lb3 += sum(a.nbytes for a in arrs)
+    cp3 = [{k: t_(v[0]) for k, v in hw.items()} for _ in range(max(2, -(-ROTATE_BYTES // lb3)))]
+    for B in (1, 2, 8):
+        xb = {k: t_(synth.bf16_bits(synth.normal_f32(synth.rng(0x67510003, 300 + B), (B, v[3]))).view(np.int16))
+              .view(torch.bfloat16) for k, v in hw.items()}
+        yb = {k: torch.empty(B, v[2], device=dev) for k, v in hw.items()}
+
+        def p3():
+            for c in cp3:
+                for k, v in hw.items():
+                    gq.gq_matvec(v[1], c[k], v[2], v[3], xb[k], yb[k], stream)
+
+        ms = Timer(torch, p3, stream).time(5) / len(cp3)
+        res["mixed_layer_h5120_bf16_b%d" % B] = {"us_per_layer": round(ms * 1e3, 2),
+                                                 "GBps": round(lb3 / (ms * 1e-3) / 1e9, 1),
+                                                 "tokens_per_s_equiv": round(B / (ms * 1e-3), 1)}
+    del cp3
+    torch.cuda.empty_cache()
+
+    # MoE routed experts: 128 experts, hidden 2816, FFN 704, 8 tokens top-8
+    E, H, F, T, k = 128, 2816, 704, 8, 8
+    g = synth.rng(0x67510004, 0)
+    ids, rw = synth.routing(g, T, E, k)
+    distinct = len(np.unique(ids))
+    ex = {"gate": synth.weight("q4_0", synth.rng(0x67510004, 1), E * F, H),
+          "up": synth.weight("q4_0", synth.rng(0x67510004, 2), E * F, H),
+          "down": synth.weight("q4_0", synth.rng(0x67510004, 3), E * H, F)}
+    layer_all = sum(v.nbytes for v in ex.values())
+    read_bytes = layer_all // E * distinct
+    cp4 = [{kk: t_(v) for kk, v in ex.items()} for _ in range(max(2, -(-ROTATE_BYTES // layer_all)))]
+    ids_t, rw_t = t_(ids), t_(rw)
+    x4 = t_(synth.normal_f32(g, (T, H)))
+    h4 = t_(synth.normal_f32(g, (T, k, F)))
+    yg = torch.empty(T, k, F, device=dev)
+    yu = torch.empty(T, k, F, device=dev)
+    yd = torch.empty(T, H, device=dev)
+    wsz = max(gq.gq_matvec_id_workspace(E, T, k, F), gq.gq_matvec_id_workspace(E, T, k, H))
+    ws = [torch.empty(wsz, dtype=torch.uint8, device=dev) for _ in range(3)]
+
+    def p4():
+        for c in cp4:
+            gq.gq_matvec_id("q4_0", c["gate"], E, F, H, ids_t, x4, False, yg, ws[0], None, stream)
+            gq.gq_matvec_id("q4_0", c["up"], E, F, H, ids_t, x4, False, yu, ws[1], None, stream)
+            gq.gq_matvec_id("q4_0", c["down"], E, H, F, ids_t, h4, True, yd, ws[2], rw_t, stream)
+
+    ms = Timer(torch, p4, stream).time(10) / len(cp4)
+    res["moe_q4_0_128x_h2816_f704_t8_top8"] = {
+        "us_per_layer": round(ms * 1e3, 2), "distinct_experts": distinct, "packed_bytes_read": read_bytes,
+        "GBps": round(read_bytes / (ms * 1e-3) / 1e9, 1),
+        "tokens_per_s_equiv_30_layers": round(T / (30 * ms * 1e-3), 1)}
+    del cp4
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":
