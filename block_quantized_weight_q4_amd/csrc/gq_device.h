@@ -21,6 +21,17 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 // 1024 leaves the ten mantissa bits free and their weight is one).
 constexpr uint32_t MAGIC = 0x64006400u;
 
+// The fp16-pair magic 0x64006400 as a register value.  gfx9 VOP3 instructions
+// take no literal operands, so with a literal the compiler splits
+// (w & mask) | MAGIC into v_and_b32 + v_or_b32; with the magic in a VGPR (and
+// the mask in an SGPR) it is one v_and_or_b32.  The asm is not volatile, so it
+// is hoisted out of loops.
+__device__ __forceinline__ uint32_t magic_vgpr() {
+    uint32_t r;
+    __asm__("v_mov_b32 %0, 0x64006400" : "=v"(r));
+    return r;
+}
+
 // Loads that may be only 2-byte aligned (Q4_0 and Q6_K blocks are 18 and 210
 // bytes long).  gfx9 global memory instructions accept unaligned addresses.
 __device__ __forceinline__ u32x4 ld16u(const uint8_t* p) {

@@ -66,13 +66,13 @@ struct Fmt<T_Q4_0> {
         unit = g;
         a = r;
     }
-    __device__ static void pairs(const Raw& r, int a, uint32_t P[NP]) {
+    __device__ static void pairs(const Raw& r, int a, uint32_t magic, uint32_t P[NP]) {
         const uint32_t mask = a == 0 ? 0x000F000Fu : 0x00F000F0u;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             uint32_t w = r.q[k];
-            P[2 * k] = (w & mask) | MAGIC;
-            P[2 * k + 1] = ((w >> 8) & mask) | MAGIC;
+            P[2 * k] = (w & mask) | magic;
+            P[2 * k + 1] = ((w >> 8) & mask) | magic;
         }
     }
     __device__ static Scl scales(const Raw& r, int) { return Scl{h2f(r.d)}; }
@@ -110,13 +110,13 @@ struct Fmt<T_Q4_K> {
         unit = g >> 1;
         a = g & 1;
     }
-    __device__ static void pairs(const Raw& r, int a, uint32_t P[NP]) {
+    __device__ static void pairs(const Raw& r, int a, uint32_t magic, uint32_t P[NP]) {
         const uint32_t mask = a == 0 ? 0x000F000Fu : 0x00F000F0u;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             uint32_t w = k < 4 ? r.q0[k] : r.q1[k - 4];
-            P[2 * k] = (w & mask) | MAGIC;
-            P[2 * k + 1] = ((w >> 8) & mask) | MAGIC;
+            P[2 * k] = (w & mask) | magic;
+            P[2 * k + 1] = ((w >> 8) & mask) | magic;
         }
     }
     // 6-bit (scale, min) of sub-blocks 2c and 2c+1: for c < 2 they are the low 6
@@ -193,7 +193,7 @@ struct Fmt<T_Q6_K> {
         unit = 4 * (g >> 3) + 2 * ((g >> 2) & 1) + r;
         a = g & 3;
     }
-    __device__ static void pairs(const Raw& r, int g, uint32_t P[NP]) {
+    __device__ static void pairs(const Raw& r, int g, uint32_t magic, uint32_t P[NP]) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
 #pragma unroll
@@ -204,7 +204,7 @@ struct Fmt<T_Q6_K> {
                 else if (g == 1) v = ((H << 2) & 0x00300030u) | (Bq & 0x000F000Fu);
                 else if (g == 2) v = ((H << 4) & 0x03000300u) | (A & 0x00F000F0u);
                 else v = ((H << 2) & 0x03000300u) | (Bq & 0x00F000F0u);
-                P[2 * k + j] = v | MAGIC;
+                P[2 * k + j] = v | magic;
             }
         }
     }
@@ -270,17 +270,24 @@ __device__ __forceinline__ int group_exp(float m) {
     return 15 - __builtin_amdgcn_frexp_expf(m);
 }
 
+// Staged activations of one K tile, unit-major: the record of (unit u,
+// vector b) is NQ fp16-pair quads followed by NF factor vectors, 16 B each, at
+// 16-byte slot (u * RS + b * (NQ + NF)).  The unit stride RS is odd (in 16-B
+// slots), so the lanes of a wave, which read consecutive units, hit distinct
+// LDS banks; all reads of one record share a base address.
 template <class F>
 struct TileLds {
-    u32x4* xq;   // [NQ][nb][U]   fp16 activation pairs in unpack order
-    f32x4* fac;  // [NF][nb][U]   corrections and per-group factors
-    int U, nb;
-    __device__ void carve(uint8_t* base, int U_, int nb_) {
+    u32x4* base;
+    int U, nb, RS;
+    static constexpr int NREC = F::NQ + F::NF;
+    __host__ __device__ static int unit_stride(int nb_) { return (NREC * nb_) | 1; }
+    __device__ void carve(uint8_t* p, int U_, int nb_) {
+        base = reinterpret_cast<u32x4*>(p);
         U = U_;
         nb = nb_;
-        xq = reinterpret_cast<u32x4*>(base);
-        fac = reinterpret_cast<f32x4*>(base + (size_t)16 * F::NQ * nb * U);
+        RS = unit_stride(nb_);
     }
+    __device__ u32x4* rec(int u, int b) const { return base + u * RS + b * NREC; }
 };
 
 // Barrier for LDS traffic only.  __syncthreads() is a full workgroup fence,
@@ -318,17 +325,17 @@ __device__ __forceinline__ void stage_write_run(const TileLds<F>& L, int b, int 
     }
 #pragma unroll
     for (int t = 0; t < RUN; ++t) sx += (float)(_Float16)r[t];
+    u32x4* rp = L.rec(u, b);
 #pragma unroll
     for (int qd = 0; qd < F::NP / 4; ++qd)
-        L.xq[((a * (F::NP / 4) + qd) * L.nb + b) * L.U + u] =
-            u32x4{P[4 * qd], P[4 * qd + 1], P[4 * qd + 2], P[4 * qd + 3]};
+        rp[a * (F::NP / 4) + qd] = u32x4{P[4 * qd], P[4 * qd + 1], P[4 * qd + 2], P[4 * qd + 3]};
     const uint32_t z = F::zero_pattern(a);
     float corr = 0.f;
 #pragma unroll
     for (int n = 0; n < F::NP; ++n) corr = dot2(z, P[n], corr);
     float sc = __builtin_ldexpf(1.0f, -e);
-    float* f0 = reinterpret_cast<float*>(&L.fac[(0 * L.nb + b) * L.U + u]);
-    float* f1 = reinterpret_cast<float*>(&L.fac[((F::NF - 1) * L.nb + b) * L.U + u]);
+    float* f0 = reinterpret_cast<float*>(rp + F::NQ);
+    float* f1 = reinterpret_cast<float*>(rp + F::NQ + F::NF - 1);
     if (F::NA == 2 && F::NF == 1) {  // Q4_0: {corr0, corr1, 2^-e, 0}
         f0[a] = corr;
         if (a == 0) f0[2] = sc;
@@ -412,11 +419,13 @@ __device__ __forceinline__ void load_units(const uint8_t* const rowp[R], int uni
     for (int i = 0; i < R; ++i) raw[i] = F::load(rowp[i], unit0 + uc);
 }
 
-// One unit of R rows against nb staged vectors.
+// One unit of R rows against nb staged vectors.  All LDS reads of a vector's
+// record are issued before its dot products, so one LDS latency is paid per
+// unit and vector.
 template <class F, int BMAX, int R>
 __device__ __forceinline__ void unit_math(const TileLds<F>& L, const typename F::Raw raw[R], int unit, int uc,
-                                          bool valid, float acc[R][BMAX]) {
-    const int U = L.U, nb = L.nb;
+                                          bool valid, uint32_t magic, float acc[R][BMAX]) {
+    const int nb = L.nb;
     typename F::Scl sc[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) sc[i] = F::scales(raw[i], unit);
@@ -424,13 +433,17 @@ __device__ __forceinline__ void unit_math(const TileLds<F>& L, const typename F:
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int a = 0; a < F::NA; ++a) F::pairs(raw[i], a, P[i][a]);
+        for (int a = 0; a < F::NA; ++a) F::pairs(raw[i], a, magic, P[i][a]);
 #pragma unroll
     for (int b = 0; b < BMAX; ++b) {
         if (b >= nb) break;
+        const u32x4* rp = L.rec(uc, b);
+        u32x4 xq[F::NQ];
         f32x4 f[F::NF];
 #pragma unroll
-        for (int j = 0; j < F::NF; ++j) f[j] = L.fac[(j * nb + b) * U + uc];
+        for (int q = 0; q < F::NQ; ++q) xq[q] = rp[q];
+#pragma unroll
+        for (int j = 0; j < F::NF; ++j) f[j] = __builtin_bit_cast(f32x4, rp[F::NQ + j]);
         float dacc[R][F::NA];
 #pragma unroll
         for (int a = 0; a < F::NA; ++a) {
@@ -439,13 +452,15 @@ __device__ __forceinline__ void unit_math(const TileLds<F>& L, const typename F:
             for (int i = 0; i < R; ++i) s[i] = 0.f;
 #pragma unroll
             for (int qd = 0; qd < F::NP / 4; ++qd) {
-                u32x4 xv = L.xq[((a * (F::NP / 4) + qd) * nb + b) * U + uc];
+                const u32x4 xv = xq[a * (F::NP / 4) + qd];
 #pragma unroll
-                for (int n4 = 0; n4 < 4; ++n4)
+                for (int n4 = 0; n4 < 4; ++n4) {
+                    const uint32_t xe = xv[n4];
 #pragma unroll
-                    for (int i = 0; i < R; ++i) s[i] = dot2(P[i][a][4 * qd + n4], xv[n4], s[i]);
+                    for (int i = 0; i < R; ++i) s[i] = dot2(P[i][a][4 * qd + n4], xe, s[i]);
+                }
             }
-            float corr = f[0][a];
+            const float corr = f[0][a];
 #pragma unroll
             for (int i = 0; i < R; ++i) dacc[i][a] = s[i] - corr;
         }
@@ -468,6 +483,7 @@ __device__ __forceinline__ void compute_tile(const TileLds<F>& L, const uint8_t*
                                              int LPR, typename F::Raw ring[D][R], float acc[R][BMAX]) {
     const int U = L.U;
     const int T = (U + LPR - 1) / LPR;
+    const uint32_t magic = magic_vgpr();
     for (int t0 = 0; t0 < T; t0 += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
@@ -481,7 +497,7 @@ __device__ __forceinline__ void compute_tile(const TileLds<F>& L, const uint8_t*
             // unconditional (clamped) refill: straight-line loads keep the
             // load-counter waits exact
             load_units<F, R>(rowp, unit0, u + LPR * D, U, ring[j]);
-            if (t < T) unit_math<F, BMAX, R>(L, cur, unit0 + uc, uc, valid, acc);
+            if (t < T) unit_math<F, BMAX, R>(L, cur, unit0 + uc, uc, valid, magic, acc);
         }
     }
 }
@@ -605,7 +621,7 @@ inline Plan plan_for(int64_t N, int64_t K, int nb) {
     const int SR = 64 / p.LPR;
     // K tile: as many units as the LDS budget allows for nb vectors, rounded
     // down to a multiple of LPR (a multiple of 4 units = whole super-blocks)
-    size_t per_unit = (size_t)16 * (F::NQ + F::NF) * nb;
+    size_t per_unit = (size_t)16 * TileLds<F>::unit_stride(nb);
     int64_t step = p.LPR;
     int64_t max_units = (int64_t)(LDS_BUDGET / per_unit) / step * step;
     if (max_units < step) max_units = step;
