@@ -1,6 +1,9 @@
 """Benchmark of the packed-weight products on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu-baseline]
+    python bench.py --pmc-pass            (the dominant kernel + a copy kernel, for rocprofv3 --pmc)
+    python bench.py --traffic-summary FETCH_DIR WRITE_DIR   (writes profiles/<kernel>_traffic.txt)
+    python bench.py --stats-summary DIR OUT.txt             (rocprofv3 --stats CSV -> text summary)
 
 The step (the headline workload) is one decoder layer of Q4_K products at
 batch 1, hidden 2560: q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up
@@ -17,12 +20,20 @@ One JSON line: value = packed-weight GB/s of the whole step; roofline = the
 dominant kernel (gate|up, 28,016,640 B per launch) timed over back-to-back
 launches of it alone; cpu_baseline = the CPU oracle on the same layer; plus
 the prefill product's TFLOP/s and the other workloads as context.
+
+roofline.traffic is the HBM bytes per launch of that kernel from two
+rocprofv3 --pmc runs of `--pmc-pass` (FETCH_SIZE, then WRITE_SIZE), each
+scaled by the factor that makes the same counter read right for a plain copy
+kernel of known size.  The summary file records a hash of the kernel's
+sources; when the sources have changed since, traffic is reported as null.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -47,7 +58,134 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline only (no context workloads)")
+    ap.add_argument("--pmc-pass", action="store_true", help="run the dominant kernel 8x and one copy kernel")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--stats-summary", nargs=2, metavar=("DIR", "OUT"))
     return ap.parse_args()
+
+
+# ------------------------------------------------------------ traffic
+GU_N, GU_K = 19456, 2560
+GU_KERNEL = "k_matvec<2, 0, 1"          # Q4_K, fp32 activations, batch 1
+COPY_BYTES = 64 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "matvec_q4k_gateup_19456x2560_b1_traffic.txt")
+KERNEL_SOURCES = ["gq_device.h", "gq_gemv_core.h", "gq_matvec.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_quantized_weight_q4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_pass():
+    """The dominant kernel (gate|up, batch 1) over 8 distinct weight copies,
+    then torch's elementwise add over a 64 MiB fp32 tensor: 64 MiB read,
+    64 MiB written, the calibration for the byte counters."""
+    import torch
+    import block_quantized_weight_q4_amd as gq
+    from block_quantized_weight_q4_amd import synth
+    dev = torch.device("cuda:0")
+    W = synth.weight("q4_k", synth.rng(0x67510002, 4), GU_N, GU_K)
+    Ws = [torch.from_numpy(W).to(dev) for _ in range(8)]
+    x = torch.from_numpy(synth.normal_f32(synth.rng(0x67510002, 100), (1, GU_K))).to(dev)
+    y = torch.empty(1, GU_N, device=dev)
+    for w in Ws:
+        gq.gq_matvec("q4_k", w, GU_N, GU_K, x, y)
+    torch.cuda.synchronize()
+    src = torch.empty(COPY_BYTES // 4, device=dev).normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    print("pmc pass done", flush=True)
+
+
+def _counter_means(d: str) -> dict:
+    import csv
+    import glob
+    vals = {}
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(p)):
+            vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+
+def traffic_summary(fetch_dir: str, write_dir: str):
+    out_lines = []
+    per = {}
+    for d, ctr in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        means, counts = _counter_means(d)
+        mv = [k for k in means if k[1] == ctr and GU_KERNEL in k[0]]
+        cp = [k for k in means if k[1] == ctr and "vectorized_elementwise_kernel" in k[0] and "add" in k[0].lower()]
+        assert len(mv) == 1 and len(cp) == 1, (mv, cp)
+        kib_mv, kib_cp = means[mv[0]], means[cp[0]]
+        factor = (COPY_BYTES / 1024.0) / kib_cp
+        per[ctr] = (kib_mv, kib_cp, factor, counts[mv[0]])
+        out_lines.append("%s: dominant kernel %.1f KiB/dispatch (mean of %d); copy kernel %.1f KiB for %d KiB "
+                         "moved -> scale %.4f -> %.0f bytes per launch"
+                         % (ctr, kib_mv, counts[mv[0]], kib_cp, COPY_BYTES // 1024, factor, kib_mv * factor * 1024))
+    traffic = sum(v[0] * v[2] * 1024 for v in per.values())
+    algo = GU_N * (GU_K // 256) * 144
+    text = ["# HBM traffic of the Q4_K gate|up product (19456 x 2560, batch 1, fp32 x)",
+            "",
+            "kernel: %s ... (Q4_K, fp32 activations, batch 1)" % GU_KERNEL,
+            "source_sha256: %s" % kernel_source_hash(),
+            "commands (from the repository root, on the GPU host):",
+            "  timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -- python3 bench.py --pmc-pass",
+            "  timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -- python3 bench.py --pmc-pass",
+            "  python bench.py --traffic-summary <FETCH_DIR> <WRITE_DIR>",
+            ""] + out_lines + [
+            "",
+            "traffic_bytes_per_launch: %.0f" % traffic,
+            "algorithmic_bytes_per_launch: %d (packed weights) + %d (x) + %d (y)" % (algo, GU_K * 4, GU_N * 4),
+            "traffic / algorithmic: %.4f" % (traffic / (algo + GU_K * 4 + GU_N * 4))]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(text) + "\n")
+    print("\n".join(text))
+
+
+def read_traffic():
+    """traffic_bytes_per_launch from the committed summary, or None when the
+    kernel sources changed since it was taken (or there is none)."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"source_sha256: (\w+)", text)
+    t = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return int(t.group(1))
+
+
+def stats_summary(d: str, out: str):
+    """rocprofv3 --kernel-trace --stats output -> short text table."""
+    import csv
+    import glob
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    assert stats and trace, d
+    lines = ["%-100s %7s %10s %10s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
+    for r in csv.DictReader(open(stats[0])):
+        lines.append("%-100s %7s %10.3f %10.3f %10.3f" % (r["Name"][:100], r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                      float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    # per (kernel, grid) averages from the trace: one kernel serves several shapes
+    per = {}
+    for r in csv.DictReader(open(trace[0])):
+        k = (r["Kernel_Name"][:80], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        per.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines += ["", "per launch shape (grid = work-items):",
+              "%-80s %9s %5s %7s %10s %10s" % ("kernel", "grid", "wg", "calls", "avg_us", "median_us")]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        v.sort()
+        lines.append("%-80s %9d %5d %7d %10.3f %10.3f" % (k[0], k[1], k[2], len(v), sum(v) / len(v), v[len(v) // 2]))
+    with open(out, "a") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 class Timer:
@@ -79,10 +217,17 @@ class Timer:
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
+    if args.stats_summary:
+        return stats_summary(*args.stats_summary)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the products shard by "
-              "output rows across GPUs; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+              "output rows across GPUs).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.pmc_pass:
+        return pmc_pass()
 
     import torch
     import block_quantized_weight_q4_amd as gq
@@ -198,7 +343,7 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s_equiv": round(value / 2.74, 1),
         "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
                      "kernel": "k_matvec<Q4_K, fp32, 1, 1, 4> gate|up 19456x2560 batch 1",
                      "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1e3, 3)},
         "cpu_baseline": cpu,
