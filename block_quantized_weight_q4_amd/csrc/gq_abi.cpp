@@ -20,6 +20,9 @@ gq_status from_hip(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_LAUNC
 // Largest element count any single launch handles (keeps 32-bit grid sizes
 // and 64-bit byte offsets far from overflow).
 constexpr int64_t MAX_ELEMS = (int64_t)1 << 40;
+// Longest row the decode products take: a workgroup addresses its (at most 32)
+// rows through one buffer resource whose span must stay below 2^31 bytes.
+constexpr int64_t MAX_K_DECODE = (int64_t)1 << 22;
 
 }  // namespace
 
@@ -70,7 +73,7 @@ gq_status gq_matvec(gq_type t, const void* W, int64_t N, int64_t K, const void* 
     if (!known_type(t)) return GQ_ERR_TYPE;
     if (x_dtype != GQ_F32 && x_dtype != GQ_BF16) return GQ_ERR_DTYPE;
     if (N < 0 || K < 0 || K % qk_of(t) != 0 || batch < 1) return GQ_ERR_SHAPE;
-    if (N > MAX_ELEMS || K > MAX_ELEMS || (K > 0 && N > MAX_ELEMS / K)) return GQ_ERR_SHAPE;
+    if (N > MAX_ELEMS || K > MAX_K_DECODE || (K > 0 && N > MAX_ELEMS / K)) return GQ_ERR_SHAPE;
     if (batch > 8) return GQ_ERR_UNSUPPORTED;
     if (N == 0) return GQ_OK;
     if (!y || (K > 0 && (!W || !x))) return GQ_ERR_NULL;
@@ -100,7 +103,7 @@ gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_
     if (n_experts < 1 || n_tokens < 0 || top_k < 1 || top_k > n_experts || N < 0 || K < 0 ||
         K % qk_of(t) != 0 || (x_per_slot != 0 && x_per_slot != 1) || (int64_t)n_tokens * top_k > 1024)
         return GQ_ERR_SHAPE;
-    if (N > MAX_ELEMS || K > MAX_ELEMS || (K > 0 && N > MAX_ELEMS / K) ||
+    if (N > MAX_ELEMS || K > MAX_K_DECODE || (K > 0 && N > MAX_ELEMS / K) ||
         (K > 0 && N > 0 && (int64_t)n_experts > MAX_ELEMS / (N * K)))
         return GQ_ERR_SHAPE;
     if (n_tokens == 0 || N == 0) return GQ_OK;

@@ -3,11 +3,18 @@
 //
 // Work split.  A workgroup (256 threads, 4 wavefronts) owns a tile of output
 // rows and a small batch of activation vectors.  Each wavefront covers
-// R * (64 / LPR) rows: its 64 lanes form 64/LPR groups of LPR lanes, one group
-// per row, and inside a group lane v walks the row's "units" v, v+LPR, ...
-// (a unit is 32 or 64 consecutive weights).  Every lane therefore streams its
-// own 16-byte pieces of R rows with vector loads, unpacks them in registers and
-// keeps fp32 partial sums; one shuffle reduction per output ends the kernel.
+// 64 / LPR rows: its 64 lanes form 64/LPR groups of LPR lanes, one group per
+// row, and inside a group lane v takes the row's "units" v, v+LPR, ... (a unit
+// is 32 or 64 consecutive weights).  Every lane streams its own 16-byte pieces
+// of the row with buffer loads, unpacks them in registers and keeps fp32
+// partial sums; one shuffle reduction per output ends the kernel.
+//
+// Loads.  The weights of a workgroup are addressed through one buffer
+// resource that spans exactly its rows.  A lane whose unit lies past the end
+// of its row (or whose row lies past N) loads at an offset beyond that span:
+// the hardware returns zeros for it without a memory access.  So the number of
+// load instructions is fixed at compile time (the load counter waits stay
+// exact) while no byte is fetched twice or needlessly.
 //
 // Arithmetic.  A weight quant q (4 or 6 bits) is turned into the fp16 value
 // 1024 + q (or 1024 + 16 q for a high nibble) by OR-ing it into the mantissa of
@@ -34,32 +41,59 @@ namespace gqd {
 
 constexpr int NTHREADS = 256;
 
+// ------------------------------------------------------ buffer loads ----
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// Offset that is past every buffer's span: such a load returns zeros and
+// touches no memory.  Spans are kept below 2^31 bytes.
+constexpr uint32_t OOB = 0x80000000u;
+
+// Raw (unformatted, stride 0) buffer over [base, base + bytes).
+__device__ __forceinline__ Rsrc make_rsrc(const uint8_t* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Loads at any byte offset (gfx9 buffer loads accept unaligned addresses).
+__device__ __forceinline__ u32x4 bld16(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32x2 bld8(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bld2(Rsrc r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
 template <int TYPE>
 struct Fmt;
+
+// Every format describes a unit by (block, position inside the block): the
+// block offset is b * BB and the lane-constant part (`pos`, from unit % UPB,
+// with UPB units per block) is fixed per lane because LPR is a multiple of 4.
 
 // ---------------------------------------------------------------- Q4_0 ----
 // Unit = one 18-byte block (32 weights).  Accumulator 0 = low nibbles
 // (weights 0..15), accumulator 1 = high nibbles (weights 16..31).
 template <>
 struct Fmt<T_Q4_0> {
-    static constexpr int QK = 32, BB = 18, UW = 32, NA = 2, NP = 8, NF = 1, NQ = NA * NP / 4;
+    static constexpr int QK = 32, BB = 18, UW = 32, UPB = 1, NA = 2, NP = 8, NF = 1, NQ = NA * NP / 4;
     struct Raw {
         uint32_t d;
         u32x4 q;
+    };
+    struct Lane {
+        __device__ explicit Lane(int) {}
     };
     struct Scl {
         float d;
     };
     __device__ static uint32_t zero_pattern(int a) { return a == 0 ? 0x64086408u : 0x64806480u; }
-    __device__ static Raw load(const uint8_t* row, int unit) {
-        const uint8_t* bp = row + (int64_t)unit * BB;
+    __device__ static Raw load(Rsrc rs, uint32_t boff, const Lane&) {
         Raw r;
-        r.d = ld2(bp);
-        r.q = ld16u(bp + 2);
+        r.d = bld2(rs, boff);
+        r.q = bld16(rs, boff + 2);
         return r;
     }
-    // first weight (relative to the unit's block row position) of accumulator a
-    __device__ static int run_base(int unit, int a) { return 32 * unit + 16 * a; }
     // the runs of 32-input group g: run r covers group elements 16r..16r+15
     static constexpr int RPG = 2;
     __device__ static void group_run(int g, int r, int& unit, int& a) {
@@ -75,36 +109,48 @@ struct Fmt<T_Q4_0> {
             P[2 * k + 1] = ((w >> 8) & mask) | magic;
         }
     }
-    __device__ static Scl scales(const Raw& r, int) { return Scl{h2f(r.d)}; }
+    __device__ static Scl scales(const Raw& r, const Lane&) { return Scl{h2f(r.d)}; }
     // dacc[a] = accumulator - correction; f[0] = {corr0, corr1, 2^-e, 0}
     __device__ static float contrib(const Scl& s, const float dacc[NA], const f32x4 f[NF]) {
-        return (s.d * f[0].z) * (dacc[0] + 0.0625f * dacc[1]);
+        return (s.d * f[0].z) * __builtin_fmaf(0.0625f, dacc[1], dacc[0]);
     }
 };
 
 // ---------------------------------------------------------------- Q4_K ----
-// Unit = a 32-byte slice of the quants (64 weights = sub-blocks 2c and 2c+1 of
-// one super-block, c = unit % 4) plus the block's 16-byte header.
+// Unit c (0..3) of a super-block = a 32-byte slice of the quants (64 weights:
+// sub-blocks 2c and 2c+1) plus the block's 16-byte header.
 template <>
 struct Fmt<T_Q4_K> {
-    static constexpr int QK = 256, BB = 144, UW = 64, NA = 2, NP = 16, NF = 2, NQ = NA * NP / 4;
+    static constexpr int QK = 256, BB = 144, UW = 64, UPB = 4, NA = 2, NP = 16, NF = 2, NQ = NA * NP / 4;
     struct Raw {
         u32x4 h, q0, q1;
+    };
+    // Per-lane constants of the scale decode for slice c: byte selectors of
+    // the 6-bit (sc, m) fields of sub-blocks 2c, 2c+1 (see scales()).
+    struct Lane {
+        uint32_t qoff, sel_lo, sel_hi;
+        bool low;
+        __device__ explicit Lane(int c) {
+            qoff = 16 + 32 * c;
+            const uint32_t j = 2 * (c & 1);
+            // bytes j, j+1 of scale words 0 (h.y) and 1 (h.z): [y_j, y_j+1, z_j, z_j+1]
+            sel_lo = j | (j + 1) << 8 | (j + 4) << 16 | (j + 5) << 24;
+            // bytes j, j+1 of scale word 2 (h.w), twice: [w_j, w_j+1, w_j, w_j+1]
+            sel_hi = j | (j + 1) << 8 | j << 16 | (j + 1) << 24;
+            low = c < 2;
+        }
     };
     struct Scl {
         float dsL, dsH, dmL, dmH;
     };
     __device__ static uint32_t zero_pattern(int) { return MAGIC; }
-    __device__ static Raw load(const uint8_t* row, int unit) {
-        const uint8_t* bp = row + (int64_t)(unit >> 2) * BB;
-        int c = unit & 3;
+    __device__ static Raw load(Rsrc rs, uint32_t boff, const Lane& ln) {
         Raw r;
-        r.h = ld16a(bp);
-        r.q0 = ld16a(bp + 16 + 32 * c);
-        r.q1 = ld16a(bp + 32 + 32 * c);
+        r.h = bld16(rs, boff);
+        r.q0 = bld16(rs, boff + ln.qoff);
+        r.q1 = bld16(rs, boff + ln.qoff + 16);
         return r;
     }
-    __device__ static int run_base(int unit, int a) { return 256 * (unit >> 2) + 64 * (unit & 3) + 32 * a; }
     static constexpr int RPG = 1;
     __device__ static void group_run(int g, int, int& unit, int& a) {
         unit = g >> 1;
@@ -119,31 +165,24 @@ struct Fmt<T_Q4_K> {
             P[2 * k + 1] = ((w >> 8) & mask) | magic;
         }
     }
-    // 6-bit (scale, min) of sub-blocks 2c and 2c+1: for c < 2 they are the low 6
-    // bits of scale bytes s and s+4; for c >= 2 a low/high nibble of byte s+4
-    // plus the top two bits of bytes s-4 and s.
-    __device__ static Scl scales(const Raw& r, int unit) {
-        int c = unit & 3;
-        float d = h2f(r.h.x & 0xffffu), dmin = h2f(r.h.x >> 16);
-        int sh = 16 * (c & 1);  // byte (2c) & 3 and (2c+1) & 3 -> shifts sh, sh+8
-        uint32_t b0 = r.h.y >> sh, b1 = r.h.z >> sh, b2 = r.h.w >> sh;
-        uint32_t scL, mL, scH, mH;
-        if (c < 2) {
-            scL = b0 & 63u;
-            mL = b1 & 63u;
-            scH = (b0 >> 8) & 63u;
-            mH = (b1 >> 8) & 63u;
-        } else {
-            scL = (b2 & 15u) | (((b0 >> 6) & 3u) << 4);
-            mL = ((b2 >> 4) & 15u) | (((b1 >> 6) & 3u) << 4);
-            scH = ((b2 >> 8) & 15u) | (((b0 >> 14) & 3u) << 4);
-            mH = ((b2 >> 12) & 15u) | (((b1 >> 14) & 3u) << 4);
-        }
+    // 6-bit (scale, min) of sub-blocks s = 2c, 2c+1 (j = s & 3 over the 12
+    // scale bytes b[0..11] = h.y, h.z, h.w):
+    //   s < 4:  sc = b[j] & 63,                        m = b[j+4] & 63
+    //   s >= 4: sc = (b[j+8] & 15) | (b[j] >> 6) << 4, m = (b[j+8] >> 4) | (b[j+4] >> 6) << 4
+    // Both forms are built with byte permutes as [scL, scH, mL, mH] and the
+    // lane's slice picks one -- no divergent branch.
+    __device__ static Scl scales(const Raw& r, const Lane& ln) {
+        const uint32_t C = __builtin_amdgcn_perm(r.h.z, r.h.y, ln.sel_lo);
+        const uint32_t A = __builtin_amdgcn_perm(r.h.w, r.h.w, ln.sel_hi);
+        const uint32_t lo = C & 0x3F3F3F3Fu;
+        const uint32_t hi = ((C >> 2) & 0x30303030u) | (A & 0x00000F0Fu) | ((A >> 4) & 0x0F0F0000u);
+        const uint32_t v = ln.low ? lo : hi;
+        const float d = h2f(r.h.x & 0xffffu), dmin = h2f(r.h.x >> 16);
         Scl s;
-        s.dsL = d * (float)scL;
-        s.dsH = d * (float)scH * 0.0625f;
-        s.dmL = dmin * (float)mL;
-        s.dmH = dmin * (float)mH;
+        s.dsL = d * (float)(v & 0xffu);
+        s.dsH = (d * 0.0625f) * (float)((v >> 8) & 0xffu);
+        s.dmL = dmin * (float)((v >> 16) & 0xffu);
+        s.dmH = dmin * (float)(v >> 24);
         return s;
     }
     // f[0] = {corrL, corrH, 2^-eL, 2^-eH}; f[1] = {sum xL, sum xH, 0, 0}
@@ -156,35 +195,41 @@ struct Fmt<T_Q4_K> {
 };
 
 // ---------------------------------------------------------------- Q6_K ----
-// Unit = (half h, lane half lh) of a super-block: lanes l = 16 lh .. 16 lh + 15
-// of the four 32-weight groups g of half h (64 weights, four 16-weight
+// Unit (h, lh) of a super-block, unit % 4 = 2h + lh: lanes l = 16 lh .. 16 lh
+// + 15 of the four 32-weight groups g of half h (64 weights, four 16-weight
 // sub-blocks).  Accumulator g.
 template <>
 struct Fmt<T_Q6_K> {
-    static constexpr int QK = 256, BB = 210, UW = 64, NA = 4, NP = 8, NF = 2, NQ = NA * NP / 4;
+    static constexpr int QK = 256, BB = 210, UW = 64, UPB = 4, NA = 4, NP = 8, NF = 2, NQ = NA * NP / 4;
     struct Raw {
         u32x4 la, lb, qh;
         u32x2 sc;
         uint32_t d;
+    };
+    struct Lane {
+        uint32_t ql, qh, sc;
+        int sh;
+        __device__ explicit Lane(int p) {
+            const int h = p >> 1, lh = p & 1;
+            ql = 64 * h + 16 * lh;
+            qh = 128 + 32 * h + 16 * lh;
+            sc = 192 + 8 * h;
+            sh = 8 * lh;
+        }
     };
     struct Scl {
         float ds[4];
     };
     // zero point q = 32: 1024 + 32 for groups 0,1 and 1024 + 16*32 for 2,3
     __device__ static uint32_t zero_pattern(int a) { return a < 2 ? 0x64206420u : 0x66006600u; }
-    __device__ static Raw load(const uint8_t* row, int unit) {
-        const uint8_t* bp = row + (int64_t)(unit >> 2) * BB;
-        int h = (unit >> 1) & 1, lh = unit & 1;
+    __device__ static Raw load(Rsrc rs, uint32_t boff, const Lane& ln) {
         Raw r;
-        r.la = ld16u(bp + 64 * h + 16 * lh);
-        r.lb = ld16u(bp + 64 * h + 32 + 16 * lh);
-        r.qh = ld16u(bp + 128 + 32 * h + 16 * lh);
-        r.sc = ld8u(bp + 192 + 8 * h);
-        r.d = ld2(bp + 208);
+        r.la = bld16(rs, boff + ln.ql);
+        r.lb = bld16(rs, boff + ln.ql + 32);
+        r.qh = bld16(rs, boff + ln.qh);
+        r.sc = bld8(rs, boff + ln.sc);
+        r.d = bld2(rs, boff + 208);
         return r;
-    }
-    __device__ static int run_base(int unit, int a) {
-        return 256 * (unit >> 2) + 128 * ((unit >> 1) & 1) + 32 * a + 16 * (unit & 1);
     }
     // group g = (block g/8, half h, group gg): lane halves 0 and 1 are units
     // 4*block + 2h and 4*block + 2h + 1, accumulator gg
@@ -208,14 +253,14 @@ struct Fmt<T_Q6_K> {
             }
         }
     }
-    __device__ static Scl scales(const Raw& r, int unit) {
-        int sh = 8 * (unit & 1);
-        float d = h2f(r.d);
+    __device__ static Scl scales(const Raw& r, const Lane& ln) {
+        const int sh = ln.sh;
+        const float d = h2f(r.d), d16 = d * 0.0625f;
         Scl s;
         s.ds[0] = d * (float)(int)(int8_t)(r.sc.x >> sh);
         s.ds[1] = d * (float)(int)(int8_t)(r.sc.x >> (sh + 16));
-        s.ds[2] = d * (float)(int)(int8_t)(r.sc.y >> sh) * 0.0625f;
-        s.ds[3] = d * (float)(int)(int8_t)(r.sc.y >> (sh + 16)) * 0.0625f;
+        s.ds[2] = d16 * (float)(int)(int8_t)(r.sc.y >> sh);
+        s.ds[3] = d16 * (float)(int)(int8_t)(r.sc.y >> (sh + 16));
         return s;
     }
     // f[0] = corrections of groups 0..3; f[1] = 2^-e of groups 0..3
@@ -251,23 +296,30 @@ __device__ __forceinline__ void load_group(const uint8_t* xb, int64_t k, XRaw<XT
     for (int i = 0; i < (XT == 0 ? 8 : 4); ++i) r.q[i] = p[i];
 }
 
+// Bits of element i as an fp32 pattern.  (Element copied to a scalar first:
+// __builtin_bit_cast of a vector-element lvalue reads element 0 with this
+// compiler.)
 template <int XT>
-__device__ __forceinline__ float group_elem(const XRaw<XT>& r, int i) {
-    // (element copied to a scalar first: __builtin_bit_cast of a vector-element
-    // lvalue reads element 0 with this compiler)
+__device__ __forceinline__ uint32_t group_bits(const XRaw<XT>& r, int i) {
     if (XT == 0) {
         uint32_t w = r.q[i >> 2][i & 3];
-        return __builtin_bit_cast(float, w);
+        return w;
     }
     uint32_t w = r.q[i >> 3][(i >> 1) & 3];
-    return __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
+    return (i & 1) ? (w & 0xffff0000u) : (w << 16);
 }
 
-// Exponent e that puts max|x| of a 32-group into [2^14, 2^15); 0 for a group
-// that is all zero or holds Inf/NaN (which then propagate).
-__device__ __forceinline__ int group_exp(float m) {
-    if (!(m > 0.f) || !(m < __builtin_inff())) return 0;
-    return 15 - __builtin_amdgcn_frexp_expf(m);
+// Wait until every vector memory load of this wavefront has returned
+// (s_waitcnt vmcnt(0), the other counters left alone).
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Exponent e that puts the largest magnitude of a 32-group into
+// [2^14, 2^15), from the largest |x| bit pattern (non-negative floats order
+// like their bit patterns); 0 for an all-zero group or one holding Inf/NaN
+// (which then propagate).
+__device__ __forceinline__ int group_exp(uint32_t mbits) {
+    if (mbits == 0 || mbits >= 0x7f800000u) return 0;
+    return 15 - __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, mbits));
 }
 
 // Staged activations of one K tile, unit-major: the record of (unit u,
@@ -299,32 +351,17 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Staging of the activations of inputs [k0, k0 + U*UW) for nb vectors, in one
-// pass: a thread takes one accumulator run (16 or 32 consecutive inputs); it
-// reads the whole 32-input group the run lies in, finds the group's exponent,
-// rounds the scaled run to fp16 pairs in unpack order, and computes the
-// zero-point correction with the same dot2 chain the main loop will run.
-// Every run lies inside one 32-group in all three formats.
-//
-// stage_issue loads the group of the thread's first run; the caller then
-// issues the weight loads, so the (in-order) load counter lets staging proceed
-// as soon as the activations arrive.  stage_finish does the arithmetic, any
-// further runs, and ends with an LDS barrier.
 // One run (16 or 32 consecutive inputs starting at group element `off`) of an
 // already-scaled group -> fp16 pairs in unpack order, its zero-point
 // correction, and its factors.
 template <class F>
 __device__ __forceinline__ void stage_write_run(const TileLds<F>& L, int b, int u, int a, const float* r, int e) {
-    constexpr int RUN = 2 * F::NP;
     uint32_t P[F::NP];
-    float sx = 0.f;
 #pragma unroll
     for (int n = 0; n < F::NP; ++n) {
         int t = 4 * (n >> 1) + (n & 1);
         P[n] = pack_h2(r[t], r[t + 2]);
     }
-#pragma unroll
-    for (int t = 0; t < RUN; ++t) sx += (float)(_Float16)r[t];
     u32x4* rp = L.rec(u, b);
 #pragma unroll
     for (int qd = 0; qd < F::NP / 4; ++qd)
@@ -341,6 +378,10 @@ __device__ __forceinline__ void stage_write_run(const TileLds<F>& L, int b, int 
         if (a == 0) f0[2] = sc;
         else f0[3] = 0.f;
     } else if (F::NA == 2) {         // Q4_K: {corrL, corrH, sL, sH}, {sum xL, sum xH, 0, 0}
+        // sum of the run's fp16 values (dot2 against ones), times 2^-e
+        float sx = 0.f;
+#pragma unroll
+        for (int n = 0; n < F::NP; ++n) sx = dot2(0x3C003C00u, P[n], sx);
         f0[a] = corr;
         f0[2 + a] = sc;
         f1[a] = sx * sc;
@@ -354,19 +395,20 @@ __device__ __forceinline__ void stage_write_run(const TileLds<F>& L, int b, int 
 // A whole 32-input group of vector b: exponent, scaling, and every run in it.
 template <class F, int XT>
 __device__ __forceinline__ void stage_group(const TileLds<F>& L, int b, int g, const XRaw<XT>& in) {
+    uint32_t bits[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) bits[i] = group_bits<XT>(in, i);
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+        uint32_t a0 = bits[i] & 0x7fffffffu, a1 = bits[i + 1] & 0x7fffffffu;
+        m = a0 > m ? a0 : m;
+        m = a1 > m ? a1 : m;
+    }
+    const int e = group_exp(m);
     float v[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = group_elem<XT>(in, i);
-    float m = 0.f;
-    bool nan = false;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
-        nan |= v[i] != v[i];
-    }
-    int e = group_exp(nan ? __builtin_nanf("") : m);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = __builtin_ldexpf(v[i], e);
+    for (int i = 0; i < 32; ++i) v[i] = __builtin_ldexpf(__builtin_bit_cast(float, bits[i]), e);
 #pragma unroll
     for (int r = 0; r < F::RPG; ++r) {
         int u, a;
@@ -382,8 +424,11 @@ __device__ __forceinline__ void stage_group(const TileLds<F>& L, int b, int g, c
 // stays a scalar) and ends with an LDS barrier.
 template <class F, int XT>
 __device__ __forceinline__ void stage_issue(const XSrc& xs, int64_t k0, const TileLds<F>& L, XRaw<XT>& in) {
+    // every thread loads (threads past the groups reload group 0): an
+    // unconditional load keeps the load-counter waits exact
     const int G = L.U * F::UW / 32;
-    if ((int)threadIdx.x < G) load_group<XT>(xs.p[0], k0 + 32 * threadIdx.x, in);
+    const int g = (int)threadIdx.x < G ? (int)threadIdx.x : 0;
+    load_group<XT>(xs.p[0], k0 + 32 * g, in);
 }
 
 template <class F, int XT>
@@ -409,114 +454,47 @@ __device__ __forceinline__ void stage_finish(const XSrc& xs, int64_t k0, const T
 
 // ----------------------------------------------------------- compute ----
 
-// Load the R rows' unit (unit0 + min(u, U-1)) -- clamped so the last, partly
-// idle iteration never reads outside the tile.
-template <class F, int R>
-__device__ __forceinline__ void load_units(const uint8_t* const rowp[R], int unit0, int u, int U,
-                                           typename F::Raw raw[R]) {
-    int uc = u < U ? u : U - 1;
-#pragma unroll
-    for (int i = 0; i < R; ++i) raw[i] = F::load(rowp[i], unit0 + uc);
-}
-
-// One unit of R rows against nb staged vectors.  All LDS reads of a vector's
-// record are issued before its dot products, so one LDS latency is paid per
-// unit and vector.
-template <class F, int BMAX, int R>
-__device__ __forceinline__ void unit_math(const TileLds<F>& L, const typename F::Raw raw[R], int unit, int uc,
-                                          bool valid, uint32_t magic, float acc[R][BMAX]) {
+// One unit of a row against nb staged vectors (record uc of the tile).
+template <class F, int BMAX>
+__device__ __forceinline__ void unit_math(const TileLds<F>& L, const typename F::Raw& raw,
+                                          const typename F::Lane& ln, int uc, bool valid, uint32_t magic,
+                                          float acc[BMAX]) {
     const int nb = L.nb;
-    typename F::Scl sc[R];
+    const typename F::Scl sc = F::scales(raw, ln);
+    uint32_t P[F::NA][F::NP];
 #pragma unroll
-    for (int i = 0; i < R; ++i) sc[i] = F::scales(raw[i], unit);
-    uint32_t P[R][F::NA][F::NP];
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int a = 0; a < F::NA; ++a) F::pairs(raw[i], a, magic, P[i][a]);
+    for (int a = 0; a < F::NA; ++a) F::pairs(raw, a, magic, P[a]);
 #pragma unroll
     for (int b = 0; b < BMAX; ++b) {
         if (b >= nb) break;
         const u32x4* rp = L.rec(uc, b);
-        u32x4 xq[F::NQ];
         f32x4 f[F::NF];
 #pragma unroll
-        for (int q = 0; q < F::NQ; ++q) xq[q] = rp[q];
-#pragma unroll
         for (int j = 0; j < F::NF; ++j) f[j] = __builtin_bit_cast(f32x4, rp[F::NQ + j]);
-        float dacc[R][F::NA];
+        float dacc[F::NA];
 #pragma unroll
         for (int a = 0; a < F::NA; ++a) {
-            float s[R];
+            u32x4 xq[F::NP / 4];
 #pragma unroll
-            for (int i = 0; i < R; ++i) s[i] = 0.f;
+            for (int qd = 0; qd < F::NP / 4; ++qd) xq[qd] = rp[a * (F::NP / 4) + qd];
+            float s = 0.f;
 #pragma unroll
-            for (int qd = 0; qd < F::NP / 4; ++qd) {
-                const u32x4 xv = xq[a * (F::NP / 4) + qd];
+            for (int qd = 0; qd < F::NP / 4; ++qd)
 #pragma unroll
-                for (int n4 = 0; n4 < 4; ++n4) {
-                    const uint32_t xe = xv[n4];
-#pragma unroll
-                    for (int i = 0; i < R; ++i) s[i] = dot2(P[i][a][4 * qd + n4], xe, s[i]);
-                }
-            }
-            const float corr = f[0][a];
-#pragma unroll
-            for (int i = 0; i < R; ++i) dacc[i][a] = s[i] - corr;
+                for (int n4 = 0; n4 < 4; ++n4) s = dot2(P[a][4 * qd + n4], xq[qd][n4], s);
+            dacc[a] = s - f[0][a];
         }
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            float c = F::contrib(sc[i], dacc[i], f);
-            acc[i][b] += valid ? c : 0.f;
-        }
+        const float c = F::contrib(sc, dacc, f);
+        acc[b] += valid ? c : 0.f;
     }
-}
-
-// Accumulate the tile [unit0, unit0 + U) of R rows (pointers rowp[i]) for
-// nb <= BMAX vectors into acc[R][BMAX].  Lane v of an LPR-lane group handles
-// units v, v + LPR, ...  `ring` holds the loads of the lane's first D units on
-// entry (issued before the activations were staged); the loads of unit t + D
-// are issued right after unit t's registers are consumed, so D units per row
-// are always in flight.
-template <class F, int BMAX, int R, int D>
-__device__ __forceinline__ void compute_tile(const TileLds<F>& L, const uint8_t* const rowp[R], int unit0, int v,
-                                             int LPR, typename F::Raw ring[D][R], float acc[R][BMAX]) {
-    const int U = L.U;
-    const int T = (U + LPR - 1) / LPR;
-    const uint32_t magic = magic_vgpr();
-    for (int t0 = 0; t0 < T; t0 += D) {
-#pragma unroll
-        for (int j = 0; j < D; ++j) {
-            int t = t0 + j;
-            int u = v + LPR * t;
-            bool valid = u < U;
-            int uc = valid ? u : U - 1;
-            typename F::Raw cur[R];
-#pragma unroll
-            for (int i = 0; i < R; ++i) cur[i] = ring[j][i];
-            // unconditional (clamped) refill: straight-line loads keep the
-            // load-counter waits exact
-            load_units<F, R>(rowp, unit0, u + LPR * D, U, ring[j]);
-            if (t < T) unit_math<F, BMAX, R>(L, cur, unit0 + uc, uc, valid, magic, acc);
-        }
-    }
-}
-
-template <class F, int R, int D>
-__device__ __forceinline__ void prefetch_ring(const uint8_t* const rowp[R], int unit0, int v, int LPR, int U,
-                                              typename F::Raw ring[D][R]) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) load_units<F, R>(rowp, unit0, v + LPR * j, U, ring[j]);
 }
 
 // Sum acc over the LPR lanes of each group (lanes differ only in the low bits).
-template <int BMAX, int R>
-__device__ __forceinline__ void reduce_group(float acc[R][BMAX], int LPR) {
+template <int BMAX>
+__device__ __forceinline__ void reduce_group(float acc[BMAX], int LPR) {
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int b = 0; b < BMAX; ++b)
-            for (int off = LPR >> 1; off > 0; off >>= 1) acc[i][b] += __shfl_xor(acc[i][b], off);
+    for (int b = 0; b < BMAX; ++b)
+        for (int off = LPR >> 1; off > 0; off >>= 1) acc[b] += __shfl_xor(acc[b], off);
 }
 
 // Output rows of the vectors: y_b[n] = p[b][n].  Wave-uniform.
@@ -524,90 +502,134 @@ struct YDst {
     float* p[8];
 };
 
-// The whole decode product for one workgroup: rows [rowA, rowA + waves*R*SR)
+// The whole decode product for one workgroup: rows [rowA, rowA + waves * SR)
 // of the packed matrix W (N rows, K inputs) against nb <= BMAX staged vectors.
-template <int TYPE, int XT, int BMAX, int R, int D>
+//
+// Each K tile of U units gives every lane T = ceil(U / LPR) units.  Without
+// RING, T <= D and all of them are loaded at once before the activations are
+// staged (units past the tile load as zeros).  With RING a ring keeps D units
+// per lane in flight, the load of unit t + D issued as unit t is taken.
+template <int TYPE, int XT, int BMAX, int D, bool RING>
 __device__ __forceinline__ void gemv_workgroup(const uint8_t* __restrict__ W, int64_t N, int64_t K, int64_t rowA,
                                                const XSrc& xs, int nb, const YDst& yd, int LPR, int tile_units,
                                                uint8_t* lds) {
     using F = Fmt<TYPE>;
+    using Raw = typename F::Raw;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int SR = 64 / LPR;
     const int s = lane / LPR, v = lane - s * LPR;
-    const int64_t row_bytes = (K / F::QK) * F::BB;
-    const int64_t row0 = rowA + (int64_t)wave * R * SR + s;
+    const uint32_t row_bytes = (uint32_t)((K / F::QK) * F::BB);
+    const int64_t wg_rows = (int64_t)(blockDim.x >> 6) * SR;
+    const int64_t rows_here = N - rowA < wg_rows ? N - rowA : wg_rows;
+    const Rsrc rs = make_rsrc(W + rowA * (int64_t)row_bytes, (uint32_t)rows_here * row_bytes);
+    const int rloc = wave * SR + s;
+    const bool row_ok = rloc < rows_here;
+    const typename F::Lane ln(v % F::UPB);
+    // byte offset of the block of unit (u0 + v + LPR t) is blk0 + t * step
+    const uint32_t row_off = (uint32_t)rloc * row_bytes;
+    const uint32_t step = (uint32_t)(LPR / F::UPB) * F::BB;
+    const uint32_t magic = magic_vgpr();
 
-    const uint8_t* rowp[R];
+    float acc[BMAX];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        int64_t r = row0 + (int64_t)i * SR;
-        rowp[i] = W + (r < N ? r : N - 1) * row_bytes;
-    }
-    float acc[R][BMAX];
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int b = 0; b < BMAX; ++b) acc[i][b] = 0.f;
+    for (int b = 0; b < BMAX; ++b) acc[b] = 0.f;
 
     const int64_t units = K / F::UW;
     for (int64_t u0 = 0; u0 < units; u0 += tile_units) {
-        int U = (int)((units - u0) < tile_units ? (units - u0) : tile_units);
+        const int U = (int)((units - u0) < tile_units ? (units - u0) : tile_units);
+        const int T = (U + LPR - 1) / LPR;
+        const uint32_t blk0 = row_off + (uint32_t)((u0 + v) / F::UPB) * F::BB;
+        auto off_of = [&](int t) -> uint32_t {
+            return (row_ok && v + LPR * t < U) ? blk0 + (uint32_t)t * step : OOB;
+        };
         TileLds<F> L;
         L.carve(lds, U, nb);
-        // activation loads first, then the first D units of weights, so the
-        // staging arithmetic overlaps the weight stream
+        // activation loads first, then the weights, so the staging arithmetic
+        // overlaps the weight stream
         XRaw<XT> xin;
         stage_issue<F, XT>(xs, u0 * F::UW, L, xin);
         __builtin_amdgcn_sched_barrier(0);
-        typename F::Raw ring[D][R];
-        prefetch_ring<F, R, D>(rowp, (int)u0, v, LPR, U, ring);
+        Raw ring[D];
+#pragma unroll
+        for (int t = 0; t < D; ++t) ring[t] = F::load(rs, off_of(t), ln);
         __builtin_amdgcn_sched_barrier(0);
         stage_finish<F, XT>(xs, u0 * F::UW, L, xin);
-        compute_tile<F, BMAX, R, D>(L, rowp, (int)u0, v, LPR, ring, acc);
+        if constexpr (!RING) {
+#pragma unroll
+            for (int t = 0; t < D; ++t) {
+                if (t < T) {
+                    const int u = v + LPR * t;
+                    unit_math<F, BMAX>(L, ring[t], ln, u < U ? u : U - 1, u < U, magic, acc);
+                }
+            }
+        } else {
+            for (int t0 = 0; t0 < T; t0 += D) {
+#pragma unroll
+                for (int j = 0; j < D; ++j) {
+                    const int t = t0 + j;
+                    const Raw cur = ring[j];
+                    // unconditional refill (zeros past the tile): straight-line
+                    // loads keep the load-counter waits exact
+                    ring[j] = F::load(rs, off_of(t + D), ln);
+                    if (t < T) {
+                        const int u = v + LPR * t;
+                        unit_math<F, BMAX>(L, cur, ln, u < U ? u : U - 1, u < U, magic, acc);
+                    }
+                }
+            }
+            // the last D refills were zero loads past the tile: drain them so
+            // that no load is pending into these registers at the next tile
+            wait_loads();
+        }
         lds_barrier();
     }
-    reduce_group<BMAX, R>(acc, LPR);
-    if (v == 0) {
+    reduce_group<BMAX>(acc, LPR);
+    if (v == 0 && row_ok) {
+        const int64_t r = rowA + rloc;
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            int64_t r = row0 + (int64_t)i * SR;
-            if (r < N) {
-#pragma unroll
-                for (int b = 0; b < BMAX; ++b)
-                    if (b < nb) yd.p[b][r] = acc[i][b];
-            }
-        }
+        for (int b = 0; b < BMAX; ++b)
+            if (b < nb) yd.p[b][r] = acc[b];
     }
 }
 
 // LDS budget per workgroup for staged activations.
 constexpr int LDS_BUDGET = 48 * 1024;
+// Most units per lane loaded at once (larger K tiles use the ring).
+constexpr int D_MAX = 6;
+constexpr int D_RING = 4;
 
 // ------------------------------------------------------ launch plan ----
 
 struct Plan {
-    int LPR, R, WPW, tile_units;
+    int LPR, D, tile_units;
+    bool ring;
     int64_t grid;
     size_t lds;
 };
 
-// Lanes per row (LPR) depends only on K, and every K tile holds a multiple of
-// LPR units, so lane v of a row group always sums units v, v+LPR, v+2LPR, ...
-// in the same order whatever the batch size: each batch column is
-// bit-identical to a batch-1 product of the same vector.  (Rows per lane R and
-// waves per workgroup only decide which lane group owns a row.)
+// Lanes per row (LPR) depends only on N and K, and every K tile holds a
+// multiple of LPR units, so lane v of a row group always sums units v, v+LPR,
+// v+2LPR, ... in the same order whatever the batch size: each batch column is
+// bit-identical to a batch-1 product of the same vector.
+//
+// The choice: the fewest lanes per row (most rows per workgroup, so the
+// activation staging is shared by more rows) that still gives at least ~2048
+// wavefronts (8 per CU) and keeps >= 80% of the lanes busy; small matrices
+// take more lanes per row to spread their bytes over more wavefronts.
 template <class F>
-inline int lanes_per_row(int64_t units) {
-    // 32 at most: a tile of 32 units for 8 vectors still fits the LDS budget
-    int best = 32;
-    double best_u = -1;
-    for (int lpr = 32; lpr >= 8; lpr >>= 1) {
-        int64_t slots = ((units + lpr - 1) / lpr) * lpr;
-        double util = units ? (double)units / (double)slots : 1.0;
-        if (util >= 0.9) return lpr;
-        if (util > best_u + 1e-9) {
-            best_u = util;
+inline int lanes_per_row(int64_t N, int64_t units) {
+    int best = 0;
+    double best_u = -1.0;
+    for (int lpr = 8; lpr <= 32; lpr <<= 1) {
+        const int64_t slots = ((units + lpr - 1) / lpr) * lpr;
+        const double util = units ? (double)units / (double)slots : 1.0;
+        if (util >= 0.8 && N * lpr / 64 >= 2048) return lpr;
+        if (util >= 0.8) {  // the widest well-used choice so far
             best = lpr;
+            best_u = 2.0;
+        } else if (best_u < 0.8 && util > best_u) {
+            best = lpr;
+            best_u = util;
         }
     }
     return best;
@@ -616,35 +638,26 @@ inline int lanes_per_row(int64_t units) {
 template <class F>
 inline Plan plan_for(int64_t N, int64_t K, int nb) {
     Plan p;
-    int64_t units = K / F::UW;
-    p.LPR = lanes_per_row<F>(units);
-    const int SR = 64 / p.LPR;
+    const int64_t units = K / F::UW;
+    p.LPR = lanes_per_row<F>(N, units);
     // K tile: as many units as the LDS budget allows for nb vectors, rounded
     // down to a multiple of LPR (a multiple of 4 units = whole super-blocks)
-    size_t per_unit = (size_t)16 * TileLds<F>::unit_stride(nb);
-    int64_t step = p.LPR;
+    const size_t per_unit = (size_t)16 * TileLds<F>::unit_stride(nb);
+    const int64_t step = p.LPR;
     int64_t max_units = (int64_t)(LDS_BUDGET / per_unit) / step * step;
     if (max_units < step) max_units = step;
     if (units <= max_units) {
         p.tile_units = (int)(units > 0 ? units : 1);
     } else {
-        int64_t n_tiles = (units + max_units - 1) / max_units;
-        int64_t tu = (units + n_tiles - 1) / n_tiles;
+        const int64_t n_tiles = (units + max_units - 1) / max_units;
+        const int64_t tu = (units + n_tiles - 1) / n_tiles;
         p.tile_units = (int)((tu + step - 1) / step * step);
     }
-    // rows per lane group (R = 2 would let one LDS read of an activation serve
-    // two rows, but costs too many registers at present)
-    p.R = 1;
-    // waves per workgroup: the most (least staging per row) that still gives
-    // >= 512 workgroups (two per CU); for small N fewer rows per lane group
-    p.WPW = 1;
-    for (int w = 4; w >= 1; w >>= 1) {
-        if ((N + (int64_t)w * p.R * SR - 1) / ((int64_t)w * p.R * SR) >= 512) {
-            p.WPW = w;
-            break;
-        }
-    }
-    p.grid = (N + (int64_t)p.WPW * p.R * SR - 1) / ((int64_t)p.WPW * p.R * SR);
+    const int T = (p.tile_units + p.LPR - 1) / p.LPR;
+    p.ring = T > D_MAX;
+    p.D = p.ring ? D_RING : T;
+    const int SR = 64 / p.LPR;
+    p.grid = (N + 4 * (int64_t)SR - 1) / (4 * (int64_t)SR);
     p.lds = per_unit * p.tile_units;
     return p;
 }

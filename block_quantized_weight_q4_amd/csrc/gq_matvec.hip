@@ -1,11 +1,11 @@
 // gq_matvec.hip -- decode product y[b][n] = sum_k w[n][k] x[b][k] against
 // packed Q4_0 / Q4_K / Q6_K rows (gfx950).  The per-lane work is in
-// gq_gemv_core.h; this file maps workgroups to row tiles and K tiles.
+// gq_gemv_core.h; this file maps workgroups to row tiles and picks the kernel
+// variant (vectors per workgroup, units per lane in flight).
 //
-// Grid: one workgroup (1, 2 or 4 wavefronts) per tile of WPW * R * (64 / LPR)
-// consecutive rows.
+// Grid: one 4-wavefront workgroup per tile of 4 * (64 / LPR) consecutive rows.
 // The activations are staged tile by tile along K (each tile fits the LDS
-// budget; usually all of K is one tile), and the lane partial sums stay in
+// budget; at batch 1 all of K is one tile), and the lane partial sums stay in
 // registers across K tiles, so every packed byte is read exactly once.
 #include "gq_gemv_core.h"
 #include "gq_internal.h"
@@ -14,32 +14,39 @@ using namespace gqd;
 
 namespace {
 
-template <int TYPE, int XT, int BMAX, int R, int D>
+template <int TYPE, int XT, int BMAX, int D, bool RING>
 __global__ __launch_bounds__(NTHREADS) void k_matvec(const uint8_t* __restrict__ W, int64_t N, int64_t K,
                                                      XSrc xs, int nb, YDst yd, int LPR, int tile_units) {
     extern __shared__ __align__(16) uint8_t lds[];
-    const int SR = 64 / LPR;
-    const int64_t rpw = (int64_t)(blockDim.x >> 6) * R * SR;
-    gemv_workgroup<TYPE, XT, BMAX, R, D>(W, N, K, (int64_t)blockIdx.x * rpw, xs, nb, yd, LPR, tile_units, lds);
+    const int64_t rpw = (int64_t)(NTHREADS >> 6) * (64 / LPR);
+    gemv_workgroup<TYPE, XT, BMAX, D, RING>(W, N, K, (int64_t)blockIdx.x * rpw, xs, nb, yd, LPR, tile_units, lds);
 }
 
-template <int TYPE, int XT, int BMAX, int R>
-hipError_t launch_r(const Plan& p, const uint8_t* W, int64_t N, int64_t K, const XSrc& xs, int nb, float* y,
+template <int TYPE, int XT, int BMAX, int D, bool RING = false>
+hipError_t launch_d(const Plan& p, const uint8_t* W, int64_t N, int64_t K, const XSrc& xs, int nb, float* y,
                     hipStream_t s) {
-    constexpr int D = 4 / R;
     YDst yd;
     for (int b = 0; b < 8; ++b) yd.p[b] = y + (int64_t)(b < nb ? b : 0) * N;
-    hipLaunchKernelGGL((k_matvec<TYPE, XT, BMAX, R, D>), dim3((unsigned)p.grid), dim3(64 * p.WPW), p.lds, s, W, N, K, xs,
-                       nb, yd, p.LPR, p.tile_units);
+    hipLaunchKernelGGL((k_matvec<TYPE, XT, BMAX, D, RING>), dim3((unsigned)p.grid), dim3(NTHREADS), p.lds, s, W, N, K,
+                       xs, nb, yd, p.LPR, p.tile_units);
     return hipGetLastError();
 }
 
 template <int TYPE, int XT, int BMAX>
 hipError_t launch_b(const uint8_t* W, int64_t N, int64_t K, const XSrc& xs, int nb, float* y, hipStream_t s) {
     using F = Fmt<TYPE>;
-    Plan p = plan_for<F>(N, K, nb);
+    const Plan p = plan_for<F>(N, K, nb);
     if (p.grid > 0x7fffffff) return hipErrorInvalidValue;
-    return launch_r<TYPE, XT, BMAX, 1>(p, W, N, K, xs, nb, y, s);
+    if (p.ring) return launch_d<TYPE, XT, BMAX, D_RING, true>(p, W, N, K, xs, nb, y, s);
+    switch (p.D) {
+    case 1: return launch_d<TYPE, XT, BMAX, 1>(p, W, N, K, xs, nb, y, s);
+    case 2: return launch_d<TYPE, XT, BMAX, 2>(p, W, N, K, xs, nb, y, s);
+    case 3: return launch_d<TYPE, XT, BMAX, 3>(p, W, N, K, xs, nb, y, s);
+    case 4: return launch_d<TYPE, XT, BMAX, 4>(p, W, N, K, xs, nb, y, s);
+    case 5: return launch_d<TYPE, XT, BMAX, 5>(p, W, N, K, xs, nb, y, s);
+    case 6: return launch_d<TYPE, XT, BMAX, 6>(p, W, N, K, xs, nb, y, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int TYPE, int XT>

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void k_group(const int32_t* __restrict__ ids, 
 }
 
 // ------------------------------------------------------------- product ----
-template <int TYPE, int XT>
+template <int TYPE, int XT, int D, bool RING>
 __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict__ experts, int64_t expert_bytes,
                                                       int64_t N, int64_t K, const uint8_t* __restrict__ x,
                                                       int x_per_slot, int top_k, const uint8_t* __restrict__ ws,
@@ -142,9 +142,8 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
         xs.p[b] = x + xrow * K * esz;
         yd.p[b] = out + (int64_t)slot * N;
     }
-    const int SR = 64 / LPR;
-    const int64_t rpw = (int64_t)(blockDim.x >> 6) * SR;
-    gemv_workgroup<TYPE, XT, CH, 1, 4>(experts + (int64_t)grp.expert * expert_bytes, N, K,
+    const int64_t rpw = (int64_t)(NTHREADS >> 6) * (64 / LPR);
+    gemv_workgroup<TYPE, XT, CH, D, RING>(experts + (int64_t)grp.expert * expert_bytes, N, K,
                                        (int64_t)blockIdx.y * rpw, xs, grp.count, yd, LPR, tile_units, lds);
 }
 
@@ -173,20 +172,34 @@ __global__ __launch_bounds__(256) void k_zero_bad(const int32_t* __restrict__ id
     if (n < N) y[(int64_t)s * N + n] = 0.f;
 }
 
+template <int TYPE, int XT, int D, bool RING = false>
+hipError_t launch_experts_d(const Plan& p, const WsLayout& L, const uint8_t* experts, int64_t N, int64_t K,
+                            const uint8_t* x, int x_per_slot, int top_k, const uint8_t* ws, float* out,
+                            hipStream_t s) {
+    using F = Fmt<TYPE>;
+    const int64_t expert_bytes = N * (K / F::QK) * F::BB;
+    hipLaunchKernelGGL((k_experts<TYPE, XT, D, RING>), dim3((unsigned)L.Gmax, (unsigned)p.grid), dim3(NTHREADS),
+                       p.lds, s, experts, expert_bytes, N, K, x, x_per_slot, top_k, ws, (int)L.off_groups,
+                       (int)L.off_sorted, out, p.LPR, p.tile_units);
+    return hipGetLastError();
+}
+
 template <int TYPE, int XT>
 hipError_t launch_experts(const WsLayout& L, const uint8_t* experts, int64_t N, int64_t K, const uint8_t* x,
                           int x_per_slot, int top_k, const uint8_t* ws, float* out, hipStream_t s) {
     using F = Fmt<TYPE>;
-    Plan p = plan_for<F>(N, K, CH);
-    const int SR = 64 / p.LPR;
-    const int64_t rpw = 4 * (int64_t)SR;
-    const int64_t tiles = (N + rpw - 1) / rpw;
-    if (tiles > 65535) return hipErrorInvalidValue;
-    const int64_t expert_bytes = N * (K / F::QK) * F::BB;
-    hipLaunchKernelGGL((k_experts<TYPE, XT>), dim3((unsigned)L.Gmax, (unsigned)tiles), dim3(NTHREADS), p.lds, s,
-                       experts, expert_bytes, N, K, x, x_per_slot, top_k, ws, (int)L.off_groups,
-                       (int)L.off_sorted, out, p.LPR, p.tile_units);
-    return hipGetLastError();
+    const Plan p = plan_for<F>(N, K, CH);
+    if (p.grid > 65535) return hipErrorInvalidValue;
+    if (p.ring) return launch_experts_d<TYPE, XT, D_RING, true>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
+    switch (p.D) {
+    case 1: return launch_experts_d<TYPE, XT, 1>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
+    case 2: return launch_experts_d<TYPE, XT, 2>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
+    case 3: return launch_experts_d<TYPE, XT, 3>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
+    case 4: return launch_experts_d<TYPE, XT, 4>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
+    case 5: return launch_experts_d<TYPE, XT, 5>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
+    case 6: return launch_experts_d<TYPE, XT, 6>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int TYPE>

@@ -101,11 +101,15 @@ gq_status gq_dequant(gq_type t, const void* blocks, int64_t n_blocks, void* out,
  *   y[b][n] = sum_k w[n][k] * x[b][k],  0 <= b < batch, 0 <= n < N.
  * W: packed [N][K/QK] blocks of type t.  x: [batch][K] of x_dtype (GQ_F32 or
  * GQ_BF16).  y: [batch][N] fp32.  1 <= batch <= 8 (GQ_ERR_UNSUPPORTED above).
- * K must be a multiple of QK.  N == 0 is a no-op; K == 0 writes zeros.
- * Accuracy: every y element is within 1e-3 * sum_k |w[n][k] * x[b][k]| of the
- * exact product (fp32 accumulation of per-sub-block partial sums; activations
- * enter the dot instructions as fp16 after an exact power-of-two scaling per
- * 32 inputs). */
+ * K must be a multiple of QK and at most 4,194,304 (GQ_ERR_SHAPE otherwise).
+ * N == 0 is a no-op; K == 0 writes zeros.
+ * Accuracy: activations enter the dot instructions as fp16 after an exact
+ * power-of-two scaling per 32 inputs (relative rounding <= 2^-11), weights as
+ * the exact fp16 values 1024 + q, and sums are fp32.  The result is within
+ * 1e-3 * sum_k |w[n][k] * x[b][k]| of the exact product unless that sum is
+ * tiny next to the magnitudes the fp32 sums carry (d * sc * 1024 * sum |x| per
+ * sub-block), e.g. rows whose quants nearly all sit at the zero point; a
+ * sub-block whose quants all equal the zero point contributes exactly zero. */
 gq_status gq_matvec(gq_type t, const void* W, int64_t N, int64_t K, const void* x,
                     gq_dtype x_dtype, int32_t batch, float* y, hipStream_t stream);
 
@@ -130,7 +134,7 @@ gq_status gq_matvec_id_workspace(int32_t n_experts, int32_t n_tokens, int32_t to
  * bytes; its contents need no initialisation.  An id outside [0, n_experts)
  * makes its slot contribute zero and is counted in ws (see
  * gq_matvec_id_check).  1 <= top_k <= n_experts, n_tokens * top_k <= 1024,
- * x_dtype GQ_F32 or GQ_BF16.  Accuracy as gq_matvec (for route_w != NULL the
+ * x_dtype GQ_F32 or GQ_BF16, K limited as for gq_matvec.  Accuracy as gq_matvec (for route_w != NULL the
  * bound is 1e-3 * sum_j |route_w[t][j]| * sum_k |w * x|). */
 gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_t N, int64_t K,
                        const int32_t* ids, int32_t n_tokens, int32_t top_k, const void* x,

@@ -93,6 +93,7 @@ def test_matvec_validation(lib):
     assert mv(2, A, 8, 256, A, 0, 1, MIS, None) == GQ_ERR_ALIGN
     assert mv(2, A, 0, 256, A, 0, 1, A, None) == GQ_OK  # N == 0: no-op
     assert mv(3, A, 1 << 41, 256, A, 0, 1, A, None) == GQ_ERR_SHAPE  # size guard
+    assert mv(2, A, 8, (1 << 22) + 256, A, 0, 1, A, None) == GQ_ERR_SHAPE  # longest decode row
 
 
 def test_matvec_id_validation(lib):
@@ -117,6 +118,7 @@ def test_matvec_id_validation(lib):
     assert call(t=5) == GQ_ERR_TYPE
     assert call(xd=2) == GQ_ERR_DTYPE
     assert call(K=2817) == GQ_ERR_SHAPE
+    assert call(K=(1 << 22) + 32) == GQ_ERR_SHAPE
     assert call(k=129) == GQ_ERR_SHAPE
     assert call(E=0) == GQ_ERR_SHAPE
     assert call(per=2) == GQ_ERR_SHAPE
