@@ -88,6 +88,16 @@ __device__ __forceinline__ float bf2f(uint16_t b) {
     return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
+// Barrier for LDS traffic only.  __syncthreads() is a full workgroup fence,
+// which on gfx950 also waits for every outstanding global load (vmcnt(0)) --
+// a kernel that keeps global loads in flight across a barrier would stall on
+// them.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8 * i)) & 0xffu; }
 
 }  // namespace gqd

@@ -342,15 +342,6 @@ struct TileLds {
     __device__ u32x4* rec(int u, int b) const { return base + u * RS + b * NREC; }
 };
 
-// Barrier for LDS traffic only.  __syncthreads() is a full workgroup fence,
-// which on gfx950 also waits for every outstanding global load (vmcnt(0)) --
-// here that would stall on the weight loads already in flight.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // One run (16 or 32 consecutive inputs starting at group element `off`) of an
 // already-scaled group -> fp16 pairs in unpack order, its zero-point
 // correction, and its factors.
@@ -502,13 +493,20 @@ struct YDst {
     float* p[8];
 };
 
+// Most units per lane in one straight-line pass (larger K tiles use the ring),
+// and how many of them are in flight before the first is taken.
+constexpr int D_MAX = 6;
+constexpr int PREFETCH = 3;
+constexpr int D_RING = 4;
+
 // The whole decode product for one workgroup: rows [rowA, rowA + waves * SR)
 // of the packed matrix W (N rows, K inputs) against nb <= BMAX staged vectors.
 //
 // Each K tile of U units gives every lane T = ceil(U / LPR) units.  Without
-// RING, T <= D and all of them are loaded at once before the activations are
-// staged (units past the tile load as zeros).  With RING a ring keeps D units
-// per lane in flight, the load of unit t + D issued as unit t is taken.
+// RING, T <= D: the loads of the first min(D, PREFETCH) units are issued
+// around the activation staging and each later one as an earlier unit is
+// taken, all in straight-line code (units past the tile load as zeros).  With
+// RING a ring keeps D units per lane in flight over any number of units.
 template <int TYPE, int XT, int BMAX, int D, bool RING>
 __device__ __forceinline__ void gemv_workgroup(const uint8_t* __restrict__ W, int64_t N, int64_t K, int64_t rowA,
                                                const XSrc& xs, int nb, const YDst& yd, int LPR, int tile_units,
@@ -549,14 +547,20 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t* __restrict__ W, in
         XRaw<XT> xin;
         stage_issue<F, XT>(xs, u0 * F::UW, L, xin);
         __builtin_amdgcn_sched_barrier(0);
+        constexpr int P = RING ? D : (D < PREFETCH ? D : PREFETCH);
+        // one unit's loads go out before the staging waits for the
+        // activations (later loads would only queue ahead of them), the rest
+        // of the prefetch right after
         Raw ring[D];
-#pragma unroll
-        for (int t = 0; t < D; ++t) ring[t] = F::load(rs, off_of(t), ln);
+        ring[0] = F::load(rs, off_of(0), ln);
         __builtin_amdgcn_sched_barrier(0);
         stage_finish<F, XT>(xs, u0 * F::UW, L, xin);
+#pragma unroll
+        for (int t = 1; t < P; ++t) ring[t] = F::load(rs, off_of(t), ln);
         if constexpr (!RING) {
 #pragma unroll
             for (int t = 0; t < D; ++t) {
+                if (t + P < D) ring[t + P] = F::load(rs, off_of(t + P), ln);
                 if (t < T) {
                     const int u = v + LPR * t;
                     unit_math<F, BMAX>(L, ring[t], ln, u < U ? u : U - 1, u < U, magic, acc);
@@ -594,9 +598,6 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t* __restrict__ W, in
 
 // LDS budget per workgroup for staged activations.
 constexpr int LDS_BUDGET = 48 * 1024;
-// Most units per lane loaded at once (larger K tiles use the ring).
-constexpr int D_MAX = 6;
-constexpr int D_RING = 4;
 
 // ------------------------------------------------------ launch plan ----
 

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void k_matmul_q4k(const uint8_t* __restrict__ 
     if (n_stages > 0) load_stage(0, cur);
     for (int st = 0; st < n_stages; ++st) {
         store_stage(st, cur);
-        __syncthreads();
+        lds_barrier();
         if (st + 1 < n_stages) load_stage(st + 1, cur);
         const int r16 = lane & 15, kq = 8 * (lane >> 4);
 #pragma unroll
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void k_matmul_q4k(const uint8_t* __restrict__ 
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // C block (i, j): lane holds rows 4*(lane/16) + v (X rows), column lane%16 (W row)
