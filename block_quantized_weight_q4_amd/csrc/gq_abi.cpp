@@ -138,6 +138,9 @@ gq_status gq_matmul(gq_type t, const void* W, int64_t N, int64_t K, const void* 
     if (N > MAX_ELEMS || K > MAX_ELEMS || M > MAX_ELEMS || (M > 0 && ldx > MAX_ELEMS / M) ||
         (M > 0 && ldy > MAX_ELEMS / M) || (K > 0 && N > MAX_ELEMS / K))
         return GQ_ERR_SHAPE;
+    // the prefill kernel addresses 256 rows of X or W through one buffer
+    // resource whose span must stay below 2^31 bytes
+    if (K > MAX_K_DECODE || ldx >= MAX_K_DECODE) return GQ_ERR_SHAPE;
     if (t != GQ_Q4_K || x_dtype != GQ_BF16) return GQ_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return GQ_OK;
     if (!Y || (K > 0 && (!W || !X))) return GQ_ERR_NULL;

@@ -7,18 +7,23 @@
 // matrix engine then multiplies); here both happen in one kernel, the weight
 // tile being expanded to bf16 in LDS right before the MFMAs read it.
 //
-// Tiling.  A workgroup (4 wavefronts) owns a BM x BN = 256 x 128 tile of Y; a
-// wavefront owns 128 x 64 of it as 8 x 4 blocks of v_mfma_f32_16x16x32_bf16
-// (fp32 accumulators).  K advances in stages of BK = 64 inputs = one 32-byte
-// slice of quants of every Q4_K super-block row (sub-blocks 2c and 2c+1).  Per
-// stage each thread
-//   * loads 128 bytes of one X row (bf16) and 16 quant bytes + the 16-byte
-//     header of one W row, for the NEXT stage, into registers, while
-//   * the MFMAs consume the current stage from LDS;
-// then the registers are written to LDS -- X as is, W expanded to bf16 with
-// w = (d * sc) * q - dmin * m in fp32, rounded to nearest even.
-// Rows of X past M are zero; W rows past N are clamped to row N-1 and their
-// outputs are never stored.
+// Tiling.  A workgroup (4 wavefronts, one per SIMD) owns a BM x BN = 256 x 256
+// tile of Y; wavefront (wm, wn) owns the 128 x 128 quarter, as 4 x 4 blocks
+// of v_mfma_f32_32x32x16_bf16 (fp32 accumulators in the AGPRs).  K advances in
+// stages of BK = 64 inputs = one 32-byte slice of quants of every Q4_K
+// super-block row (sub-blocks 2c and 2c+1).
+//
+// Pipeline.  LDS holds two stage buffers.  While the MFMAs of stage s read
+// buffer s & 1, the same wavefronts write stage s+1 -- its X rows as loaded and
+// its W rows expanded to bf16 with w = (d * sc) * q - dmin * m in fp32, one
+// rounding to nearest even -- into the other buffer, in four slices placed
+// between the four 16-deep k steps; then they issue the global loads of stage
+// s+3 into the registers just freed (two register sets alternate, so a load
+// has more than a stage of MFMA work to arrive).  One LDS-only barrier per
+// stage.
+//
+// Rows of X past M and of W past N are read as zeros (buffer loads beyond
+// the resource's span); their outputs are never stored.
 #include "gq_device.h"
 #include "gq_internal.h"
 
@@ -27,143 +32,209 @@ using namespace gqd;
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 128, BK = 64;
-constexpr int LDX = BK + 8;  // bf16 per LDS row (+16 B pad: conflict-free b128 reads)
-constexpr int LDS_X = BM * LDX * 2, LDS_W = BN * LDX * 2;
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int LDX = BK + 8;                   // bf16 per LDS row (+16 B pad: conflict-free b128 reads)
+constexpr int ROWB = LDX * 2;                 // bytes per LDS row
+constexpr int BUF = (BM + BN) * ROWB;         // one stage buffer: X rows then W rows
+constexpr int LDS_BYTES = 2 * BUF;            // 147,456 B
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bld16(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// Global data of one stage for this thread: eight 16-byte chunks of X (one
+// from each of eight rows 32 apart), the 16-byte header and the 32-byte
+// quant slice of its W row.
+struct StageRegs {
+    u32x4 x[8];
+    u32x4 h, q0, q1;
+};
+
+// The (d*sc, dmin*m) pairs of sub-blocks 2c and 2c+1 (c uniform).
+struct Scales {
+    float dsL, dmL, dsH, dmH;
+};
+
+// Selects rather than branches: the decode sits in the same scheduling region
+// as the MFMAs it is interleaved with.
+__device__ __forceinline__ Scales q4k_scales(u32x4 hdr, int c) {
+    const float d = h2f(hdr.x & 0xffffu), dmin = h2f(hdr.x >> 16);
+    const int sh = 16 * (c & 1);
+    const uint32_t b0 = hdr.y >> sh, b1 = hdr.z >> sh, b2 = hdr.w >> sh;
+    const bool low = c < 2;
+    const uint32_t scL = low ? (b0 & 63u) : ((b2 & 15u) | (((b0 >> 6) & 3u) << 4));
+    const uint32_t mL = low ? (b1 & 63u) : (((b2 >> 4) & 15u) | (((b1 >> 6) & 3u) << 4));
+    const uint32_t scH = low ? ((b0 >> 8) & 63u) : (((b2 >> 8) & 15u) | (((b0 >> 14) & 3u) << 4));
+    const uint32_t mH = low ? ((b1 >> 8) & 63u) : (((b2 >> 12) & 15u) | (((b1 >> 14) & 3u) << 4));
+    return Scales{d * (float)scL, dmin * (float)mL, d * (float)scH, dmin * (float)mH};
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }
 
-// (scale, min) of sub-block s from the 12 scale bytes (hdr.y, hdr.z, hdr.w)
-__device__ __forceinline__ void q4k_sm(u32x4 hdr, int s, float d, float dmin, float& ds, float& dm) {
-    int j = s & 3;
-    uint32_t b0 = (hdr.y >> (8 * j)) & 0xffu, b1 = (hdr.z >> (8 * j)) & 0xffu, b2 = (hdr.w >> (8 * j)) & 0xffu;
-    uint32_t sc, m;
-    if (s < 4) {
-        sc = b0 & 63u;
-        m = b1 & 63u;
-    } else {
-        sc = (b2 & 15u) | ((b0 >> 6) << 4);
-        m = (b2 >> 4) | ((b1 >> 6) << 4);
+// Expand quant bytes 8j..8j+7 of the slice (dwords w0, w1): low nibbles are
+// k = 8j..8j+7, high nibbles k = 32+8j..32+8j+7 -> two 16-byte rows of bf16.
+__device__ __forceinline__ void expand8(uint32_t w0, uint32_t w1, const Scales& s, u32x4& lo, u32x4& hi) {
+    const uint32_t l0 = w0 & 0x0F0F0F0Fu, l1 = w1 & 0x0F0F0F0Fu;
+    const uint32_t h0 = (w0 >> 4) & 0x0F0F0F0Fu, h1 = (w1 >> 4) & 0x0F0F0F0Fu;
+    float a[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = (float)((l0 >> (8 * i)) & 0xffu);
+        a[4 + i] = (float)((l1 >> (8 * i)) & 0xffu);
+        b[i] = (float)((h0 >> (8 * i)) & 0xffu);
+        b[4 + i] = (float)((h1 >> (8 * i)) & 0xffu);
     }
-    ds = d * (float)sc;
-    dm = dmin * (float)m;
-}
-
-struct StageRegs {
-    u32x4 x[8];     // 128 B of one X row (64 bf16)
-    u32x4 q, hdr;   // 16 quant bytes and the header of one W row
-};
-
-__global__ __launch_bounds__(256) void k_matmul_q4k(const uint8_t* __restrict__ W, int64_t N, int64_t K,
-                                                    const uint16_t* __restrict__ X, int64_t M, int64_t ldx,
-                                                    float* __restrict__ Y, int64_t ldy) {
-    extern __shared__ __align__(16) uint8_t lds[];
-    uint16_t* Xs = reinterpret_cast<uint16_t*>(lds);
-    uint16_t* Ws = reinterpret_cast<uint16_t*>(lds + LDS_X);
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t row_bytes = (K / 256) * 144;
-
-    // this thread's X row (one of 256) and W row / half (128 rows x 2 halves)
-    const int64_t xm = m0 + tid;
-    const bool x_ok = xm < M;
-    const uint16_t* xrow = X + (x_ok ? xm : 0) * ldx;
-    const int wr = tid >> 1, wh = tid & 1;
-    const int64_t wnr = n0 + wr < N ? n0 + wr : N - 1;
-    const uint8_t* wrow = W + wnr * row_bytes;
-
-    auto load_stage = [&](int st, StageRegs& r) {
-        const int64_t k0 = (int64_t)st * BK;
-        const u32x4* xp = reinterpret_cast<const u32x4*>(xrow + k0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r.x[i] = x_ok ? xp[i] : u32x4{0, 0, 0, 0};
-        const uint8_t* bp = wrow + (k0 >> 8) * 144;
-        const int c = (int)((k0 >> 6) & 3);
-        r.hdr = ld16a(bp);
-        r.q = ld16a(bp + 16 + 32 * c + 16 * wh);
-    };
-    auto store_stage = [&](int st, const StageRegs& r) {
-        u32x4* xd = reinterpret_cast<u32x4*>(Xs + tid * LDX);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xd[i] = r.x[i];
-        // expand 32 weights: low nibbles -> sub-block 2c (k 16*wh + t),
-        // high nibbles -> sub-block 2c+1 (k 32 + 16*wh + t)
-        const int c = (int)((((int64_t)st * BK) >> 6) & 3);
-        float d = h2f(r.hdr.x & 0xffffu), dmin = h2f(r.hdr.x >> 16);
-        float dsL, dmL, dsH, dmH;
-        q4k_sm(r.hdr, 2 * c, d, dmin, dsL, dmL);
-        q4k_sm(r.hdr, 2 * c + 1, d, dmin, dsH, dmH);
-        uint32_t lo[8], hi[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t w = r.q[i];
-            float ql[4], qh[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                uint32_t byte = (w >> (8 * b)) & 0xffu;
-                ql[b] = (float)(byte & 15u);
-                qh[b] = (float)(byte >> 4);
-            }
-            // w = (d*sc)*q - dmin*m: both products exact, one rounding
-            lo[2 * i] = pack_bf16x2(__builtin_fmaf(dsL, ql[0], -dmL), __builtin_fmaf(dsL, ql[1], -dmL));
-            lo[2 * i + 1] = pack_bf16x2(__builtin_fmaf(dsL, ql[2], -dmL), __builtin_fmaf(dsL, ql[3], -dmL));
-            hi[2 * i] = pack_bf16x2(__builtin_fmaf(dsH, qh[0], -dmH), __builtin_fmaf(dsH, qh[1], -dmH));
-            hi[2 * i + 1] = pack_bf16x2(__builtin_fmaf(dsH, qh[2], -dmH), __builtin_fmaf(dsH, qh[3], -dmH));
-        }
-        uint16_t* wd = Ws + wr * LDX + 16 * wh;
-        reinterpret_cast<u32x4*>(wd)[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-        reinterpret_cast<u32x4*>(wd)[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
-        reinterpret_cast<u32x4*>(wd + 32)[0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        reinterpret_cast<u32x4*>(wd + 32)[1] = u32x4{hi[4], hi[5], hi[6], hi[7]};
-    };
-
-    f32x4v acc[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
-
-    const int n_stages = (int)(K / BK);
-    StageRegs cur;
-    if (n_stages > 0) load_stage(0, cur);
-    for (int st = 0; st < n_stages; ++st) {
-        store_stage(st, cur);
-        lds_barrier();
-        if (st + 1 < n_stages) load_stage(st + 1, cur);
-        const int r16 = lane & 15, kq = 8 * (lane >> 4);
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            bf16x8 a[8], b[4];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(Xs + (wm * 128 + 16 * i + r16) * LDX + kk + kq);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = *reinterpret_cast<const bf16x8*>(Ws + (wn * 64 + 16 * j + r16) * LDX + kk + kq);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        lds_barrier();
-    }
-
-    // C block (i, j): lane holds rows 4*(lane/16) + v (X rows), column lane%16 (W row)
+    // w = (d*sc) * q - dmin*m: both products exact in fp32, one rounding
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+        a[i] = __builtin_fmaf(s.dsL, a[i], -s.dmL);
+        b[i] = __builtin_fmaf(s.dsH, b[i], -s.dmH);
+    }
+    lo = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])};
+    hi = u32x4{pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]), pack_bf16x2(b[4], b[5]), pack_bf16x2(b[6], b[7])};
+}
+
+__global__ __launch_bounds__(256, 1) void k_matmul_q4k(const uint8_t* __restrict__ W, int64_t N, int64_t K,
+                                                       const uint16_t* __restrict__ X, int64_t M, int64_t ldx,
+                                                       float* __restrict__ Y, int64_t ldy) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
+    const uint32_t row_bytes = (uint32_t)((K / 256) * 144);
+    const int S = (int)(K / BK);
+
+    // X: thread tid stages 16-byte chunk tid % 8 of rows tid / 8 + 32 i
+    // (i = 0..7): eight lanes cover one row's 128 bytes, so every load
+    // instruction reads whole cache lines.  W: thread tid stages row n0 + tid.
+    const int64_t rows_x = M - m0 < BM ? M - m0 : BM, rows_w = N - n0 < BN ? N - n0 : BN;
+    const Rsrc xr = make_rsrc(X + m0 * ldx, (uint32_t)(rows_x * ldx * 2));
+    const Rsrc wr = make_rsrc(W + n0 * (int64_t)row_bytes, (uint32_t)rows_w * row_bytes);
+    const int xrow = tid >> 3, xchunk = tid & 7;
+    const uint32_t xstride = (uint32_t)(32 * ldx * 2);
+    const uint32_t xoff = (uint32_t)xrow * (uint32_t)(ldx * 2) + 16 * xchunk, woff = (uint32_t)tid * row_bytes;
+
+    // a stage past the last loads zeros without touching memory (offset past
+    // the buffers), so every load is unconditional and the load-counter waits
+    // stay exact
+    auto load_stage = [&](int s, StageRegs& r) {
+        const bool ok = s < S;
+        const uint32_t xo = ok ? xoff + (uint32_t)s * (BK * 2) : 0x80000000u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r.x[i] = bld16(xr, ok ? xo + (uint32_t)i * xstride : xo);
+        const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * 144 : 0x80000000u;
+        r.h = bld16(wr, bo);
+        r.q0 = bld16(wr, bo + 16 + 32 * (s & 3));
+        r.q1 = bld16(wr, bo + 32 + 32 * (s & 3));
+    };
+    // slice j (0..3) of the stage's LDS writes: X chunks 2j, 2j+1 and W quant
+    // bytes 8j..8j+7 expanded to k = 8j..8j+7 and 32+8j..32+8j+7
+    auto store_slice = [&](int s, const StageRegs& r, const Scales& sc, int buf, int j) {
+        uint8_t* xs = lds + buf * BUF + xrow * ROWB + 16 * xchunk;
+        uint8_t* ws = lds + buf * BUF + BM * ROWB + tid * ROWB;
+        *reinterpret_cast<u32x4*>(xs + (2 * j) * 32 * ROWB) = r.x[2 * j];
+        *reinterpret_cast<u32x4*>(xs + (2 * j + 1) * 32 * ROWB) = r.x[2 * j + 1];
+        const u32x4 q = j < 2 ? r.q0 : r.q1;
+        u32x4 lo, hi;
+        expand8(q[2 * (j & 1)], q[2 * (j & 1) + 1], sc, lo, hi);
+        reinterpret_cast<u32x4*>(ws)[j] = lo;
+        reinterpret_cast<u32x4*>(ws + 64)[j] = hi;
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+    // fragment addresses: A (X rows) lane l -> row 32*mi + l%32, k 8*(l/32);
+    // B (W rows) lane l -> row 32*ni + l%32, same k
+    const int fr = lane & 31, fk = 8 * (lane >> 5);
+    const uint32_t a_base = (uint32_t)((wm * 128 + fr) * ROWB + fk * 2);
+    const uint32_t b_base = (uint32_t)(BM * ROWB + (wn * 128 + fr) * ROWB + fk * 2);
+
+    // stage s's global data lives in register set s & 1; it is loaded two
+    // stages before its LDS writes, which happen during stage s-1's MFMAs
+    auto stage_body = [&](int s, StageRegs& nxt) {
+        const int cur = s & 1;
+        const uint8_t* buf = lds + cur * BUF;
+        // stage s+1's data arrived during the previous stage; past the last
+        // stage it is zeros, written to a buffer nobody reads
+        const Scales sc = q4k_scales(nxt.h, (s + 1) & 3);
+        bf16x8 a[2][4], b[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[0][i] = *reinterpret_cast<const bf16x8*>(buf + a_base + i * 32 * ROWB);
+            b[0][i] = *reinterpret_cast<const bf16x8*>(buf + b_base + i * 32 * ROWB);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int p = ks & 1;
+            if (ks < 3) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a[p ^ 1][i] = *reinterpret_cast<const bf16x8*>(buf + a_base + i * 32 * ROWB + (ks + 1) * 32);
+                    b[p ^ 1][i] = *reinterpret_cast<const bf16x8*>(buf + b_base + i * 32 * ROWB + (ks + 1) * 32);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[p][i], b[p][j], acc[i][j], 0, 0, 0);
+            store_slice(s + 1, nxt, sc, cur ^ 1, ks);
+            // one k step = one scheduling region: each MFMA is followed by a
+            // few VALU instructions of the expansion and the LDS traffic, so
+            // they issue while the matrix core is busy
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                if (ks < 3 && i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+                if ((i & 3) == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        load_stage(s + 3, nxt);
+        lds_barrier();
+    };
+
+    // S is a multiple of 4 (K is whole super-blocks)
+    StageRegs r0, r1;
+    if (S > 0) {
+        load_stage(0, r0);
+        load_stage(1, r1);
+        const Scales sc0 = q4k_scales(r0.h, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store_slice(0, r0, sc0, 0, j);
+        load_stage(2, r0);
+        lds_barrier();
+    }
+    for (int s = 0; s < S; s += 2) {
+        stage_body(s, r1);      // writes stage s+1 (set 1), then loads s+3 into set 1
+        stage_body(s + 1, r0);  // writes stage s+2 (set 0), then loads s+4 into set 0
+    }
+
+    // C block (i, j): lane holds W row 32*j + lane%32 (column of Y) and X rows
+    // 32*i + 8*(r/4) + 4*(lane/32) + r%4 for register r
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + wn * 64 + 16 * j + (lane & 15);
+            const int64_t n = n0 + wn * 128 + 32 * j + (lane & 31);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t m = m0 + wm * 128 + 16 * i + 4 * (lane >> 4) + v;
-                if (m < M && n < N) Y[m * ldy + n] = acc[i][j][v];
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (m < M && n < N) Y[m * ldy + n] = acc[i][j][r];
             }
         }
     }
@@ -177,8 +248,11 @@ hipError_t gqk_matmul(int type, const void* W, int64_t N, int64_t K, const void*
     (void)x_dtype;  // validated by the ABI: Q4_K weights, bf16 activations
     const int64_t gn = (N + BN - 1) / BN, gm = (M + BM - 1) / BM;
     if (gn > 0x7fffffff || gm > 65535) return hipErrorInvalidValue;
-    const size_t lds = (size_t)LDS_X + LDS_W;
-    hipLaunchKernelGGL(k_matmul_q4k, dim3((unsigned)gn, (unsigned)gm), dim3(256), lds, s,
+    // LDS above the default per-workgroup size (gfx950 allows 160 KB)
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul_q4k),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_matmul_q4k, dim3((unsigned)gn, (unsigned)gm), dim3(256), LDS_BYTES, s,
                        static_cast<const uint8_t*>(W), N, K, static_cast<const uint16_t*>(X), M, ldx, Y, ldy);
     return hipGetLastError();
 }
