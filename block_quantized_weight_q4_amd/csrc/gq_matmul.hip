@@ -76,15 +76,22 @@ __device__ __forceinline__ Scales q4k_scales(u32x4 hdr, int c) {
     return Scales{d * (float)scL, dmin * (float)mL, d * (float)scH, dmin * (float)mH};
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Expand quant bytes 8j..8j+7 of the slice (dwords w0, w1): low nibbles are
 // k = 8j..8j+7, high nibbles k = 32+8j..32+8j+7 -> two 16-byte rows of bf16.
 __device__ __forceinline__ void expand8(uint32_t w0, uint32_t w1, const Scales& s, u32x4& lo, u32x4& hi) {
-    const uint32_t l0 = w0 & 0x0F0F0F0Fu, l1 = w1 & 0x0F0F0F0Fu;
-    const uint32_t h0 = (w0 >> 4) & 0x0F0F0F0Fu, h1 = (w1 >> 4) & 0x0F0F0F0Fu;
+    uint32_t l0 = w0 & 0x0F0F0F0Fu, l1 = w1 & 0x0F0F0F0Fu;
+    uint32_t h0 = (w0 >> 4) & 0x0F0F0F0Fu, h1 = (w1 >> 4) & 0x0F0F0F0Fu;
+    // hide the known-zero bits: otherwise each byte is first extracted with a
+    // bit-field instruction instead of being converted by v_cvt_f32_ubyteN
+    __asm__("" : "+v"(l0), "+v"(l1), "+v"(h0), "+v"(h1));
     float a[8], b[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
