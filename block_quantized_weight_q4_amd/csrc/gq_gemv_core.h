@@ -618,10 +618,10 @@ struct Plan {
 // wavefronts (8 per CU) and keeps >= 80% of the lanes busy; small matrices
 // take more lanes per row to spread their bytes over more wavefronts.
 template <class F>
-inline int lanes_per_row(int64_t N, int64_t units) {
+inline int lanes_per_row(int64_t N, int64_t units, int min_lpr = 8) {
     int best = 0;
     double best_u = -1.0;
-    for (int lpr = 8; lpr <= 32; lpr <<= 1) {
+    for (int lpr = min_lpr; lpr <= 32; lpr <<= 1) {
         const int64_t slots = ((units + lpr - 1) / lpr) * lpr;
         const double util = units ? (double)units / (double)slots : 1.0;
         if (util >= 0.8 && N * lpr / 64 >= 2048) return lpr;
@@ -637,10 +637,14 @@ inline int lanes_per_row(int64_t N, int64_t units) {
 }
 
 template <class F>
-inline Plan plan_for(int64_t N, int64_t K, int nb) {
+inline Plan plan_for(int64_t N, int64_t K, int nb, int64_t rows_in_flight = -1, int min_lpr = 8) {
+    // rows_in_flight: rows of all products sharing the launch (several
+    // experts' matrices in a routed product), which decides the lanes per row;
+    // min_lpr 4 lets such a launch give a workgroup 64 rows, which spreads its
+    // fixed costs (the grouping, the activation staging) over more rows
     Plan p;
     const int64_t units = K / F::UW;
-    p.LPR = lanes_per_row<F>(N, units);
+    p.LPR = lanes_per_row<F>(rows_in_flight > 0 ? rows_in_flight : N, units, min_lpr);
     // K tile: as many units as the LDS budget allows for nb vectors, rounded
     // down to a multiple of LPR (a multiple of 4 units = whole super-blocks)
     const size_t per_unit = (size_t)16 * TileLds<F>::unit_stride(nb);

@@ -4,18 +4,21 @@
 // the routed 4-bit experts of the Architecture section of "Show HN: Gemma 4
 // 26B-A4B at up to 100+ tokens/s on a 16 GB Mac").
 //
-// Three launches on the caller's stream, no host synchronisation:
-//  1. k_group (one workgroup): rank-sorts the slots s = t*top_k + j by
-//     (expert id, s) on the device and cuts each expert's run of slots into
-//     groups of at most CH; ids outside [0, n_experts) are counted and left out.
-//  2. k_experts: one workgroup per (group, row tile) runs the shared decode
-//     product on that expert's rows with the group's activation vectors
-//     (gathered by slot), writing one output row per slot.  Workgroups whose
-//     group index is past the number of groups exit at once (the grid is sized
-//     for the worst case, because the host never reads the ids).
-//  3. k_combine (route_w given): y[t][n] = sum_j route_w[t][j] * slot[t][j][n],
-//     j in increasing order; or k_zero_bad (no route_w): zero the output rows of
-//     out-of-range slots.
+// One or two launches on the caller's stream, no host synchronisation:
+//  1. k_experts: one workgroup per (group, row tile).  The slots
+//     s = t*top_k + j are ordered by expert id and each expert's slots are
+//     cut into groups of at most CH; every workgroup derives that grouping
+//     from the ids itself (a histogram and a scan in LDS) and keeps the group
+//     whose index is its own.  It then
+//     runs the shared decode product on that expert's rows with the group's
+//     activation vectors (gathered by slot), writing one output row per slot.
+//     Workgroups past the number of groups exit after the grouping (the grid
+//     is sized for the worst case, because the host never reads the ids).
+//     Ids outside [0, n_experts) are left out; workgroup (0, 0) counts them
+//     into the workspace header and the group-0 workgroups zero the per-slot
+//     output rows of such slots.
+//  2. k_combine (route_w given): y[t][n] = sum_j route_w[t][j] * slot[t][j][n],
+//     j in increasing order.
 #include "gq_gemv_core.h"
 #include "gq_internal.h"
 
@@ -24,127 +27,141 @@ using namespace gqd;
 namespace {
 
 constexpr int CH = 4;           // slots per group = vectors per product workgroup
-constexpr int MAX_SLOTS = 1024; // n_tokens * top_k handled by k_group
+constexpr int MAX_SLOTS = 1024; // n_tokens * top_k
+constexpr int MAX_EXPERTS_LDS = 1024;  // experts counted with an LDS histogram
 
 struct WsLayout {
     int S, Gmax;
-    size_t off_groups, off_sorted, off_out, total;
+    size_t off_out, total;
 };
 
 WsLayout layout(int n_experts, int n_tokens, int top_k, int64_t N) {
     WsLayout L;
     L.S = n_tokens * top_k;
-    int distinct = L.S < n_experts ? L.S : n_experts;
+    const int distinct = L.S < n_experts ? L.S : n_experts;
     L.Gmax = distinct + L.S / CH + 1;
-    L.off_groups = 16;
-    L.off_sorted = (L.off_groups + 16 * (size_t)L.Gmax + 15) & ~size_t(15);
-    L.off_out = (L.off_sorted + 4 * (size_t)L.S + 255) & ~size_t(255);
+    L.off_out = 256;
     L.total = L.off_out + 4 * (size_t)L.S * (size_t)N;
     return L;
-}
-
-struct Group {
-    int expert, start, count, pad;
-};
-
-// ---------------------------------------------------------------- group ----
-__global__ __launch_bounds__(256) void k_group(const int32_t* __restrict__ ids, int S, int n_experts,
-                                               uint8_t* __restrict__ ws, int off_groups, int off_sorted) {
-    __shared__ int key[MAX_SLOTS];      // expert id, or INT_MAX for an invalid id
-    __shared__ int head[MAX_SLOTS];     // 1 where a group starts (by sorted position)
-    __shared__ int head_e[MAX_SLOTS];   // expert of the slot at that sorted position
-    __shared__ int head_cnt[MAX_SLOTS]; // group size if it starts there
-    __shared__ int part[256];
-    __shared__ int bad_total;
-    const int tid = threadIdx.x;
-    int* sorted = reinterpret_cast<int*>(ws + off_sorted);
-    Group* groups = reinterpret_cast<Group*>(ws + off_groups);
-    if (tid == 0) bad_total = 0;
-    __syncthreads();
-    int bad = 0;
-    for (int i = tid; i < S; i += 256) {
-        int e = ids[i];
-        bool ok = e >= 0 && e < n_experts;
-        key[i] = ok ? e : 0x7fffffff;
-        bad += ok ? 0 : 1;
-        head[i] = 0;
-    }
-    if (bad) atomicAdd(&bad_total, bad);
-    __syncthreads();
-    // rank of slot i in (expert, slot) order; first = rank of the expert's
-    // first slot; cnt = slots routed to the same expert
-    for (int i = tid; i < S; i += 256) {
-        int ki = key[i];
-        int less = 0, same_before = 0, same = 0;
-        for (int j = 0; j < S; ++j) {
-            int kj = key[j];
-            less += kj < ki;
-            same += kj == ki;
-            same_before += (kj == ki) & (j < i);
-        }
-        int pos = less + same_before;
-        sorted[pos] = i;
-        if (ki != 0x7fffffff && same_before % CH == 0) {
-            head[pos] = 1;
-            head_e[pos] = ki;
-            int left = same - same_before;
-            head_cnt[pos] = left < CH ? left : CH;
-        }
-    }
-    __syncthreads();
-    // exclusive scan of the head flags over sorted positions: group numbers
-    const int per = (S + 255) / 256;
-    int lo = tid * per, hi = lo + per < S ? lo + per : S;
-    int c = 0;
-    for (int p = lo; p < hi; ++p) c += head[p];
-    part[tid] = c;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        int v = tid >= off ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    int g = part[tid] - c;
-    for (int p = lo; p < hi; ++p) {
-        if (head[p]) {
-            groups[g] = Group{head_e[p], p, head_cnt[p], 0};
-            ++g;
-        }
-    }
-    if (tid == 255) {
-        int* hdr = reinterpret_cast<int*>(ws);
-        hdr[0] = bad_total;
-        hdr[1] = part[255];
-    }
 }
 
 // ------------------------------------------------------------- product ----
 template <int TYPE, int XT, int D, bool RING>
 __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict__ experts, int64_t expert_bytes,
                                                       int64_t N, int64_t K, const uint8_t* __restrict__ x,
-                                                      int x_per_slot, int top_k, const uint8_t* __restrict__ ws,
-                                                      int off_groups, int off_sorted, float* __restrict__ out,
-                                                      int LPR, int tile_units) {
+                                                      int x_per_slot, int top_k, const int32_t* __restrict__ ids,
+                                                      int S, int n_experts, int* __restrict__ ws_hdr,
+                                                      float* __restrict__ out, int LPR, int tile_units) {
     extern __shared__ __align__(16) uint8_t lds[];
-    const int* hdr = reinterpret_cast<const int*>(ws);
-    const int gi = blockIdx.x;
-    if (gi >= hdr[1]) return;
-    const Group grp = reinterpret_cast<const Group*>(ws + off_groups)[gi];
-    const int* sorted = reinterpret_cast<const int*>(ws + off_sorted);
+    // Grouping.  rank = position of a slot among the slots of its expert in
+    // slot order; first[e] = number of groups of the experts before e (a scan
+    // of ceil(count / CH) over the experts, counts from an LDS histogram).
+    // Slot s belongs to group first[e_s] + rank_s / CH.  Every workgroup must
+    // derive exactly the same grouping, so nothing here depends on timing.
+    // More than MAX_EXPERTS_LDS experts: first[] by direct counting.
+    __shared__ int4 key4[MAX_SLOTS / 4];
+    __shared__ int rank[MAX_SLOTS];
+    __shared__ int cnt[MAX_EXPERTS_LDS + 1];
+    __shared__ int part[NTHREADS];
+    __shared__ int sel[CH];
+    __shared__ int n_sel, n_bad;
+    const int tid = threadIdx.x, g = blockIdx.x;
+    const bool small_e = n_experts <= MAX_EXPERTS_LDS;
+    int* key = reinterpret_cast<int*>(key4);
+    const int S4 = (S + 3) >> 2;
+    if (tid == 0) {
+        n_sel = 0;
+        n_bad = 0;
+    }
+    if (small_e)
+        for (int e = tid; e < n_experts; e += NTHREADS) cnt[e] = 0;
+    for (int s = tid; s < 4 * S4; s += NTHREADS) {
+        const int e = s < S ? ids[s] : -2;
+        key[s] = s >= S ? -2 : ((e >= 0 && e < n_experts) ? e : -1);  // -2: padding
+    }
+    __syncthreads();
+    int bad = 0;
+    for (int s = tid; s < S; s += NTHREADS) {
+        const int e = key[s];
+        int r = 0;
+        for (int j4 = 0; 4 * j4 < s; ++j4) {
+            const int4 k = key4[j4];
+            const int j = 4 * j4;
+            r += (k.x == e) + ((k.y == e) & (j + 1 < s)) + ((k.z == e) & (j + 2 < s)) + ((k.w == e) & (j + 3 < s));
+        }
+        rank[s] = r;
+        if (e < 0) ++bad;
+        else if (small_e) atomicAdd(&cnt[e], 1);
+    }
+    if (bad) atomicAdd(&n_bad, bad);
+    __syncthreads();
+    if (small_e) {
+        // exclusive scan of ceil(cnt / CH) over the experts: each thread a
+        // contiguous run of experts, then a scan of the 256 run totals
+        const int per = (n_experts + NTHREADS - 1) / NTHREADS;
+        const int lo = tid * per, hi = lo + per < n_experts ? lo + per : n_experts;
+        int sum = 0;
+        for (int e = lo; e < hi; ++e) sum += (cnt[e] + CH - 1) / CH;
+        part[tid] = sum;
+        __syncthreads();
+        for (int off = 1; off < NTHREADS; off <<= 1) {
+            const int v = tid >= off ? part[tid - off] : 0;
+            __syncthreads();
+            part[tid] += v;
+            __syncthreads();
+        }
+        int run = part[tid] - sum;
+        for (int e = lo; e < hi; ++e) {
+            const int c = (cnt[e] + CH - 1) / CH;
+            cnt[e] = run;  // now: groups before expert e
+            run += c;
+        }
+        __syncthreads();
+    }
+    for (int s = tid; s < S; s += NTHREADS) {
+        const int e = key[s];
+        if (e < 0) continue;
+        int before;
+        if (small_e) {
+            before = cnt[e];
+        } else {
+            // groups of experts ordered before e: one head slot (rank % CH == 0) each
+            before = 0;
+            for (int j = 0; j < S; ++j) before += (key[j] >= 0) & (key[j] < e) & (rank[j] % CH == 0);
+        }
+        if (before + rank[s] / CH == g) {
+            sel[rank[s] % CH] = s;
+            atomicAdd(&n_sel, 1);
+        }
+    }
+    __syncthreads();
+    const int64_t rpw = (int64_t)(NTHREADS >> 6) * (64 / LPR);
+    const int64_t rowA = (int64_t)blockIdx.y * rpw;
+    if (g == 0) {
+        if (blockIdx.y == 0 && tid == 0) ws_hdr[0] = n_bad;
+        // out-of-range slots give zero rows (this workgroup's row range)
+        if (n_bad) {
+            const int64_t rows = N - rowA < rpw ? N - rowA : rpw;
+            for (int s = 0; s < S; ++s)
+                if (key[s] < 0)
+                    for (int64_t n = tid; n < rows; n += NTHREADS) out[(int64_t)s * N + rowA + n] = 0.f;
+        }
+    }
+    const int nb = n_sel;
+    if (nb == 0) return;
+    const int e = key[sel[0]];
     const int esz = XT == 0 ? 4 : 2;
     XSrc xs;
     YDst yd;
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-        int slot = sorted[grp.start + (b < grp.count ? b : 0)];
-        int64_t xrow = x_per_slot ? slot : slot / top_k;
+        const int slot = sel[b < nb ? b : 0];
+        const int64_t xrow = x_per_slot ? slot : slot / top_k;
         xs.p[b] = x + xrow * K * esz;
         yd.p[b] = out + (int64_t)slot * N;
     }
-    const int64_t rpw = (int64_t)(NTHREADS >> 6) * (64 / LPR);
-    gemv_workgroup<TYPE, XT, CH, D, RING>(experts + (int64_t)grp.expert * expert_bytes, N, K,
-                                       (int64_t)blockIdx.y * rpw, xs, grp.count, yd, LPR, tile_units, lds);
+    gemv_workgroup<TYPE, XT, CH, D, RING>(experts + (int64_t)e * expert_bytes, N, K, rowA, xs, nb, yd, LPR,
+                                          tile_units, lds);
 }
 
 // ------------------------------------------------------------- combine ----
@@ -163,51 +180,50 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ slot_
     y[(int64_t)t * N + n] = acc;
 }
 
-__global__ __launch_bounds__(256) void k_zero_bad(const int32_t* __restrict__ ids, int n_experts, int64_t N,
-                                                  float* __restrict__ y) {
-    const int s = blockIdx.y;
-    const int e = ids[s];
-    if (e >= 0 && e < n_experts) return;
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (n < N) y[(int64_t)s * N + n] = 0.f;
-}
-
 template <int TYPE, int XT, int D, bool RING = false>
 hipError_t launch_experts_d(const Plan& p, const WsLayout& L, const uint8_t* experts, int64_t N, int64_t K,
-                            const uint8_t* x, int x_per_slot, int top_k, const uint8_t* ws, float* out,
-                            hipStream_t s) {
+                            const uint8_t* x, int x_per_slot, int top_k, const int32_t* ids, int n_experts,
+                            int* ws_hdr, float* out, hipStream_t s) {
     using F = Fmt<TYPE>;
     const int64_t expert_bytes = N * (K / F::QK) * F::BB;
     hipLaunchKernelGGL((k_experts<TYPE, XT, D, RING>), dim3((unsigned)L.Gmax, (unsigned)p.grid), dim3(NTHREADS),
-                       p.lds, s, experts, expert_bytes, N, K, x, x_per_slot, top_k, ws, (int)L.off_groups,
-                       (int)L.off_sorted, out, p.LPR, p.tile_units);
+                       p.lds, s, experts, expert_bytes, N, K, x, x_per_slot, top_k, ids, L.S, n_experts, ws_hdr,
+                       out, p.LPR, p.tile_units);
     return hipGetLastError();
 }
 
 template <int TYPE, int XT>
 hipError_t launch_experts(const WsLayout& L, const uint8_t* experts, int64_t N, int64_t K, const uint8_t* x,
-                          int x_per_slot, int top_k, const uint8_t* ws, float* out, hipStream_t s) {
+                          int x_per_slot, int top_k, const int32_t* ids, int n_experts, int* ws_hdr, float* out,
+                          hipStream_t s) {
     using F = Fmt<TYPE>;
-    const Plan p = plan_for<F>(N, K, CH);
+    // the launch covers the rows of up to min(S, n_experts) experts
+    const int64_t distinct = L.S < n_experts ? L.S : n_experts;
+    const Plan p = plan_for<F>(N, K, CH, N * distinct, 4);
     if (p.grid > 65535) return hipErrorInvalidValue;
-    if (p.ring) return launch_experts_d<TYPE, XT, D_RING, true>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
+#define GQ_LAUNCH(DD, RR) \
+    launch_experts_d<TYPE, XT, DD, RR>(p, L, experts, N, K, x, x_per_slot, top_k, ids, n_experts, ws_hdr, out, s)
+    if (p.ring) return GQ_LAUNCH(D_RING, true);
     switch (p.D) {
-    case 1: return launch_experts_d<TYPE, XT, 1>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
-    case 2: return launch_experts_d<TYPE, XT, 2>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
-    case 3: return launch_experts_d<TYPE, XT, 3>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
-    case 4: return launch_experts_d<TYPE, XT, 4>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
-    case 5: return launch_experts_d<TYPE, XT, 5>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
-    case 6: return launch_experts_d<TYPE, XT, 6>(p, L, experts, N, K, x, x_per_slot, top_k, ws, out, s);
+    case 1: return GQ_LAUNCH(1, false);
+    case 2: return GQ_LAUNCH(2, false);
+    case 3: return GQ_LAUNCH(3, false);
+    case 4: return GQ_LAUNCH(4, false);
+    case 5: return GQ_LAUNCH(5, false);
+    case 6: return GQ_LAUNCH(6, false);
     default: return hipErrorInvalidValue;
     }
+#undef GQ_LAUNCH
 }
 
 template <int TYPE>
 hipError_t launch_experts_x(const WsLayout& L, const uint8_t* experts, int64_t N, int64_t K, const void* x,
-                            int x_dtype, int x_per_slot, int top_k, const uint8_t* ws, float* out, hipStream_t s) {
+                            int x_dtype, int x_per_slot, int top_k, const int32_t* ids, int n_experts, int* ws_hdr,
+                            float* out, hipStream_t s) {
     const uint8_t* xb = static_cast<const uint8_t*>(x);
-    if (x_dtype == DT_F32) return launch_experts<TYPE, 0>(L, experts, N, K, xb, x_per_slot, top_k, ws, out, s);
-    return launch_experts<TYPE, 1>(L, experts, N, K, xb, x_per_slot, top_k, ws, out, s);
+    if (x_dtype == DT_F32)
+        return launch_experts<TYPE, 0>(L, experts, N, K, xb, x_per_slot, top_k, ids, n_experts, ws_hdr, out, s);
+    return launch_experts<TYPE, 1>(L, experts, N, K, xb, x_per_slot, top_k, ids, n_experts, ws_hdr, out, s);
 }
 
 }  // namespace
@@ -219,27 +235,21 @@ size_t gqk_matvec_id_ws_bytes(int n_experts, int n_tokens, int top_k, int64_t N)
 hipError_t gqk_matvec_id(int type, const void* experts, int n_experts, int64_t N, int64_t K, const int32_t* ids,
                          int n_tokens, int top_k, const void* x, int x_dtype, int x_per_slot, const float* route_w,
                          float* y, void* ws, hipStream_t s) {
-    WsLayout L = layout(n_experts, n_tokens, top_k, N);
+    const WsLayout L = layout(n_experts, n_tokens, top_k, N);
     if (L.S > MAX_SLOTS) return hipErrorInvalidValue;
     uint8_t* w = static_cast<uint8_t*>(ws);
-    hipLaunchKernelGGL(k_group, dim3(1), dim3(256), 0, s, ids, L.S, n_experts, w, (int)L.off_groups,
-                       (int)L.off_sorted);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    int* hdr = reinterpret_cast<int*>(w);
     // per-slot outputs: straight into y when there is no routing combine
     float* out = route_w ? reinterpret_cast<float*>(w + L.off_out) : y;
     const uint8_t* ex = static_cast<const uint8_t*>(experts);
-    if (type == T_Q4_0) e = launch_experts_x<T_Q4_0>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, w, out, s);
-    else if (type == T_Q4_K) e = launch_experts_x<T_Q4_K>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, w, out, s);
-    else e = launch_experts_x<T_Q6_K>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, w, out, s);
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (type == T_Q4_0) e = launch_experts_x<T_Q4_0>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, ids, n_experts, hdr, out, s);
+    else if (type == T_Q4_K) e = launch_experts_x<T_Q4_K>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, ids, n_experts, hdr, out, s);
+    else e = launch_experts_x<T_Q6_K>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, ids, n_experts, hdr, out, s);
+    if (e != hipSuccess || !route_w) return e;
     const unsigned nx = (unsigned)((N + 255) / 256);
-    if (route_w) {
-        hipLaunchKernelGGL(k_combine, dim3(nx, (unsigned)n_tokens), dim3(256), 0, s, out, ids, route_w, n_experts,
-                           top_k, N, y);
-    } else {
-        hipLaunchKernelGGL(k_zero_bad, dim3(nx, (unsigned)L.S), dim3(256), 0, s, ids, n_experts, N, y);
-    }
+    hipLaunchKernelGGL(k_combine, dim3(nx, (unsigned)n_tokens), dim3(256), 0, s, out, ids, route_w, n_experts,
+                       top_k, N, y);
     return hipGetLastError();
 }
 

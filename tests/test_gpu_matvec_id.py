@@ -112,7 +112,8 @@ def test_matvec_id_shapes(gq, orc, t, xdt):
 def test_matvec_id_single_expert_equals_matvec(gq, t):
     """Every slot routed to one expert (groups of 4 slots, several groups):
     each output row equals gq_matvec of that expert on the same vector, bit for
-    bit."""
+    bit (at this size both launches take the same lanes per row, which fixes
+    the summation order)."""
     g = synth.rng(0x67510004, 20)
     E, N, K, T, k = 6, 96, 1024, 7, 2
     ex = synth.weight(t, g, E * N, K)
