@@ -279,6 +279,14 @@ struct Fmt<T_Q6_K> {
 // (0 = fp32, 1 = bf16).  Only ever indexed with a wave-uniform b.
 struct XSrc {
     const uint8_t* p[8];
+    // p[b] for a wave-uniform b without indexing the array by a variable
+    // (which would put a local copy of it in scratch memory)
+    __device__ __forceinline__ const uint8_t* at(int b) const {
+        const uint8_t* r = p[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) r = b == i ? p[i] : r;
+        return r;
+    }
 };
 
 // One 32-input group of raw activation bits (fp32: 8 x 16 B, bf16: 4 x 16 B),
@@ -426,18 +434,26 @@ template <class F, int XT>
 __device__ __forceinline__ void stage_finish(const XSrc& xs, int64_t k0, const TileLds<F>& L,
                                              const XRaw<XT>& first) {
     const int G = L.U * F::UW / 32;
-    if ((int)threadIdx.x < G) stage_group<F, XT>(L, 0, threadIdx.x, first);
-    for (int g = threadIdx.x + blockDim.x; g < G; g += blockDim.x) {
-        XRaw<XT> in;
-        load_group<XT>(xs.p[0], k0 + 32 * g, in);
-        stage_group<F, XT>(L, 0, g, in);
-    }
-    for (int b = 1; b < L.nb; ++b) {
-        const uint8_t* xb = xs.p[b];
-        for (int g = threadIdx.x; g < G; g += blockDim.x) {
-            XRaw<XT> in;
-            load_group<XT>(xb, k0 + 32 * g, in);
-            stage_group<F, XT>(L, b, g, in);
+    const int tid = (int)threadIdx.x;
+    // work items: (vector b, round r) -> group tid + 256 r of vector b
+    const int rounds = (G + NTHREADS - 1) / NTHREADS;
+    const int items = L.nb * rounds;
+    if (items == 1) {
+        if (tid < G) stage_group<F, XT>(L, 0, tid, first);
+    } else {
+        // the next item's activations are loaded while this one is staged; the
+        // load is unconditional (the last item reloads itself) so that the
+        // load-counter wait stays exact
+        XRaw<XT> cur = first;
+#pragma unroll 1
+        for (int i = 0; i < items; ++i) {
+            const int in = i + 1 < items ? i + 1 : i;
+            const int gn = tid + NTHREADS * (in % rounds);
+            XRaw<XT> nxt;
+            load_group<XT>(xs.at(in / rounds), k0 + 32 * (gn < G ? gn : 0), nxt);
+            const int g = tid + NTHREADS * (i % rounds);
+            if (g < G) stage_group<F, XT>(L, i / rounds, g, cur);
+            cur = nxt;
         }
     }
     lds_barrier();

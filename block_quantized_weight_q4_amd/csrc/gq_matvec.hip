@@ -51,9 +51,9 @@ hipError_t launch_b(const uint8_t* W, int64_t N, int64_t K, const XSrc& xs, int 
 
 template <int TYPE, int XT>
 hipError_t launch_t(const uint8_t* W, int64_t N, int64_t K, const XSrc& xs, int nb, float* y, hipStream_t s) {
+    // (3..8 vectors share one variant: a 4-vector one needs no fewer registers)
     if (nb == 1) return launch_b<TYPE, XT, 1>(W, N, K, xs, nb, y, s);
     if (nb == 2) return launch_b<TYPE, XT, 2>(W, N, K, xs, nb, y, s);
-    if (nb <= 4) return launch_b<TYPE, XT, 4>(W, N, K, xs, nb, y, s);
     return launch_b<TYPE, XT, 8>(W, N, K, xs, nb, y, s);
 }
 

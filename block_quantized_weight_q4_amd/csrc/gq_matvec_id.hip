@@ -150,17 +150,20 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
     const int nb = n_sel;
     if (nb == 0) return;
     const int e = key[sel[0]];
-    const int esz = XT == 0 ? 4 : 2;
-    XSrc xs;
-    YDst yd;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const int slot = sel[b < nb ? b : 0];
+    // the group's vector and output pointers live in LDS: the staging picks
+    // them by a loop index, which a private copy would turn into scratch
+    // memory accesses
+    __shared__ XSrc xs;
+    __shared__ YDst yd;
+    if (tid < 8) {
+        const int esz = XT == 0 ? 4 : 2;
+        const int slot = sel[tid < nb ? tid : 0];
         const int64_t xrow = x_per_slot ? slot : slot / top_k;
-        xs.p[b] = x + xrow * K * esz;
-        yd.p[b] = out + (int64_t)slot * N;
+        xs.p[tid] = x + xrow * K * esz;
+        yd.p[tid] = out + (int64_t)slot * N;
     }
-    gemv_workgroup<TYPE, XT, CH, D, RING>(experts + (int64_t)e * expert_bytes, N, K, rowA, xs, nb, yd, LPR,
+    __syncthreads();
+    gemv_workgroup<TYPE, XT, 8, D, RING>(experts + (int64_t)e * expert_bytes, N, K, rowA, xs, nb, yd, LPR,
                                           tile_units, lds);
 }
 
