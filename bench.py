@@ -427,15 +427,19 @@ def bench_context(torch, gq, synth, dev, stream, t_):
     # MoE routed experts: 128 experts, hidden 2816, FFN 704, 8 tokens top-8
     E, H, F, T, k = 128, 2816, 704, 8, 8
     g = synth.rng(0x67510004, 0)
-    ids, rw = synth.routing(g, T, E, k)
-    distinct = len(np.unique(ids))
+    logits = synth.router_logits(g, T, E)
+    lg_t = t_(logits)
+    ids_t = torch.empty((T, k), dtype=torch.int32, device=dev)
+    rw_t = torch.empty((T, k), device=dev)
+    gq.gq_route_topk(lg_t, k, ids_t, rw_t, stream)
+    stream.synchronize()
+    distinct = len(np.unique(ids_t.cpu().numpy()))
     ex = {"gate": synth.weight("q4_0", synth.rng(0x67510004, 1), E * F, H),
           "up": synth.weight("q4_0", synth.rng(0x67510004, 2), E * F, H),
           "down": synth.weight("q4_0", synth.rng(0x67510004, 3), E * H, F)}
     layer_all = sum(v.nbytes for v in ex.values())
     read_bytes = layer_all // E * distinct
     cp4 = [{kk: t_(v) for kk, v in ex.items()} for _ in range(max(2, -(-ROTATE_BYTES // layer_all)))]
-    ids_t, rw_t = t_(ids), t_(rw)
     x4 = t_(synth.normal_f32(g, (T, H)))
     h4 = t_(synth.normal_f32(g, (T, k, F)))
     yg = torch.empty(T, k, F, device=dev)
@@ -446,12 +450,14 @@ def bench_context(torch, gq, synth, dev, stream, t_):
 
     def p4():
         for c in cp4:
+            gq.gq_route_topk(lg_t, k, ids_t, rw_t, stream)
             gq.gq_matvec_id("q4_0", c["gate"], E, F, H, ids_t, x4, False, yg, ws[0], None, stream)
             gq.gq_matvec_id("q4_0", c["up"], E, F, H, ids_t, x4, False, yu, ws[1], None, stream)
             gq.gq_matvec_id("q4_0", c["down"], E, H, F, ids_t, h4, True, yd, ws[2], rw_t, stream)
 
     ms = Timer(torch, p4, stream).time(10) / len(cp4)
     res["moe_q4_0_128x_h2816_f704_t8_top8"] = {
+        "launches": "route_topk, gate, up, down (weighted)",
         "us_per_layer": round(ms * 1e3, 2), "distinct_experts": distinct, "packed_bytes_read": read_bytes,
         "GBps": round(read_bytes / (ms * 1e-3) / 1e9, 1),
         "tokens_per_s_equiv_30_layers": round(T / (30 * ms * 1e-3), 1)}

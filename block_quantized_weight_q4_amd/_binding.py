@@ -37,8 +37,9 @@ _lib.gq_matvec_id_workspace.argtypes = [I32, I32, I32, I64, ctypes.POINTER(SZ)]
 _lib.gq_matvec_id.argtypes = [ctypes.c_int, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, I32, P, P, P, SZ, P]
 _lib.gq_matvec_id_check.argtypes = [P, P, ctypes.POINTER(I32)]
 _lib.gq_matmul.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I64, I64, P, I64, P]
+_lib.gq_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
 for _f in ("gq_block_info", "gq_dequant", "gq_matvec", "gq_matvec_id_workspace", "gq_matvec_id",
-           "gq_matvec_id_check", "gq_matmul"):
+           "gq_matvec_id_check", "gq_matmul", "gq_route_topk"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -127,6 +128,20 @@ def gq_matmul(t, W: torch.Tensor, N: int, K: int, X: torch.Tensor, Y: torch.Tens
     _check("gq_matmul", _lib.gq_matmul(_type(t), _ptr(W), N, K, _ptr(X), _DTYPES[X.dtype], M, ldx, _ptr(Y), ldy,
                                        _stream(stream)))
     return Y
+
+
+def gq_route_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor, weights: torch.Tensor,
+                  stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """ids / weights [n_tokens][top_k] (int32 / fp32) of the softmax + top-k
+    routing of fp32 ``logits`` [n_tokens][n_experts]."""
+    n_tokens, n_experts = logits.shape
+    if logits.dtype != torch.float32 or ids.dtype != torch.int32 or weights.dtype != torch.float32:
+        raise TypeError("logits and weights must be float32, ids int32")
+    if ids.numel() != n_tokens * top_k or weights.numel() != n_tokens * top_k:
+        raise ValueError("ids / weights must hold n_tokens * top_k elements")
+    _check("gq_route_topk", _lib.gq_route_topk(_ptr(logits), n_tokens, n_experts, top_k, _ptr(ids),
+                                               _ptr(weights), _stream(stream)))
+    return ids, weights
 
 
 # raw handle for the tests that check the exported symbols

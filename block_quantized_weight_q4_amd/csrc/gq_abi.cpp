@@ -130,6 +130,21 @@ gq_status gq_matvec_id_check(const void* ws, hipStream_t stream, int32_t* n_bad_
     }
 }
 
+gq_status gq_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t top_k, int32_t* ids,
+                        float* weights, hipStream_t stream) {
+    if (n_tokens < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts) return GQ_ERR_SHAPE;
+    if ((int64_t)n_tokens * n_experts > MAX_ELEMS) return GQ_ERR_SHAPE;
+    if (n_experts > 4096 || top_k > 64) return GQ_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return GQ_OK;
+    if (!logits || !ids || !weights) return GQ_ERR_NULL;
+    if (!aligned16(logits) || !aligned16(ids) || !aligned16(weights)) return GQ_ERR_ALIGN;
+    try {
+        return from_hip(gqk_route_topk(logits, n_tokens, n_experts, top_k, ids, weights, stream));
+    } catch (...) {
+        return GQ_ERR_LAUNCH;
+    }
+}
+
 gq_status gq_matmul(gq_type t, const void* W, int64_t N, int64_t K, const void* X, gq_dtype x_dtype, int64_t M,
                     int64_t ldx, float* Y, int64_t ldy, hipStream_t stream) {
     if (!known_type(t)) return GQ_ERR_TYPE;

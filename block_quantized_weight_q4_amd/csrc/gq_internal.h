@@ -21,3 +21,6 @@ hipError_t gqk_matvec_id_bad_count(const void* ws, hipStream_t s, int32_t* n_bad
 
 hipError_t gqk_matmul(int type, const void* W, int64_t N, int64_t K, const void* X, int x_dtype,
                       int64_t M, int64_t ldx, float* Y, int64_t ldy, hipStream_t s);
+
+hipError_t gqk_route_topk(const float* logits, int n_tokens, int n_experts, int top_k, int32_t* ids, float* w,
+                          hipStream_t s);

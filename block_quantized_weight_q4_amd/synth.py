@@ -95,13 +95,6 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def routing(g: np.random.Generator, n_tokens: int, n_experts: int, top_k: int):
-    """Seeded routing inputs: logits ~ N(0,1) [n_tokens][n_experts]; ids = the
-    top_k logits per token (descending, ties to the lower id); weights = softmax
-    over the selected logits, in fp64, stored fp32."""
-    logits = g.standard_normal((n_tokens, n_experts))
-    order = np.argsort(-logits, axis=1, kind="stable")[:, :top_k]
-    sel = np.take_along_axis(logits, order, axis=1)
-    e = np.exp(sel - sel.max(axis=1, keepdims=True))
-    w = e / e.sum(axis=1, keepdims=True)
-    return order.astype(np.int32), w.astype(np.float32)
+def router_logits(g: np.random.Generator, n_tokens: int, n_experts: int) -> np.ndarray:
+    """Seeded router scores: N(0,1) logits [n_tokens][n_experts], fp32."""
+    return g.standard_normal((n_tokens, n_experts)).astype(np.float32)

@@ -145,6 +145,26 @@ gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_
  * that used `ws` were outside [0, n_experts). */
 gq_status gq_matvec_id_check(const void* ws, hipStream_t stream, int32_t* n_bad_ids);
 
+/* Expert routing ("GGUF in transformers", section "Reusing ggml's Metal
+ * kernels", kernel table row "topk": the softmax and the top-k choice in one
+ * kernel; the Gemma 4 26B-A4B Show HN page routes 8 of 128 experts per token).
+ * logits: fp32 [n_tokens][n_experts] (device).  For each token t:
+ *   ids[t][0..top_k-1]: the experts of the top_k largest logits, in
+ *     decreasing logit order; among equal logits the lower id comes first
+ *     (-0 and +0 are equal).  Bit-exact: the choice compares the fp32 logits.
+ *   weights[t][j] = exp(l[ids[t][j]] - l[ids[t][0]]) / sum_i exp(l[ids[t][i]] - l[ids[t][0]]),
+ *     the softmax over the selected logits (equal to the softmax over all
+ *     experts renormalised over the selected ones), in fp32: within
+ *     (top_k + 8) * 2^-24 of the exact value.
+ * ids: int32 [n_tokens][top_k], weights: fp32 [n_tokens][top_k] (device),
+ * ready to be passed to gq_matvec_id as ids and route_w.
+ * 1 <= top_k <= n_experts; n_experts <= 4096 and top_k <= 64
+ * (GQ_ERR_UNSUPPORTED beyond).  n_tokens == 0 is a no-op.  NaN logits leave
+ * ids distinct and in range but their order unspecified; weights are NaN when
+ * the largest selected logit is infinite. */
+gq_status gq_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                        int32_t* ids, float* weights, hipStream_t stream);
+
 /* Prefill product Y[m][n] = sum_k X[m][k] * w[n][k] for 0 <= m < M, 0 <= n < N.
  * X: [M][ldx] of x_dtype (row stride ldx >= K elements); Y: [M][ldy] fp32
  * (ldy >= N).  Weight tiles are dequantised to bf16 in LDS and multiplied on

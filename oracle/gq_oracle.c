@@ -517,5 +517,51 @@ int oracle_quantize(int type, const float* x, int64_t n_blocks, uint8_t* out) {
 }
 
 /* Exposed for the tests' fp16 pins. */
+/* ------------------------------------------------------------ routing ---- */
+
+/*
+ * Softmax + top-k routing of mixture-of-experts tokens: the "topk" row of the
+ * kernel table in "GGUF in transformers" (section "Reusing ggml's Metal
+ * kernels") combines the two steps; the Show HN README ("How it works") has
+ * the router score all 128 experts of a token and keep the top 8.
+ *
+ * For token t, ids[t][0..k) are the k experts with the largest logit, in
+ * decreasing order of logit; equal logits go to the lower expert id first.
+ * The weights are the softmax of the selected logits,
+ *   weights[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0),   l_0 = the largest,
+ * evaluated in fp64 (the fp32 logits convert exactly).  Logits are finite.
+ */
+int oracle_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                      int32_t* ids, double* weights) {
+    if (n_tokens < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts) return 1;
+    unsigned char* taken = (unsigned char*)malloc((size_t)n_experts);
+    if (!taken) return 2;
+    for (int32_t t = 0; t < n_tokens; ++t) {
+        const float* l = logits + (int64_t)t * n_experts;
+        memset(taken, 0, (size_t)n_experts);
+        for (int32_t j = 0; j < top_k; ++j) {
+            /* largest remaining logit; scanning ids upwards with a strict
+               comparison keeps the lower id among equal logits */
+            int32_t best = -1;
+            for (int32_t e = 0; e < n_experts; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || l[e] > l[best]) best = e;
+            }
+            taken[best] = 1;
+            ids[(int64_t)t * top_k + j] = best;
+        }
+        const double l0 = (double)l[ids[(int64_t)t * top_k]];
+        double sum = 0.0;
+        for (int32_t j = 0; j < top_k; ++j) {
+            double e = exp((double)l[ids[(int64_t)t * top_k + j]] - l0);
+            weights[(int64_t)t * top_k + j] = e;
+            sum += e;
+        }
+        for (int32_t j = 0; j < top_k; ++j) weights[(int64_t)t * top_k + j] /= sum;
+    }
+    free(taken);
+    return 0;
+}
+
 float oracle_half_to_float(uint16_t h) { return orc_half_to_float(h); }
 uint16_t oracle_float_to_half(float f) { return orc_float_to_half(f); }

@@ -52,6 +52,7 @@ def _setup(cdll):
                                             ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(ctypes.c_double)]
     cdll.oracle_quantize.argtypes = [ctypes.c_int, P, I64, P]
+    cdll.oracle_route_topk.argtypes = [P, I32, I32, I32, P, P]
     cdll.oracle_half_to_float.argtypes = [ctypes.c_uint16]
     cdll.oracle_half_to_float.restype = ctypes.c_float
     cdll.oracle_float_to_half.argtypes = [ctypes.c_float]
@@ -166,6 +167,17 @@ def matvec_id(t, experts: np.ndarray, n_experts: int, N: int, K: int, ids: np.nd
     if rc:
         raise RuntimeError("oracle_matvec_id failed")
     return y, a
+
+
+def route_topk(logits: np.ndarray, top_k: int):
+    """(ids int32 [T][k], weights fp64 [T][k]) of the softmax + top-k routing."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, top_k), np.int32)
+    w = np.empty((T, top_k))
+    if lib().oracle_route_topk(_p(logits), T, E, top_k, _p(ids), _p(w)):
+        raise RuntimeError("oracle_route_topk failed")
+    return ids, w
 
 
 def matmul_rows(t, W: np.ndarray, N: int, K: int, X: np.ndarray, rows):

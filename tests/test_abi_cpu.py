@@ -31,6 +31,7 @@ def lib(gq_lib_path):
     L.gq_matvec_id_check.argtypes = [P, P, ctypes.POINTER(I32)]
     L.gq_matmul.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I64, I64, P, I64, P]
     L.gq_block_info.argtypes = [ctypes.c_int, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+    L.gq_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
     return L
 
 
@@ -42,7 +43,7 @@ def declared_functions() -> list[str]:
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -165,3 +166,20 @@ def test_binding_refuses_without_library(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError, match="libgq.so is not built"):
         spec.loader.exec_module(mod)
+
+
+def test_route_topk_validation(lib):
+    r = lib.gq_route_topk
+    assert r(A, -1, 128, 8, A, A, None) == GQ_ERR_SHAPE
+    assert r(A, 8, 0, 1, A, A, None) == GQ_ERR_SHAPE
+    assert r(A, 8, 128, 0, A, A, None) == GQ_ERR_SHAPE
+    assert r(A, 8, 4, 5, A, A, None) == GQ_ERR_SHAPE  # top_k > n_experts
+    assert r(A, 8, 4097, 8, A, A, None) == GQ_ERR_UNSUPPORTED
+    assert r(A, 8, 128, 65, A, A, None) == GQ_ERR_UNSUPPORTED
+    assert r(None, 8, 128, 8, A, A, None) == GQ_ERR_NULL
+    assert r(A, 8, 128, 8, None, A, None) == GQ_ERR_NULL
+    assert r(A, 8, 128, 8, A, None, None) == GQ_ERR_NULL
+    assert r(MIS, 8, 128, 8, A, A, None) == GQ_ERR_ALIGN
+    assert r(A, 8, 128, 8, MIS, A, None) == GQ_ERR_ALIGN
+    assert r(A, 8, 128, 8, A, MIS, None) == GQ_ERR_ALIGN
+    assert r(None, 0, 128, 8, None, None, None) == GQ_OK  # no tokens: no-op

@@ -62,11 +62,20 @@ def run_id(gq, t, experts_np, E, N, K, ids_np, x_t, per_slot, route_w=None):
 
 
 def test_moe_workload_gate_up_down(gq, orc):
-    """128 experts, hidden 2816, expert FFN 704 (Q4_0); 8 tokens, top-8 seeded
-    routing with softmax weights on the down projection."""
+    """128 experts, hidden 2816, expert FFN 704 (Q4_0); 8 tokens routed top-8
+    on the device (gq_route_topk over seeded logits), softmax weights on the
+    down projection.  The oracle products take the oracle's own routing, which
+    the device's ids match bit for bit."""
     E, H, F, T, k = 128, 2816, 704, 8, 8
     g = synth.rng(0x67510004, 0)
-    ids, rw = synth.routing(g, T, E, k)
+    logits = synth.router_logits(g, T, E)
+    ids_t = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    rw_t = torch.empty((T, k), device="cuda")
+    gq.gq_route_topk(dev(logits), k, ids_t, rw_t)
+    ids, rw64 = orc.route_topk(logits, k)
+    assert np.array_equal(ids_t.cpu().numpy(), ids)
+    rw = rw_t.cpu().numpy()
+    assert np.abs(rw - rw64).max() <= (k + 8) * 2.0 ** -24
     print("distinct experts:", len(np.unique(ids)))
     x = synth.normal_f32(g, (T, H))
     for name, N, K in (("gate", F, H), ("up", F, H)):

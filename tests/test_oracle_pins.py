@@ -246,6 +246,60 @@ def test_matvec_integer_exact(orc):
     assert np.array_equal(y, exp.astype(np.float64))
 
 
+# ---------------------------------------------------------------- routing ----
+# Softmax + top-k routing ("GGUF in transformers", kernel table row "topk";
+# Show HN README, "How it works": top 8 of 128 experts per token).
+
+def test_route_closed_form(orc):
+    """Logits log(1), log(3), log(2), log(1/2): the top two are experts 1 and 2
+    and their weights are 3/5 and 2/5 (up to the fp32 rounding of the logs)."""
+    l = np.log(np.array([[1.0, 3.0, 2.0, 0.5]])).astype(np.float32)
+    ids, w = orc.route_topk(l, 2)
+    assert ids.tolist() == [[1, 2]]
+    assert abs(w[0, 0] - 0.6) < 1e-6 and abs(w[0, 1] - 0.4) < 1e-6
+
+
+def test_route_ties_go_to_the_lower_id(orc):
+    l = np.array([[1.0, 5.0, 5.0, 2.0, 5.0]], np.float32)
+    ids, w = orc.route_topk(l, 3)
+    assert ids.tolist() == [[1, 2, 4]]
+    assert np.all(w == 1.0 / 3.0)
+
+
+def test_route_full_top_k_is_a_stable_descending_sort(orc):
+    g = np.random.default_rng(7)
+    l = np.round(g.standard_normal((16, 40)), 1).astype(np.float32)  # many ties
+    ids, _ = orc.route_topk(l, 40)
+    assert np.array_equal(ids, np.argsort(-l, axis=1, kind="stable"))
+
+
+def test_route_invariants_and_renormalised_softmax(orc):
+    """Brute-force checks on random logits: ids distinct, logits non-increasing
+    along j, no unselected logit above the smallest selected one; weights equal
+    the softmax over all experts renormalised over the selected ones."""
+    g = np.random.default_rng(8)
+    l = (3.0 * g.standard_normal((64, 128))).astype(np.float32)
+    ids, w = orc.route_topk(l, 8)
+    ld = l.astype(np.float64)
+    full = np.exp(ld - ld.max(axis=1, keepdims=True))
+    full /= full.sum(axis=1, keepdims=True)
+    for t in range(64):
+        sel = ids[t]
+        assert len(set(sel.tolist())) == 8
+        assert np.all(np.diff(l[t, sel]) <= 0)
+        rest = np.delete(l[t], sel)
+        assert rest.max() <= l[t, sel].min()
+        ref = full[t, sel] / full[t, sel].sum()
+        assert np.allclose(w[t], ref, rtol=1e-12, atol=0)
+        assert abs(w[t].sum() - 1.0) < 1e-14
+
+
+def test_route_large_logits_do_not_overflow(orc):
+    l = np.array([[1e30, 1e30, -1e30, 3e29]], np.float32)
+    ids, w = orc.route_topk(l, 2)
+    assert ids.tolist() == [[0, 1]] and np.all(w == 0.5)
+
+
 def test_matvec_id_reduces_to_matvec(orc):
     g = np.random.default_rng(5)
     E, N, K, T, k = 6, 9, 64, 3, 4
@@ -450,6 +504,12 @@ MUTATIONS = {
                             "for (int64_t k = 0; k + 1 < K; ++k) {\n                double p = (double)row[k] * (double)xb[k];"),
     "matvec_id ignores routing weight": ("y[(int64_t)t * N + n] += r * s;", "y[(int64_t)t * N + n] += s;"),
     "checksum transposed": ("wv[k] += v[n] * (double)wrow[k];", "wv[k] += v[k % N] * (double)wrow[k];"),
+    "route ties to the higher id": ("if (best < 0 || l[e] > l[best]) best = e;",
+                                    "if (best < 0 || l[e] >= l[best]) best = e;"),
+    "route softmax without the max shift": ("double e = exp((double)l[ids[(int64_t)t * top_k + j]] - l0);",
+                                            "double e = exp((double)l[ids[(int64_t)t * top_k + j]]);"),
+    "route denominator misses one": ("        weights[(int64_t)t * top_k + j] = e;\n            sum += e;",
+                                     "        weights[(int64_t)t * top_k + j] = e;\n            if (j) sum += e;"),
 }
 
 PINS = [
@@ -463,6 +523,11 @@ PINS = [
     lambda o: test_matvec_brute_force_fsum(o, "q4_0", 160),
     lambda o: test_matvec_id_reduces_to_matvec(o),
     lambda o: test_matmul_rows_cols_checksum(o),
+    lambda o: test_route_closed_form(o),
+    lambda o: test_route_ties_go_to_the_lower_id(o),
+    lambda o: test_route_full_top_k_is_a_stable_descending_sort(o),
+    lambda o: test_route_invariants_and_renormalised_softmax(o),
+    lambda o: test_route_large_logits_do_not_overflow(o),
 ]
 
 
