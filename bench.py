@@ -407,7 +407,7 @@ def bench_context(torch, gq, synth, dev, stream, t_):
         hw[name] = (np.concatenate(arrs), t, sum(n for _, n in parts), K)
         lb3 += sum(a.nbytes for a in arrs)
     cp3 = [{k: t_(v[0]) for k, v in hw.items()} for _ in range(max(2, -(-ROTATE_BYTES // lb3)))]
-    for B in (1, 2, 8):
+    for B in (1, 2, 8, 16):
         xb = {k: t_(synth.bf16_bits(synth.normal_f32(synth.rng(0x67510003, 300 + B), (B, v[3]))).view(np.int16))
               .view(torch.bfloat16) for k, v in hw.items()}
         yb = {k: torch.empty(B, v[2], device=dev) for k, v in hw.items()}

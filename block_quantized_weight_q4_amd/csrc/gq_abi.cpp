@@ -24,6 +24,12 @@ constexpr int64_t MAX_ELEMS = (int64_t)1 << 40;
 // rows through one buffer resource whose span must stay below 2^31 bytes.
 constexpr int64_t MAX_K_DECODE = (int64_t)1 << 22;
 
+// Decode products for more than 8 vectors run on the matrix cores, and so do
+// Q4_0 / Q4_K products for 5..8 vectors, where the matrix cores were measured
+// faster (the dot-product path's work grows with every vector, the matrix-core
+// path's per-weight work does not); everything else on the dot-product path.
+bool use_matrix_cores(int batch, int type) { return batch > 8 || (batch >= 5 && type != GQ_Q6_K); }
+
 }  // namespace
 
 extern "C" {
@@ -74,11 +80,12 @@ gq_status gq_matvec(gq_type t, const void* W, int64_t N, int64_t K, const void* 
     if (x_dtype != GQ_F32 && x_dtype != GQ_BF16) return GQ_ERR_DTYPE;
     if (N < 0 || K < 0 || K % qk_of(t) != 0 || batch < 1) return GQ_ERR_SHAPE;
     if (N > MAX_ELEMS || K > MAX_K_DECODE || (K > 0 && N > MAX_ELEMS / K)) return GQ_ERR_SHAPE;
-    if (batch > 8) return GQ_ERR_UNSUPPORTED;
+    if (batch > 16) return GQ_ERR_UNSUPPORTED;
     if (N == 0) return GQ_OK;
     if (!y || (K > 0 && (!W || !x))) return GQ_ERR_NULL;
     if (!aligned16(y) || (K > 0 && (!aligned16(W) || !aligned16(x)))) return GQ_ERR_ALIGN;
     try {
+        if (use_matrix_cores(batch, t)) return from_hip(gqk_mmv(t, W, N, K, x, x_dtype, batch, y, stream));
         return from_hip(gqk_matvec(t, W, N, K, x, x_dtype, batch, y, stream));
     } catch (...) {
         return GQ_ERR_LAUNCH;

@@ -11,6 +11,9 @@ hipError_t gqk_dequant(int type, const void* blocks, int64_t n_blocks, void* out
 
 hipError_t gqk_matvec(int type, const void* W, int64_t N, int64_t K, const void* x, int x_dtype,
                       int batch, float* y, hipStream_t s);
+// The same product on the matrix cores, batch 1..16 (gq_mmv.hip).
+hipError_t gqk_mmv(int type, const void* W, int64_t N, int64_t K, const void* x, int x_dtype, int batch,
+                   float* y, hipStream_t s);
 
 // Routed experts.  Workspace layout is private to gq_matvec_id.hip.
 size_t gqk_matvec_id_ws_bytes(int n_experts, int n_tokens, int top_k, int64_t N);

@@ -100,16 +100,23 @@ gq_status gq_dequant(gq_type t, const void* blocks, int64_t n_blocks, void* out,
 /* Decode matrix-vector product for a small batch:
  *   y[b][n] = sum_k w[n][k] * x[b][k],  0 <= b < batch, 0 <= n < N.
  * W: packed [N][K/QK] blocks of type t.  x: [batch][K] of x_dtype (GQ_F32 or
- * GQ_BF16).  y: [batch][N] fp32.  1 <= batch <= 8 (GQ_ERR_UNSUPPORTED above).
+ * GQ_BF16).  y: [batch][N] fp32.  1 <= batch <= 16 (GQ_ERR_UNSUPPORTED above;
+ * the Gemma 4 26B-A4B Show HN page verifies blocks of up to 16 draft tokens).
  * K must be a multiple of QK and at most 4,194,304 (GQ_ERR_SHAPE otherwise).
  * N == 0 is a no-op; K == 0 writes zeros.
- * Accuracy: activations enter the dot instructions as fp16 after an exact
- * power-of-two scaling per 32 inputs (relative rounding <= 2^-11), weights as
- * the exact fp16 values 1024 + q, and sums are fp32.  The result is within
- * 1e-3 * sum_k |w[n][k] * x[b][k]| of the exact product unless that sum is
- * tiny next to the magnitudes the fp32 sums carry (d * sc * 1024 * sum |x| per
- * sub-block), e.g. rows whose quants nearly all sit at the zero point; a
- * sub-block whose quants all equal the zero point contributes exactly zero. */
+ * Two paths compute it: batch > 8, and Q4_0 / Q4_K at batch 5..8, run on the
+ * matrix cores; the rest on the packed fp16 dot instructions.
+ * Accuracy, dot path: activations enter as fp16 after an exact power-of-two
+ * scaling per 32 inputs (relative rounding <= 2^-11), weights as the exact
+ * fp16 values 1024 + q, sums are fp32.  Matrix-core path: bf16 activations
+ * enter exactly, fp32 ones as a bf16 pair hi + lo (relative error <= 2^-17),
+ * weights as the exact bf16 values 128 + q, sums are fp32.  Either way the
+ * result is within 1e-3 * sum_k |w[n][k] * x[b][k]| of the exact product
+ * unless that sum is tiny next to the magnitudes the fp32 sums carry (d * sc *
+ * 1024 (dot) or 160 (matrix cores) * sum |x| per sub-block), e.g. rows whose
+ * quants nearly all sit at the zero point; a sub-block whose quants all equal
+ * the zero point contributes exactly zero.  Each vector's result depends on
+ * that vector alone (bit for bit) within one path. */
 gq_status gq_matvec(gq_type t, const void* W, int64_t N, int64_t K, const void* x,
                     gq_dtype x_dtype, int32_t batch, float* y, hipStream_t stream);
 

@@ -85,7 +85,7 @@ def test_matvec_validation(lib):
     assert mv(2, A, -1, 256, A, 0, 1, A, None) == GQ_ERR_SHAPE
     assert mv(2, A, 8, -256, A, 0, 1, A, None) == GQ_ERR_SHAPE
     assert mv(2, A, 8, 256, A, 0, 0, A, None) == GQ_ERR_SHAPE
-    assert mv(2, A, 8, 256, A, 0, 9, A, None) == GQ_ERR_UNSUPPORTED
+    assert mv(2, A, 8, 256, A, 0, 17, A, None) == GQ_ERR_UNSUPPORTED
     assert mv(2, None, 8, 256, A, 0, 1, A, None) == GQ_ERR_NULL
     assert mv(2, A, 8, 256, None, 0, 1, A, None) == GQ_ERR_NULL
     assert mv(2, A, 8, 256, A, 0, 1, None, None) == GQ_ERR_NULL
