@@ -295,6 +295,21 @@ def main():
                "tokens_per_s": round(M / (ms_mm * 1e-3), 1)}
     del tp, W5, X5, Y5
     torch.cuda.empty_cache()
+    # the same prefill length through the other formats of a Q4_K_M layer:
+    # the Q6_K down projection (5120 x 17408) and a Q4_0 matrix of the c5 shape
+    others = {}
+    for t5, N6, K6 in (("q6_k", 5120, 17408), ("q4_0", 17408, 5120)):
+        W6 = t_(synth.weight(t5, synth.rng(0x67510005, 2), N6, K6))
+        X6 = t_(synth.bf16_bits(synth.normal_f32(synth.rng(0x67510005, 3), (M, K6))).view(np.int16)).view(
+            torch.bfloat16)
+        Y6 = torch.empty(M, N6, device=dev)
+        tp = Timer(torch, lambda: gq.gq_matmul(t5, W6, N6, K6, X6, Y6, stream), stream)
+        ms6 = tp.time(10)
+        others["%s_prefill_%dx%dx%d_bf16" % (t5, M, N6, K6)] = {
+            "ms": round(ms6, 4), "TFLOPs": round(2.0 * M * N6 * K6 / (ms6 * 1e-3) / 1e12, 2)}
+        del tp, W6, X6, Y6
+        torch.cuda.empty_cache()
+    prefill["other_formats"] = others
 
     if not args.quick:
         context = bench_context(torch, gq, synth, dev, stream, t_)

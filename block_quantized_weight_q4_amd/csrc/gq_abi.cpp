@@ -163,7 +163,7 @@ gq_status gq_matmul(gq_type t, const void* W, int64_t N, int64_t K, const void* 
     // the prefill kernel addresses 256 rows of X or W through one buffer
     // resource whose span must stay below 2^31 bytes
     if (K > MAX_K_DECODE || ldx >= MAX_K_DECODE) return GQ_ERR_SHAPE;
-    if (t != GQ_Q4_K || x_dtype != GQ_BF16) return GQ_ERR_UNSUPPORTED;
+    if (x_dtype != GQ_BF16) return GQ_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return GQ_OK;
     if (!Y || (K > 0 && (!W || !X))) return GQ_ERR_NULL;
     if (!aligned16(Y) || (K > 0 && (!aligned16(W) || !aligned16(X)))) return GQ_ERR_ALIGN;

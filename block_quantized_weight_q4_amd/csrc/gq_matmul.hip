@@ -1,29 +1,30 @@
-// gq_matmul.hip -- prefill product Y[m][n] = sum_k X[m][k] w[n][k] with Q4_K
-// weights and bf16 activations on the CDNA4 matrix cores (gfx950).
+// gq_matmul.hip -- prefill product Y[m][n] = sum_k X[m][k] w[n][k] with Q4_0,
+// Q4_K or Q6_K weights and bf16 activations on the CDNA4 matrix cores (gfx950).
 //
 // The dequantise-then-matrix-engine step follows the prefill design of "Show
 // HN: Gemma 4 26B-A4B at up to 100+ tokens/s on a 16 GB Mac" (Architecture
 // section: the GPU expands the 4-bit experts to a dense 16-bit format which a
 // matrix engine then multiplies); here both happen in one kernel, the weight
-// tile being expanded to bf16 in LDS right before the MFMAs read it.
+// tile being expanded to bf16 in LDS right before the MFMAs read it.  A
+// Q4_K_M checkpoint ("GGUF in transformers", section on the GGUF format) mixes
+// Q4_K with Q6_K tensors, so a layer's prefill needs both.
 //
 // Tiling.  A workgroup (4 wavefronts, one per SIMD) owns a BM x BN = 256 x 256
 // tile of Y; wavefront (wm, wn) owns the 128 x 128 quarter, as 4 x 4 blocks
 // of v_mfma_f32_32x32x16_bf16 (fp32 accumulators in the AGPRs).  K advances in
-// stages of BK = 64 inputs = one 32-byte slice of quants of every Q4_K
-// super-block row (sub-blocks 2c and 2c+1).
+// stages of BK = 64 inputs: one 32-byte slice of quants of a Q4_K super-block,
+// a quarter of a Q6_K super-block, or two Q4_0 blocks.
 //
 // Pipeline.  LDS holds two stage buffers.  While the MFMAs of stage s read
 // buffer s & 1, the same wavefronts write stage s+1 -- its X rows as loaded and
-// its W rows expanded to bf16 with w = (d * sc) * q - dmin * m in fp32, one
-// rounding to nearest even -- into the other buffer, in four slices placed
-// between the four 16-deep k steps; then they issue the global loads of stage
-// s+3 into the registers just freed (two register sets alternate, so a load
-// has more than a stage of MFMA work to arrive).  One LDS-only barrier per
-// stage.
+// its W rows expanded to bf16 (the format's fp32 weight, one rounding to
+// nearest even) -- into the other buffer, in four slices placed between the
+// four 16-deep k steps; then they issue the global loads of stage s+3 into the
+// registers just freed (two register sets alternate, so a load has more than a
+// stage of MFMA work to arrive).  One LDS-only barrier per stage.
 //
-// Rows of X past M and of W past N are read as zeros (buffer loads beyond
-// the resource's span); their outputs are never stored.
+// Rows of X past M and of W past N, and inputs past K, are read as zeros
+// (buffer loads beyond the resource's span); their outputs are never stored.
 #include "gq_device.h"
 #include "gq_internal.h"
 
@@ -49,33 +50,6 @@ __device__ __forceinline__ u32x4 bld16(Rsrc r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-// Global data of one stage for this thread: eight 16-byte chunks of X (one
-// from each of eight rows 32 apart), the 16-byte header and the 32-byte
-// quant slice of its W row.
-struct StageRegs {
-    u32x4 x[8];
-    u32x4 h, q0, q1;
-};
-
-// The (d*sc, dmin*m) pairs of sub-blocks 2c and 2c+1 (c uniform).
-struct Scales {
-    float dsL, dmL, dsH, dmH;
-};
-
-// Selects rather than branches: the decode sits in the same scheduling region
-// as the MFMAs it is interleaved with.
-__device__ __forceinline__ Scales q4k_scales(u32x4 hdr, int c) {
-    const float d = h2f(hdr.x & 0xffffu), dmin = h2f(hdr.x >> 16);
-    const int sh = 16 * (c & 1);
-    const uint32_t b0 = hdr.y >> sh, b1 = hdr.z >> sh, b2 = hdr.w >> sh;
-    const bool low = c < 2;
-    const uint32_t scL = low ? (b0 & 63u) : ((b2 & 15u) | (((b0 >> 6) & 3u) << 4));
-    const uint32_t mL = low ? (b1 & 63u) : (((b2 >> 4) & 15u) | (((b1 >> 6) & 3u) << 4));
-    const uint32_t scH = low ? ((b0 >> 8) & 63u) : (((b2 >> 8) & 15u) | (((b0 >> 14) & 3u) << 4));
-    const uint32_t mH = low ? ((b1 >> 8) & 63u) : (((b2 >> 12) & 15u) | (((b1 >> 14) & 3u) << 4));
-    return Scales{d * (float)scL, dmin * (float)mL, d * (float)scH, dmin * (float)mH};
-}
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
@@ -84,41 +58,178 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Expand quant bytes 8j..8j+7 of the slice (dwords w0, w1): low nibbles are
-// k = 8j..8j+7, high nibbles k = 32+8j..32+8j+7 -> two 16-byte rows of bf16.
-__device__ __forceinline__ void expand8(uint32_t w0, uint32_t w1, const Scales& s, u32x4& lo, u32x4& hi) {
-    uint32_t l0 = w0 & 0x0F0F0F0Fu, l1 = w1 & 0x0F0F0F0Fu;
-    uint32_t h0 = (w0 >> 4) & 0x0F0F0F0Fu, h1 = (w1 >> 4) & 0x0F0F0F0Fu;
+// Eight weights w_i = fmaf(s, q_i, -c) (q_i the bytes of two dwords whose
+// every byte is below 256) packed to bf16.
+__device__ __forceinline__ u32x4 expand_bytes(uint32_t w0, uint32_t w1, float s, float c) {
     // hide the known-zero bits: otherwise each byte is first extracted with a
     // bit-field instruction instead of being converted by v_cvt_f32_ubyteN
-    __asm__("" : "+v"(l0), "+v"(l1), "+v"(h0), "+v"(h1));
-    float a[8], b[8];
+    __asm__("" : "+v"(w0), "+v"(w1));
+    float a[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        a[i] = (float)((l0 >> (8 * i)) & 0xffu);
-        a[4 + i] = (float)((l1 >> (8 * i)) & 0xffu);
-        b[i] = (float)((h0 >> (8 * i)) & 0xffu);
-        b[4 + i] = (float)((h1 >> (8 * i)) & 0xffu);
+        a[i] = (float)((w0 >> (8 * i)) & 0xffu);
+        a[4 + i] = (float)((w1 >> (8 * i)) & 0xffu);
     }
-    // w = (d*sc) * q - dmin*m: both products exact in fp32, one rounding
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        a[i] = __builtin_fmaf(s.dsL, a[i], -s.dmL);
-        b[i] = __builtin_fmaf(s.dsH, b[i], -s.dmH);
-    }
-    lo = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])};
-    hi = u32x4{pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]), pack_bf16x2(b[4], b[5]), pack_bf16x2(b[6], b[7])};
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_fmaf(s, a[i], -c);
+    return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])};
 }
 
-__global__ __launch_bounds__(256, 1) void k_matmul_q4k(const uint8_t* __restrict__ W, int64_t N, int64_t K,
-                                                       const uint16_t* __restrict__ X, int64_t M, int64_t ldx,
-                                                       float* __restrict__ Y, int64_t ldy) {
+// Weight formats.  For one W row and stage s a format loads its bytes (Regs,
+// from the row's buffer offset woff; ok == false loads zeros), decodes the
+// stage's scales (Scl) and expands slice j (0..3): lo = stage inputs
+// 8j..8j+7, hi = 32+8j..32+8j+7, as bf16.
+template <int TYPE>
+struct WF;
+
+// Q4_K: stage s = slice c = s % 4 of super-block s / 4: quant bytes
+// 32c..32c+31 (low nibbles: sub-block 2c = inputs 0..31 of the stage, high
+// nibbles: 2c+1 = inputs 32..63) and the header.  w = (d sc) q - dmin m.
+template <>
+struct WF<T_Q4_K> {
+    static constexpr int QK = 256, BB = 144;
+    struct Regs {
+        u32x4 h, q0, q1;
+    };
+    struct Scl {
+        float dsL, dmL, dsH, dmH;
+    };
+    __device__ static void load(Rsrc wr, uint32_t woff, int s, bool ok, bool, Regs& r) {
+        const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * BB : 0x80000000u;
+        r.h = bld16(wr, bo);
+        r.q0 = bld16(wr, bo + 16 + 32 * (s & 3));
+        r.q1 = bld16(wr, bo + 32 + 32 * (s & 3));
+    }
+    // Selects rather than branches: the decode sits in the same scheduling
+    // region as the MFMAs it is interleaved with.
+    __device__ static Scl scales(const Regs& r, int s) {
+        const int c = s & 3;
+        const float d = h2f(r.h.x & 0xffffu), dmin = h2f(r.h.x >> 16);
+        const int sh = 16 * (c & 1);
+        const uint32_t b0 = r.h.y >> sh, b1 = r.h.z >> sh, b2 = r.h.w >> sh;
+        const bool low = c < 2;
+        const uint32_t scL = low ? (b0 & 63u) : ((b2 & 15u) | (((b0 >> 6) & 3u) << 4));
+        const uint32_t mL = low ? (b1 & 63u) : (((b2 >> 4) & 15u) | (((b1 >> 6) & 3u) << 4));
+        const uint32_t scH = low ? ((b0 >> 8) & 63u) : (((b2 >> 8) & 15u) | (((b0 >> 14) & 3u) << 4));
+        const uint32_t mH = low ? ((b1 >> 8) & 63u) : (((b2 >> 12) & 15u) | (((b1 >> 14) & 3u) << 4));
+        return Scl{d * (float)scL, dmin * (float)mL, d * (float)scH, dmin * (float)mH};
+    }
+    // quant bytes 8j..8j+7: low nibbles are inputs 8j.., high nibbles 32+8j..
+    // w = (d*sc) * q - dmin*m: both products exact in fp32, one rounding
+    __device__ static void expand(const Regs& r, const Scl& sc, int, int j, u32x4& lo, u32x4& hi) {
+        const u32x4 q = j < 2 ? r.q0 : r.q1;
+        const uint32_t w0 = q[2 * (j & 1)], w1 = q[2 * (j & 1) + 1];
+        lo = expand_bytes(w0 & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, sc.dsL, sc.dmL);
+        hi = expand_bytes((w0 >> 4) & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu, sc.dsH, sc.dmH);
+    }
+};
+
+// Q4_0: stage s = blocks 2s (inputs 0..31) and 2s+1 (32..63), 36 bytes from
+// row offset 36 s: block A = bytes 0..17 (d, then quants 2..17), block B =
+// bytes 18..35.  Input i < 16 of a block is the low nibble of its quant byte
+// i, input i >= 16 the high nibble of byte i-16.  w = d (q - 8), exact in fp32.
+template <>
+struct WF<T_Q4_0> {
+    static constexpr int QK = 32, BB = 18;
+    struct Regs {
+        u32x4 a, b;
+        uint32_t c;
+    };
+    struct Scl {
+        float dA, dB;
+    };
+    // full == false: the row ends after block A, and block B's bytes belong
+    // to the next row or lie past the buffer (where a load that straddles the
+    // end returns zeros as a whole) -- block A's last two quant bytes come
+    // from a dword that ends with them, the rest is zero (d_B = 0)
+    __device__ static void load(Rsrc wr, uint32_t woff, int s, bool ok, bool full, Regs& r) {
+        const uint32_t bo = ok ? woff + (uint32_t)s * (2 * BB) : 0x80000000u;
+        r.a = bld16(wr, bo);
+        r.b = bld16(wr, bo + 16);
+        r.c = __builtin_amdgcn_raw_buffer_load_b32(wr, (int)(bo + 32), 0, 0);
+        const uint32_t tail = __builtin_amdgcn_raw_buffer_load_b32(wr, (int)(bo + 14), 0, 0);
+        r.b = full ? r.b : u32x4{tail >> 16, 0u, 0u, 0u};
+        r.c = full ? r.c : 0u;
+    }
+    __device__ static Scl scales(const Regs& r, int) { return Scl{h2f(r.a.x & 0xffffu), h2f(r.b.x >> 16)}; }
+    __device__ static void expand(const Regs& r, const Scl& sc, int, int j, u32x4& lo, u32x4& hi) {
+        // quant dwords: A = bytes 2..17 (straddling dwords), B = bytes 20..35
+        const uint32_t qa[4] = {__builtin_amdgcn_alignbyte(r.a.y, r.a.x, 2), __builtin_amdgcn_alignbyte(r.a.z, r.a.y, 2),
+                                __builtin_amdgcn_alignbyte(r.a.w, r.a.z, 2), __builtin_amdgcn_alignbyte(r.b.x, r.a.w, 2)};
+        const uint32_t qb[4] = {r.b.y, r.b.z, r.b.w, r.c};
+        const int k = 2 * (j & 1), sh = j < 2 ? 0 : 4;
+        lo = expand_bytes((qa[k] >> sh) & 0x0F0F0F0Fu, (qa[k + 1] >> sh) & 0x0F0F0F0Fu, sc.dA, 8.0f * sc.dA);
+        hi = expand_bytes((qb[k] >> sh) & 0x0F0F0F0Fu, (qb[k + 1] >> sh) & 0x0F0F0F0Fu, sc.dB, 8.0f * sc.dB);
+    }
+};
+
+// Q6_K: stage s = quarter pair c = s % 4 of super-block s / 4: half h = c / 2,
+// quarters jq = 2 (c & 1) (inputs 0..31 of the stage) and jq + 1 (32..63).
+// Input l of quarter jq: q = nibble of ql[64h + 32 (jq & 1) + l] (low for
+// jq < 2) | bits 2jq, 2jq+1 of qh[32h + l] << 4; sub-block 8h + 2jq + l/16.
+// w = (d sc) (q - 32), one rounding.
+template <>
+struct WF<T_Q6_K> {
+    static constexpr int QK = 256, BB = 210;
+    struct Regs {
+        u32x4 l0, l1, l2, l3, h0, h1;
+        uint32_t sc, d;
+    };
+    struct Scl {
+        float s[4];  // (jq, sh 0), (jq, sh 1), (jq + 1, sh 0), (jq + 1, sh 1)
+    };
+    __device__ static void load(Rsrc wr, uint32_t woff, int s, bool ok, bool, Regs& r) {
+        const int c = s & 3, h = c >> 1;
+        const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * BB : 0x80000000u;
+        r.l0 = bld16(wr, bo + 64 * h);
+        r.l1 = bld16(wr, bo + 64 * h + 16);
+        r.l2 = bld16(wr, bo + 64 * h + 32);
+        r.l3 = bld16(wr, bo + 64 * h + 48);
+        r.h0 = bld16(wr, bo + 128 + 32 * h);
+        r.h1 = bld16(wr, bo + 128 + 32 * h + 16);
+        r.sc = __builtin_amdgcn_raw_buffer_load_b32(wr, (int)(bo + 192 + 8 * h + 4 * (c & 1)), 0, 0);
+        r.d = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 208), 0, 0);
+    }
+    __device__ static Scl scales(const Regs& r, int) {
+        const float d = h2f(r.d);
+        Scl o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o.s[i] = d * (float)(int)(int8_t)((r.sc >> (8 * i)) & 0xffu);
+        return o;
+    }
+    __device__ static void expand(const Regs& r, const Scl& sc, int s, int j, u32x4& lo, u32x4& hi) {
+        const uint32_t sh = 4u * (uint32_t)(s & 1);  // nibble shift; qh bits 2jq = sh, 2(jq+1) = sh + 2
+        const u32x4 la = j < 2 ? r.l0 : r.l1, lb = j < 2 ? r.l2 : r.l3, hq = j < 2 ? r.h0 : r.h1;
+        const int k = 2 * (j & 1), i = j >> 1;  // inputs 8j.. lie in sub-block i of each quarter
+        const uint32_t a0 = ((la[k] >> sh) & 0x0F0F0F0Fu) | (((hq[k] >> sh) & 0x03030303u) << 4);
+        const uint32_t a1 = ((la[k + 1] >> sh) & 0x0F0F0F0Fu) | (((hq[k + 1] >> sh) & 0x03030303u) << 4);
+        const uint32_t b0 = ((lb[k] >> sh) & 0x0F0F0F0Fu) | (((hq[k] >> (sh + 2)) & 0x03030303u) << 4);
+        const uint32_t b1 = ((lb[k + 1] >> sh) & 0x0F0F0F0Fu) | (((hq[k + 1] >> (sh + 2)) & 0x03030303u) << 4);
+        lo = expand_bytes(a0, a1, sc.s[i], 32.0f * sc.s[i]);
+        hi = expand_bytes(b0, b1, sc.s[2 + i], 32.0f * sc.s[2 + i]);
+    }
+};
+
+// Global data of one stage for this thread: eight 16-byte chunks of X (one
+// from each of eight rows 32 apart) and the stage's bytes of its W row.
+template <int TYPE>
+struct StageRegs {
+    u32x4 x[8];
+    typename WF<TYPE>::Regs w;
+};
+
+template <int TYPE>
+__global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W, int64_t N, int64_t K,
+                                                   const uint16_t* __restrict__ X, int64_t M, int64_t ldx,
+                                                   float* __restrict__ Y, int64_t ldy) {
+    using F = WF<TYPE>;
+    using SR = StageRegs<TYPE>;
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
-    const uint32_t row_bytes = (uint32_t)((K / 256) * 144);
-    const int S = (int)(K / BK);
+    const uint32_t row_bytes = (uint32_t)((K / F::QK) * F::BB);
+    const int S = (int)((K + BK - 1) / BK);  // a Q4_0 row may end half way into a stage
 
     // X: thread tid stages 16-byte chunk tid % 8 of rows tid / 8 + 32 i
     // (i = 0..7): eight lanes cover one row's 128 bytes, so every load
@@ -133,26 +244,24 @@ __global__ __launch_bounds__(256, 1) void k_matmul_q4k(const uint8_t* __restrict
     // a stage past the last loads zeros without touching memory (offset past
     // the buffers), so every load is unconditional and the load-counter waits
     // stay exact
-    auto load_stage = [&](int s, StageRegs& r) {
+    auto load_stage = [&](int s, SR& r) {
         const bool ok = s < S;
-        const uint32_t xo = ok ? xoff + (uint32_t)s * (BK * 2) : 0x80000000u;
+        // inputs past K (the second half of a Q4_0 row's last stage) read as zeros
+        const bool xok = ok && (TYPE != T_Q4_0 || (int64_t)s * BK + 8 * xchunk < K);
+        const uint32_t xo = xok ? xoff + (uint32_t)s * (BK * 2) : 0x80000000u;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r.x[i] = bld16(xr, ok ? xo + (uint32_t)i * xstride : xo);
-        const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * 144 : 0x80000000u;
-        r.h = bld16(wr, bo);
-        r.q0 = bld16(wr, bo + 16 + 32 * (s & 3));
-        r.q1 = bld16(wr, bo + 32 + 32 * (s & 3));
+        for (int i = 0; i < 8; ++i) r.x[i] = bld16(xr, xok ? xo + (uint32_t)i * xstride : xo);
+        F::load(wr, woff, s, ok, (int64_t)s * BK + 32 < K, r.w);
     };
     // slice j (0..3) of the stage's LDS writes: X chunks 2j, 2j+1 and W quant
     // bytes 8j..8j+7 expanded to k = 8j..8j+7 and 32+8j..32+8j+7
-    auto store_slice = [&](int s, const StageRegs& r, const Scales& sc, int buf, int j) {
+    auto store_slice = [&](int s, const SR& r, const typename F::Scl& sc, int buf, int j) {
         uint8_t* xs = lds + buf * BUF + xrow * ROWB + 16 * xchunk;
         uint8_t* ws = lds + buf * BUF + BM * ROWB + tid * ROWB;
         *reinterpret_cast<u32x4*>(xs + (2 * j) * 32 * ROWB) = r.x[2 * j];
         *reinterpret_cast<u32x4*>(xs + (2 * j + 1) * 32 * ROWB) = r.x[2 * j + 1];
-        const u32x4 q = j < 2 ? r.q0 : r.q1;
         u32x4 lo, hi;
-        expand8(q[2 * (j & 1)], q[2 * (j & 1) + 1], sc, lo, hi);
+        F::expand(r.w, sc, s, j, lo, hi);
         reinterpret_cast<u32x4*>(ws)[j] = lo;
         reinterpret_cast<u32x4*>(ws + 64)[j] = hi;
     };
@@ -171,12 +280,12 @@ __global__ __launch_bounds__(256, 1) void k_matmul_q4k(const uint8_t* __restrict
 
     // stage s's global data lives in register set s & 1; it is loaded two
     // stages before its LDS writes, which happen during stage s-1's MFMAs
-    auto stage_body = [&](int s, StageRegs& nxt) {
+    auto stage_body = [&](int s, SR& nxt) {
         const int cur = s & 1;
         const uint8_t* buf = lds + cur * BUF;
         // stage s+1's data arrived during the previous stage; past the last
         // stage it is zeros, written to a buffer nobody reads
-        const Scales sc = q4k_scales(nxt.h, (s + 1) & 3);
+        const typename F::Scl sc = F::scales(nxt.w, s + 1);
         bf16x8 a[2][4], b[2][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -215,12 +324,12 @@ __global__ __launch_bounds__(256, 1) void k_matmul_q4k(const uint8_t* __restrict
         lds_barrier();
     };
 
-    // S is a multiple of 4 (K is whole super-blocks)
-    StageRegs r0, r1;
+    // an odd S runs one stage of zeros at the end
+    SR r0, r1;
     if (S > 0) {
         load_stage(0, r0);
         load_stage(1, r1);
-        const Scales sc0 = q4k_scales(r0.h, 0);
+        const typename F::Scl sc0 = F::scales(r0.w, 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) store_slice(0, r0, sc0, 0, j);
         load_stage(2, r0);
@@ -249,17 +358,28 @@ __global__ __launch_bounds__(256, 1) void k_matmul_q4k(const uint8_t* __restrict
 
 }  // namespace
 
-hipError_t gqk_matmul(int type, const void* W, int64_t N, int64_t K, const void* X, int x_dtype, int64_t M,
-                      int64_t ldx, float* Y, int64_t ldy, hipStream_t s) {
-    (void)type;
-    (void)x_dtype;  // validated by the ABI: Q4_K weights, bf16 activations
+namespace {
+
+template <int TYPE>
+hipError_t launch(const void* W, int64_t N, int64_t K, const void* X, int64_t M, int64_t ldx, float* Y, int64_t ldy,
+                  hipStream_t s) {
     const int64_t gn = (N + BN - 1) / BN, gm = (M + BM - 1) / BM;
     if (gn > 0x7fffffff || gm > 65535) return hipErrorInvalidValue;
     // LDS above the default per-workgroup size (gfx950 allows 160 KB)
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul_q4k),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul<TYPE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_matmul_q4k, dim3((unsigned)gn, (unsigned)gm), dim3(256), LDS_BYTES, s,
+    hipLaunchKernelGGL(k_matmul<TYPE>, dim3((unsigned)gn, (unsigned)gm), dim3(256), LDS_BYTES, s,
                        static_cast<const uint8_t*>(W), N, K, static_cast<const uint16_t*>(X), M, ldx, Y, ldy);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t gqk_matmul(int type, const void* W, int64_t N, int64_t K, const void* X, int x_dtype, int64_t M,
+                      int64_t ldx, float* Y, int64_t ldy, hipStream_t s) {
+    (void)x_dtype;  // validated by the ABI: bf16 activations
+    if (type == T_Q4_0) return launch<T_Q4_0>(W, N, K, X, M, ldx, Y, ldy, s);
+    if (type == T_Q6_K) return launch<T_Q6_K>(W, N, K, X, M, ldx, Y, ldy, s);
+    return launch<T_Q4_K>(W, N, K, X, M, ldx, Y, ldy, s);
 }

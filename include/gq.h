@@ -175,9 +175,10 @@ gq_status gq_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts
 /* Prefill product Y[m][n] = sum_k X[m][k] * w[n][k] for 0 <= m < M, 0 <= n < N.
  * X: [M][ldx] of x_dtype (row stride ldx >= K elements); Y: [M][ldy] fp32
  * (ldy >= N).  Weight tiles are dequantised to bf16 in LDS and multiplied on
- * the matrix cores with fp32 accumulation.  This build implements t = GQ_Q4_K
- * with x_dtype = GQ_BF16 (other combinations: GQ_ERR_UNSUPPORTED).  K must be a
- * multiple of 256; M == 0 or N == 0 is a no-op. */
+ * the matrix cores with fp32 accumulation.  Every block type is accepted (a
+ * Q4_K_M layer mixes Q4_K and Q6_K tensors); x_dtype must be GQ_BF16
+ * (GQ_ERR_UNSUPPORTED otherwise).  K must be a multiple of the type's QK;
+ * M == 0 or N == 0 is a no-op. */
 gq_status gq_matmul(gq_type t, const void* W, int64_t N, int64_t K, const void* X,
                     gq_dtype x_dtype, int64_t M, int64_t ldx, float* Y, int64_t ldy,
                     hipStream_t stream);

@@ -144,7 +144,7 @@ def test_matmul_validation(lib):
     assert mm(2, A, 64, 256, A, 1, 16, 255, A, 64, None) == GQ_ERR_SHAPE  # ldx < K
     assert mm(2, A, 64, 256, A, 1, 16, 256, A, 63, None) == GQ_ERR_SHAPE  # ldy < N
     assert mm(2, A, 64, 256, A, 1, -1, 256, A, 64, None) == GQ_ERR_SHAPE
-    assert mm(1, A, 64, 256, A, 1, 16, 256, A, 64, None) == GQ_ERR_UNSUPPORTED
+    assert mm(1, A, 64, 48, A, 1, 16, 48, A, 64, None) == GQ_ERR_SHAPE  # Q4_0: whole 32-blocks
     assert mm(2, A, 64, 256, A, 0, 16, 256, A, 64, None) == GQ_ERR_UNSUPPORTED
     assert mm(2, None, 64, 256, A, 1, 16, 256, A, 64, None) == GQ_ERR_NULL
     assert mm(2, A, 64, 256, A, 1, 16, 256, MIS, 64, None) == GQ_ERR_ALIGN

@@ -1,10 +1,11 @@
-"""GPU parity of gq_matmul (Q4_K x bf16 prefill product on the matrix cores)
-against the CPU oracle.
+"""GPU parity of gq_matmul (Q4_0 / Q4_K / Q6_K x bf16 prefill product on the
+matrix cores) against the CPU oracle.
 
 Bar: |Y - Y_ref| <= 1e-3 * sum_k |X w| per element (weights enter the matrix
 cores as bf16, the rounding that the prefill reading fixes; Y_ref uses the exact
 fp32 weights).  Small shapes are compared element by element; the full
-3015 x 17408 x 5120 workload on sampled full rows and columns plus a
+3015 x 17408 x 5120 Q4_K workload (and the Q6_K down projection of the same
+layer family, 3015 x 5120 x 17408) on sampled full rows and columns plus a
 Freivalds checksum of the whole output."""
 from __future__ import annotations
 
@@ -63,36 +64,45 @@ def make_X(g, M, K, ldx=None):
 # rounding (2^-9 relative) and the errors average over K, so it is asserted
 # for K >= 1024 (the workload has K = 5120); test_matmul_is_bf16_weight_product
 # checks the arithmetic itself at any K.
-@pytest.mark.parametrize("M,N,K,padx,pady", [
-    (1, 64, 1024, 0, 0), (37, 130, 1024, 8, 6), (256, 128, 2048, 0, 0), (300, 257, 1024, 0, 3),
-    (513, 200, 1536, 64, 12), (7, 1000, 2048, 0, 0), (12, 40, 5120, 0, 0)])
-def test_matmul_small_full_compare(gq, orc, M, N, K, padx, pady):
-    g = synth.rng(0x67510005, M * 7 + N)
-    W = synth.weight("q4_k", g, N, K)
+SMALL = [(1, 64, 1024, 0, 0), (37, 130, 1024, 8, 6), (256, 128, 2048, 0, 0), (300, 257, 1024, 0, 3),
+         (513, 200, 1536, 64, 12), (7, 1000, 2048, 0, 0), (12, 40, 5120, 0, 0)]
+# Q4_0 rows may end half way into a 64-input stage (K = 32 mod 64)
+SMALL_Q4_0 = [(1, 64, 1056, 0, 0), (37, 130, 1024, 8, 6), (300, 257, 2080, 0, 3), (513, 200, 1536, 64, 12),
+              (7, 1000, 2048, 0, 0)]
+
+
+@pytest.mark.parametrize("t,M,N,K,padx,pady", [("q4_k",) + c for c in SMALL] + [("q6_k",) + c for c in SMALL]
+                         + [("q4_0",) + c for c in SMALL_Q4_0])
+def test_matmul_small_full_compare(gq, orc, t, M, N, K, padx, pady):
+    g = synth.rng(0x67510005, M * 7 + N + 100000 * ("q4_k", "q6_k", "q4_0").index(t))
+    W = synth.weight(t, g, N, K)
     xf, X = make_X(g, M, K, K + padx)
     Y = torch.full((M, N + pady), float("nan"), device="cuda")
-    gq.gq_matmul("q4_k", dev(W), N, K, X, Y)
+    gq.gq_matmul(t, dev(W), N, K, X, Y)
     torch.cuda.synchronize()
     y = Y.cpu().numpy()
-    yref, sa = orc.matmul_rows("q4_k", W, N, K, xf, np.arange(M))
-    r = check_bound(y[:, :N], yref, sa, "M=%d N=%d K=%d" % (M, N, K))
+    yref, sa = orc.matmul_rows(t, W, N, K, xf, np.arange(M))
+    r = check_bound(y[:, :N], yref, sa, "%s M=%d N=%d K=%d" % (t, M, N, K))
     if pady:
         assert np.all(np.isnan(y[:, N:])), "padding columns of Y were written"
     print("worst err/bound %.4f" % r)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (37, 132, 512), (256, 128, 256), (300, 260, 768)])
-def test_matmul_is_bf16_weight_product(gq, orc, M, N, K):
+@pytest.mark.parametrize("t,M,N,K", [("q4_k", 1, 64, 256), ("q4_k", 37, 132, 512), ("q4_k", 256, 128, 256),
+                                     ("q4_k", 300, 260, 768), ("q6_k", 1, 64, 256), ("q6_k", 37, 132, 512),
+                                     ("q6_k", 300, 260, 768), ("q4_0", 1, 64, 32), ("q4_0", 37, 132, 96),
+                                     ("q4_0", 256, 128, 64), ("q4_0", 300, 260, 544)])
+def test_matmul_is_bf16_weight_product(gq, orc, t, M, N, K):
     """The kernel computes sum_k X[m][k] * bf16(w[n][k]) with w the exact fp32
     weight (oracle dequant) rounded to nearest even: compared with an fp64
     product of those rounded weights, within an fp32 accumulation bound."""
-    g = synth.rng(0x67510005, 500 + M)
-    W = synth.weight("q4_k", g, N, K)
+    g = synth.rng(0x67510005, 500 + M + 1000 * ("q4_k", "q6_k", "q4_0").index(t))
+    W = synth.weight(t, g, N, K)
     xf, X = make_X(g, M, K)
     Y = torch.empty((M, N), device="cuda")
-    gq.gq_matmul("q4_k", dev(W), N, K, X, Y)
+    gq.gq_matmul(t, dev(W), N, K, X, Y)
     torch.cuda.synchronize()
-    wb = synth.bf16_to_f32(synth.bf16_bits(orc.dequant("q4_k", W))).reshape(N, K).astype(np.float64)
+    wb = synth.bf16_to_f32(synth.bf16_bits(orc.dequant(t, W))).reshape(N, K).astype(np.float64)
     ref = xf.astype(np.float64) @ wb.T
     absref = np.abs(xf.astype(np.float64)) @ np.abs(wb).T
     err = np.abs(Y.cpu().numpy().astype(np.float64) - ref)
@@ -142,4 +152,33 @@ def test_matmul_prefill_workload(gq, orc):
     got1 = float(Yd.sum())
     want1, tol1 = orc.matmul_checksum("q4_k", W, N, K, xf, ones_m, ones_n)
     assert abs(got1 - want1) <= 1e-3 * tol1
+    print("rows worst %.4f cols worst %.4f checksum |err|/tol %.2e" % (r1, r2, abs(got - want) / tol))
+
+
+def test_matmul_q6_k_down_prefill_workload(gq, orc):
+    """The Q6_K down projection of the hidden-5120 layer at the prefill length:
+    X bf16 [3015][17408] N(0,1) against Q6_K 5120 x 17408; 12 sampled full
+    rows (4 from the last partial 256-row tile), 12 sampled full columns and a
+    Freivalds checksum of all of Y."""
+    M, N, K = 3015, 5120, 17408
+    g = synth.rng(0x67510005, 1)
+    W = synth.weight("q6_k", g, N, K)
+    xf, X = make_X(g, M, K)
+    Y = torch.empty((M, N), device="cuda")
+    gq.gq_matmul("q6_k", dev(W), N, K, X, Y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Y).all())
+    s = np.random.default_rng(4321)
+    rows = np.unique(np.concatenate([[0, M - 1], s.choice(np.arange(2816, M - 1), 4, replace=False),
+                                     s.choice(np.arange(1, 2816), 6, replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], s.choice(np.arange(1, N - 1), 10, replace=False)]))
+    ref, sa = orc.matmul_rows("q6_k", W, N, K, xf, rows)
+    r1 = check_bound(Y[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, sa, "sampled rows")
+    refc, sac = orc.matmul_cols("q6_k", W, N, K, xf, cols)
+    r2 = check_bound(Y[:, torch.from_numpy(cols).cuda()].cpu().numpy(), refc, sac, "sampled columns")
+    u = s.choice([-1.0, 1.0], M)
+    v = s.choice([-1.0, 1.0], N)
+    got = float(torch.from_numpy(u).cuda() @ Y.double() @ torch.from_numpy(v).cuda())
+    want, tol = orc.matmul_checksum("q6_k", W, N, K, xf, u, v)
+    assert abs(got - want) <= 1e-3 * tol, (got, want, tol)
     print("rows worst %.4f cols worst %.4f checksum |err|/tol %.2e" % (r1, r2, abs(got - want) / tol))
