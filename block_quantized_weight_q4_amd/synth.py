@@ -11,6 +11,8 @@ Block fields written here (byte offsets inside one block):
   128 quant bytes at 16.
 * Q6_K (210 B): 128 low-bit bytes at 0, 64 high-bit bytes at 128, 16 int8
   scales at 192, fp16 ``d`` at 208.
+* Q5_K (176 B): fp16 ``d`` at 0, fp16 ``dmin`` at 2, 12 scale bytes at 4,
+  32 fifth-bit bytes at 16, 128 quant bytes at 48.
 
 Uniform quants and uniform 6-bit (scale, min) pairs are produced by uniform
 random *bytes*: every bit of the quant bytes and of Q4_K's 12 scale bytes
@@ -25,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-BLOCK = {"q4_0": (32, 18), "q4_k": (256, 144), "q6_k": (256, 210)}
+BLOCK = {"q4_0": (32, 18), "q4_k": (256, 144), "q6_k": (256, 210), "q5_k": (256, 176)}
 SEED_BASE = 0x67510000
 
 
@@ -68,8 +70,18 @@ def blocks_q6_k(g: np.random.Generator, n_blocks: int, d_scale: float = 1e-3,
     return out
 
 
+def blocks_q5_k(g: np.random.Generator, n_blocks: int, d_scale: float = 1e-3) -> np.ndarray:
+    """d, dmin = fp16(|N(0,1)| * d_scale); scales/mins uniform 0..63; 5-bit
+    quants uniform 0..31 (uniform quant and fifth-bit bytes)."""
+    out = np.empty((n_blocks, 176), np.uint8)
+    out[:, 0:2] = _f16_bytes(np.abs(g.standard_normal(n_blocks)) * d_scale)
+    out[:, 2:4] = _f16_bytes(np.abs(g.standard_normal(n_blocks)) * d_scale)
+    out[:, 4:176] = g.integers(0, 256, size=(n_blocks, 172), dtype=np.uint8)
+    return out
+
+
 def blocks(t: str, g: np.random.Generator, n_blocks: int) -> np.ndarray:
-    return {"q4_0": blocks_q4_0, "q4_k": blocks_q4_k, "q6_k": blocks_q6_k}[t](g, n_blocks)
+    return {"q4_0": blocks_q4_0, "q4_k": blocks_q4_k, "q6_k": blocks_q6_k, "q5_k": blocks_q5_k}[t](g, n_blocks)
 
 
 def weight(t: str, g: np.random.Generator, N: int, K: int) -> np.ndarray:

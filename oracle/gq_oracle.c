@@ -1,6 +1,6 @@
 /*
  * gq_oracle.c -- plain, slow, CPU reference for products against ggml
- * block-quantized weights (Q4_0, Q4_K, Q6_K).
+ * block-quantized weights (Q4_0, Q4_K, Q5_K, Q6_K).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
  * load this file; only the tests, the package smoke check and the benchmark's
@@ -20,6 +20,10 @@
  *      Q4_0: 32 weights / 18 B,  w = d * (q - 8)
  *      Q4_K: 256 weights / 144 B, w = (d * sc) * q - dmin * m
  *      Q6_K: 256 weights / 210 B, w = (d * sc) * (q - 32)
+ *      Q5_K: 256 weights / 176 B, w = (d * sc) * q - dmin * m (q 5-bit)
+ *    The Q5_K layout is the least supported reading: the pages give only the
+ *    Q5_K_M variant's file size; its pins are the size table and the
+ *    reduction to Q4_K when the fifth-bit plane is zero.
  *  - Each factor is converted to fp32 first and the formula is evaluated left
  *    to right in fp32 (the only rounding step is Q4_K's subtraction; every
  *    product here is exact in fp32).  Dot products accumulate in fp64, one term
@@ -36,6 +40,7 @@
 #define ORC_Q4_0 1
 #define ORC_Q4_K 2
 #define ORC_Q6_K 3
+#define ORC_Q5_K 4
 
 /* ---------------------------------------------------------------- fp16 ---- */
 
@@ -67,6 +72,7 @@ int oracle_block_info(int type, int32_t* elems, int32_t* bytes) {
     case ORC_Q4_0: *elems = 32;  *bytes = 2 + 16;             return 0;
     case ORC_Q4_K: *elems = 256; *bytes = 2 + 2 + 12 + 128;   return 0;
     case ORC_Q6_K: *elems = 256; *bytes = 128 + 64 + 16 + 2;  return 0;
+    case ORC_Q5_K: *elems = 256; *bytes = 2 + 2 + 12 + 32 + 128; return 0;
     default: return -1;
     }
 }
@@ -144,6 +150,33 @@ static void orc_dequant_q6_k(const uint8_t* b, float* w) {
     }
 }
 
+/* Q5_K super-block: Q4_K's header (d, dmin, the same 12 scale bytes) @0, then
+ * 32 bytes of fifth bits (qh) @16, then Q4_K's 128 quant bytes @48.  Weight i
+ * (chunk c = i/64, j = i%64) takes its low four bits exactly as in Q4_K and
+ * its fifth bit from bit 2c (j < 32) or 2c+1 (j >= 32) of qh[j % 32]:
+ * q = low | fifth << 4 (0..31).  w = (d * sc) * q - dmin * m. */
+static void orc_dequant_q5_k(const uint8_t* b, float* w) {
+    float d = orc_half_to_float(orc_rd16(b));
+    float dmin = orc_half_to_float(orc_rd16(b + 2));
+    const uint8_t* sb = b + 4;
+    const uint8_t* qh = b + 16;
+    const uint8_t* qs = b + 48;
+    for (int i = 0; i < 256; ++i) {
+        int c = i / 64, j = i % 64;
+        int upper = j >= 32;
+        int sub = 2 * c + upper;
+        int low = upper ? (qs[32 * c + j - 32] >> 4) : (qs[32 * c + j] & 0x0f);
+        int fifth = (qh[j % 32] >> sub) & 1;
+        int q = low | (fifth << 4);
+        int sc, m;
+        orc_q4k_scale_min(sb, sub, &sc, &m);
+        float a = d * (float)sc;
+        float p = a * (float)q;
+        float mn = dmin * (float)m;
+        w[i] = p - mn;
+    }
+}
+
 int oracle_dequant(int type, const uint8_t* blocks, int64_t n_blocks, float* out) {
     int32_t elems, bytes;
     if (oracle_block_info(type, &elems, &bytes)) return -1;
@@ -152,6 +185,7 @@ int oracle_dequant(int type, const uint8_t* blocks, int64_t n_blocks, float* out
         float* w = out + i * elems;
         if (type == ORC_Q4_0) orc_dequant_q4_0(b, w);
         else if (type == ORC_Q4_K) orc_dequant_q4_k(b, w);
+        else if (type == ORC_Q5_K) orc_dequant_q5_k(b, w);
         else orc_dequant_q6_k(b, w);
     }
     return 0;
@@ -507,7 +541,7 @@ static void orc_quant_q6_k(const float* x, uint8_t* b) {
 
 int oracle_quantize(int type, const float* x, int64_t n_blocks, uint8_t* out) {
     int32_t elems, bytes;
-    if (oracle_block_info(type, &elems, &bytes)) return -1;
+    if (oracle_block_info(type, &elems, &bytes) || type == ORC_Q5_K) return -1;  /* no Q5_K quantiser */
     for (int64_t i = 0; i < n_blocks; ++i) {
         if (type == ORC_Q4_0) orc_quant_q4_0(x + i * elems, out + i * bytes);
         else if (type == ORC_Q4_K) orc_quant_q4_k(x + i * elems, out + i * bytes);

@@ -22,8 +22,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gq_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-Q4_0, Q4_K, Q6_K = 1, 2, 3
-TYPES = {"q4_0": Q4_0, "q4_k": Q4_K, "q6_k": Q6_K}
+Q4_0, Q4_K, Q6_K, Q5_K = 1, 2, 3, 4
+TYPES = {"q4_0": Q4_0, "q4_k": Q4_K, "q6_k": Q6_K, "q5_k": Q5_K}
 
 CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared"]
 

@@ -16,6 +16,9 @@ Layout (byte offsets within one block):
       fp16 d @208.  Weight i: h = i // 128, r = i % 128, g = r // 32, l = r % 32;
       low 4 bits -> ql[64h + l + 32(g % 2)] (low nibble if g < 2, else high);
       high 2 bits -> bits 2g..2g+1 of qh[32h + l]; scale index 8h + r // 16.
+  Q5_K (256 weights, 176 B): Q4_K's 16-byte header, 32 fifth-bit bytes @16,
+      Q4_K's 128 quant bytes @48 (low four bits as in Q4_K).  Weight i
+      (c = i // 64, j = i % 64): fifth bit = bit 2c + (j >= 32) of qh[j % 32].
 """
 from __future__ import annotations
 
@@ -90,3 +93,17 @@ def q4_k_sub(i: int) -> int:
 def q6_k_sub(i: int) -> int:
     """Scale index (0..15) of weight i in a Q6_K block (16 consecutive weights)."""
     return i // 16
+
+
+def pack_q5_k(d_bits: int, dmin_bits: int, sc, m, q) -> np.ndarray:
+    q = [int(v) for v in q]
+    assert len(q) == 256 and all(0 <= v < 32 for v in q)
+    base = pack_q4_k(d_bits, dmin_bits, sc, m, [v & 15 for v in q])
+    b = np.zeros(176, np.uint8)
+    b[0:16] = base[0:16]
+    b[48:176] = base[16:144]
+    for i in range(256):
+        c, j = divmod(i, 64)
+        if q[i] >> 4:
+            b[16 + j % 32] |= 1 << (2 * c + (j >= 32))
+    return b

@@ -91,6 +91,38 @@ def test_q6_k_closed_form(orc):
     assert w.tolist() == exp
 
 
+def test_q5_k_closed_form(orc):
+    sc = [63, 48, 32, 17, 5, 60, 2, 40]
+    m = [33, 63, 1, 48, 59, 3, 62, 16]
+    q = [(i * 7 + 3) % 32 for i in range(256)]
+    w = orc.dequant("q5_k", packing.pack_q5_k(ONE, ONE, sc, m, q))
+    exp = [float(sc[packing.q4_k_sub(i)] * q[i] - m[packing.q4_k_sub(i)]) for i in range(256)]
+    assert w.tolist() == exp
+
+
+def test_q5_k_reduces_to_q4_k(orc):
+    """With its fifth-bit plane zero a Q5_K block is the Q4_K block made of its
+    header and quant bytes, weight for weight and bit for bit."""
+    from block_quantized_weight_q4_amd import synth
+    b5 = synth.blocks("q5_k", synth.rng(7, 7), 64)
+    b5[:, 16:48] = 0
+    b4 = np.concatenate([b5[:, 0:16], b5[:, 48:176]], axis=1)
+    w5 = orc.dequant("q5_k", b5.reshape(-1))
+    w4 = orc.dequant("q4_k", b4.reshape(-1))
+    assert np.array_equal(w5.view(np.uint32), w4.view(np.uint32))
+
+
+def test_q5_k_fifth_bit_positions(orc):
+    """One weight at a time carries q = 16 (only its fifth bit set): each weight
+    index maps to its own bit of the plane."""
+    for i in range(256):
+        q = [0] * 256
+        q[i] = 16
+        w = orc.dequant("q5_k", packing.pack_q5_k(ONE, ONE, [1] * 8, [0] * 8, q))
+        nz = np.nonzero(w)[0]
+        assert nz.tolist() == [i] and w[i] == 16.0
+
+
 def test_q6_k_quant_positions(orc):
     sc = [1] * 16
     for i in range(256):
@@ -175,6 +207,23 @@ def test_dequant_exact_rational(orc, seed):
                     sgn = 1.0
             else:
                 sgn = 1.0
+            assert w[i].view(np.uint32) == _f32_of_exact(e, sgn).view(np.uint32), (i, db, mb)
+    # Q5_K: Q4_K's arithmetic with 5-bit quants
+    for _ in range(6):
+        db, mb = _rand_f16(g, 2)
+        sc = g.integers(0, 64, 8)
+        m = g.integers(0, 64, 8)
+        q = g.integers(0, 32, 256)
+        w = orc.dequant("q5_k", packing.pack_q5_k(db, mb, sc, m, q))
+        d, dm = _exact_f16(db), _exact_f16(mb)
+        ds = -1.0 if db >> 15 else 1.0
+        ms = -1.0 if mb >> 15 else 1.0
+        for i in range(256):
+            s_ = packing.q4_k_sub(i)
+            p = d * int(sc[s_]) * int(q[i])
+            mm = dm * int(m[s_])
+            e = p - mm
+            sgn = (-1.0 if (ds < 0 and ms > 0) else 1.0) if (e == 0 and p == 0 and mm == 0) else 1.0
             assert w[i].view(np.uint32) == _f32_of_exact(e, sgn).view(np.uint32), (i, db, mb)
     # Q6_K
     for _ in range(12):
@@ -473,12 +522,15 @@ def test_file_size_table_bits_per_weight(orc):
         tab = json.load(f)
     gb = {r["variant"]: r["gigabytes"] for r in tab["rows"]}
     params = gb["BF16"] * 1e9 / 2.0
-    bpw = {t: orc.block_info(t)[1] * 8 / orc.block_info(t)[0] for t in ("q4_0", "q4_k", "q6_k")}
-    assert bpw == {"q4_0": 4.5, "q4_k": 4.5, "q6_k": 6.5625}
+    bpw = {t: orc.block_info(t)[1] * 8 / orc.block_info(t)[0] for t in ("q4_0", "q4_k", "q5_k", "q6_k")}
+    assert bpw == {"q4_0": 4.5, "q4_k": 4.5, "q5_k": 5.5, "q6_k": 6.5625}
     q6 = gb["Q6_K"] * 8e9 / params
     q4m = gb["Q4_K_M"] * 8e9 / params
+    q5m = gb["Q5_K_M"] * 8e9 / params
     assert bpw["q6_k"] <= q6 < bpw["q6_k"] + 0.5
     assert bpw["q4_k"] < q4m < bpw["q6_k"]
+    # Q5_K_M mixes Q5_K with higher-precision (Q6_K) tensors
+    assert bpw["q5_k"] < q5m < bpw["q6_k"]
     assert gb["Q4_K_M"] < gb["Q5_K_M"] < gb["Q6_K"] < gb["BF16"]
 
 
@@ -504,6 +556,10 @@ MUTATIONS = {
                             "for (int64_t k = 0; k + 1 < K; ++k) {\n                double p = (double)row[k] * (double)xb[k];"),
     "matvec_id ignores routing weight": ("y[(int64_t)t * N + n] += r * s;", "y[(int64_t)t * N + n] += s;"),
     "checksum transposed": ("wv[k] += v[n] * (double)wrow[k];", "wv[k] += v[k % N] * (double)wrow[k];"),
+    "q5_k fifth bit from the chunk's plane only": ("int fifth = (qh[j % 32] >> sub) & 1;",
+                                                  "int fifth = (qh[j % 32] >> (2 * c)) & 1;"),
+    "q5_k fifth bit weight 8": ("int q = low | (fifth << 4);", "int q = low | (fifth << 3);"),
+    "q5_k quants read from the fifth-bit plane": ("const uint8_t* qs = b + 48;", "const uint8_t* qs = b + 16;"),
     "route ties to the higher id": ("if (best < 0 || l[e] > l[best]) best = e;",
                                     "if (best < 0 || l[e] >= l[best]) best = e;"),
     "route softmax without the max shift": ("double e = exp((double)l[ids[(int64_t)t * top_k + j]] - l0);",
@@ -519,6 +575,9 @@ PINS = [
         ([s + 1 for s in range(8)], list(range(8))),
         ([1, 2, 3, 4, 32, 48, 63, 33], [0, 5, 10, 63, 16, 48, 63, 1]))],
     lambda o: test_q6_k_closed_form(o),
+    lambda o: test_q5_k_closed_form(o),
+    lambda o: test_q5_k_reduces_to_q4_k(o),
+    lambda o: test_q5_k_fifth_bit_positions(o),
     lambda o: test_dequant_exact_rational(o, 0),
     lambda o: test_matvec_brute_force_fsum(o, "q4_0", 160),
     lambda o: test_matvec_id_reduces_to_matvec(o),
