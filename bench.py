@@ -390,6 +390,24 @@ def bench_context(torch, gq, synth, dev, stream, t_):
     res["q4_0_2048x2048_b1"] = {"us": round(ms * 1e3, 3), "GBps": round(w1.nbytes / (ms * 1e-3) / 1e9, 1)}
     del c1
 
+    # Q5_K (the Q5_K_M variant's main type) at the hidden-5120 gate shape, batch 1 and 8, bf16
+    w5 = synth.weight("q5_k", synth.rng(0x67510007, 0), 17408, 5120)
+    c5 = [t_(w5) for _ in range(max(2, -(-ROTATE_BYTES // w5.nbytes)))]
+    for B in (1, 8):
+        x5 = t_(synth.bf16_bits(synth.normal_f32(synth.rng(0x67510007, B), (B, 5120))).view(np.int16)).view(
+            torch.bfloat16)
+        y5 = torch.empty(B, 17408, device=dev)
+
+        def p5():
+            for c in c5:
+                gq.gq_matvec("q5_k", c, 17408, 5120, x5, y5, stream)
+
+        ms = Timer(torch, p5, stream).time(10) / len(c5)
+        res["q5_k_17408x5120_bf16_b%d" % B] = {"us": round(ms * 1e3, 3),
+                                               "GBps": round(w5.nbytes / (ms * 1e-3) / 1e9, 1)}
+    del c5
+    torch.cuda.empty_cache()
+
     # dense layer at batch 4
     mats = {name: synth.weight("q4_k", synth.rng(0x67510002, i), N, K) for i, (name, N, K) in enumerate(DENSE)}
     host = {"qkv": (np.concatenate([mats["q"], mats["k"], mats["v"]]), 6144, 2560), "o": (mats["o"], 2560, 4096),

@@ -22,7 +22,7 @@ if not os.path.exists(lib_path):
 
 _lib = ctypes.CDLL(lib_path)
 
-TYPES = {"q4_0": 1, "q4_k": 2, "q6_k": 3}
+TYPES = {"q4_0": 1, "q4_k": 2, "q6_k": 3, "q5_k": 4}
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 _STATUS = {}
 

@@ -8,10 +8,10 @@
 
 namespace {
 
-bool known_type(int t) { return t == GQ_Q4_0 || t == GQ_Q4_K || t == GQ_Q6_K; }
+bool known_type(int t) { return t == GQ_Q4_0 || t == GQ_Q4_K || t == GQ_Q6_K || t == GQ_Q5_K; }
 
 int qk_of(int t) { return t == GQ_Q4_0 ? 32 : 256; }
-int bytes_of(int t) { return t == GQ_Q4_0 ? 18 : (t == GQ_Q4_K ? 144 : 210); }
+int bytes_of(int t) { return t == GQ_Q4_0 ? 18 : (t == GQ_Q4_K ? 144 : (t == GQ_Q5_K ? 176 : 210)); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -7,6 +7,7 @@
 //   Q4_0  w = d * (q - 8)
 //   Q4_K  w = (d * sc) * q - dmin * m
 //   Q6_K  w = (d * sc) * (q - 32)
+//   Q5_K  w = (d * sc) * q - dmin * m   (Q4_K's, with 5-bit q)
 // Every product is exact in fp32 (fp16 d has 11 significant bits, the integer
 // factors at most 12), so the fp32 result is unique; bf16/fp16 outputs are that
 // fp32 value rounded to nearest even.
@@ -73,6 +74,30 @@ __device__ __forceinline__ void dq_q4_k(const uint8_t* blk, int part, float w[8]
     }
 }
 
+__device__ __forceinline__ void dq_q5_k(const uint8_t* blk, int part, float w[8]) {
+    // as Q4_K with the quants 32 bytes further (after the fifth-bit plane);
+    // weight 8p + i takes its fifth bit from bit `sub` of plane byte (j0 & 31) + i
+    u32x4 hdr = ld16a(blk);
+    int c = part >> 3, j0 = 8 * (part & 7);
+    int hi = j0 >= 32;
+    int sub = 2 * c + hi;
+    u32x2 q = *reinterpret_cast<const u32x2*>(blk + 48 + 32 * c + (j0 & 31));
+    u32x2 qh = *reinterpret_cast<const u32x2*>(blk + 16 + (j0 & 31));
+    int sc, m;
+    q4k_scale_min(hdr, sub, sc, m);
+    float d = h2f(hdr.x & 0xffffu), dmin = h2f(hdr.x >> 16);
+    float a = d * (float)sc;
+    float mm = dmin * (float)m;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t byte = (q[i >> 2] >> (8 * (i & 3))) & 0xffu;
+        uint32_t hb = (qh[i >> 2] >> (8 * (i & 3))) & 0xffu;
+        int qq = (int)((hi ? (byte >> 4) : (byte & 15u)) | (((hb >> sub) & 1u) << 4));
+        float p = a * (float)qq;
+        w[i] = p - mm;
+    }
+}
+
 __device__ __forceinline__ void dq_q6_k(const uint8_t* blk, int part, float w[8]) {
     // part p: weights 8p..8p+7 -> half h = p/16, r0 = 8*(p%16), group g = r0/32,
     // lane l0 = r0%32.
@@ -97,7 +122,7 @@ template <int TYPE, int OUT>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ blocks, int64_t n_parts,
                                                  void* __restrict__ out) {
     constexpr int QK = TYPE == T_Q4_0 ? 32 : 256;
-    constexpr int BB = TYPE == T_Q4_0 ? 18 : (TYPE == T_Q4_K ? 144 : 210);
+    constexpr int BB = TYPE == T_Q4_0 ? 18 : (TYPE == T_Q4_K ? 144 : (TYPE == T_Q5_K ? 176 : 210));
     constexpr int PPB = QK / 8;
     int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= n_parts) return;
@@ -107,6 +132,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ blo
     float w[8];
     if (TYPE == T_Q4_0) dq_q4_0(bp, part, w);
     else if (TYPE == T_Q4_K) dq_q4_k(bp, part, w);
+    else if (TYPE == T_Q5_K) dq_q5_k(bp, part, w);
     else dq_q6_k(bp, part, w);
     if (OUT == DT_F32) {
         f32x4* o = reinterpret_cast<f32x4*>(out) + 2 * gid;
@@ -143,5 +169,6 @@ hipError_t gqk_dequant(int type, const void* blocks, int64_t n_blocks, void* out
     if (n_blocks == 0) return hipSuccess;
     if (type == T_Q4_0) return launch_t<T_Q4_0>(blocks, n_blocks, out, out_dtype, s);
     if (type == T_Q4_K) return launch_t<T_Q4_K>(blocks, n_blocks, out, out_dtype, s);
+    if (type == T_Q5_K) return launch_t<T_Q5_K>(blocks, n_blocks, out, out_dtype, s);
     return launch_t<T_Q6_K>(blocks, n_blocks, out, out_dtype, s);
 }

@@ -13,7 +13,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Block geometry (weights per block, bytes per block) of the three formats.
-enum { T_Q4_0 = 1, T_Q4_K = 2, T_Q6_K = 3 };
+enum { T_Q4_0 = 1, T_Q4_K = 2, T_Q6_K = 3, T_Q5_K = 4 };
 enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 
 // fp16 pair (1024, 1024): OR-ing a small integer n into the low mantissa bits

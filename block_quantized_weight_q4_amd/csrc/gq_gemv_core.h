@@ -194,6 +194,52 @@ struct Fmt<T_Q4_K> {
     }
 };
 
+// ---------------------------------------------------------------- Q5_K ----
+// Q4_K with a plane of fifth bits (32 bytes at 16; the quants move to 48).
+// Unit c as for Q4_K; the pair of sub-block 2c (low nibbles, value 1024 + q)
+// takes bit 2c of the plane byte as its bit 4, the pair of 2c+1 (high nibbles
+// in place, 1024 + 16 q) takes bit 2c+1 as its bit 8: one rotate and one
+// and-or per pair.
+template <>
+struct Fmt<T_Q5_K> : Fmt<T_Q4_K> {
+    static constexpr int BB = 176;
+    struct Raw : Fmt<T_Q4_K>::Raw {
+        u32x4 f0, f1;
+        uint32_t rlo, rhi;
+    };
+    struct Lane : Fmt<T_Q4_K>::Lane {
+        uint32_t rlo, rhi;  // right rotations: plane bit 2c -> bit 4, bit 2c+1 -> bit 8
+        __device__ explicit Lane(int c) : Fmt<T_Q4_K>::Lane(c) {
+            qoff = 48 + 32 * c;
+            rlo = (uint32_t)(2 * c - 4) & 31u;
+            rhi = (uint32_t)(2 * c + 1 - 8) & 31u;
+        }
+    };
+    __device__ static Raw load(Rsrc rs, uint32_t boff, const Lane& ln) {
+        Raw r;
+        r.h = bld16(rs, boff);
+        r.q0 = bld16(rs, boff + ln.qoff);
+        r.q1 = bld16(rs, boff + ln.qoff + 16);
+        r.f0 = bld16(rs, boff + 16);
+        r.f1 = bld16(rs, boff + 32);
+        r.rlo = ln.rlo;
+        r.rhi = ln.rhi;
+        return r;
+    }
+    __device__ static void pairs(const Raw& r, int a, uint32_t magic, uint32_t P[NP]) {
+        const uint32_t mask = a == 0 ? 0x000F000Fu : 0x00F000F0u;
+        const uint32_t fm = a == 0 ? 0x00100010u : 0x01000100u;
+        const uint32_t rot = a == 0 ? r.rlo : r.rhi;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t w = k < 4 ? r.q0[k] : r.q1[k - 4];
+            const uint32_t f = k < 4 ? r.f0[k] : r.f1[k - 4];
+            P[2 * k] = ((w & mask) | magic) | (__builtin_amdgcn_alignbit(f, f, rot) & fm);
+            P[2 * k + 1] = (((w >> 8) & mask) | magic) | (__builtin_amdgcn_alignbit(f, f, rot + 8u) & fm);
+        }
+    }
+};
+
 // ---------------------------------------------------------------- Q6_K ----
 // Unit (h, lh) of a super-block, unit % 4 = 2h + lh: lanes l = 16 lh .. 16 lh
 // + 15 of the four 32-weight groups g of half h (64 weights, four 16-weight

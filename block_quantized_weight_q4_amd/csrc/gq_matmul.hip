@@ -124,6 +124,41 @@ struct WF<T_Q4_K> {
     }
 };
 
+// Q5_K: Q4_K with a 32-byte plane of fifth bits at 16 (quants at 48): input
+// 8j + i of slice j (low nibble, sub-block 2c) takes bit 2c of plane byte
+// 8j + i as its bit 4, input 32 + 8j + i (high nibble) bit 2c + 1.
+template <>
+struct WF<T_Q5_K> {
+    static constexpr int QK = 256, BB = 176;
+    struct Regs {
+        u32x4 h, q0, q1, f0, f1;
+    };
+    using Scl = WF<T_Q4_K>::Scl;
+    __device__ static void load(Rsrc wr, uint32_t woff, int s, bool ok, bool, Regs& r) {
+        const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * BB : 0x80000000u;
+        r.h = bld16(wr, bo);
+        r.q0 = bld16(wr, bo + 48 + 32 * (s & 3));
+        r.q1 = bld16(wr, bo + 64 + 32 * (s & 3));
+        r.f0 = bld16(wr, bo + 16);
+        r.f1 = bld16(wr, bo + 32);
+    }
+    __device__ static Scl scales(const Regs& r, int s) {
+        WF<T_Q4_K>::Regs h4;
+        h4.h = r.h;
+        return WF<T_Q4_K>::scales(h4, s);
+    }
+    __device__ static void expand(const Regs& r, const Scl& sc, int s, int j, u32x4& lo, u32x4& hi) {
+        const u32x4 q = j < 2 ? r.q0 : r.q1, f = j < 2 ? r.f0 : r.f1;
+        const int k = 2 * (j & 1);
+        const uint32_t sl = 2u * (uint32_t)(s & 3), sh = sl + 1u;
+        const uint32_t w0 = q[k], w1 = q[k + 1], f0 = f[k], f1 = f[k + 1];
+        lo = expand_bytes((w0 & 0x0F0F0F0Fu) | (((f0 >> sl) & 0x01010101u) << 4),
+                          (w1 & 0x0F0F0F0Fu) | (((f1 >> sl) & 0x01010101u) << 4), sc.dsL, sc.dmL);
+        hi = expand_bytes(((w0 >> 4) & 0x0F0F0F0Fu) | (((f0 >> sh) & 0x01010101u) << 4),
+                          ((w1 >> 4) & 0x0F0F0F0Fu) | (((f1 >> sh) & 0x01010101u) << 4), sc.dsH, sc.dmH);
+    }
+};
+
 // Q4_0: stage s = blocks 2s (inputs 0..31) and 2s+1 (32..63), 36 bytes from
 // row offset 36 s: block A = bytes 0..17 (d, then quants 2..17), block B =
 // bytes 18..35.  Input i < 16 of a block is the low nibble of its quant byte
@@ -381,5 +416,6 @@ hipError_t gqk_matmul(int type, const void* W, int64_t N, int64_t K, const void*
     (void)x_dtype;  // validated by the ABI: bf16 activations
     if (type == T_Q4_0) return launch<T_Q4_0>(W, N, K, X, M, ldx, Y, ldy, s);
     if (type == T_Q6_K) return launch<T_Q6_K>(W, N, K, X, M, ldx, Y, ldy, s);
+    if (type == T_Q5_K) return launch<T_Q5_K>(W, N, K, X, M, ldx, Y, ldy, s);
     return launch<T_Q4_K>(W, N, K, X, M, ldx, Y, ldy, s);
 }

@@ -76,5 +76,6 @@ hipError_t gqk_matvec(int type, const void* W, int64_t N, int64_t K, const void*
     const uint8_t* w = static_cast<const uint8_t*>(W);
     if (type == T_Q4_0) return launch_x<T_Q4_0>(w, N, K, xs, x_dtype, batch, y, s);
     if (type == T_Q4_K) return launch_x<T_Q4_K>(w, N, K, xs, x_dtype, batch, y, s);
+    if (type == T_Q5_K) return launch_x<T_Q5_K>(w, N, K, xs, x_dtype, batch, y, s);
     return launch_x<T_Q6_K>(w, N, K, xs, x_dtype, batch, y, s);
 }

@@ -248,6 +248,7 @@ hipError_t gqk_matvec_id(int type, const void* experts, int n_experts, int64_t N
     hipError_t e;
     if (type == T_Q4_0) e = launch_experts_x<T_Q4_0>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, ids, n_experts, hdr, out, s);
     else if (type == T_Q4_K) e = launch_experts_x<T_Q4_K>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, ids, n_experts, hdr, out, s);
+    else if (type == T_Q5_K) e = launch_experts_x<T_Q5_K>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, ids, n_experts, hdr, out, s);
     else e = launch_experts_x<T_Q6_K>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, ids, n_experts, hdr, out, s);
     if (e != hipSuccess || !route_w) return e;
     const unsigned nx = (unsigned)((N + 255) / 256);

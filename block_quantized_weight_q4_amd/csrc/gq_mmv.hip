@@ -219,8 +219,11 @@ struct MU<T_Q4_K, XT> {
     // b[0..11] = h.y, h.z, h.w, j = 2 (c & 1):
     //   c < 2:  sc = b[j] & 63,                        m = b[j+4] & 63
     //   c >= 2: sc = (b[j+8] & 15) | (b[j] >> 6) << 4, m = (b[j+8] >> 4) | (b[j+4] >> 6) << 4
-    // both built as bytes [scL, scH, mL, mH] with permutes.
-    __device__ void compute(int c, f32x4& y) const {
+    // both built as bytes [scL, scH, mL, mH] with permutes.  With FIFTH, f
+    // holds the fifth bits of the lane's eight weights (Q5_K): bit 2c for
+    // sub-block 2c and 2c+1 for 2c+1.
+    template <bool FIFTH>
+    __device__ void compute_q(int c, const u32x2& f, f32x4& y) const {
         const uint32_t j = 2u * (uint32_t)(c & 1);
         const uint32_t C = __builtin_amdgcn_perm(h.z, h.y, j | (j + 1) << 8 | (j + 4) << 16 | (j + 5) << 24);
         const uint32_t A = __builtin_amdgcn_perm(h.w, h.w, j | (j + 1) << 8 | j << 16 | (j + 1) << 24);
@@ -231,8 +234,17 @@ struct MU<T_Q4_K, XT> {
         const float mL = (dmin * (float)((v >> 16) & 0xffu)) * 0.0078125f;
         const float mH = (dmin * (float)(v >> 24)) * 0.0078125f;
         const uint32_t t0 = perm(q.x, SEL01), t1 = perm(q.x, SEL23), t2 = perm(q.y, SEL01), t3 = perm(q.y, SEL23);
-        const u32x4 bl = {nib_lo(t0), nib_lo(t1), nib_lo(t2), nib_lo(t3)};
-        const u32x4 bh = {nib_hi(t0), nib_hi(t1), nib_hi(t2), nib_hi(t3)};
+        u32x4 bl = {nib_lo(t0), nib_lo(t1), nib_lo(t2), nib_lo(t3)};
+        u32x4 bh = {nib_hi(t0), nib_hi(t1), nib_hi(t2), nib_hi(t3)};
+        if constexpr (FIFTH) {
+            const uint32_t u[4] = {perm(f.x, SEL01), perm(f.x, SEL23), perm(f.y, SEL01), perm(f.y, SEL23)};
+            const uint32_t sl = 2u * (uint32_t)c, sh = sl + 1u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bl[i] |= ((u[i] >> sl) & 0x00010001u) << 4;
+                bh[i] |= ((u[i] >> sh) & 0x00010001u) << 4;
+            }
+        }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f}, az = acc;
         xa.mma(bl, BMAG, acc, az);
         add_sub_block_min(y, sL, mL, acc, az);
@@ -241,6 +253,25 @@ struct MU<T_Q4_K, XT> {
         xb.mma(bh, BMAG, acc, az);
         add_sub_block_min(y, sH, mH, acc, az);
     }
+    __device__ void compute(int c, f32x4& y) const { compute_q<false>(c, u32x2{0u, 0u}, y); }
+};
+
+// Q5_K: Q4_K with a 32-byte plane of fifth bits at 16 (quants at 48).  Group g
+// also loads plane bytes 8g..8g+7: bit 2c of byte 8g + j is the fifth bit of
+// k-slot j in sub-block 2c, bit 2c+1 in sub-block 2c+1.  Operands 128 + q,
+// q <= 31, stay exact in bf16.
+template <int XT>
+struct MU<T_Q5_K, XT> : MU<T_Q4_K, XT> {
+    static constexpr int BB = 176;
+    u32x2 f;
+    __device__ void load(Rsrc ws, uint32_t bo, int g, Rsrc xs, uint32_t xo, uint32_t k, int c) {
+        this->h = bld16(ws, bo);
+        this->q = bld8(ws, bo + 48 + 32 * c + 8 * g);
+        f = bld8(ws, bo + 16 + 8 * g);
+        this->xa.load8(xs, xo, k + 8 * g);
+        this->xb.load8(xs, xo, k + 32 + 8 * g);
+    }
+    __device__ void compute(int c, f32x4& y) const { this->template compute_q<true>(c, f, y); }
 };
 
 // Q6_K: unit u % 4 = 2h + a of a super-block: half h, quarters jq = a (low
@@ -393,5 +424,6 @@ hipError_t gqk_mmv(int type, const void* W, int64_t N, int64_t K, const void* x,
     const uint8_t* xb = static_cast<const uint8_t*>(x);
     if (type == T_Q4_0) return launch_x<T_Q4_0>(w, N, K, xb, x_dtype, batch, y, s);
     if (type == T_Q4_K) return launch_x<T_Q4_K>(w, N, K, xb, x_dtype, batch, y, s);
+    if (type == T_Q5_K) return launch_x<T_Q5_K>(w, N, K, xb, x_dtype, batch, y, s);
     return launch_x<T_Q6_K>(w, N, K, xb, x_dtype, batch, y, s);
 }

@@ -28,6 +28,12 @@
  *   GQ_Q6_K: 256 weights, 210 B.  128 B low 4-bit parts @0, 64 B high 2-bit
  *             parts @128, 16 int8 scales @192 (one per 16 weights), fp16 d @208.
  *             w = (d * sc) * (q - 32), q in 0..63.
+ *   GQ_Q5_K: 256 weights, 176 B.  Q4_K's 16-byte header @0, 32 bytes of fifth
+ *             bits @16, Q4_K's 128 quant bytes @48.  Weight i (chunk c = i/64,
+ *             j = i%64) has Q4_K's low four bits and, as bit 4, bit 2c + (j >=
+ *             32) of fifth-bit byte j % 32.  w = (d * sc) * q - dmin * m, q in
+ *             0..31.  (The pages list the Q5_K_M variant in the size table of
+ *             "GGUF in transformers" but print no layout; this is ggml's.)
  *
  * Matrix layout: a matrix with N output rows and K inputs is N rows of K/QK
  * consecutive blocks each (QK = 32 or 256), rows back to back with no padding.
@@ -58,7 +64,7 @@ extern "C" {
 
 #define GQ_ABI_VERSION 1
 
-typedef enum { GQ_Q4_0 = 1, GQ_Q4_K = 2, GQ_Q6_K = 3 } gq_type;
+typedef enum { GQ_Q4_0 = 1, GQ_Q4_K = 2, GQ_Q6_K = 3, GQ_Q5_K = 4 } gq_type;
 
 typedef enum { GQ_F32 = 0, GQ_BF16 = 1, GQ_F16 = 2 } gq_dtype;
 

@@ -57,10 +57,10 @@ def test_version_and_status_strings(lib):
 
 def test_block_info(lib):
     e, b = ctypes.c_int32(), ctypes.c_int32()
-    for t, want in ((1, (32, 18)), (2, (256, 144)), (3, (256, 210))):
+    for t, want in ((1, (32, 18)), (2, (256, 144)), (3, (256, 210)), (4, (256, 176))):
         assert lib.gq_block_info(t, ctypes.byref(e), ctypes.byref(b)) == GQ_OK
         assert (e.value, b.value) == want
-    assert lib.gq_block_info(4, ctypes.byref(e), ctypes.byref(b)) == GQ_ERR_TYPE
+    assert lib.gq_block_info(5, ctypes.byref(e), ctypes.byref(b)) == GQ_ERR_TYPE
     assert lib.gq_block_info(0, ctypes.byref(e), ctypes.byref(b)) == GQ_ERR_TYPE
     assert lib.gq_block_info(2, None, ctypes.byref(b)) == GQ_ERR_NULL
 

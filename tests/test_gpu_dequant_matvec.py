@@ -18,7 +18,7 @@ from tests import packing
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-3
-TYPES = ("q4_0", "q4_k", "q6_k")
+TYPES = ("q4_0", "q4_k", "q6_k", "q5_k")
 
 
 @pytest.fixture(autouse=True)
@@ -81,11 +81,13 @@ def special_blocks(t: str, g) -> np.ndarray:
         b = synth.blocks(t, g, 1)[0].copy()
         if t == "q4_0":
             b[0], b[1] = s & 0xFF, s >> 8
-        elif t == "q4_k":
+        elif t in ("q4_k", "q5_k"):
             s2 = specials[(i + 3) % len(specials)]
             b[0], b[1], b[2], b[3] = s & 0xFF, s >> 8, s2 & 0xFF, s2 >> 8
             if i % 2:
                 b[4:16] = 0xFF  # all scale/min bits set (63)
+            if t == "q5_k" and i % 3 == 0:
+                b[16:48] = 0xFF  # every fifth bit set
         else:
             b[208], b[209] = s & 0xFF, s >> 8
             if i % 3 == 0:
@@ -132,6 +134,7 @@ SHAPES = {
     "q4_0": [(1, 32), (3, 96), (705, 2048), (37, 2816), (64, 704), (257, 4096)],
     "q4_k": [(1, 256), (3, 512), (705, 2560), (130, 9728), (64, 17408), (9, 4096)],
     "q6_k": [(1, 256), (5, 512), (333, 5120), (70, 17408), (41, 1024)],
+    "q5_k": [(1, 256), (3, 512), (705, 2560), (130, 9728), (9, 4096)],
 }
 
 
@@ -220,7 +223,7 @@ def test_matvec_zero_point_rows_are_exactly_zero(gq, orc, t):
     N, K = 12, 512
     W = synth.weight(t, g, N, K).copy()
     nb = K // (32 if t == "q4_0" else 256)
-    bb = {"q4_0": 18, "q4_k": 144, "q6_k": 210}[t]
+    bb = {"q4_0": 18, "q4_k": 144, "q6_k": 210, "q5_k": 176}[t]
     for r in range(0, N, 2):
         for j in range(nb):
             blk = W[r, j * bb:(j + 1) * bb]
@@ -230,8 +233,9 @@ def test_matvec_zero_point_rows_are_exactly_zero(gq, orc, t):
                 blk[0:128] = 0x00
                 blk[128:192] = 0xAA  # high parts 2 -> q = 32
             else:
-                blk[:] = packing.pack_q4_k(int(blk[0]) | int(blk[1]) << 8, int(blk[2]) | int(blk[3]) << 8,
-                                           [int(v) for v in g.integers(0, 64, 8)], [0] * 8, [0] * 256)
+                pack = packing.pack_q4_k if t == "q4_k" else packing.pack_q5_k
+                blk[:] = pack(int(blk[0]) | int(blk[1]) << 8, int(blk[2]) | int(blk[3]) << 8,
+                              [int(v) for v in g.integers(0, 64, 8)], [0] * 8, [0] * 256)
     x = synth.normal_f32(g, (3, K))
     y = run_matvec(gq, t, W, N, K, dev(x), 3)
     yref, sa = orc.matvec(t, W, N, K, x)

@@ -72,9 +72,9 @@ SMALL_Q4_0 = [(1, 64, 1056, 0, 0), (37, 130, 1024, 8, 6), (300, 257, 2080, 0, 3)
 
 
 @pytest.mark.parametrize("t,M,N,K,padx,pady", [("q4_k",) + c for c in SMALL] + [("q6_k",) + c for c in SMALL]
-                         + [("q4_0",) + c for c in SMALL_Q4_0])
+                         + [("q4_0",) + c for c in SMALL_Q4_0] + [("q5_k",) + c for c in SMALL[:4]])
 def test_matmul_small_full_compare(gq, orc, t, M, N, K, padx, pady):
-    g = synth.rng(0x67510005, M * 7 + N + 100000 * ("q4_k", "q6_k", "q4_0").index(t))
+    g = synth.rng(0x67510005, M * 7 + N + 100000 * ("q4_k", "q6_k", "q4_0", "q5_k").index(t))
     W = synth.weight(t, g, N, K)
     xf, X = make_X(g, M, K, K + padx)
     Y = torch.full((M, N + pady), float("nan"), device="cuda")
@@ -91,12 +91,13 @@ def test_matmul_small_full_compare(gq, orc, t, M, N, K, padx, pady):
 @pytest.mark.parametrize("t,M,N,K", [("q4_k", 1, 64, 256), ("q4_k", 37, 132, 512), ("q4_k", 256, 128, 256),
                                      ("q4_k", 300, 260, 768), ("q6_k", 1, 64, 256), ("q6_k", 37, 132, 512),
                                      ("q6_k", 300, 260, 768), ("q4_0", 1, 64, 32), ("q4_0", 37, 132, 96),
-                                     ("q4_0", 256, 128, 64), ("q4_0", 300, 260, 544)])
+                                     ("q4_0", 256, 128, 64), ("q4_0", 300, 260, 544), ("q5_k", 37, 132, 512),
+                                     ("q5_k", 300, 260, 768)])
 def test_matmul_is_bf16_weight_product(gq, orc, t, M, N, K):
     """The kernel computes sum_k X[m][k] * bf16(w[n][k]) with w the exact fp32
     weight (oracle dequant) rounded to nearest even: compared with an fp64
     product of those rounded weights, within an fp32 accumulation bound."""
-    g = synth.rng(0x67510005, 500 + M + 1000 * ("q4_k", "q6_k", "q4_0").index(t))
+    g = synth.rng(0x67510005, 500 + M + 1000 * ("q4_k", "q6_k", "q4_0", "q5_k").index(t))
     W = synth.weight(t, g, N, K)
     xf, X = make_X(g, M, K)
     Y = torch.empty((M, N), device="cuda")

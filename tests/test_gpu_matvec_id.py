@@ -15,8 +15,8 @@ from block_quantized_weight_q4_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-BB = {"q4_0": 18, "q4_k": 144, "q6_k": 210}
-QK = {"q4_0": 32, "q4_k": 256, "q6_k": 256}
+BB = {"q4_0": 18, "q4_k": 144, "q6_k": 210, "q5_k": 176}
+QK = {"q4_0": 32, "q4_k": 256, "q6_k": 256, "q5_k": 256}
 
 
 @pytest.fixture(autouse=True)
@@ -93,10 +93,10 @@ def test_moe_workload_gate_up_down(gq, orc):
     print("down (routed) worst err/bound %.4f" % r)
 
 
-@pytest.mark.parametrize("t", ["q4_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("t", ["q4_0", "q4_k", "q6_k", "q5_k"])
 @pytest.mark.parametrize("xdt", ["f32", "bf16"])
 def test_matvec_id_shapes(gq, orc, t, xdt):
-    g = synth.rng(0x67510004, 10 + ["q4_0", "q4_k", "q6_k"].index(t))
+    g = synth.rng(0x67510004, 10 + ["q4_0", "q4_k", "q6_k", "q5_k"].index(t))
     for (E, N, K, T, k) in ((5, 37, 512, 3, 2), (16, 130, 1024, 6, 4), (9, 64, 2048, 16, 3)):
         ex = synth.weight(t, g, E * N, K)
         ids = g.integers(0, E, (T, k)).astype(np.int32)

@@ -59,7 +59,8 @@ def test_matvec_mma_zero_point_rows_are_exactly_zero(gq, orc, t):
     N, K = 40, 1024
     W = synth.weight(t, g, N, K).copy()
     nb = K // (32 if t == "q4_0" else 256)
-    bb = {"q4_0": 18, "q4_k": 144, "q6_k": 210}[t]
+    bb = {"q4_0": 18, "q4_k": 144, "q6_k": 210, "q5_k": 176}[t]
+    pack = packing.pack_q4_k if t == "q4_k" else packing.pack_q5_k
     for r in range(0, N, 2):
         for j in range(nb):
             blk = W[r, j * bb:(j + 1) * bb]
@@ -69,11 +70,11 @@ def test_matvec_mma_zero_point_rows_are_exactly_zero(gq, orc, t):
                 blk[0:128] = 0x00
                 blk[128:192] = 0xAA  # high parts 2 -> q = 32
             elif r % 4 == 0:
-                blk[:] = packing.pack_q4_k(int(blk[0]) | int(blk[1]) << 8, int(blk[2]) | int(blk[3]) << 8,
-                                           [int(v) for v in g.integers(0, 64, 8)], [0] * 8, [0] * 256)
+                blk[:] = pack(int(blk[0]) | int(blk[1]) << 8, int(blk[2]) | int(blk[3]) << 8,
+                              [int(v) for v in g.integers(0, 64, 8)], [0] * 8, [0] * 256)
             else:  # zero scales and mins, any quants
-                blk[:] = packing.pack_q4_k(int(blk[0]) | int(blk[1]) << 8, int(blk[2]) | int(blk[3]) << 8,
-                                           [0] * 8, [0] * 8, [int(v) for v in g.integers(0, 16, 256)])
+                blk[:] = pack(int(blk[0]) | int(blk[1]) << 8, int(blk[2]) | int(blk[3]) << 8,
+                              [0] * 8, [0] * 8, [int(v) for v in g.integers(0, 16, 256)])
     for xdt in ("f32", "bf16"):
         x, x_t = make_x(g, 13, K, xdt)
         y = run_matvec(gq, t, W, N, K, x_t, 13)
