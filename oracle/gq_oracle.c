@@ -550,6 +550,32 @@ int oracle_quantize(int type, const float* x, int64_t n_blocks, uint8_t* out) {
     return 0;
 }
 
+/* ----------------------------------------------------- gated unit ---- */
+
+/*
+ * Gated feed-forward unit: h = act(g) * u elementwise, where g and u are the
+ * gate and up products of the same vector.  "GGUF in transformers" (section
+ * "Reusing ggml's Metal kernels") notes that a specialised kernel may merge
+ * several operations; the models on the pages use gated blocks (Qwen3.5:
+ * SiLU; Gemma 4: tanh-approximated GELU).  In fp64, by the definitions:
+ *   act 0 (SiLU):      g / (1 + exp(-g))
+ *   act 1 (GELU tanh): g/2 * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3)))
+ */
+int oracle_glu(const double* g, const double* u, int64_t n, int act, double* h) {
+    if (act != 0 && act != 1) return 1;
+    for (int64_t i = 0; i < n; ++i) {
+        double a;
+        if (act == 0) {
+            a = g[i] / (1.0 + exp(-g[i]));
+        } else {
+            double c = sqrt(2.0 / acos(-1.0));  /* sqrt(2/pi) */
+            a = 0.5 * g[i] * (1.0 + tanh(c * (g[i] + 0.044715 * g[i] * g[i] * g[i])));
+        }
+        h[i] = a * u[i];
+    }
+    return 0;
+}
+
 /* Exposed for the tests' fp16 pins. */
 /* ------------------------------------------------------------ routing ---- */
 

@@ -53,6 +53,7 @@ def _setup(cdll):
                                             ctypes.POINTER(ctypes.c_double)]
     cdll.oracle_quantize.argtypes = [ctypes.c_int, P, I64, P]
     cdll.oracle_route_topk.argtypes = [P, I32, I32, I32, P, P]
+    cdll.oracle_glu.argtypes = [P, P, I64, ctypes.c_int, P]
     cdll.oracle_half_to_float.argtypes = [ctypes.c_uint16]
     cdll.oracle_half_to_float.restype = ctypes.c_float
     cdll.oracle_float_to_half.argtypes = [ctypes.c_float]
@@ -178,6 +179,17 @@ def route_topk(logits: np.ndarray, top_k: int):
     if lib().oracle_route_topk(_p(logits), T, E, top_k, _p(ids), _p(w)):
         raise RuntimeError("oracle_route_topk failed")
     return ids, w
+
+
+def glu(g: np.ndarray, u: np.ndarray, act: str) -> np.ndarray:
+    """h = act(g) * u elementwise in fp64; act "silu" or "gelu_tanh"."""
+    g = _c(g, np.float64)
+    u = _c(u, np.float64)
+    assert g.shape == u.shape
+    h = np.empty(g.shape)
+    if lib().oracle_glu(_p(g), _p(u), g.size, {"silu": 0, "gelu_tanh": 1}[act], _p(h)):
+        raise RuntimeError("oracle_glu failed")
+    return h
 
 
 def matmul_rows(t, W: np.ndarray, N: int, K: int, X: np.ndarray, rows):

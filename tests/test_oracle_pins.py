@@ -349,6 +349,39 @@ def test_route_large_logits_do_not_overflow(orc):
     assert ids.tolist() == [[0, 1]] and np.all(w == 0.5)
 
 
+# ------------------------------------------------------------ gated unit ----
+
+def test_glu_silu_is_x_times_logistic(orc):
+    """SiLU against scipy's logistic function (an independent library routine)."""
+    from scipy.special import expit
+    g = np.linspace(-40, 40, 2001)
+    h = orc.glu(g, np.ones_like(g), "silu")
+    assert np.allclose(h, g * expit(g), rtol=1e-14, atol=1e-300)
+    assert orc.glu(np.array([0.0]), np.array([1.0]), "silu")[0] == 0.0
+
+
+def test_glu_gelu_tanh_close_to_exact_gelu(orc):
+    """The tanh form stays within 5e-4 of the exact GELU x * Phi(x) (scipy's
+    normal cdf) everywhere; a wrong constant in it does not."""
+    from scipy.special import ndtr
+    g = np.linspace(-8, 8, 4001)
+    h = orc.glu(g, np.ones_like(g), "gelu_tanh")
+    assert np.max(np.abs(h - g * ndtr(g))) < 5e-4
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
+def test_glu_odd_part_and_product(orc, act):
+    """Both activations satisfy act(x) - act(-x) = x (their non-linear part is
+    even), and h is linear in the up value."""
+    g = np.random.default_rng(3).standard_normal(500) * 4
+    one = np.ones_like(g)
+    d = orc.glu(g, one, act) - orc.glu(-g, one, act)
+    assert np.allclose(d, g, rtol=1e-12, atol=1e-12)
+    u = np.random.default_rng(4).standard_normal(500)
+    assert np.allclose(orc.glu(g, u, act), orc.glu(g, one, act) * u, rtol=1e-15, atol=0)
+    assert np.all(orc.glu(g, np.zeros_like(g), act) == 0)
+
+
 def test_matvec_id_reduces_to_matvec(orc):
     g = np.random.default_rng(5)
     E, N, K, T, k = 6, 9, 64, 3, 4
@@ -560,6 +593,9 @@ MUTATIONS = {
                                                   "int fifth = (qh[j % 32] >> (2 * c)) & 1;"),
     "q5_k fifth bit weight 8": ("int q = low | (fifth << 4);", "int q = low | (fifth << 3);"),
     "q5_k quants read from the fifth-bit plane": ("const uint8_t* qs = b + 48;", "const uint8_t* qs = b + 16;"),
+    "silu uses e^+g": ("a = g[i] / (1.0 + exp(-g[i]));", "a = g[i] / (1.0 + exp(g[i]));"),
+    "gelu cubic coefficient": ("(g[i] + 0.044715 * g[i] * g[i] * g[i])", "(g[i] + 0.44715 * g[i] * g[i] * g[i])"),
+    "glu drops the up value": ("h[i] = a * u[i];", "h[i] = a;"),
     "route ties to the higher id": ("if (best < 0 || l[e] > l[best]) best = e;",
                                     "if (best < 0 || l[e] >= l[best]) best = e;"),
     "route softmax without the max shift": ("double e = exp((double)l[ids[(int64_t)t * top_k + j]] - l0);",
@@ -582,6 +618,9 @@ PINS = [
     lambda o: test_matvec_brute_force_fsum(o, "q4_0", 160),
     lambda o: test_matvec_id_reduces_to_matvec(o),
     lambda o: test_matmul_rows_cols_checksum(o),
+    lambda o: test_glu_silu_is_x_times_logistic(o),
+    lambda o: test_glu_gelu_tanh_close_to_exact_gelu(o),
+    lambda o: [test_glu_odd_part_and_product(o, a) for a in ("silu", "gelu_tanh")],
     lambda o: test_route_closed_form(o),
     lambda o: test_route_ties_go_to_the_lower_id(o),
     lambda o: test_route_full_top_k_is_a_stable_descending_sort(o),
