@@ -408,6 +408,34 @@ def bench_context(torch, gq, synth, dev, stream, t_):
     del c5
     torch.cuda.empty_cache()
 
+    # dense layer at batch 1 with the fused gated unit: qkv, o, then
+    # h = silu(gate x) * (up x) in one launch feeding the down projection
+    mats = {name: synth.weight("q4_k", synth.rng(0x67510002, i), N, K) for i, (name, N, K) in enumerate(DENSE)}
+    lb = sum(m.nbytes for m in mats.values())
+    qkv = np.concatenate([mats["q"], mats["k"], mats["v"]])
+    cpf = [{"qkv": t_(qkv), "o": t_(mats["o"]), "gate": t_(mats["gate"]), "up": t_(mats["up"]),
+            "down": t_(mats["down"])} for _ in range(max(2, -(-ROTATE_BYTES // lb)))]
+    gx = synth.rng(0x67510002, 100)
+    xq = t_(synth.normal_f32(gx, (1, 2560)))
+    xo = t_(synth.normal_f32(gx, (1, 4096)))
+    xf = t_(synth.normal_f32(gx, (1, 2560)))
+    yq, yo = torch.empty(1, 6144, device=dev), torch.empty(1, 2560, device=dev)
+    hf, yd = torch.empty(1, 9728, device=dev), torch.empty(1, 2560, device=dev)
+
+    def pf():
+        for c in cpf:
+            gq.gq_matvec("q4_k", c["qkv"], 6144, 2560, xq, yq, stream)
+            gq.gq_matvec("q4_k", c["o"], 2560, 4096, xo, yo, stream)
+            gq.gq_matvec_glu("q4_k", c["gate"], c["up"], 9728, 2560, xf, "silu", hf, stream)
+            gq.gq_matvec("q4_k", c["down"], 2560, 9728, hf, yd, stream)
+
+    ms = Timer(torch, pf, stream).time(20) / len(cpf)
+    res["q4_k_dense_layer_b1_fused_glu"] = {
+        "launches": "qkv, o, silu(gate)*up, down(h)", "us_per_layer": round(ms * 1e3, 2),
+        "GBps": round(lb / (ms * 1e-3) / 1e9, 1)}
+    del cpf
+    torch.cuda.empty_cache()
+
     # dense layer at batch 4
     mats = {name: synth.weight("q4_k", synth.rng(0x67510002, i), N, K) for i, (name, N, K) in enumerate(DENSE)}
     host = {"qkv": (np.concatenate([mats["q"], mats["k"], mats["v"]]), 6144, 2560), "o": (mats["o"], 2560, 4096),

@@ -38,8 +38,10 @@ _lib.gq_matvec_id.argtypes = [ctypes.c_int, P, I32, I64, I64, P, I32, I32, P, ct
 _lib.gq_matvec_id_check.argtypes = [P, P, ctypes.POINTER(I32)]
 _lib.gq_matmul.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I64, I64, P, I64, P]
 _lib.gq_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
+_lib.gq_matvec_glu.argtypes = [ctypes.c_int, P, P, I64, I64, P, ctypes.c_int, I32, ctypes.c_int, P, ctypes.c_int, P]
+ACTS = {"silu": 0, "gelu_tanh": 1}
 for _f in ("gq_block_info", "gq_dequant", "gq_matvec", "gq_matvec_id_workspace", "gq_matvec_id",
-           "gq_matvec_id_check", "gq_matmul", "gq_route_topk"):
+           "gq_matvec_id_check", "gq_matmul", "gq_route_topk", "gq_matvec_glu"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -96,6 +98,15 @@ def gq_matvec(t, W: torch.Tensor, N: int, K: int, x: torch.Tensor, y: torch.Tens
     _check("gq_matvec", _lib.gq_matvec(_type(t), _ptr(W), N, K, _ptr(x), _DTYPES[x.dtype], batch, _ptr(y),
                                        _stream(stream)))
     return y
+
+
+def gq_matvec_glu(t, W_gate: torch.Tensor, W_up: torch.Tensor, N: int, K: int, x: torch.Tensor, act: str,
+                  h: torch.Tensor, stream=None) -> torch.Tensor:
+    """h[b][n] = act(w_gate[n] . x[b]) * (w_up[n] . x[b]); x [batch][K] fp32/bf16, h [batch][N] fp32/bf16."""
+    batch = x.numel() // K if K else (h.numel() // N if N else 1)
+    _check("gq_matvec_glu", _lib.gq_matvec_glu(_type(t), _ptr(W_gate), _ptr(W_up), N, K, _ptr(x), _DTYPES[x.dtype],
+                                               batch, ACTS[act], _ptr(h), _DTYPES[h.dtype], _stream(stream)))
+    return h
 
 
 def gq_matvec_id_workspace(n_experts: int, n_tokens: int, top_k: int, N: int) -> int:

@@ -92,6 +92,24 @@ gq_status gq_matvec(gq_type t, const void* W, int64_t N, int64_t K, const void* 
     }
 }
 
+gq_status gq_matvec_glu(gq_type t, const void* W_gate, const void* W_up, int64_t N, int64_t K, const void* x,
+                        gq_dtype x_dtype, int32_t batch, gq_act act, void* h, gq_dtype h_dtype, hipStream_t stream) {
+    if (!known_type(t)) return GQ_ERR_TYPE;
+    if (x_dtype != GQ_F32 && x_dtype != GQ_BF16) return GQ_ERR_DTYPE;
+    if (h_dtype != GQ_F32 && h_dtype != GQ_BF16) return GQ_ERR_DTYPE;
+    if (N < 0 || K < 0 || K % qk_of(t) != 0 || batch < 1) return GQ_ERR_SHAPE;
+    if (N > MAX_ELEMS || K > MAX_K_DECODE || (K > 0 && N > MAX_ELEMS / K)) return GQ_ERR_SHAPE;
+    if (batch > 8 || (act != GQ_ACT_SILU && act != GQ_ACT_GELU_TANH)) return GQ_ERR_UNSUPPORTED;
+    if (N == 0) return GQ_OK;
+    if (!h || (K > 0 && (!W_gate || !W_up || !x))) return GQ_ERR_NULL;
+    if (!aligned16(h) || (K > 0 && (!aligned16(W_gate) || !aligned16(W_up) || !aligned16(x)))) return GQ_ERR_ALIGN;
+    try {
+        return from_hip(gqk_matvec_glu(t, W_gate, W_up, N, K, x, x_dtype, batch, act, h, h_dtype, stream));
+    } catch (...) {
+        return GQ_ERR_LAUNCH;
+    }
+}
+
 gq_status gq_matvec_id_workspace(int32_t n_experts, int32_t n_tokens, int32_t top_k, int64_t N, size_t* bytes) {
     if (!bytes) return GQ_ERR_NULL;
     if (n_experts < 1 || n_tokens < 0 || top_k < 1 || top_k > n_experts || N < 0 ||

@@ -561,8 +561,11 @@ constexpr int D_MAX = 6;
 constexpr int PREFETCH = 3;
 constexpr int D_RING = 4;
 
-// The whole decode product for one workgroup: rows [rowA, rowA + waves * SR)
-// of the packed matrix W (N rows, K inputs) against nb <= BMAX staged vectors.
+// The whole decode product for one workgroup: rows [rowA, rowA + wcount * SR)
+// of the packed matrix W (N rows, K inputs) against nb <= BMAX staged vectors;
+// this wavefront is number wslot of the wcount that share those rows (all
+// wavefronts of the workgroup stage the activations together, so wavefronts
+// of one workgroup may work on different matrices with the same K).
 //
 // Each K tile of U units gives every lane T = ceil(U / LPR) units.  Without
 // RING, T <= D: the loads of the first min(D, PREFETCH) units are issued
@@ -572,17 +575,17 @@ constexpr int D_RING = 4;
 template <int TYPE, int XT, int BMAX, int D, bool RING>
 __device__ __forceinline__ void gemv_workgroup(const uint8_t* __restrict__ W, int64_t N, int64_t K, int64_t rowA,
                                                const XSrc& xs, int nb, const YDst& yd, int LPR, int tile_units,
-                                               uint8_t* lds) {
+                                               uint8_t* lds, int wslot, int wcount) {
     using F = Fmt<TYPE>;
     using Raw = typename F::Raw;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int SR = 64 / LPR;
     const int s = lane / LPR, v = lane - s * LPR;
     const uint32_t row_bytes = (uint32_t)((K / F::QK) * F::BB);
-    const int64_t wg_rows = (int64_t)(blockDim.x >> 6) * SR;
+    const int64_t wg_rows = (int64_t)wcount * SR;
     const int64_t rows_here = N - rowA < wg_rows ? N - rowA : wg_rows;
     const Rsrc rs = make_rsrc(W + rowA * (int64_t)row_bytes, (uint32_t)rows_here * row_bytes);
-    const int rloc = wave * SR + s;
+    const int rloc = wslot * SR + s;
     const bool row_ok = rloc < rows_here;
     const typename F::Lane ln(v % F::UPB);
     // byte offset of the block of unit (u0 + v + LPR t) is blk0 + t * step

@@ -11,6 +11,9 @@ hipError_t gqk_dequant(int type, const void* blocks, int64_t n_blocks, void* out
 
 hipError_t gqk_matvec(int type, const void* W, int64_t N, int64_t K, const void* x, int x_dtype,
                       int batch, float* y, hipStream_t s);
+// Gated unit: h = act(W_gate x) * (W_up x), batch 1..8 (gq_matvec.hip).
+hipError_t gqk_matvec_glu(int type, const void* Wg, const void* Wu, int64_t N, int64_t K, const void* x, int x_dtype,
+                          int batch, int act, void* h, int h_dtype, hipStream_t s);
 // The same product on the matrix cores, batch 1..16 (gq_mmv.hip).
 hipError_t gqk_mmv(int type, const void* W, int64_t N, int64_t K, const void* x, int x_dtype, int batch,
                    float* y, hipStream_t s);

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
     }
     __syncthreads();
     gemv_workgroup<TYPE, XT, 8, D, RING>(experts + (int64_t)e * expert_bytes, N, K, rowA, xs, nb, yd, LPR,
-                                          tile_units, lds);
+                                          tile_units, lds, (int)(threadIdx.x >> 6), NTHREADS >> 6);
 }
 
 // ------------------------------------------------------------- combine ----

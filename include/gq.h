@@ -68,6 +68,9 @@ typedef enum { GQ_Q4_0 = 1, GQ_Q4_K = 2, GQ_Q6_K = 3, GQ_Q5_K = 4 } gq_type;
 
 typedef enum { GQ_F32 = 0, GQ_BF16 = 1, GQ_F16 = 2 } gq_dtype;
 
+/* Activations of a gated feed-forward unit (gq_matvec_glu). */
+typedef enum { GQ_ACT_SILU = 0, GQ_ACT_GELU_TANH = 1 } gq_act;
+
 typedef enum {
     GQ_OK = 0,
     GQ_ERR_TYPE = 1,        /* unknown block type */
@@ -125,6 +128,27 @@ gq_status gq_dequant(gq_type t, const void* blocks, int64_t n_blocks, void* out,
  * that vector alone (bit for bit) within one path. */
 gq_status gq_matvec(gq_type t, const void* W, int64_t N, int64_t K, const void* x,
                     gq_dtype x_dtype, int32_t batch, float* y, hipStream_t stream);
+
+/* Gated feed-forward unit in one launch: for 0 <= b < batch, 0 <= n < N,
+ *   h[b][n] = act(g) * u,  g = sum_k w_gate[n][k] x[b][k],  u = sum_k w_up[n][k] x[b][k].
+ * "GGUF in transformers" (section "Reusing ggml's Metal kernels") notes that a
+ * specialised kernel can merge several operations; this one merges the gate
+ * and up projections with the activation and product between them, so that h
+ * can feed the down projection directly.  The two products share the staged
+ * activations and each weight byte is read once.
+ *   act GQ_ACT_SILU:      act(g) = g / (1 + e^-g)  (SwiGLU, Qwen-style blocks)
+ *   act GQ_ACT_GELU_TANH: act(g) = g/2 (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3)))
+ *                         (GeGLU, Gemma-style blocks)
+ * W_gate, W_up: packed [N][K/QK] blocks of type t (separate matrices, or the
+ * two halves of one [2N] gate|up matrix).  x: [batch][K] of x_dtype (GQ_F32 or
+ * GQ_BF16).  h: [batch][N] of h_dtype (GQ_F32, or GQ_BF16 rounded to nearest
+ * even).  1 <= batch <= 8 (GQ_ERR_UNSUPPORTED above, and for an unknown act).
+ * K limited as for gq_matvec; N == 0 is a no-op; K == 0 writes zeros.
+ * Accuracy: g and u as gq_matvec's dot-product path; act in fp32 (expf,
+ * tanhf), then one fp32 product (and the bf16 rounding). */
+gq_status gq_matvec_glu(gq_type t, const void* W_gate, const void* W_up, int64_t N, int64_t K, const void* x,
+                        gq_dtype x_dtype, int32_t batch, gq_act act, void* h, gq_dtype h_dtype,
+                        hipStream_t stream);
 
 /* Workspace bytes needed by gq_matvec_id for these sizes (host only). */
 gq_status gq_matvec_id_workspace(int32_t n_experts, int32_t n_tokens, int32_t top_k, int64_t N,

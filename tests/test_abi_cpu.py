@@ -32,6 +32,7 @@ def lib(gq_lib_path):
     L.gq_matmul.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I64, I64, P, I64, P]
     L.gq_block_info.argtypes = [ctypes.c_int, ctypes.POINTER(I32), ctypes.POINTER(I32)]
     L.gq_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
+    L.gq_matvec_glu.argtypes = [ctypes.c_int, P, P, I64, I64, P, ctypes.c_int, I32, ctypes.c_int, P, ctypes.c_int, P]
     return L
 
 
@@ -43,7 +44,7 @@ def declared_functions() -> list[str]:
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -183,3 +184,21 @@ def test_route_topk_validation(lib):
     assert r(A, 8, 128, 8, MIS, A, None) == GQ_ERR_ALIGN
     assert r(A, 8, 128, 8, A, MIS, None) == GQ_ERR_ALIGN
     assert r(None, 0, 128, 8, None, None, None) == GQ_OK  # no tokens: no-op
+
+
+def test_matvec_glu_validation(lib):
+    f = lib.gq_matvec_glu
+    assert f(9, A, A, 8, 256, A, 0, 1, 0, A, 0, None) == GQ_ERR_TYPE
+    assert f(2, A, A, 8, 256, A, 2, 1, 0, A, 0, None) == GQ_ERR_DTYPE  # fp16 activations
+    assert f(2, A, A, 8, 256, A, 0, 1, 0, A, 2, None) == GQ_ERR_DTYPE  # fp16 output
+    assert f(2, A, A, 8, 100, A, 0, 1, 0, A, 0, None) == GQ_ERR_SHAPE
+    assert f(2, A, A, 8, 256, A, 0, 0, 0, A, 0, None) == GQ_ERR_SHAPE
+    assert f(2, A, A, 8, (1 << 22) + 256, A, 0, 1, 0, A, 0, None) == GQ_ERR_SHAPE
+    assert f(2, A, A, 8, 256, A, 0, 9, 0, A, 0, None) == GQ_ERR_UNSUPPORTED
+    assert f(2, A, A, 8, 256, A, 0, 1, 2, A, 0, None) == GQ_ERR_UNSUPPORTED  # unknown activation
+    assert f(2, None, A, 8, 256, A, 0, 1, 0, A, 0, None) == GQ_ERR_NULL
+    assert f(2, A, None, 8, 256, A, 0, 1, 0, A, 0, None) == GQ_ERR_NULL
+    assert f(2, A, A, 8, 256, A, 0, 1, 0, None, 0, None) == GQ_ERR_NULL
+    assert f(2, A, MIS, 8, 256, A, 0, 1, 0, A, 0, None) == GQ_ERR_ALIGN
+    assert f(2, A, A, 8, 256, A, 0, 1, 0, MIS, 1, None) == GQ_ERR_ALIGN
+    assert f(2, A, A, 0, 256, A, 0, 1, 0, A, 0, None) == GQ_OK  # N == 0: no-op
