@@ -107,7 +107,9 @@ def _counter_means(d: str) -> dict:
     import csv
     import glob
     vals = {}
-    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+    # the newest run in the directory only
+    runs = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True), key=os.path.getmtime)
+    for p in runs[-1:]:
         for r in csv.DictReader(open(p)):
             vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
@@ -124,6 +126,7 @@ def traffic_summary(fetch_dir: str, write_dir: str):
         kib_mv, kib_cp = means[mv[0]], means[cp[0]]
         factor = (COPY_BYTES / 1024.0) / kib_cp
         per[ctr] = (kib_mv, kib_cp, factor, counts[mv[0]])
+        kname = mv[0][0]
         out_lines.append("%s: dominant kernel %.1f KiB/dispatch (mean of %d); copy kernel %.1f KiB for %d KiB "
                          "moved -> scale %.4f -> %.0f bytes per launch"
                          % (ctr, kib_mv, counts[mv[0]], kib_cp, COPY_BYTES // 1024, factor, kib_mv * factor * 1024))
@@ -131,7 +134,7 @@ def traffic_summary(fetch_dir: str, write_dir: str):
     algo = GU_N * (GU_K // 256) * 144
     text = ["# HBM traffic of the Q4_K gate|up product (19456 x 2560, batch 1, fp32 x)",
             "",
-            "kernel: %s ... (Q4_K, fp32 activations, batch 1)" % GU_KERNEL,
+            "kernel: %s (Q4_K, fp32 activations, batch 1)" % kname.split("(unsigned")[0].replace("void ", ""),
             "source_sha256: %s" % kernel_source_hash(),
             "commands (from the repository root, on the GPU host):",
             "  timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -- python3 bench.py --pmc-pass",
@@ -359,7 +362,7 @@ def main():
         "tokens_per_s_equiv": round(value / 2.74, 1),
         "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
-                     "kernel": "k_matvec<Q4_K, fp32, 1, 1, 4> gate|up 19456x2560 batch 1",
+                     "kernel": "k_matvec<Q4_K, fp32, batch 1> gate|up 19456x2560",
                      "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "prefill": prefill,
