@@ -207,7 +207,10 @@ gq_status gq_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts
  * (ldy >= N).  Weight tiles are dequantised to bf16 in LDS and multiplied on
  * the matrix cores with fp32 accumulation.  Every block type is accepted (a
  * Q4_K_M layer mixes Q4_K and Q6_K tensors); x_dtype must be GQ_BF16
- * (GQ_ERR_UNSUPPORTED otherwise).  K must be a multiple of the type's QK;
+ * (GQ_ERR_UNSUPPORTED otherwise).  K must be a multiple of the type's QK and
+ * at most 4,194,304, and ldx below 4,194,304 (GQ_ERR_SHAPE otherwise: 256 rows
+ * of X are addressed through one buffer resource whose span stays below 2^31
+ * bytes); ldx * 2 and ldy * 4 must be multiples of 16 (GQ_ERR_ALIGN).
  * M == 0 or N == 0 is a no-op. */
 gq_status gq_matmul(gq_type t, const void* W, int64_t N, int64_t K, const void* X,
                     gq_dtype x_dtype, int64_t M, int64_t ldx, float* Y, int64_t ldy,
