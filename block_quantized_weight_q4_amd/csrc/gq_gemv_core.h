@@ -476,13 +476,14 @@ __device__ __forceinline__ void stage_issue(const XSrc& xs, int64_t k0, const Ti
     load_group<XT>(xs.p[0], k0 + 32 * g, in);
 }
 
-template <class F, int XT>
+template <class F, int XT, int NT>
 __device__ __forceinline__ void stage_finish(const XSrc& xs, int64_t k0, const TileLds<F>& L,
                                              const XRaw<XT>& first) {
     const int G = L.U * F::UW / 32;
     const int tid = (int)threadIdx.x;
-    // work items: (vector b, round r) -> group tid + 256 r of vector b
-    const int rounds = (G + NTHREADS - 1) / NTHREADS;
+    constexpr int nthreads = NT;
+    // work items: (vector b, round r) -> group tid + nthreads r of vector b
+    const int rounds = (G + nthreads - 1) / nthreads;
     const int items = L.nb * rounds;
     if (items == 1) {
         if (tid < G) stage_group<F, XT>(L, 0, tid, first);
@@ -494,10 +495,10 @@ __device__ __forceinline__ void stage_finish(const XSrc& xs, int64_t k0, const T
 #pragma unroll 1
         for (int i = 0; i < items; ++i) {
             const int in = i + 1 < items ? i + 1 : i;
-            const int gn = tid + NTHREADS * (in % rounds);
+            const int gn = tid + nthreads * (in % rounds);
             XRaw<XT> nxt;
             load_group<XT>(xs.at(in / rounds), k0 + 32 * (gn < G ? gn : 0), nxt);
-            const int g = tid + NTHREADS * (i % rounds);
+            const int g = tid + nthreads * (i % rounds);
             if (g < G) stage_group<F, XT>(L, i / rounds, g, cur);
             cur = nxt;
         }
@@ -572,7 +573,7 @@ constexpr int D_RING = 4;
 // around the activation staging and each later one as an earlier unit is
 // taken, all in straight-line code (units past the tile load as zeros).  With
 // RING a ring keeps D units per lane in flight over any number of units.
-template <int TYPE, int XT, int BMAX, int D, bool RING>
+template <int TYPE, int XT, int BMAX, int D, bool RING, int NT = NTHREADS>
 __device__ __forceinline__ void gemv_workgroup(const uint8_t* __restrict__ W, int64_t N, int64_t K, int64_t rowA,
                                                const XSrc& xs, int nb, const YDst& yd, int LPR, int tile_units,
                                                uint8_t* lds, int wslot, int wcount) {
@@ -619,7 +620,7 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t* __restrict__ W, in
         Raw ring[D];
         ring[0] = F::load(rs, off_of(0), ln);
         __builtin_amdgcn_sched_barrier(0);
-        stage_finish<F, XT>(xs, u0 * F::UW, L, xin);
+        stage_finish<F, XT, NT>(xs, u0 * F::UW, L, xin);
 #pragma unroll
         for (int t = 1; t < P; ++t) ring[t] = F::load(rs, off_of(t), ln);
         if constexpr (!RING) {

@@ -14,23 +14,46 @@ using namespace gqd;
 
 namespace {
 
-template <int TYPE, int XT, int BMAX, int D, bool RING>
-__global__ __launch_bounds__(NTHREADS) void k_matvec(const uint8_t* __restrict__ W, int64_t N, int64_t K,
+// WGW wavefronts per workgroup: 4, or 8 for batch-1 products whose 8-wave
+// grid holds 150..256 workgroups -- twice the rows then share each staged
+// activation tile and the staging has twice the threads, while every
+// workgroup still gets a CU of its own (measured: the 2560-row projections of
+// the hidden-2560 layer gain 10-20%; grids of 64-128 workgroups lose, since
+// fewer CUs then pull the weights).
+template <int TYPE, int XT, int BMAX, int D, bool RING, int WGW>
+__global__ __launch_bounds__(64 * WGW) void k_matvec(const uint8_t* __restrict__ W, int64_t N, int64_t K,
                                                      XSrc xs, int nb, YDst yd, int LPR, int tile_units) {
     extern __shared__ __align__(16) uint8_t lds[];
-    const int64_t rpw = (int64_t)(NTHREADS >> 6) * (64 / LPR);
-    gemv_workgroup<TYPE, XT, BMAX, D, RING>(W, N, K, (int64_t)blockIdx.x * rpw, xs, nb, yd, LPR, tile_units, lds,
-                                            (int)(threadIdx.x >> 6), NTHREADS >> 6);
+    const int64_t rpw = (int64_t)WGW * (64 / LPR);
+    gemv_workgroup<TYPE, XT, BMAX, D, RING, 64 * WGW>(W, N, K, (int64_t)blockIdx.x * rpw, xs, nb, yd, LPR, tile_units, lds,
+                                            (int)(threadIdx.x >> 6), WGW);
 }
 
-template <int TYPE, int XT, int BMAX, int D, bool RING = false>
+template <int TYPE, int XT, int BMAX, int WGW, int D, bool RING = false>
 hipError_t launch_d(const Plan& p, const uint8_t* W, int64_t N, int64_t K, const XSrc& xs, int nb, float* y,
                     hipStream_t s) {
     YDst yd;
     for (int b = 0; b < 8; ++b) yd.p[b] = y + (int64_t)(b < nb ? b : 0) * N;
-    hipLaunchKernelGGL((k_matvec<TYPE, XT, BMAX, D, RING>), dim3((unsigned)p.grid), dim3(NTHREADS), p.lds, s, W, N, K,
-                       xs, nb, yd, p.LPR, p.tile_units);
+    const int64_t rows = (int64_t)WGW * (64 / p.LPR);
+    const int64_t grid = (N + rows - 1) / rows;
+    hipLaunchKernelGGL((k_matvec<TYPE, XT, BMAX, D, RING, WGW>), dim3((unsigned)grid), dim3(64 * WGW), p.lds, s, W,
+                       N, K, xs, nb, yd, p.LPR, p.tile_units);
     return hipGetLastError();
+}
+
+template <int TYPE, int XT, int BMAX, int WGW>
+hipError_t launch_w(const Plan& p, const uint8_t* W, int64_t N, int64_t K, const XSrc& xs, int nb, float* y,
+                    hipStream_t s) {
+    if (p.ring) return launch_d<TYPE, XT, BMAX, WGW, D_RING, true>(p, W, N, K, xs, nb, y, s);
+    switch (p.D) {
+    case 1: return launch_d<TYPE, XT, BMAX, WGW, 1>(p, W, N, K, xs, nb, y, s);
+    case 2: return launch_d<TYPE, XT, BMAX, WGW, 2>(p, W, N, K, xs, nb, y, s);
+    case 3: return launch_d<TYPE, XT, BMAX, WGW, 3>(p, W, N, K, xs, nb, y, s);
+    case 4: return launch_d<TYPE, XT, BMAX, WGW, 4>(p, W, N, K, xs, nb, y, s);
+    case 5: return launch_d<TYPE, XT, BMAX, WGW, 5>(p, W, N, K, xs, nb, y, s);
+    case 6: return launch_d<TYPE, XT, BMAX, WGW, 6>(p, W, N, K, xs, nb, y, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int TYPE, int XT, int BMAX>
@@ -38,16 +61,12 @@ hipError_t launch_b(const uint8_t* W, int64_t N, int64_t K, const XSrc& xs, int 
     using F = Fmt<TYPE>;
     const Plan p = plan_for<F>(N, K, nb);
     if (p.grid > 0x7fffffff) return hipErrorInvalidValue;
-    if (p.ring) return launch_d<TYPE, XT, BMAX, D_RING, true>(p, W, N, K, xs, nb, y, s);
-    switch (p.D) {
-    case 1: return launch_d<TYPE, XT, BMAX, 1>(p, W, N, K, xs, nb, y, s);
-    case 2: return launch_d<TYPE, XT, BMAX, 2>(p, W, N, K, xs, nb, y, s);
-    case 3: return launch_d<TYPE, XT, BMAX, 3>(p, W, N, K, xs, nb, y, s);
-    case 4: return launch_d<TYPE, XT, BMAX, 4>(p, W, N, K, xs, nb, y, s);
-    case 5: return launch_d<TYPE, XT, BMAX, 5>(p, W, N, K, xs, nb, y, s);
-    case 6: return launch_d<TYPE, XT, BMAX, 6>(p, W, N, K, xs, nb, y, s);
-    default: return hipErrorInvalidValue;
+    if constexpr (BMAX == 1) {
+        const int64_t rows8 = 8 * (int64_t)(64 / p.LPR);
+        const int64_t g8 = (N + rows8 - 1) / rows8;
+        if (g8 >= 150 && g8 <= 256) return launch_w<TYPE, XT, BMAX, 8>(p, W, N, K, xs, nb, y, s);
     }
+    return launch_w<TYPE, XT, BMAX, 4>(p, W, N, K, xs, nb, y, s);
 }
 
 template <int TYPE, int XT>
