@@ -253,18 +253,31 @@ struct StageRegs {
     typename WF<TYPE>::Regs w;
 };
 
+// Grid: one workgroup per output tile, tiles numbered n-tile fastest (gn of
+// them per row of tiles).  When the tile count leaves a last round that
+// would fill only part of the GPU, its tiles (those from n_full on) are each
+// split in two workgroups along K -- stages [0, s_split) and [s_split, S) --
+// that add their partial tiles into Y, which the launcher has zeroed there:
+// the tail round then takes half as long.  Two fp32 additions into zero give
+// the same bits in either order, so the result stays deterministic.
 template <int TYPE>
 __global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W, int64_t N, int64_t K,
                                                    const uint16_t* __restrict__ X, int64_t M, int64_t ldx,
-                                                   float* __restrict__ Y, int64_t ldy) {
+                                                   float* __restrict__ Y, int64_t ldy, int gn, int n_full,
+                                                   int s_split) {
     using F = WF<TYPE>;
     using SR = StageRegs<TYPE>;
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
-    const uint32_t row_bytes = (uint32_t)((K / F::QK) * F::BB);
     const int S = (int)((K + BK - 1) / BK);  // a Q4_0 row may end half way into a stage
+    const int wg = (int)blockIdx.x;
+    const bool split = wg >= n_full;
+    const int tile = split ? n_full + ((wg - n_full) >> 1) : wg;
+    const int s0 = split && ((wg - n_full) & 1) ? s_split : 0;
+    const int s1 = split && !((wg - n_full) & 1) ? s_split : S;
+    const int64_t n0 = (int64_t)(tile % gn) * BN, m0 = (int64_t)(tile / gn) * BM;
+    const uint32_t row_bytes = (uint32_t)((K / F::QK) * F::BB);
 
     // X: thread tid stages 16-byte chunk tid % 8 of rows tid / 8 + 32 i
     // (i = 0..7): eight lanes cover one row's 128 bytes, so every load
@@ -280,7 +293,7 @@ __global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W
     // the buffers), so every load is unconditional and the load-counter waits
     // stay exact
     auto load_stage = [&](int s, SR& r) {
-        const bool ok = s < S;
+        const bool ok = s < s1;
         // inputs past K (the second half of a Q4_0 row's last stage) read as zeros
         const bool xok = ok && (TYPE != T_Q4_0 || (int64_t)s * BK + 8 * xchunk < K);
         const uint32_t xo = xok ? xoff + (uint32_t)s * (BK * 2) : 0x80000000u;
@@ -316,7 +329,7 @@ __global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W
     // stage s's global data lives in register set s & 1; it is loaded two
     // stages before its LDS writes, which happen during stage s-1's MFMAs
     auto stage_body = [&](int s, SR& nxt) {
-        const int cur = s & 1;
+        const int cur = (s - s0) & 1;
         const uint8_t* buf = lds + cur * BUF;
         // stage s+1's data arrived during the previous stage; past the last
         // stage it is zeros, written to a buffer nobody reads
@@ -359,18 +372,18 @@ __global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W
         lds_barrier();
     };
 
-    // an odd S runs one stage of zeros at the end
+    // an odd stage count runs one stage of zeros at the end
     SR r0, r1;
-    if (S > 0) {
-        load_stage(0, r0);
-        load_stage(1, r1);
-        const typename F::Scl sc0 = F::scales(r0.w, 0);
+    if (s1 > s0) {
+        load_stage(s0, r0);
+        load_stage(s0 + 1, r1);
+        const typename F::Scl sc0 = F::scales(r0.w, s0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) store_slice(0, r0, sc0, 0, j);
-        load_stage(2, r0);
+        for (int j = 0; j < 4; ++j) store_slice(s0, r0, sc0, 0, j);
+        load_stage(s0 + 2, r0);
         lds_barrier();
     }
-    for (int s = 0; s < S; s += 2) {
+    for (int s = s0; s < s1; s += 2) {
         stage_body(s, r1);      // writes stage s+1 (set 1), then loads s+3 into set 1
         stage_body(s + 1, r0);  // writes stage s+2 (set 0), then loads s+4 into set 0
     }
@@ -385,7 +398,10 @@ __global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m < M && n < N) Y[m * ldy + n] = acc[i][j][r];
+                if (m < M && n < N) {
+                    if (split) unsafeAtomicAdd(&Y[m * ldy + n], acc[i][j][r]);
+                    else Y[m * ldy + n] = acc[i][j][r];
+                }
             }
         }
     }
@@ -395,17 +411,54 @@ __global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W
 
 namespace {
 
+// Zeroes the output tiles from n_full on (clipped to M x N) before their two
+// K halves are added in.
+__global__ __launch_bounds__(256) void k_zero_tiles(float* __restrict__ Y, int64_t ldy, int64_t M, int64_t N, int gn,
+                                                    int n_full) {
+    const int tile = n_full + (int)blockIdx.y;
+    const int64_t n0 = (int64_t)(tile % gn) * BN, m0 = (int64_t)(tile / gn) * BM;
+    const int64_t m = m0 + blockIdx.x;
+    if (m >= M) return;
+    const int64_t n = n0 + threadIdx.x;
+    if (n < N) Y[m * ldy + n] = 0.f;
+}
+
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <int TYPE>
 hipError_t launch(const void* W, int64_t N, int64_t K, const void* X, int64_t M, int64_t ldx, float* Y, int64_t ldy,
                   hipStream_t s) {
     const int64_t gn = (N + BN - 1) / BN, gm = (M + BM - 1) / BM;
-    if (gn > 0x7fffffff || gm > 65535) return hipErrorInvalidValue;
+    const int64_t tiles = gn * gm;
+    if (tiles > 0x3fffffff) return hipErrorInvalidValue;
+    // one workgroup per CU (the LDS holds one): split a short last round
+    const int cus = cu_count();
+    const int64_t tail = tiles % cus;
+    const int S = (int)((K + BK - 1) / BK);
+    const bool split = tiles > cus && tail > 0 && tail <= cus / 2 && S >= 4;
+    const int n_full = (int)(split ? tiles - tail : tiles);
+    const int64_t grid = split ? n_full + 2 * tail : tiles;
+    if (split) {
+        hipLaunchKernelGGL(k_zero_tiles, dim3(BM, (unsigned)tail), dim3(BN), 0, s, Y, ldy, M, N, (int)gn, n_full);
+        hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) return e0;
+    }
     // LDS above the default per-workgroup size (gfx950 allows 160 KB)
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul<TYPE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_matmul<TYPE>, dim3((unsigned)gn, (unsigned)gm), dim3(256), LDS_BYTES, s,
-                       static_cast<const uint8_t*>(W), N, K, static_cast<const uint16_t*>(X), M, ldx, Y, ldy);
+    hipLaunchKernelGGL(k_matmul<TYPE>, dim3((unsigned)grid), dim3(256), LDS_BYTES, s, static_cast<const uint8_t*>(W),
+                       N, K, static_cast<const uint16_t*>(X), M, ldx, Y, ldy, (int)gn, n_full, S / 2);
     return hipGetLastError();
 }
 

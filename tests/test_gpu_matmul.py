@@ -183,3 +183,32 @@ def test_matmul_q6_k_down_prefill_workload(gq, orc):
     want, tol = orc.matmul_checksum("q6_k", W, N, K, xf, u, v)
     assert abs(got - want) <= 1e-3 * tol, (got, want, tol)
     print("rows worst %.4f cols worst %.4f checksum |err|/tol %.2e" % (r1, r2, abs(got - want) / tol))
+
+
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q4_0"])
+def test_matmul_tail_round_split_along_k(gq, orc, t):
+    """4000 x 4352 outputs = 16 x 17 tiles of 256: on 256 CUs the last 16
+    tiles form a short last round, which the kernel runs as two K halves added
+    into zeroed output.  Sampled rows of the last (partial) row of tiles and
+    columns of the split tiles are compared in full; a second call gives the
+    same bits."""
+    M, N, K = 4000, 4352, 1024
+    g = synth.rng(0x67510005, 700 + ("q4_k", "q6_k", "q4_0").index(t))
+    W = synth.weight(t, g, N, K)
+    xf, X = make_X(g, M, K)
+    Wd = dev(W)
+    Y = torch.full((M, N), float("nan"), device="cuda")
+    gq.gq_matmul(t, Wd, N, K, X, Y)
+    Y2 = torch.full((M, N), float("nan"), device="cuda")
+    gq.gq_matmul(t, Wd, N, K, X, Y2)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Y).all())
+    assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32))
+    s = np.random.default_rng(99)
+    rows = np.unique(np.concatenate([[0, 3840, M - 1], s.choice(np.arange(3841, M - 1), 12, replace=False),
+                                     s.choice(np.arange(1, 3840), 6, replace=False)]))
+    cols = np.unique(np.concatenate([[0, 255, 256, N - 1], s.choice(np.arange(257, N - 1), 8, replace=False)]))
+    ref, sa = orc.matmul_rows(t, W, N, K, xf, rows)
+    check_bound(Y[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, sa, "rows")
+    refc, sac = orc.matmul_cols(t, W, N, K, xf, cols)
+    check_bound(Y[:, torch.from_numpy(cols).cuda()].cpu().numpy(), refc, sac, "cols")
