@@ -9,9 +9,11 @@
 // Q4_K_M checkpoint ("GGUF in transformers", section on the GGUF format) mixes
 // Q4_K with Q6_K tensors, so a layer's prefill needs both.
 //
-// Tiling.  A workgroup (4 wavefronts, one per SIMD) owns a BM x BN = 256 x 256
-// tile of Y; wavefront (wm, wn) owns the 128 x 128 quarter, as 4 x 4 blocks
-// of v_mfma_f32_32x32x16_bf16 (fp32 accumulators in the AGPRs).  K advances in
+// Tiling.  A workgroup owns a BM x BN = 256 x 256 tile of Y.  With 4
+// wavefronts (one per SIMD; Q6_K) wavefront (wm, wn) owns a 128 x 128 quarter
+// as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators); with 8
+// (two per SIMD; the other formats) a 128 x 64 eighth as 4 x 2 blocks, so one
+// wavefront's MFMAs run while the other expands weights or waits on LDS.  K advances in
 // stages of BK = 64 inputs: one 32-byte slice of quants of a Q4_K super-block,
 // a quarter of a Q6_K super-block, or two Q4_0 blocks.
 //
@@ -411,6 +413,127 @@ __global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W
 
 namespace {
 
+// 8-wavefront variant: wavefront (wm, wn) = (wave / 4, wave % 4) owns a
+// 128 x 64 quarter-column of the 256 x 256 tile (4 x 2 blocks of 32x32x16
+// MFMAs, 128 accumulators), so two wavefronts share each SIMD.
+template <int TYPE>
+__global__ __launch_bounds__(512, 1) void k_matmul8(const uint8_t* __restrict__ W, int64_t N, int64_t K,
+                                                    const uint16_t* __restrict__ X, int64_t M, int64_t ldx,
+                                                    float* __restrict__ Y, int64_t ldy, int gn, int n_full,
+                                                    int s_split) {
+    using F = WF<TYPE>;
+    struct SR8 {
+        u32x4 x[4];
+        typename F::Regs w;
+    };
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int S = (int)((K + BK - 1) / BK);
+    const int wg = (int)blockIdx.x;
+    const bool split = wg >= n_full;
+    const int tile = split ? n_full + ((wg - n_full) >> 1) : wg;
+    const int s0 = split && ((wg - n_full) & 1) ? s_split : 0;
+    const int s1 = split && !((wg - n_full) & 1) ? s_split : S;
+    const int64_t n0 = (int64_t)(tile % gn) * BN, m0 = (int64_t)(tile / gn) * BM;
+    const uint32_t row_bytes = (uint32_t)((K / F::QK) * F::BB);
+
+    const int64_t rows_x = M - m0 < BM ? M - m0 : BM, rows_w = N - n0 < BN ? N - n0 : BN;
+    const Rsrc xr = make_rsrc(X + m0 * ldx, (uint32_t)(rows_x * ldx * 2));
+    const Rsrc wr = make_rsrc(W + n0 * (int64_t)row_bytes, (uint32_t)rows_w * row_bytes);
+    const int xrow = tid >> 3, xchunk = tid & 7;
+    const uint32_t xstride = (uint32_t)(64 * ldx * 2);
+    const uint32_t xoff = (uint32_t)xrow * (uint32_t)(ldx * 2) + 16 * xchunk;
+    const int wrow = tid & 255, whalf = wave >> 2;
+    const uint32_t woff = (uint32_t)wrow * row_bytes;
+
+    auto load_stage = [&](int s, SR8& r) {
+        const bool ok = s < s1;
+        const bool xok = ok && (TYPE != T_Q4_0 || (int64_t)s * BK + 8 * xchunk < K);
+        const uint32_t xo = xok ? xoff + (uint32_t)s * (BK * 2) : 0x80000000u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.x[i] = bld16(xr, xok ? xo + (uint32_t)i * xstride : xo);
+        F::load(wr, woff, s, ok, (int64_t)s * BK + 32 < K, r.w);
+    };
+    auto store_x = [&](const SR8& r, int buf, int i) {
+        uint8_t* xs = lds + buf * BUF + (xrow + 64 * i) * ROWB + 16 * xchunk;
+        *reinterpret_cast<u32x4*>(xs) = r.x[i];
+    };
+    auto store_w = [&](int s, const SR8& r, const typename F::Scl& sc, int buf, int j) {
+        uint8_t* ws = lds + buf * BUF + BM * ROWB + wrow * ROWB;
+        u32x4 lo, hi;
+        F::expand(r.w, sc, s, j, lo, hi);
+        reinterpret_cast<u32x4*>(ws)[j] = lo;
+        reinterpret_cast<u32x4*>(ws + 64)[j] = hi;
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+    const int fr = lane & 31, fk = 8 * (lane >> 5);
+    const uint32_t a_base = (uint32_t)((wm * 128 + fr) * ROWB + fk * 2);
+    const uint32_t b_base = (uint32_t)(BM * ROWB + (wn * 64 + fr) * ROWB + fk * 2);
+
+    auto stage_body = [&](int s, SR8& nxt) {
+        const int cur = (s - s0) & 1;
+        const uint8_t* buf = lds + cur * BUF;
+        const typename F::Scl sc = F::scales(nxt.w, s + 1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 a[4], b[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(buf + a_base + i * 32 * ROWB + ks * 32);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const bf16x8*>(buf + b_base + j * 32 * ROWB + ks * 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            store_x(nxt, cur ^ 1, ks);
+            if ((ks & 1) == 0) store_w(s + 1, nxt, sc, cur ^ 1, 2 * whalf + (ks >> 1));
+        }
+        load_stage(s + 3, nxt);
+        lds_barrier();
+    };
+
+    SR8 r0, r1;
+    if (s1 > s0) {
+        load_stage(s0, r0);
+        load_stage(s0 + 1, r1);
+        const typename F::Scl sc0 = F::scales(r0.w, s0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_x(r0, 0, i);
+        store_w(s0, r0, sc0, 0, 2 * whalf);
+        store_w(s0, r0, sc0, 0, 2 * whalf + 1);
+        load_stage(s0 + 2, r0);
+        lds_barrier();
+    }
+    for (int s = s0; s < s1; s += 2) {
+        stage_body(s, r1);
+        stage_body(s + 1, r0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t n = n0 + wn * 64 + 32 * j + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (m < M && n < N) {
+                    if (split) unsafeAtomicAdd(&Y[m * ldy + n], acc[i][j][r]);
+                    else Y[m * ldy + n] = acc[i][j][r];
+                }
+            }
+        }
+    }
+}
+
 // Zeroes the output tiles from n_full on (clipped to M x N) before their two
 // K halves are added in.
 __global__ __launch_bounds__(256) void k_zero_tiles(float* __restrict__ Y, int64_t ldy, int64_t M, int64_t N, int gn,
@@ -454,11 +577,23 @@ hipError_t launch(const void* W, int64_t N, int64_t K, const void* X, int64_t M,
         if (e0 != hipSuccess) return e0;
     }
     // LDS above the default per-workgroup size (gfx950 allows 160 KB)
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul<TYPE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_matmul<TYPE>, dim3((unsigned)grid), dim3(256), LDS_BYTES, s, static_cast<const uint8_t*>(W),
-                       N, K, static_cast<const uint16_t*>(X), M, ldx, Y, ldy, (int)gn, n_full, S / 2);
+    // eight wavefronts (two per SIMD) where the format's registers allow
+    // it; Q6_K's larger stage registers keep the four-wavefront kernel
+    if constexpr (TYPE != T_Q6_K) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul8<TYPE>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_matmul8<TYPE>, dim3((unsigned)grid), dim3(512), LDS_BYTES, s,
+                           static_cast<const uint8_t*>(W), N, K, static_cast<const uint16_t*>(X), M, ldx, Y, ldy,
+                           (int)gn, n_full, S / 2);
+    } else {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul<TYPE>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_matmul<TYPE>, dim3((unsigned)grid), dim3(256), LDS_BYTES, s,
+                           static_cast<const uint8_t*>(W), N, K, static_cast<const uint16_t*>(X), M, ldx, Y, ldy,
+                           (int)gn, n_full, S / 2);
+    }
     return hipGetLastError();
 }
 
