@@ -536,14 +536,22 @@ __global__ __launch_bounds__(512, 1) void k_matmul8(const uint8_t* __restrict__ 
 
 // Zeroes the output tiles from n_full on (clipped to M x N) before their two
 // K halves are added in.
+// Workgroup (r, t): rows 4r..4r+3 of split tile t, 64 threads per row, four
+// columns per thread (16-byte stores: rows of Y are 16-byte aligned and the
+// tile starts at a multiple of 256 columns).
 __global__ __launch_bounds__(256) void k_zero_tiles(float* __restrict__ Y, int64_t ldy, int64_t M, int64_t N, int gn,
                                                     int n_full) {
     const int tile = n_full + (int)blockIdx.y;
     const int64_t n0 = (int64_t)(tile % gn) * BN, m0 = (int64_t)(tile / gn) * BM;
-    const int64_t m = m0 + blockIdx.x;
+    const int64_t m = m0 + 4 * (int64_t)blockIdx.x + (threadIdx.x >> 6);
     if (m >= M) return;
-    const int64_t n = n0 + threadIdx.x;
-    if (n < N) Y[m * ldy + n] = 0.f;
+    const int64_t n = n0 + 4 * (int64_t)(threadIdx.x & 63);
+    float* y = Y + m * ldy + n;
+    if (n + 4 <= N) {
+        *reinterpret_cast<f32x4*>(y) = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+        for (int i = 0; n + i < N; ++i) y[i] = 0.f;
+    }
 }
 
 int cu_count() {
@@ -572,7 +580,7 @@ hipError_t launch(const void* W, int64_t N, int64_t K, const void* X, int64_t M,
     const int n_full = (int)(split ? tiles - tail : tiles);
     const int64_t grid = split ? n_full + 2 * tail : tiles;
     if (split) {
-        hipLaunchKernelGGL(k_zero_tiles, dim3(BM, (unsigned)tail), dim3(BN), 0, s, Y, ldy, M, N, (int)gn, n_full);
+        hipLaunchKernelGGL(k_zero_tiles, dim3(BM / 4, (unsigned)tail), dim3(256), 0, s, Y, ldy, M, N, (int)gn, n_full);
         hipError_t e0 = hipGetLastError();
         if (e0 != hipSuccess) return e0;
     }
