@@ -525,6 +525,23 @@ def bench_context(torch, gq, synth, dev, stream, t_):
         "us_per_layer": round(ms * 1e3, 2), "distinct_experts": distinct, "packed_bytes_read": read_bytes,
         "GBps": round(read_bytes / (ms * 1e-3) / 1e9, 1),
         "tokens_per_s_equiv_30_layers": round(T / (30 * ms * 1e-3), 1)}
+
+    # the same layer with the routed gated unit in one launch; h (bf16) feeds
+    # the down projection directly
+    hb = torch.empty((T, k, F), device=dev, dtype=torch.bfloat16)
+
+    def p5():
+        for c in cp4:
+            gq.gq_route_topk(lg_t, k, ids_t, rw_t, stream)
+            gq.gq_matvec_id_glu("q4_0", c["gate"], c["up"], E, F, H, ids_t, x4, "silu", hb, ws[0], stream)
+            gq.gq_matvec_id("q4_0", c["down"], E, H, F, ids_t, hb, True, yd, ws[2], rw_t, stream)
+
+    ms = Timer(torch, p5, stream).time(10) / len(cp4)
+    res["moe_q4_0_128x_h2816_f704_t8_top8_fused_glu"] = {
+        "launches": "route_topk, gate|up + SiLU (bf16 h), down (weighted)",
+        "us_per_layer": round(ms * 1e3, 2), "distinct_experts": distinct, "packed_bytes_read": read_bytes,
+        "GBps": round(read_bytes / (ms * 1e-3) / 1e9, 1),
+        "tokens_per_s_equiv_30_layers": round(T / (30 * ms * 1e-3), 1)}
     del cp4
     torch.cuda.empty_cache()
     return res

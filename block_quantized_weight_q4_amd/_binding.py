@@ -39,9 +39,11 @@ _lib.gq_matvec_id_check.argtypes = [P, P, ctypes.POINTER(I32)]
 _lib.gq_matmul.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I64, I64, P, I64, P]
 _lib.gq_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
 _lib.gq_matvec_glu.argtypes = [ctypes.c_int, P, P, I64, I64, P, ctypes.c_int, I32, ctypes.c_int, P, ctypes.c_int, P]
+_lib.gq_matvec_id_glu.argtypes = [ctypes.c_int, P, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, ctypes.c_int, P,
+                                  ctypes.c_int, P, SZ, P]
 ACTS = {"silu": 0, "gelu_tanh": 1}
 for _f in ("gq_block_info", "gq_dequant", "gq_matvec", "gq_matvec_id_workspace", "gq_matvec_id",
-           "gq_matvec_id_check", "gq_matmul", "gq_route_topk", "gq_matvec_glu"):
+           "gq_matvec_id_check", "gq_matmul", "gq_route_topk", "gq_matvec_glu", "gq_matvec_id_glu"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -123,6 +125,21 @@ def gq_matvec_id(t, experts: torch.Tensor, n_experts: int, N: int, K: int, ids: 
                                              _ptr(x), _DTYPES[x.dtype], 1 if x_per_slot else 0, _ptr(route_w),
                                              _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return y
+
+
+MATVEC_ID_GLU_WS_BYTES = 256
+
+
+def gq_matvec_id_glu(t, experts_gate: torch.Tensor, experts_up: torch.Tensor, n_experts: int, N: int, K: int,
+                     ids: torch.Tensor, x: torch.Tensor, act: str, h: torch.Tensor, ws: torch.Tensor,
+                     stream=None) -> torch.Tensor:
+    """h[t][j][n] = act(gate_e[n] . x[t]) * (up_e[n] . x[t]) with e = ids[t][j]; h [n_tokens][top_k][N]."""
+    n_tokens, top_k = ids.shape
+    _check("gq_matvec_id_glu", _lib.gq_matvec_id_glu(_type(t), _ptr(experts_gate), _ptr(experts_up), n_experts, N,
+                                                     K, _ptr(ids), n_tokens, top_k, _ptr(x), _DTYPES[x.dtype],
+                                                     ACTS[act], _ptr(h), _DTYPES[h.dtype], _ptr(ws),
+                                                     ws.numel() * ws.element_size(), _stream(stream)))
+    return h
 
 
 def gq_matvec_id_check(ws: torch.Tensor, stream=None) -> int:

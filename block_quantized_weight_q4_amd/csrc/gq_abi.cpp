@@ -20,15 +20,23 @@ gq_status from_hip(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_LAUNC
 // Largest element count any single launch handles (keeps 32-bit grid sizes
 // and 64-bit byte offsets far from overflow).
 constexpr int64_t MAX_ELEMS = (int64_t)1 << 40;
-// Longest row the decode products take: a workgroup addresses its (at most 32)
+// Longest row the decode products take: a workgroup addresses its (at most 64)
 // rows through one buffer resource whose span must stay below 2^31 bytes.
 constexpr int64_t MAX_K_DECODE = (int64_t)1 << 22;
 
-// Decode products for more than 8 vectors run on the matrix cores, and so do
-// Q4_0 / Q4_K products for 5..8 vectors, where the matrix cores were measured
-// faster (the dot-product path's work grows with every vector, the matrix-core
-// path's per-weight work does not); everything else on the dot-product path.
-bool use_matrix_cores(int batch, int type) { return batch > 8 || (batch >= 5 && type != GQ_Q6_K); }
+// Which decode path: the dot-product path's work grows with every vector, the
+// matrix-core path's per-weight work does not, but it carries more fixed cost
+// per row tile.  Measured crossovers (MI355X, Q4_0 / Q4_K / Q5_K / Q6_K at
+// hidden 2560..5120 and the routed-expert shapes): from 5 vectors the matrix
+// cores win for every type and shape; at 4 they win for the 4/5-bit types
+// unless N > 4 K (many short rows, where the dot path stages few activations
+// per row), at 3 only for N <= 1.25 K; at 1..2 and for Q6_K below 5 the dot
+// path wins.
+bool use_matrix_cores(int batch, int type, int64_t N, int64_t K) {
+    if (batch >= 5) return true;
+    if (type == GQ_Q6_K || batch < 3) return false;
+    return batch == 4 ? N <= 4 * K : 4 * N <= 5 * K;
+}
 
 }  // namespace
 
@@ -85,7 +93,7 @@ gq_status gq_matvec(gq_type t, const void* W, int64_t N, int64_t K, const void* 
     if (!y || (K > 0 && (!W || !x))) return GQ_ERR_NULL;
     if (!aligned16(y) || (K > 0 && (!aligned16(W) || !aligned16(x)))) return GQ_ERR_ALIGN;
     try {
-        if (use_matrix_cores(batch, t)) return from_hip(gqk_mmv(t, W, N, K, x, x_dtype, batch, y, stream));
+        if (use_matrix_cores(batch, t, N, K)) return from_hip(gqk_mmv(t, W, N, K, x, x_dtype, batch, y, stream));
         return from_hip(gqk_matvec(t, W, N, K, x, x_dtype, batch, y, stream));
     } catch (...) {
         return GQ_ERR_LAUNCH;
@@ -140,6 +148,34 @@ gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_
     try {
         return from_hip(gqk_matvec_id(t, experts, n_experts, N, K, ids, n_tokens, top_k, x, x_dtype, x_per_slot,
                                       route_w, y, ws, stream));
+    } catch (...) {
+        return GQ_ERR_LAUNCH;
+    }
+}
+
+gq_status gq_matvec_id_glu(gq_type t, const void* experts_gate, const void* experts_up, int32_t n_experts, int64_t N,
+                           int64_t K, const int32_t* ids, int32_t n_tokens, int32_t top_k, const void* x,
+                           gq_dtype x_dtype, gq_act act, void* h, gq_dtype h_dtype, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+    if (!known_type(t)) return GQ_ERR_TYPE;
+    if (x_dtype != GQ_F32 && x_dtype != GQ_BF16) return GQ_ERR_DTYPE;
+    if (h_dtype != GQ_F32 && h_dtype != GQ_BF16) return GQ_ERR_DTYPE;
+    if (n_experts < 1 || n_tokens < 0 || top_k < 1 || top_k > n_experts || N < 0 || K < 0 ||
+        K % qk_of(t) != 0 || (int64_t)n_tokens * top_k > 1024)
+        return GQ_ERR_SHAPE;
+    if (N > MAX_ELEMS || K > MAX_K_DECODE || (K > 0 && N > MAX_ELEMS / K) ||
+        (K > 0 && N > 0 && (int64_t)n_experts > MAX_ELEMS / (N * K)))
+        return GQ_ERR_SHAPE;
+    if (act != GQ_ACT_SILU && act != GQ_ACT_GELU_TANH) return GQ_ERR_UNSUPPORTED;
+    if (n_tokens == 0 || N == 0) return GQ_OK;
+    if (!ids || !h || !ws || (K > 0 && (!experts_gate || !experts_up || !x))) return GQ_ERR_NULL;
+    if (!aligned16(ids) || !aligned16(h) || !aligned16(ws) ||
+        (K > 0 && (!aligned16(experts_gate) || !aligned16(experts_up) || !aligned16(x))))
+        return GQ_ERR_ALIGN;
+    if (ws_bytes < GQ_MATVEC_ID_GLU_WS_BYTES) return GQ_ERR_WORKSPACE;
+    try {
+        return from_hip(gqk_matvec_id_glu(t, experts_gate, experts_up, n_experts, N, K, ids, n_tokens, top_k, x,
+                                          x_dtype, act, h, h_dtype, ws, stream));
     } catch (...) {
         return GQ_ERR_LAUNCH;
     }

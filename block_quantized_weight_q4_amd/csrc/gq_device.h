@@ -100,4 +100,13 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8 * i)) & 0xffu; }
 
+// Activation of a gated feed-forward unit, in fp32:
+// act 0: silu(g) = g / (1 + e^-g);
+// act 1: gelu_tanh(g) = g/2 (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))).
+__device__ __forceinline__ float act_fn(int act, float g) {
+    if (act == 0) return g / (1.0f + expf(-g));
+    const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * g, g * g, g);
+    return 0.5f * g * (1.0f + tanhf(u));
+}
+
 }  // namespace gqd

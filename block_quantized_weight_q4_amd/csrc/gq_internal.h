@@ -23,6 +23,11 @@ size_t gqk_matvec_id_ws_bytes(int n_experts, int n_tokens, int top_k, int64_t N)
 hipError_t gqk_matvec_id(int type, const void* experts, int n_experts, int64_t N, int64_t K,
                          const int32_t* ids, int n_tokens, int top_k, const void* x, int x_dtype,
                          int x_per_slot, const float* route_w, float* y, void* ws, hipStream_t s);
+// Routed gated unit: h[t][j][n] = act(gate_e[n] . x_t) * (up_e[n] . x_t), e = ids[t][j];
+// ws needs only its 256-byte header (the bad-id count).
+hipError_t gqk_matvec_id_glu(int type, const void* experts_gate, const void* experts_up, int n_experts, int64_t N,
+                             int64_t K, const int32_t* ids, int n_tokens, int top_k, const void* x, int x_dtype,
+                             int act, void* h, int h_dtype, void* ws, hipStream_t s);
 hipError_t gqk_matvec_id_bad_count(const void* ws, hipStream_t s, int32_t* n_bad);
 
 hipError_t gqk_matmul(int type, const void* W, int64_t N, int64_t K, const void* X, int x_dtype,

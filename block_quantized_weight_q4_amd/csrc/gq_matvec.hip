@@ -93,13 +93,6 @@ hipError_t launch_x(const uint8_t* W, int64_t N, int64_t K, const XSrc& xs, int 
 // activations together; the two partial tiles meet in LDS, where wavefronts
 // 0, 1 apply the activation and store h.
 
-// silu(g) = g / (1 + e^-g);  gelu_tanh(g) = g/2 (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3)))
-__device__ __forceinline__ float act_fn(int act, float g) {
-    if (act == 0) return g / (1.0f + expf(-g));
-    const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * g, g * g, g);
-    return 0.5f * g * (1.0f + tanhf(u));
-}
-
 template <int TYPE, int XT, int BMAX, int D, bool RING>
 __global__ __launch_bounds__(NTHREADS) void k_glu(const uint8_t* __restrict__ Wg, const uint8_t* __restrict__ Wu,
                                                   int64_t N, int64_t K, XSrc xs, int nb, int act, void* __restrict__ h,

@@ -19,6 +19,10 @@
 //     output rows of such slots.
 //  2. k_combine (route_w given): y[t][n] = sum_j route_w[t][j] * slot[t][j][n],
 //     j in increasing order.
+// The gated unit of a routed feed-forward block (gate and up stacks, the
+// activation between them) is the same k_experts launch in its GLU form: one
+// launch writes h[t][j][n] = act(gate_e[n] . x_t) * (up_e[n] . x_t), e =
+// ids[t][j], which the down projection then takes as its per-slot vectors.
 #include "gq_gemv_core.h"
 #include "gq_internal.h"
 
@@ -46,12 +50,19 @@ WsLayout layout(int n_experts, int n_tokens, int top_k, int64_t N) {
 }
 
 // ------------------------------------------------------------- product ----
-template <int TYPE, int XT, int D, bool RING>
-__global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict__ experts, int64_t expert_bytes,
+// GLU: the gated unit of the routed feed-forward block instead of one
+// product.  experts is then the gate stack and experts_up the up stack; a
+// workgroup covers 2 SR rows, wavefronts 0, 1 computing the gate rows and
+// wavefronts 2, 3 the same rows of the up matrix (on the activations they
+// stage together), and out[slot][n] = act(gate) * up, fp32 or bf16 (out_bf16).
+template <int TYPE, int XT, int D, bool RING, bool GLU>
+__global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict__ experts,
+                                                      const uint8_t* __restrict__ experts_up, int64_t expert_bytes,
                                                       int64_t N, int64_t K, const uint8_t* __restrict__ x,
                                                       int x_per_slot, int top_k, const int32_t* __restrict__ ids,
                                                       int S, int n_experts, int* __restrict__ ws_hdr,
-                                                      float* __restrict__ out, int LPR, int tile_units) {
+                                                      void* __restrict__ out, int out_bf16, int act, int LPR,
+                                                      int tile_units) {
     extern __shared__ __align__(16) uint8_t lds[];
     // Grouping.  rank = position of a slot among the slots of its expert in
     // slot order; first[e] = number of groups of the experts before e (a scan
@@ -135,7 +146,7 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
         }
     }
     __syncthreads();
-    const int64_t rpw = (int64_t)(NTHREADS >> 6) * (64 / LPR);
+    const int64_t rpw = (int64_t)(GLU ? 2 : NTHREADS >> 6) * (64 / LPR);
     const int64_t rowA = (int64_t)blockIdx.y * rpw;
     if (g == 0) {
         if (blockIdx.y == 0 && tid == 0) ws_hdr[0] = n_bad;
@@ -144,7 +155,11 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
             const int64_t rows = N - rowA < rpw ? N - rowA : rpw;
             for (int s = 0; s < S; ++s)
                 if (key[s] < 0)
-                    for (int64_t n = tid; n < rows; n += NTHREADS) out[(int64_t)s * N + rowA + n] = 0.f;
+                    for (int64_t n = tid; n < rows; n += NTHREADS) {
+                        const int64_t o = (int64_t)s * N + rowA + n;
+                        if (out_bf16) static_cast<uint16_t*>(out)[o] = 0;
+                        else static_cast<float*>(out)[o] = 0.f;
+                    }
         }
     }
     const int nb = n_sel;
@@ -160,11 +175,34 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
         const int slot = sel[tid < nb ? tid : 0];
         const int64_t xrow = x_per_slot ? slot : slot / top_k;
         xs.p[tid] = x + xrow * K * esz;
-        yd.p[tid] = out + (int64_t)slot * N;
+        yd.p[tid] = static_cast<float*>(out) + (int64_t)slot * N;
     }
     __syncthreads();
-    gemv_workgroup<TYPE, XT, 8, D, RING>(experts + (int64_t)e * expert_bytes, N, K, rowA, xs, nb, yd, LPR,
-                                          tile_units, lds, (int)(threadIdx.x >> 6), NTHREADS >> 6);
+    if constexpr (!GLU) {
+        gemv_workgroup<TYPE, XT, 8, D, RING>(experts + (int64_t)e * expert_bytes, N, K, rowA, xs, nb, yd, LPR,
+                                              tile_units, lds, (int)(threadIdx.x >> 6), NTHREADS >> 6);
+    } else {
+        // [gate | up][vector][row in tile]; 2 SR <= 32 rows (LPR >= 4)
+        __shared__ float gu[2][CH][32];
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), half = wave >> 1;
+        const int64_t row_bytes = (K / Fmt<TYPE>::QK) * Fmt<TYPE>::BB;
+        YDst yp;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) yp.p[b] = &gu[half][b < CH ? b : 0][0];
+        const uint8_t* W = (half ? experts_up : experts) + (int64_t)e * expert_bytes + rowA * row_bytes;
+        gemv_workgroup<TYPE, XT, 8, D, RING>(W, N - rowA, K, 0, xs, nb, yp, LPR, tile_units, lds, wave & 1, 2);
+        __syncthreads();
+        const int rows = (int)rpw;
+        const int64_t nr = N - rowA < rpw ? N - rowA : rpw;
+        for (int i = tid; i < nb * rows; i += NTHREADS) {
+            const int b = i / rows, r = i - b * rows;
+            if (r >= nr) continue;
+            const float v = act_fn(act, gu[0][b][r]) * gu[1][b][r];
+            const int64_t o = (int64_t)sel[b] * N + rowA + r;
+            if (out_bf16) static_cast<uint16_t*>(out)[o] = f2bf(v);
+            else static_cast<float*>(out)[o] = v;
+        }
+    }
 }
 
 // ------------------------------------------------------------- combine ----
@@ -183,29 +221,48 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ slot_
     y[(int64_t)t * N + n] = acc;
 }
 
+// What one launch computes: a plain routed product (up == nullptr, fp32 out)
+// or the gated unit (gate stack in experts, up stack in up).
+struct Job {
+    const uint8_t* experts;
+    const uint8_t* up;
+    int64_t N, K;
+    const uint8_t* x;
+    int x_per_slot, top_k, n_experts;
+    const int32_t* ids;
+    int* ws_hdr;
+    void* out;
+    int out_bf16, act;
+};
+
 template <int TYPE, int XT, int D, bool RING = false>
-hipError_t launch_experts_d(const Plan& p, const WsLayout& L, const uint8_t* experts, int64_t N, int64_t K,
-                            const uint8_t* x, int x_per_slot, int top_k, const int32_t* ids, int n_experts,
-                            int* ws_hdr, float* out, hipStream_t s) {
+hipError_t launch_experts_d(const Plan& p, const WsLayout& L, const Job& j, hipStream_t s) {
     using F = Fmt<TYPE>;
-    const int64_t expert_bytes = N * (K / F::QK) * F::BB;
-    hipLaunchKernelGGL((k_experts<TYPE, XT, D, RING>), dim3((unsigned)L.Gmax, (unsigned)p.grid), dim3(NTHREADS),
-                       p.lds, s, experts, expert_bytes, N, K, x, x_per_slot, top_k, ids, L.S, n_experts, ws_hdr,
-                       out, p.LPR, p.tile_units);
+    const int64_t expert_bytes = j.N * (j.K / F::QK) * F::BB;
+    const bool glu = j.up != nullptr;
+    const int64_t rpw = (int64_t)(glu ? 2 : NTHREADS >> 6) * (64 / p.LPR);
+    const int64_t gy = (j.N + rpw - 1) / rpw;
+    if (gy > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)L.Gmax, (unsigned)gy);
+    if (glu)
+        hipLaunchKernelGGL((k_experts<TYPE, XT, D, RING, true>), grid, dim3(NTHREADS), p.lds, s, j.experts, j.up,
+                           expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.ids, L.S, j.n_experts, j.ws_hdr,
+                           j.out, j.out_bf16, j.act, p.LPR, p.tile_units);
+    else
+        hipLaunchKernelGGL((k_experts<TYPE, XT, D, RING, false>), grid, dim3(NTHREADS), p.lds, s, j.experts, j.up,
+                           expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.ids, L.S, j.n_experts, j.ws_hdr,
+                           j.out, 0, 0, p.LPR, p.tile_units);
     return hipGetLastError();
 }
 
 template <int TYPE, int XT>
-hipError_t launch_experts(const WsLayout& L, const uint8_t* experts, int64_t N, int64_t K, const uint8_t* x,
-                          int x_per_slot, int top_k, const int32_t* ids, int n_experts, int* ws_hdr, float* out,
-                          hipStream_t s) {
+hipError_t launch_experts(const WsLayout& L, const Job& j, hipStream_t s) {
     using F = Fmt<TYPE>;
-    // the launch covers the rows of up to min(S, n_experts) experts
-    const int64_t distinct = L.S < n_experts ? L.S : n_experts;
-    const Plan p = plan_for<F>(N, K, CH, N * distinct, 4);
-    if (p.grid > 65535) return hipErrorInvalidValue;
-#define GQ_LAUNCH(DD, RR) \
-    launch_experts_d<TYPE, XT, DD, RR>(p, L, experts, N, K, x, x_per_slot, top_k, ids, n_experts, ws_hdr, out, s)
+    // the launch covers the rows of up to min(S, n_experts) experts (twice
+    // as many for the gated unit)
+    const int64_t distinct = L.S < j.n_experts ? L.S : j.n_experts;
+    const Plan p = plan_for<F>(j.N, j.K, CH, (j.up ? 2 : 1) * j.N * distinct, 4);
+#define GQ_LAUNCH(DD, RR) launch_experts_d<TYPE, XT, DD, RR>(p, L, j, s)
     if (p.ring) return GQ_LAUNCH(D_RING, true);
     switch (p.D) {
     case 1: return GQ_LAUNCH(1, false);
@@ -220,13 +277,16 @@ hipError_t launch_experts(const WsLayout& L, const uint8_t* experts, int64_t N, 
 }
 
 template <int TYPE>
-hipError_t launch_experts_x(const WsLayout& L, const uint8_t* experts, int64_t N, int64_t K, const void* x,
-                            int x_dtype, int x_per_slot, int top_k, const int32_t* ids, int n_experts, int* ws_hdr,
-                            float* out, hipStream_t s) {
-    const uint8_t* xb = static_cast<const uint8_t*>(x);
-    if (x_dtype == DT_F32)
-        return launch_experts<TYPE, 0>(L, experts, N, K, xb, x_per_slot, top_k, ids, n_experts, ws_hdr, out, s);
-    return launch_experts<TYPE, 1>(L, experts, N, K, xb, x_per_slot, top_k, ids, n_experts, ws_hdr, out, s);
+hipError_t launch_experts_x(const WsLayout& L, const Job& j, int x_dtype, hipStream_t s) {
+    if (x_dtype == DT_F32) return launch_experts<TYPE, 0>(L, j, s);
+    return launch_experts<TYPE, 1>(L, j, s);
+}
+
+hipError_t launch_type(int type, const WsLayout& L, const Job& j, int x_dtype, hipStream_t s) {
+    if (type == T_Q4_0) return launch_experts_x<T_Q4_0>(L, j, x_dtype, s);
+    if (type == T_Q4_K) return launch_experts_x<T_Q4_K>(L, j, x_dtype, s);
+    if (type == T_Q5_K) return launch_experts_x<T_Q5_K>(L, j, x_dtype, s);
+    return launch_experts_x<T_Q6_K>(L, j, x_dtype, s);
 }
 
 }  // namespace
@@ -244,17 +304,25 @@ hipError_t gqk_matvec_id(int type, const void* experts, int n_experts, int64_t N
     int* hdr = reinterpret_cast<int*>(w);
     // per-slot outputs: straight into y when there is no routing combine
     float* out = route_w ? reinterpret_cast<float*>(w + L.off_out) : y;
-    const uint8_t* ex = static_cast<const uint8_t*>(experts);
-    hipError_t e;
-    if (type == T_Q4_0) e = launch_experts_x<T_Q4_0>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, ids, n_experts, hdr, out, s);
-    else if (type == T_Q4_K) e = launch_experts_x<T_Q4_K>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, ids, n_experts, hdr, out, s);
-    else if (type == T_Q5_K) e = launch_experts_x<T_Q5_K>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, ids, n_experts, hdr, out, s);
-    else e = launch_experts_x<T_Q6_K>(L, ex, N, K, x, x_dtype, x_per_slot, top_k, ids, n_experts, hdr, out, s);
+    const Job j{static_cast<const uint8_t*>(experts), nullptr, N, K, static_cast<const uint8_t*>(x), x_per_slot,
+                top_k, n_experts, ids, hdr, out, 0, 0};
+    const hipError_t e = launch_type(type, L, j, x_dtype, s);
     if (e != hipSuccess || !route_w) return e;
     const unsigned nx = (unsigned)((N + 255) / 256);
     hipLaunchKernelGGL(k_combine, dim3(nx, (unsigned)n_tokens), dim3(256), 0, s, out, ids, route_w, n_experts,
                        top_k, N, y);
     return hipGetLastError();
+}
+
+hipError_t gqk_matvec_id_glu(int type, const void* experts_gate, const void* experts_up, int n_experts, int64_t N,
+                             int64_t K, const int32_t* ids, int n_tokens, int top_k, const void* x, int x_dtype,
+                             int act, void* h, int h_dtype, void* ws, hipStream_t s) {
+    const WsLayout L = layout(n_experts, n_tokens, top_k, N);
+    if (L.S > MAX_SLOTS) return hipErrorInvalidValue;
+    const Job j{static_cast<const uint8_t*>(experts_gate), static_cast<const uint8_t*>(experts_up), N, K,
+                static_cast<const uint8_t*>(x), 0, top_k, n_experts, ids, static_cast<int*>(ws), h,
+                h_dtype == DT_BF16 ? 1 : 0, act};
+    return launch_type(type, L, j, x_dtype, s);
 }
 
 hipError_t gqk_matvec_id_bad_count(const void* ws, hipStream_t s, int32_t* n_bad) {

@@ -1,6 +1,6 @@
 // gq_mmv.hip -- decode product y[b][n] = sum_k w[n][k] x[b][k] for a batch of
 // up to 16 vectors on the matrix cores (gfx950), against packed Q4_0 / Q4_K /
-// Q6_K rows.
+// Q5_K / Q6_K rows.
 //
 // Small batches are what a speculative-decoding verify step or a few
 // concurrent sequences present: the Gemma 4 26B-A4B Show HN page (sections
@@ -9,31 +9,38 @@
 // the dot-product path a full pass of VALU work per weight; here the weights
 // are expanded once and the products for all vectors run on the matrix cores.
 //
-// Tile: one wavefront computes a 16 (rows) x 16 (vectors) output tile with
-// v_mfma_f32_16x16x32_bf16 (Q4_0, Q4_K: one MFMA per 32-weight sub-block) or
-// v_mfma_f32_16x16x16_bf16 (Q6_K: one per 16-weight sub-block):
+// Tile: a wavefront computes R output tiles of 16 (rows) x 16 (vectors) with
+// v_mfma_f32_16x16x32_bf16 (Q4_0, Q4_K, Q5_K: one MFMA per 32-weight
+// sub-block) or v_mfma_f32_16x16x16_bf16 (Q6_K: one per 16-weight sub-block):
 //   A (16 x K) = the activations, vector t in row t (rows >= batch read zeros),
-//   B (K x 16) = the weights of the tile's 16 rows, expanded in registers to
+//   B (K x 16) = the weights of a tile's 16 rows, expanded in registers to
 //                the exact bf16 values 128 + q (OR-ing q into bf16 128.0),
 //   C lane l, register r = output (vector 4 (l/16) + r, row l % 16).
 // With acc = A B and az = A Z (the same MFMA against the constant Z = 128 +
 // the format's zero point, i.e. the operand of a sub-block whose quants all sit
 // on the zero point), a sub-block adds s (acc - az) to the output, s = d * sc
-// its scale; Q4_K also subtracts dmin m (az / 128).  Every product in the MFMAs
-// is exact (8-bit by 8-bit significands) and the sums are fp32; a sub-block
-// whose quants all equal the zero point gives acc == az bit for bit and so
-// contributes exactly zero.
+// its scale; Q4_K / Q5_K also subtract dmin m (az / 128).  Every product in
+// the MFMAs is exact (8-bit by 8-bit significands) and the sums are fp32; a
+// sub-block whose quants all equal the zero point gives acc == az bit for bit
+// and so contributes exactly zero.  az depends on the activations only, so
+// the R tiles of a wavefront share it (and the A operand).
 // fp32 activations enter as x = hi + lo with hi the bf16 truncation of x and
 // lo the bf16 rounding of the exact remainder (|x - hi - lo| <= 2^-17 |x|),
 // two MFMAs each.
 //
-// Lane l of a tile holds row l % 16 and reads the quants of k-slot group
-// g = l / 16; the weight bytes are spread with byte permutes so that k-slots
-// follow the activation order and activations load as they lie in memory.
+// Loads.  Lane l = 16 g + n (row n of a tile, lane group g) reads 16
+// contiguous bytes of its row per load, the four groups together one 64-byte
+// run, so that every load instruction fetches whole 64-byte lines: the L1
+// tag lookups, not the bytes, are what limits a load pattern that scatters
+// small pieces over many lines.  The bytes then move between lane groups
+// with the gfx950 lane-swap instructions (v_permlane32_swap: groups 2, 3 <->
+// 0, 1; v_permlane16_swap: groups 1, 3 <-> 0, 2) into the k-slot order of
+// the MFMA operand, and the activations are read in that same order.
 //
-// Workgroup: the W wavefronts of a workgroup share one 16-row tile and split
-// its K range into contiguous runs of units; their partial tiles are summed
-// in LDS in wavefront order (deterministic), and wavefront 0 stores.
+// Workgroup: its W wavefronts share 16 R rows and split the K range into
+// contiguous runs of steps; their partial tiles are summed in LDS in
+// wavefront order (deterministic), and wavefront 0 stores.  R and W depend on
+// N and K only, so every output column is the same whatever the batch.
 #include "gq_gemv_core.h"
 #include "gq_internal.h"
 
@@ -44,7 +51,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int WMAX = 16;                 // wavefronts per workgroup
+constexpr int WMAX = 8;                   // wavefronts per workgroup
 constexpr uint32_t BMAG = 0x43004300u;    // bf16 pair (128, 128)
 constexpr uint32_t M4 = 0x000F000Fu;
 // byte permutes [b0, 0, b1, 0] and [b2, 0, b3, 0] of one dword
@@ -81,78 +88,140 @@ __device__ __forceinline__ uint32_t split_lo(uint32_t e0, uint32_t e1) {
     return pk_bf16(r0, r1);
 }
 
-// -------------------------------------------------- activation fragments ----
-// Eight activations of one vector for one K=32 MFMA (two runs of four for
-// Q4_0, one run of eight otherwise), kept as loaded.
+// ------------------------------------------------------ lane exchanges ----
+// a of groups 2, 3 <-> b of groups 0, 1 (lane l <-> lane l - 32)
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+// a of groups 1, 3 <-> b of groups 0, 2 (lane l <-> lane l - 16)
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+
+// Group g holds the 16-byte piece g of a 64-byte run (bytes 16 g .. 16 g + 15).
+// After: (x, y) = bytes off(g) .. off(g) + 7 of the run's first 32 bytes and
+// (z, w) = the same bytes of its last 32, off = 0, 16, 8, 24 for g = 0..3.
+__device__ __forceinline__ void pair_swap(u32x4& v) {
+    uint32_t a = v.x, b = v.y, c = v.z, d = v.w;
+    swap32(a, c);
+    swap32(b, d);
+    v = u32x4{a, b, c, d};
+}
+__device__ __forceinline__ uint32_t pair_off(int g) { return (uint32_t)(((g & 1) << 4) | ((g >> 1) << 3)); }
+
+// Group g holds dwords 0..3 of a 16-byte piece P_g.  After: dword j = dword g
+// of piece P_j (a 4 x 4 transpose of (group, dword)).
+__device__ __forceinline__ void transpose4(u32x4& v) {
+    uint32_t a = v.x, b = v.y, c = v.z, d = v.w;
+    swap32(a, c);  // groups 0,1: (P_g.0, P_g.1, P_g+2.0, P_g+2.1); 2,3: (P_g-2.2, P_g-2.3, P_g.2, P_g.3)
+    swap32(b, d);
+    swap16(a, b);
+    swap16(c, d);
+    v = u32x4{a, b, c, d};
+}
+
+// The value v_g of group g, for every g, in every lane: out[j] = v_j.
+__device__ __forceinline__ void gather4(uint32_t v, uint32_t out[4]) {
+    uint32_t a = v, b = v;
+    swap32(a, b);  // a = v_(g&1), b = v_(2+(g&1))
+    uint32_t a1 = a, b1 = b;
+    swap16(a, a1);  // a = v_0, a1 = v_1
+    swap16(b, b1);  // b = v_2, b1 = v_3
+    out[0] = a;
+    out[1] = a1;
+    out[2] = b;
+    out[3] = b1;
+}
+
+// -------------------------------------------------- activation operands ----
+// The A operand of one K=32 MFMA (8 k-slots per lane) as loaded, and prepared
+// (bf16 as given; fp32 as the hi / lo pair).
 template <int XT>
-struct X8;
+struct XA8;
 
 template <>
-struct X8<0> {
-    u32x4 v0, v1;
-    __device__ void load8(Rsrc xs, uint32_t xo, uint32_t k) {
-        v0 = bld16(xs, xo + 4 * k);
-        v1 = bld16(xs, xo + 4 * k + 16);
-    }
-    __device__ void load44(Rsrc xs, uint32_t xo, uint32_t k0, uint32_t k1) {
-        v0 = bld16(xs, xo + 4 * k0);
-        v1 = bld16(xs, xo + 4 * k1);
-    }
-    // acc += A B, az += A Z for the weight operand b and the zero operand z
-    __device__ void mma(const u32x4& b, uint32_t z, f32x4& acc, f32x4& az) const {
-        const u32x4 zz = {z, z, z, z};
-        const u32x4 hi = {split_hi(v0.x, v0.y), split_hi(v0.z, v0.w), split_hi(v1.x, v1.y), split_hi(v1.z, v1.w)};
-        const u32x4 lo = {split_lo(v0.x, v0.y), split_lo(v0.z, v0.w), split_lo(v1.x, v1.y), split_lo(v1.z, v1.w)};
-        acc = mma32(hi, b, acc);
-        acc = mma32(lo, b, acc);
-        az = mma32(hi, zz, az);
-        az = mma32(lo, zz, az);
-    }
-};
-
-template <>
-struct X8<1> {
+struct XA8<1> {
     u32x4 v;
-    __device__ void load8(Rsrc xs, uint32_t xo, uint32_t k) { v = bld16(xs, xo + 2 * k); }
-    __device__ void load44(Rsrc xs, uint32_t xo, uint32_t k0, uint32_t k1) {
-        const u32x2 a = bld8(xs, xo + 2 * k0), b = bld8(xs, xo + 2 * k1);
+    __device__ void load8(Rsrc xs, uint32_t o) { v = bld16(xs, o); }
+    __device__ void load44(Rsrc xs, uint32_t o0, uint32_t o1) {
+        const u32x2 a = bld8(xs, o0), b = bld8(xs, o1);
         v = u32x4{a.x, a.y, b.x, b.y};
     }
-    __device__ void mma(const u32x4& b, uint32_t z, f32x4& acc, f32x4& az) const {
-        const u32x4 zz = {z, z, z, z};
-        acc = mma32(v, b, acc);
-        az = mma32(v, zz, az);
+};
+
+template <>
+struct XA8<0> {
+    u32x4 v0, v1;
+    __device__ void load8(Rsrc xs, uint32_t o) {
+        v0 = bld16(xs, o);
+        v1 = bld16(xs, o + 16);
+    }
+    __device__ void load44(Rsrc xs, uint32_t o0, uint32_t o1) {
+        v0 = bld16(xs, o0);
+        v1 = bld16(xs, o1);
     }
 };
 
-// Four activations of one vector for one K=16 MFMA.
 template <int XT>
-struct X4;
+struct AO8;
 
 template <>
-struct X4<0> {
-    u32x4 v;
-    __device__ void load4(Rsrc xs, uint32_t xo, uint32_t k) { v = bld16(xs, xo + 4 * k); }
-    __device__ void mma(const u32x2& b, uint32_t z, f32x4& acc, f32x4& az) const {
-        const u32x2 zz = {z, z};
-        const u32x2 hi = {split_hi(v.x, v.y), split_hi(v.z, v.w)};
-        const u32x2 lo = {split_lo(v.x, v.y), split_lo(v.z, v.w)};
-        acc = mma16(hi, b, acc);
-        acc = mma16(lo, b, acc);
-        az = mma16(hi, zz, az);
-        az = mma16(lo, zz, az);
-    }
+struct AO8<1> {
+    u32x4 hi;
+    __device__ explicit AO8(const XA8<1>& a) : hi(a.v) {}
+    __device__ f32x4 mm(const u32x4& b) const { return mma32(hi, b, f32x4{0.f, 0.f, 0.f, 0.f}); }
 };
 
 template <>
-struct X4<1> {
-    u32x2 v;
-    __device__ void load4(Rsrc xs, uint32_t xo, uint32_t k) { v = bld8(xs, xo + 2 * k); }
-    __device__ void mma(const u32x2& b, uint32_t z, f32x4& acc, f32x4& az) const {
-        const u32x2 zz = {z, z};
-        acc = mma16(v, b, acc);
-        az = mma16(v, zz, az);
+struct AO8<0> {
+    u32x4 hi, lo;
+    __device__ explicit AO8(const XA8<0>& a) {
+        hi = u32x4{split_hi(a.v0.x, a.v0.y), split_hi(a.v0.z, a.v0.w), split_hi(a.v1.x, a.v1.y),
+                   split_hi(a.v1.z, a.v1.w)};
+        lo = u32x4{split_lo(a.v0.x, a.v0.y), split_lo(a.v0.z, a.v0.w), split_lo(a.v1.x, a.v1.y),
+                   split_lo(a.v1.z, a.v1.w)};
     }
+    __device__ f32x4 mm(const u32x4& b) const { return mma32(lo, b, mma32(hi, b, f32x4{0.f, 0.f, 0.f, 0.f})); }
+};
+
+// The same for a K=16 MFMA (4 k-slots per lane).
+template <int XT>
+struct XA4;
+
+template <>
+struct XA4<1> {
+    u32x2 v;
+    __device__ void load4(Rsrc xs, uint32_t o) { v = bld8(xs, o); }
+};
+
+template <>
+struct XA4<0> {
+    u32x4 v;
+    __device__ void load4(Rsrc xs, uint32_t o) { v = bld16(xs, o); }
+};
+
+template <int XT>
+struct AO4;
+
+template <>
+struct AO4<1> {
+    u32x2 hi;
+    __device__ explicit AO4(const XA4<1>& a) : hi(a.v) {}
+    __device__ f32x4 mm(const u32x2& b) const { return mma16(hi, b, f32x4{0.f, 0.f, 0.f, 0.f}); }
+};
+
+template <>
+struct AO4<0> {
+    u32x2 hi, lo;
+    __device__ explicit AO4(const XA4<0>& a) {
+        hi = u32x2{split_hi(a.v.x, a.v.y), split_hi(a.v.z, a.v.w)};
+        lo = u32x2{split_lo(a.v.x, a.v.y), split_lo(a.v.z, a.v.w)};
+    }
+    __device__ f32x4 mm(const u32x2& b) const { return mma16(lo, b, mma16(hi, b, f32x4{0.f, 0.f, 0.f, 0.f})); }
 };
 
 // y += s (acc - az)
@@ -167,75 +236,76 @@ __device__ __forceinline__ void add_sub_block_min(f32x4& y, float s, float m, co
 }
 
 // ------------------------------------------------------------- formats ----
-// A unit is the K range one lane loads and reduces in one step.  load() gets
-// the weight offset of the unit's block (bo, OOB for rows past N or units past
-// the wavefront's range), the lane's k-slot group g, the activation offset of
-// the lane's vector (xo, OOB for vectors past the batch) and the unit's first
-// weight index k.
+// A step is the K range one iteration covers: one super-block (Q4_K, Q5_K,
+// Q6_K) or four 32-weight blocks (Q4_0).  load_w() gets the byte offset of
+// the row's step (OOB for rows past N or steps past the wavefront's range);
+// load_x() the offset of the lane's vector (OOB for vectors past the batch)
+// and the step's first weight index k0.
 
-template <int TYPE, int XT>
-struct MU;
+// Q4_K: header (d, dmin, 12 scale bytes) then 128 quant bytes; quant byte j of
+// chunk c = bytes 32c..32c+31 holds weight 64c + j (low nibble, sub-block 2c)
+// and 64c + 32 + j (high nibble, sub-block 2c + 1).  Group g loads quant bytes
+// 16g.. of chunks (0, 1) and (2, 3); after pair_swap its k-slots j = 0..7 of
+// sub-block s are weights 32 s + off(g) + j.  w = d sc q - dmin m: s = d sc,
+// Z = 128, and the min term dmin m sum x with sum x = az / 128.
+template <int TYPE>
+struct MF;
 
-// Q4_0: unit = one 18-byte block of 32 weights.  Group g holds quant bytes
-// 4g..4g+3: k-slots 0..3 = weights 4g..4g+3 (low nibbles), 4..7 = weights
-// 16+4g..16+4g+3 (high nibbles).  w = d (q - 8): s = d, Z = 128 + 8.
-template <int XT>
-struct MU<T_Q4_0, XT> {
-    static constexpr int QK = 32, BB = 18, UW = 32;
-    uint32_t d, q;
-    X8<XT> x;
-    __device__ void load(Rsrc ws, uint32_t bo, int g, Rsrc xs, uint32_t xo, uint32_t k, int) {
-        d = bld2(ws, bo);
-        q = __builtin_amdgcn_raw_buffer_load_b32(ws, (int)(bo + 2 + 4 * g), 0, 0);
-        x.load44(xs, xo, k + 4 * g, k + 16 + 4 * g);
+template <>
+struct MF<T_Q4_K> {
+    static constexpr int QK = 256, BB = 144, BPS = 1, QOFF = 16;
+    struct W {
+        u32x4 h, qa, qb;
+    };
+    template <int XT>
+    struct X {
+        XA8<XT> a[8];
+    };
+    __device__ static void load_w(Rsrc ws, uint32_t bo, int g, W& w) {
+        w.h = bld16(ws, bo);
+        w.qa = bld16(ws, bo + QOFF + 16 * g);
+        w.qb = bld16(ws, bo + QOFF + 64 + 16 * g);
     }
-    __device__ void compute(int, f32x4& y) const {
-        const uint32_t t0 = perm(q, SEL01), t1 = perm(q, SEL23);
-        const u32x4 b = {nib_lo(t0), nib_lo(t1), nib_hi(t0), nib_hi(t1)};
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, az = acc;
-        x.mma(b, 0x43084308u, acc, az);
-        add_sub_block(y, h2f(d), acc, az);
+    template <int XT>
+    __device__ static void load_x(Rsrc xs, uint32_t xo, uint32_t k0, int g, X<XT>& x) {
+        constexpr uint32_t ESZ = XT == 0 ? 4 : 2;
+        const uint32_t base = xo + ESZ * (k0 + pair_off(g));
+#pragma unroll
+        for (int s = 0; s < 8; ++s) x.a[s].load8(xs, base + ESZ * 32 * s);
     }
-};
-
-// Q4_K: unit c (0..3) of a super-block = quant bytes 32c..32c+31 (sub-blocks
-// 2c: low nibbles, 2c+1: high nibbles) and the 16-byte header.  Group g holds
-// bytes 32c+8g..32c+8g+7: k-slot j = weight 8g + j of either sub-block.
-// w = d sc q - dmin m: s = d sc, Z = 128, and the min term dmin m sum x with
-// sum x = az / 128.
-template <int XT>
-struct MU<T_Q4_K, XT> {
-    static constexpr int QK = 256, BB = 144, UW = 64;
-    u32x4 h;
-    u32x2 q;
-    X8<XT> xa, xb;
-    __device__ void load(Rsrc ws, uint32_t bo, int g, Rsrc xs, uint32_t xo, uint32_t k, int c) {
-        h = bld16(ws, bo);
-        q = bld8(ws, bo + 16 + 32 * c + 8 * g);
-        xa.load8(xs, xo, k + 8 * g);
-        xb.load8(xs, xo, k + 32 + 8 * g);
-    }
-    // (scale, min) 6-bit pairs of sub-blocks 2c, 2c+1 from the 12 scale bytes
-    // b[0..11] = h.y, h.z, h.w, j = 2 (c & 1):
-    //   c < 2:  sc = b[j] & 63,                        m = b[j+4] & 63
-    //   c >= 2: sc = (b[j+8] & 15) | (b[j] >> 6) << 4, m = (b[j+8] >> 4) | (b[j+4] >> 6) << 4
-    // both built as bytes [scL, scH, mL, mH] with permutes.  With FIFTH, f
-    // holds the fifth bits of the lane's eight weights (Q5_K): bit 2c for
-    // sub-block 2c and 2c+1 for 2c+1.
+    // 6-bit (scale, min) of the eight sub-blocks, as bytes [s0..s3], [s4..s7]
+    // (b[0..11] = h.y, h.z, h.w):
+    //   s < 4:  sc = b[s] & 63,                          m = b[s+4] & 63
+    //   s >= 4: sc = (b[s+4] & 15) | (b[s-4] >> 6) << 4, m = (b[s+4] >> 4) | (b[s] >> 6) << 4
+    struct Scl {
+        float d, dm;
+        uint32_t sc0, sc1, m0, m1;
+        __device__ explicit Scl(const u32x4& h) {
+            d = h2f(h.x & 0xffffu);
+            dm = h2f(h.x >> 16) * 0.0078125f;  // dmin / 128 (exact)
+            sc0 = h.y & 0x3F3F3F3Fu;
+            m0 = h.z & 0x3F3F3F3Fu;
+            sc1 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+            m1 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+        }
+        __device__ float s(int sb) const {
+            const uint32_t v = sb < 4 ? sc0 : sc1;
+            return d * (float)((v >> (8 * (sb & 3))) & 0xffu);
+        }
+        __device__ float m(int sb) const {
+            const uint32_t v = sb < 4 ? m0 : m1;
+            return dm * (float)((v >> (8 * (sb & 3))) & 0xffu);
+        }
+    };
+    // weight operands of chunk c from the swapped quant registers (plus, for
+    // Q5_K, the fifth bits: bit sb of plane byte off(g) + j for k-slot j)
     template <bool FIFTH>
-    __device__ void compute_q(int c, const u32x2& f, f32x4& y) const {
-        const uint32_t j = 2u * (uint32_t)(c & 1);
-        const uint32_t C = __builtin_amdgcn_perm(h.z, h.y, j | (j + 1) << 8 | (j + 4) << 16 | (j + 5) << 24);
-        const uint32_t A = __builtin_amdgcn_perm(h.w, h.w, j | (j + 1) << 8 | j << 16 | (j + 1) << 24);
-        const uint32_t v = c < 2 ? (C & 0x3F3F3F3Fu)
-                                 : (((C >> 2) & 0x30303030u) | (A & 0x00000F0Fu) | ((A >> 4) & 0x0F0F0000u));
-        const float d = h2f(h.x & 0xffffu), dmin = h2f(h.x >> 16);
-        const float sL = d * (float)(v & 0xffu), sH = d * (float)((v >> 8) & 0xffu);
-        const float mL = (dmin * (float)((v >> 16) & 0xffu)) * 0.0078125f;
-        const float mH = (dmin * (float)(v >> 24)) * 0.0078125f;
-        const uint32_t t0 = perm(q.x, SEL01), t1 = perm(q.x, SEL23), t2 = perm(q.y, SEL01), t3 = perm(q.y, SEL23);
-        u32x4 bl = {nib_lo(t0), nib_lo(t1), nib_lo(t2), nib_lo(t3)};
-        u32x4 bh = {nib_hi(t0), nib_hi(t1), nib_hi(t2), nib_hi(t3)};
+    __device__ static void chunk_ops(const W& w, int c, const u32x2& f, u32x4& bl, u32x4& bh) {
+        const uint32_t q0 = c == 0 ? w.qa.x : c == 1 ? w.qa.z : c == 2 ? w.qb.x : w.qb.z;
+        const uint32_t q1 = c == 0 ? w.qa.y : c == 1 ? w.qa.w : c == 2 ? w.qb.y : w.qb.w;
+        const uint32_t t0 = perm(q0, SEL01), t1 = perm(q0, SEL23), t2 = perm(q1, SEL01), t3 = perm(q1, SEL23);
+        bl = u32x4{nib_lo(t0), nib_lo(t1), nib_lo(t2), nib_lo(t3)};
+        bh = u32x4{nib_hi(t0), nib_hi(t1), nib_hi(t2), nib_hi(t3)};
         if constexpr (FIFTH) {
             const uint32_t u[4] = {perm(f.x, SEL01), perm(f.x, SEL23), perm(f.y, SEL01), perm(f.y, SEL23)};
             const uint32_t sl = 2u * (uint32_t)c, sh = sl + 1u;
@@ -245,174 +315,327 @@ struct MU<T_Q4_K, XT> {
                 bh[i] |= ((u[i] >> sh) & 0x00010001u) << 4;
             }
         }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, az = acc;
-        xa.mma(bl, BMAG, acc, az);
-        add_sub_block_min(y, sL, mL, acc, az);
-        acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        az = acc;
-        xb.mma(bh, BMAG, acc, az);
-        add_sub_block_min(y, sH, mH, acc, az);
     }
-    __device__ void compute(int c, f32x4& y) const { compute_q<false>(c, u32x2{0u, 0u}, y); }
-};
-
-// Q5_K: Q4_K with a 32-byte plane of fifth bits at 16 (quants at 48).  Group g
-// also loads plane bytes 8g..8g+7: bit 2c of byte 8g + j is the fifth bit of
-// k-slot j in sub-block 2c, bit 2c+1 in sub-block 2c+1.  Operands 128 + q,
-// q <= 31, stay exact in bf16.
-template <int XT>
-struct MU<T_Q5_K, XT> : MU<T_Q4_K, XT> {
-    static constexpr int BB = 176;
-    u32x2 f;
-    __device__ void load(Rsrc ws, uint32_t bo, int g, Rsrc xs, uint32_t xo, uint32_t k, int c) {
-        this->h = bld16(ws, bo);
-        this->q = bld8(ws, bo + 48 + 32 * c + 8 * g);
-        f = bld8(ws, bo + 16 + 8 * g);
-        this->xa.load8(xs, xo, k + 8 * g);
-        this->xb.load8(xs, xo, k + 32 + 8 * g);
-    }
-    __device__ void compute(int c, f32x4& y) const { this->template compute_q<true>(c, f, y); }
-};
-
-// Q6_K: unit u % 4 = 2h + a of a super-block: half h, quarters jq = a (low
-// nibbles of ql, qh bits 2a..2a+1) and jq = a + 2 (high nibbles, bits
-// 2a+4..2a+5), each as two 16-weight sub-blocks sh = 0, 1 (sub-block index
-// 8h + 2jq + sh, weights 128h + 32jq + 16sh + 0..15).  Group g holds the
-// bytes 16sh+4g..16sh+4g+3 of the quarter's ql and qh runs: k-slot i = weight
-// 16sh + 4g + i.  w = d sc (q - 32): s = d sc, Z = 128 + 32.
-template <int XT>
-struct MU<T_Q6_K, XT> {
-    static constexpr int QK = 256, BB = 210, UW = 64;
-    uint32_t l0, l1, h0, h1, d;
-    u32x2 sc;
-    X4<XT> x[4];  // [jq = a, sh 0], [a, 1], [a + 2, 0], [a + 2, 1]
-    __device__ void load(Rsrc ws, uint32_t bo, int g, Rsrc xs, uint32_t xo, uint32_t k, int p) {
-        const int hh = p >> 1, a = p & 1;
-        const uint32_t ql = bo + 64 * hh + 32 * a + 4 * g, qh = bo + 128 + 32 * hh + 4 * g;
-        l0 = __builtin_amdgcn_raw_buffer_load_b32(ws, (int)ql, 0, 0);
-        l1 = __builtin_amdgcn_raw_buffer_load_b32(ws, (int)(ql + 16), 0, 0);
-        h0 = __builtin_amdgcn_raw_buffer_load_b32(ws, (int)qh, 0, 0);
-        h1 = __builtin_amdgcn_raw_buffer_load_b32(ws, (int)(qh + 16), 0, 0);
-        sc = bld8(ws, bo + 192 + 8 * hh);
-        d = bld2(ws, bo + 208);
-        // k is the unit's first weight 256 b + 128 h; quarter jq starts 32 jq later
-        const uint32_t k0 = k - 64 * (uint32_t)a;  // 256 b + 128 h
-        x[0].load4(xs, xo, k0 + 32 * a + 4 * g);
-        x[1].load4(xs, xo, k0 + 32 * a + 16 + 4 * g);
-        x[2].load4(xs, xo, k0 + 32 * (a + 2) + 4 * g);
-        x[3].load4(xs, xo, k0 + 32 * (a + 2) + 16 + 4 * g);
-    }
-    __device__ void compute(int p, f32x4& y) const {
-        const int a = p & 1;
-        const float dd = h2f(d);
-        // scale bytes 2jq + sh of the half: a: 2a, 2a+1; a+2: 2a+4, 2a+5
-        const uint32_t s01 = a ? (sc.x >> 16) : sc.x, s23 = a ? (sc.y >> 16) : sc.y;
-        const float s[4] = {dd * (float)(int)(int8_t)(s01 & 0xffu), dd * (float)(int)(int8_t)((s01 >> 8) & 0xffu),
-                            dd * (float)(int)(int8_t)(s23 & 0xffu), dd * (float)(int)(int8_t)((s23 >> 8) & 0xffu)};
-        const uint32_t L[2] = {l0, l1}, H[2] = {h0, h1};
-        const uint32_t shl = 4u - 2u * (uint32_t)a, shr = 2u * (uint32_t)a;
+    template <int XT, int R, bool FIFTH = false>
+    __device__ static void compute_k(W (&w)[R], const X<XT>& x, const u32x2 (&f)[R], f32x4 (&y)[R]) {
 #pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-            const uint32_t t0 = perm(L[sh], SEL01), t1 = perm(L[sh], SEL23);
-            const uint32_t u0 = perm(H[sh], SEL01), u1 = perm(H[sh], SEL23);
-            // quarter a: q = low nibble | qh bits (2a, 2a+1) << 4
-            const u32x2 bl = {(t0 & M4) | ((u0 << shl) & 0x00300030u) | BMAG,
-                              (t1 & M4) | ((u1 << shl) & 0x00300030u) | BMAG};
-            // quarter a + 2: q = high nibble | qh bits (2a+4, 2a+5) << 4
-            const u32x2 bh = {((t0 >> 4) & M4) | ((u0 >> shr) & 0x00300030u) | BMAG,
-                              ((t1 >> 4) & M4) | ((u1 >> shr) & 0x00300030u) | BMAG};
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, az = acc;
-            x[sh].mma(bl, 0x43204320u, acc, az);
-            add_sub_block(y, s[sh], acc, az);
-            acc = f32x4{0.f, 0.f, 0.f, 0.f};
-            az = acc;
-            x[2 + sh].mma(bh, 0x43204320u, acc, az);
-            add_sub_block(y, s[2 + sh], acc, az);
+        for (int t = 0; t < R; ++t) {
+            pair_swap(w[t].qa);
+            pair_swap(w[t].qb);
+        }
+        const u32x4 zz = {BMAG, BMAG, BMAG, BMAG};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const AO8<XT> al(x.a[2 * c]), ah(x.a[2 * c + 1]);
+            const f32x4 azl = al.mm(zz), azh = ah.mm(zz);
+#pragma unroll
+            for (int t = 0; t < R; ++t) {
+                u32x4 bl, bh;
+                chunk_ops<FIFTH>(w[t], c, f[t], bl, bh);
+                const Scl sc(w[t].h);
+                add_sub_block_min(y[t], sc.s(2 * c), sc.m(2 * c), al.mm(bl), azl);
+                add_sub_block_min(y[t], sc.s(2 * c + 1), sc.m(2 * c + 1), ah.mm(bh), azh);
+            }
+        }
+    }
+    template <int XT, int R>
+    __device__ static void compute(W (&w)[R], const X<XT>& x, int, f32x4 (&y)[R]) {
+        u32x2 f[R];
+#pragma unroll
+        for (int t = 0; t < R; ++t) f[t] = u32x2{0u, 0u};
+        compute_k<XT, R, false>(w, x, f, y);
+    }
+};
+
+// Q5_K: the Q4_K header, a 32-byte plane of fifth bits at 16 (bit s of byte
+// j: weight 32 s + j), the quants at 48.  Operands 128 + q, q <= 31, stay
+// exact in bf16.
+template <>
+struct MF<T_Q5_K> : MF<T_Q4_K> {
+    static constexpr int BB = 176, QOFF = 48;
+    struct W : MF<T_Q4_K>::W {
+        u32x2 f;
+    };
+    __device__ static void load_w(Rsrc ws, uint32_t bo, int g, W& w) {
+        w.h = bld16(ws, bo);
+        w.qa = bld16(ws, bo + QOFF + 16 * g);
+        w.qb = bld16(ws, bo + QOFF + 64 + 16 * g);
+        w.f = bld8(ws, bo + 16 + pair_off(g));
+    }
+    template <int XT, int R>
+    __device__ static void compute(W (&w)[R], const X<XT>& x, int, f32x4 (&y)[R]) {
+        MF<T_Q4_K>::W b[R];
+        u32x2 f[R];
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            b[t] = w[t];
+            f[t] = w[t].f;
+        }
+        compute_k<XT, R, true>(b, x, f, y);
+    }
+};
+
+// Q4_0: a step is four 18-byte blocks (d, then 16 quant bytes: byte j holds
+// weight j in its low nibble and 16 + j in its high one).  Group g loads block
+// g's quants; after transpose4 its dword j holds bytes 4g..4g+3 of block j:
+// k-slots 0..3 = weights 4g..4g+3, 4..7 = weights 16 + 4g..16 + 4g + 3.
+// w = d (q - 8): s = d, Z = 128 + 8.
+template <>
+struct MF<T_Q4_0> {
+    static constexpr int QK = 32, BB = 18, BPS = 4;
+    struct W {
+        u32x4 q;
+        uint32_t d;
+    };
+    template <int XT>
+    struct X {
+        XA8<XT> a[4];
+    };
+    // bo: offset of the step's first block (the lane loads block g, or a zero
+    // block past the row's last one)
+    __device__ static void load_w(Rsrc ws, uint32_t bo, int g, W& w, bool blk_ok) {
+        const uint32_t o = blk_ok ? bo + (uint32_t)(18 * g) : OOB;
+        w.d = bld2(ws, o);
+        w.q = bld16(ws, o + 2);
+    }
+    template <int XT>
+    __device__ static void load_x(Rsrc xs, uint32_t xo, uint32_t k0, int g, int nvalid, X<XT>& x) {
+        constexpr uint32_t ESZ = XT == 0 ? 4 : 2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t base = j < nvalid ? xo + ESZ * (k0 + 32 * j + 4 * g) : OOB;
+            x.a[j].load44(xs, base, base + ESZ * 16);
+        }
+    }
+    template <int XT, int R>
+    __device__ static void compute(W (&w)[R], const X<XT>& x, int, f32x4 (&y)[R]) {
+        uint32_t d[R][4];
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            transpose4(w[t].q);
+            gather4(w[t].d, d[t]);
+        }
+        const u32x4 zz = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const AO8<XT> a(x.a[j]);
+            const f32x4 az = a.mm(zz);
+#pragma unroll
+            for (int t = 0; t < R; ++t) {
+                const uint32_t q = w[t].q[j];
+                const uint32_t t0 = perm(q, SEL01), t1 = perm(q, SEL23);
+                const u32x4 b = {nib_lo(t0), nib_lo(t1), nib_hi(t0), nib_hi(t1)};
+                add_sub_block(y[t], h2f(d[t][j]), a.mm(b), az);
+            }
+        }
+    }
+};
+
+// Q6_K: ql (128 B) at 0, qh (64 B) at 128, 16 int8 scales at 192, d at 208.
+// Weight i = 128 h + 32 q4 + l (l < 32): low 4 bits = nibble q4 >> 1 of
+// ql[64 h + 32 (q4 & 1) + l], high 2 bits = bits 2 q4, 2 q4 + 1 of
+// qh[32 h + l]; sub-block (16 weights) 8 h + 2 q4 + l / 16.  Group g loads
+// 16-byte piece g of ql[0..63], ql[64..127] and qh; after transpose4 its dword
+// j of each holds bytes 16 j + 4 g .. 16 j + 4 g + 3, so for sub-block
+// (h, q4, a = l / 16) its k-slots i = 0..3 are l = 16 a + 4 g + i: ql dword
+// 2 (q4 & 1) + a of half h, qh dword 2 h + a.  w = d sc (q - 32): s = d sc,
+// Z = 128 + 32.
+template <>
+struct MF<T_Q6_K> {
+    static constexpr int QK = 256, BB = 210, BPS = 1;
+    struct W {
+        u32x4 l0, l1, qh, sc;
+        uint32_t d;
+    };
+    template <int XT>
+    struct X {
+        XA4<XT> a[16];  // sub-block index 8 h + 2 q4 + a
+    };
+    __device__ static void load_w(Rsrc ws, uint32_t bo, int g, W& w) {
+        w.l0 = bld16(ws, bo + 16 * g);
+        w.l1 = bld16(ws, bo + 64 + 16 * g);
+        w.qh = bld16(ws, bo + 128 + 16 * g);
+        w.sc = bld16(ws, bo + 192);
+        w.d = bld2(ws, bo + 208);
+    }
+    template <int XT>
+    __device__ static void load_x(Rsrc xs, uint32_t xo, uint32_t k0, int g, X<XT>& x) {
+        constexpr uint32_t ESZ = XT == 0 ? 4 : 2;
+        const uint32_t base = xo + ESZ * (k0 + 4 * g);
+#pragma unroll
+        for (int sb = 0; sb < 16; ++sb) x.a[sb].load4(xs, base + ESZ * 16 * sb);
+    }
+    template <int XT, int R>
+    __device__ static void compute(W (&w)[R], const X<XT>& x, int, f32x4 (&y)[R]) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            transpose4(w[t].l0);
+            transpose4(w[t].l1);
+            transpose4(w[t].qh);
+        }
+        const u32x2 zz = {0x43204320u, 0x43204320u};
+#pragma unroll
+        for (int sb = 0; sb < 16; ++sb) {
+            const int h = sb >> 3, q4 = (sb >> 1) & 3, a = sb & 1;
+            const AO4<XT> ao(x.a[sb]);
+            const f32x4 az = ao.mm(zz);
+#pragma unroll
+            for (int t = 0; t < R; ++t) {
+                const uint32_t L = (h ? w[t].l1 : w[t].l0)[2 * (q4 & 1) + a];
+                const uint32_t H = w[t].qh[2 * h + a];
+                const uint32_t t0 = perm(L, SEL01), t1 = perm(L, SEL23);
+                const uint32_t u0 = perm(H, SEL01), u1 = perm(H, SEL23);
+                const int ns = 4 * (q4 >> 1), hs = 2 * q4;
+                const u32x2 b = {((t0 >> ns) & M4) | (((u0 >> hs) & 0x00030003u) << 4) | BMAG,
+                                 ((t1 >> ns) & M4) | (((u1 >> hs) & 0x00030003u) << 4) | BMAG};
+                const float s = h2f(w[t].d) * (float)(int)(int8_t)(w[t].sc[sb >> 2] >> (8 * (sb & 3)));
+                add_sub_block(y[t], s, ao.mm(b), az);
+            }
+        }
+    }
+};
+
+// Uniform load interface over the formats (Q4_0 needs the block count to
+// zero the blocks past the row's end).
+template <int TYPE, int XT>
+struct Step {
+    using F = MF<TYPE>;
+    __device__ static void load(Rsrc ws, uint32_t ro, int step, int nblk, int g, typename F::W& w) {
+        if constexpr (TYPE == T_Q4_0) {
+            const bool ok = ro != OOB && 4 * step + g < nblk;
+            F::load_w(ws, ro + (uint32_t)step * (4 * F::BB), g, w, ok);
+        } else {
+            F::load_w(ws, ro == OOB ? OOB : ro + (uint32_t)step * F::BB, g, w);
+        }
+    }
+    __device__ static void load_x(Rsrc xs, uint32_t xo, int step, int nblk, int g, typename F::template X<XT>& x) {
+        if constexpr (TYPE == T_Q4_0) {
+            const int nvalid = xo == OOB ? 0 : nblk - 4 * step;
+            F::template load_x<XT>(xs, xo, (uint32_t)step * 128u, g, nvalid, x);
+        } else {
+            F::template load_x<XT>(xs, xo, (uint32_t)step * F::QK, g, x);
         }
     }
 };
 
 // --------------------------------------------------------------- kernel ----
 
-// Units in flight per lane: P.  Unit u of a row: block u / UPB, position
-// u % UPB inside it (UPB = QK / UW).
-template <int TYPE, int XT, int P>
+// R row tiles per wavefront, P steps in flight per lane.
+template <int TYPE, int XT, int R, int P>
 __global__ __launch_bounds__(64 * WMAX) void k_mmv(const uint8_t* __restrict__ W, int64_t N, int64_t K,
                                                    const uint8_t* __restrict__ x, int batch, float* __restrict__ y) {
-    using U = MU<TYPE, XT>;
-    constexpr int UPB = U::QK / U::UW;
+    using F = MF<TYPE>;
+    using S = Step<TYPE, XT>;
     constexpr int ESZ = XT == 0 ? 4 : 2;
-    __shared__ f32x4 red[WMAX - 1][64];
+    __shared__ f32x4 red[WMAX - 1][R][64];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int nw = (int)(blockDim.x >> 6);
     const int nl = lane & 15, g = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int rows = (int)(N - n0 < 16 ? N - n0 : 16);
-    const uint32_t row_bytes = (uint32_t)(K / U::QK) * U::BB;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * R);
+    const int rows = (int)(N - n0 < 16 * R ? N - n0 : 16 * R);
+    const uint32_t row_bytes = (uint32_t)(K / F::QK) * F::BB;
     const Rsrc ws = make_rsrc(W + n0 * (int64_t)row_bytes, (uint32_t)rows * row_bytes);
     const Rsrc xs = make_rsrc(x, (uint32_t)((int64_t)batch * K * ESZ));
-    const uint32_t roff = nl < rows ? (uint32_t)nl * row_bytes : OOB;
+    uint32_t roff[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) roff[t] = 16 * t + nl < rows ? (uint32_t)(16 * t + nl) * row_bytes : OOB;
     const uint32_t xoff = nl < batch ? (uint32_t)((int64_t)nl * K * ESZ) : OOB;
 
-    const int nu = (int)(K / U::UW);
-    const int u0 = (int)((int64_t)wave * nu / nw), u1 = (int)((int64_t)(wave + 1) * nu / nw);
-    const int n = u1 - u0;
+    const int nblk = (int)(K / F::QK);
+    const int steps = (nblk + F::BPS - 1) / F::BPS;
+    const int s0 = wave * steps / nw, s1 = (wave + 1) * steps / nw;
+    const int n = s1 - s0;
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    U ring[P];
-    auto issue = [&](U& r, int i) {
+    f32x4 acc[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    typename F::W wr[P][R];
+    typename F::template X<XT> xr[P];
+    auto issue = [&](int j, int i) {
         const bool ok = i < n;
-        const int u = ok ? u0 + i : u0;
-        const int blk = u / UPB, pos = u % UPB;
-        r.load(ws, ok ? roff + (uint32_t)blk * U::BB : OOB, g, xs, ok ? xoff : OOB, (uint32_t)u * U::UW, pos);
+        const int st = s0 + (ok ? i : 0);
+#pragma unroll
+        for (int t = 0; t < R; ++t) S::load(ws, ok ? roff[t] : OOB, st, nblk, g, wr[j][t]);
+        S::load_x(xs, ok ? xoff : OOB, st, nblk, g, xr[j]);
     };
 #pragma unroll
-    for (int j = 0; j < P; ++j) issue(ring[j], j);
+    for (int j = 0; j < P; ++j) issue(j, j);
     for (int i = 0; i < n; i += P) {
 #pragma unroll
         for (int j = 0; j < P; ++j) {
-            if (i + j < n) ring[j].compute((u0 + i + j) % UPB, acc);
-            issue(ring[j], i + j + P);
+            if (i + j < n) F::template compute<XT, R>(wr[j], xr[j], g, acc);
+            issue(j, i + j + P);
         }
     }
 
     if (nw > 1) {
-        if (wave > 0) red[wave - 1][lane] = acc;
+        if (wave > 0)
+#pragma unroll
+            for (int t = 0; t < R; ++t) red[wave - 1][t][lane] = acc[t];
         __syncthreads();
         if (wave != 0) return;
-        for (int w = 0; w < nw - 1; ++w) acc += red[w][lane];
-    }
-    const int64_t nn = n0 + nl;
-    if (nl < rows) {
+        for (int w = 0; w < nw - 1; ++w)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * g + r;
-            if (t < batch) y[(int64_t)t * N + nn] = acc[r];
+            for (int t = 0; t < R; ++t) acc[t] += red[w][t][lane];
+    }
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const int row = 16 * t + nl;
+        if (row < rows) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int v = 4 * g + r;
+                if (v < batch) y[(int64_t)v * N + n0 + row] = acc[t][r];
+            }
         }
     }
 }
 
-template <int TYPE, int XT, int P>
-hipError_t launch(const uint8_t* W, int64_t N, int64_t K, const uint8_t* x, int batch, float* y, hipStream_t s) {
-    using U = MU<TYPE, XT>;
-    const int64_t tiles = (N + 15) / 16;
-    if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-    // wavefronts per workgroup: enough to put about four per SIMD on the chip
-    // (2 x 2048 wavefronts), each with at least three units of K
-    const int64_t nu = K / U::UW;
-    int nw = 1;
-    while (nw < WMAX && tiles * nw < 4096 && nu >= 3 * (2 * nw)) nw *= 2;
-    hipLaunchKernelGGL((k_mmv<TYPE, XT, P>), dim3((unsigned)tiles), dim3(64 * nw), 0, s, W, N, K, x, batch, y);
+template <int TYPE, int XT, int R>
+hipError_t launch_r(const uint8_t* W, int64_t N, int64_t K, const uint8_t* x, int batch, float* y, int nw,
+                    hipStream_t s) {
+    // steps in flight: enough to cover the memory latency within the
+    // register budget of two wavefronts per SIMD (256 registers)
+    constexpr int P = R == 1 && XT == 1 ? 3 : 2;
+    const int64_t groups = (N + 16 * R - 1) / (16 * R);
+    if (groups > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_mmv<TYPE, XT, R, P>), dim3((unsigned)groups), dim3(64 * nw), 0, s, W, N, K, x, batch, y);
     return hipGetLastError();
+}
+
+template <int TYPE, int XT>
+hipError_t launch(const uint8_t* W, int64_t N, int64_t K, const uint8_t* x, int batch, float* y, hipStream_t s) {
+    using F = MF<TYPE>;
+    const int64_t tiles = (N + 15) / 16;
+    const int64_t steps = (K / F::QK + F::BPS - 1) / F::BPS;
+    // Row tiles per wavefront R (each activation fragment serves R tiles) and
+    // wavefronts per workgroup (splitting K): the largest R whose launch still
+    // holds >= 1024 wavefronts, each workgroup doubling its wavefronts while
+    // the launch holds < 2048 and each keeps >= 2 steps.
+    auto waves = [&](int R, int& nw) {
+        const int64_t groups = (tiles + R - 1) / R;
+        nw = 1;
+        while (nw < WMAX && groups * nw < 2048 && steps >= 2 * (2 * nw)) nw *= 2;
+        return groups * nw;
+    };
+    int nw;
+    // four tiles fit the register budget with bf16 activations and the
+    // 32-weight sub-blocks; fp32 (hi and lo operands) and Q6_K (16 operands
+    // per step) take at most two
+    if constexpr (XT == 1 && TYPE != T_Q6_K)
+        if (waves(4, nw) >= 1024) return launch_r<TYPE, XT, 4>(W, N, K, x, batch, y, nw, s);
+    if (waves(2, nw) >= 1024) return launch_r<TYPE, XT, 2>(W, N, K, x, batch, y, nw, s);
+    waves(1, nw);
+    return launch_r<TYPE, XT, 1>(W, N, K, x, batch, y, nw, s);
 }
 
 template <int TYPE>
 hipError_t launch_x(const uint8_t* W, int64_t N, int64_t K, const uint8_t* x, int x_dtype, int batch, float* y,
                     hipStream_t s) {
-    if (x_dtype == DT_F32) return launch<TYPE, 0, 3>(W, N, K, x, batch, y, s);
-    return launch<TYPE, 1, 4>(W, N, K, x, batch, y, s);
+    if (x_dtype == DT_F32) return launch<TYPE, 0>(W, N, K, x, batch, y, s);
+    return launch<TYPE, 1>(W, N, K, x, batch, y, s);
 }
 
 }  // namespace

@@ -113,8 +113,9 @@ gq_status gq_dequant(gq_type t, const void* blocks, int64_t n_blocks, void* out,
  * the Gemma 4 26B-A4B Show HN page verifies blocks of up to 16 draft tokens).
  * K must be a multiple of QK and at most 4,194,304 (GQ_ERR_SHAPE otherwise).
  * N == 0 is a no-op; K == 0 writes zeros.
- * Two paths compute it: batch > 8, and Q4_0 / Q4_K at batch 5..8, run on the
- * matrix cores; the rest on the packed fp16 dot instructions.
+ * Two paths compute it: batch >= 5, Q4_0 / Q4_K / Q5_K at batch 4 with
+ * N <= 4 K and at batch 3 with 4 N <= 5 K run on the matrix cores (the
+ * measured crossovers); the rest on the packed fp16 dot instructions.
  * Accuracy, dot path: activations enter as fp16 after an exact power-of-two
  * scaling per 32 inputs (relative rounding <= 2^-11), weights as the exact
  * fp16 values 1024 + q, sums are fp32.  Matrix-core path: bf16 activations
@@ -125,7 +126,7 @@ gq_status gq_dequant(gq_type t, const void* blocks, int64_t n_blocks, void* out,
  * 1024 (dot) or 160 (matrix cores) * sum |x| per sub-block), e.g. rows whose
  * quants nearly all sit at the zero point; a sub-block whose quants all equal
  * the zero point contributes exactly zero.  Each vector's result depends on
- * that vector alone (bit for bit) within one path. */
+ * that vector and on N, K alone (bit for bit) within one path. */
 gq_status gq_matvec(gq_type t, const void* W, int64_t N, int64_t K, const void* x,
                     gq_dtype x_dtype, int32_t batch, float* y, hipStream_t stream);
 
@@ -178,8 +179,35 @@ gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_
                        gq_dtype x_dtype, int32_t x_per_slot, const float* route_w, float* y,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Waits for `stream`, then reports how many ids of the last gq_matvec_id call
- * that used `ws` were outside [0, n_experts). */
+/* Workspace bytes gq_matvec_id_glu needs (any gq_matvec_id_workspace size is
+ * at least this). */
+#define GQ_MATVEC_ID_GLU_WS_BYTES 256
+
+/* Routed gated unit: the gate and up products of a routed feed-forward block
+ * and the activation between them, in one launch (the routed 4-bit experts of
+ * the Architecture section of the Gemma 4 26B-A4B Show HN page; the
+ * ggml-quantization row of the kernel table in "GGUF in transformers").
+ * experts_gate, experts_up: packed [n_experts][N][K/QK] blocks of type t;
+ * ids: [n_tokens][top_k] int32 (device); x: [n_tokens][K] of x_dtype (GQ_F32
+ * or GQ_BF16), read by every slot of its token.  For each slot (t, j) with
+ * e = ids[t][j]:
+ *   h[t][j][n] = act(sum_k gate_e[n][k] x_t[k]) * (sum_k up_e[n][k] x_t[k]),
+ * h: [n_tokens][top_k][N] of h_dtype (GQ_F32 or GQ_BF16) -- the per-slot
+ * vectors a down projection takes as gq_matvec_id's x with x_per_slot == 1.
+ * Each distinct expert's rows of both stacks are read once for all its slots.
+ * act as for gq_matvec_glu.  ws: device workspace of at least
+ * GQ_MATVEC_ID_GLU_WS_BYTES bytes, no initialisation needed; an id outside
+ * [0, n_experts) gives its slot a zero row of h and is counted in ws (see
+ * gq_matvec_id_check).  Shapes and limits as gq_matvec_id; n_tokens == 0 or
+ * N == 0 is a no-op.  Accuracy: g and u as gq_matvec_id, act and the product
+ * as gq_matvec_glu. */
+gq_status gq_matvec_id_glu(gq_type t, const void* experts_gate, const void* experts_up, int32_t n_experts,
+                           int64_t N, int64_t K, const int32_t* ids, int32_t n_tokens, int32_t top_k,
+                           const void* x, gq_dtype x_dtype, gq_act act, void* h, gq_dtype h_dtype, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* Waits for `stream`, then reports how many ids of the last gq_matvec_id or
+ * gq_matvec_id_glu call that used `ws` were outside [0, n_experts). */
 gq_status gq_matvec_id_check(const void* ws, hipStream_t stream, int32_t* n_bad_ids);
 
 /* Expert routing ("GGUF in transformers", section "Reusing ggml's Metal

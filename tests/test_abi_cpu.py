@@ -33,6 +33,8 @@ def lib(gq_lib_path):
     L.gq_block_info.argtypes = [ctypes.c_int, ctypes.POINTER(I32), ctypes.POINTER(I32)]
     L.gq_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
     L.gq_matvec_glu.argtypes = [ctypes.c_int, P, P, I64, I64, P, ctypes.c_int, I32, ctypes.c_int, P, ctypes.c_int, P]
+    L.gq_matvec_id_glu.argtypes = [ctypes.c_int, P, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, ctypes.c_int, P,
+                                   ctypes.c_int, P, SZ, P]
     return L
 
 
@@ -44,7 +46,7 @@ def declared_functions() -> list[str]:
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -202,3 +204,33 @@ def test_matvec_glu_validation(lib):
     assert f(2, A, MIS, 8, 256, A, 0, 1, 0, A, 0, None) == GQ_ERR_ALIGN
     assert f(2, A, A, 8, 256, A, 0, 1, 0, MIS, 1, None) == GQ_ERR_ALIGN
     assert f(2, A, A, 0, 256, A, 0, 1, 0, A, 0, None) == GQ_OK  # N == 0: no-op
+
+
+def test_matvec_id_glu_validation(lib):
+    f = lib.gq_matvec_id_glu
+    # (type, gate, up, n_experts, N, K, ids, n_tokens, top_k, x, x_dtype, act, h, h_dtype, ws, ws_bytes, stream)
+    ok = [2, A, A, 128, 704, 2816, A, 8, 8, A, 0, 0, A, 0, A, 256, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a0=9) == GQ_ERR_TYPE
+    assert call(a10=2) == GQ_ERR_DTYPE  # fp16 activations
+    assert call(a13=2) == GQ_ERR_DTYPE  # fp16 output
+    assert call(a5=100) == GQ_ERR_SHAPE  # K not whole blocks
+    assert call(a3=0) == GQ_ERR_SHAPE
+    assert call(a8=0) == GQ_ERR_SHAPE
+    assert call(a8=129) == GQ_ERR_SHAPE  # top_k > n_experts
+    assert call(a7=129) == GQ_ERR_SHAPE  # 129 * 8 slots > 1024
+    assert call(a5=(1 << 22) + 256) == GQ_ERR_SHAPE
+    assert call(a11=2) == GQ_ERR_UNSUPPORTED  # unknown activation
+    for i in (1, 2, 6, 9, 12, 14):
+        assert call(**{"a%d" % i: None}) == GQ_ERR_NULL, i
+    for i in (1, 2, 6, 9, 12, 14):
+        assert call(**{"a%d" % i: MIS}) == GQ_ERR_ALIGN, i
+    assert call(a15=255) == GQ_ERR_WORKSPACE
+    assert call(a7=0, a1=None, a2=None, a6=None, a9=None, a12=None, a14=None) == GQ_OK  # no tokens: no-op
+    assert call(a4=0) == GQ_OK  # N == 0: no-op

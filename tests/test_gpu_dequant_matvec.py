@@ -154,18 +154,22 @@ def test_matvec_parity(gq, orc, t, xdt, B):
 
 
 @pytest.mark.parametrize("t", TYPES)
-def test_matvec_batch_columns_bit_identical(gq, t):
-    """Each column of a batch-4 product equals the batch-1 product of that
-    vector bit for bit (the dot-product path's multi-vector kernels agree with
-    its one-vector kernel)."""
+@pytest.mark.parametrize("B", [2, 4])
+def test_matvec_batch_columns_bit_identical(gq, t, B):
+    """Each column of a multi-vector dot-path product equals the batch-1
+    product of that vector bit for bit (the dot-product path's multi-vector
+    kernels agree with its one-vector kernel).  N > 4 K keeps batch 4 on the
+    dot path."""
     N, K = (300, 4096) if t == "q4_0" else (300, 5120)
+    if B == 4:
+        N, K = (20000, 2048) if t == "q4_0" else (21000, 2560)
     g = synth.rng(0x67510000, 77)
     W = dev(synth.weight(t, g, N, K))
     for xdt in ("f32", "bf16"):
-        x, x_t = make_x(g, 4, K, xdt)
-        y8 = torch.empty(4, N, device="cuda")
+        x, x_t = make_x(g, B, K, xdt)
+        y8 = torch.empty(B, N, device="cuda")
         gq.gq_matvec(t, W, N, K, x_t, y8)
-        for b in range(4):
+        for b in range(B):
             y1 = torch.empty(1, N, device="cuda")
             gq.gq_matvec(t, W, N, K, x_t[b:b + 1].contiguous(), y1)
             torch.cuda.synchronize()

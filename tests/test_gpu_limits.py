@@ -45,10 +45,11 @@ def check_bound(y, yref, sumabs, what):
     assert not bad.any(), "%s: %d elements outside the bound" % (what, bad.sum())
 
 
-@pytest.mark.parametrize("t,B", [("q4_0", 1), ("q4_k", 1), ("q4_k", 5), ("q6_k", 2), ("q5_k", 1), ("q4_k", 9)])
+@pytest.mark.parametrize("t,B", [("q4_0", 1), ("q4_k", 1), ("q4_k", 5), ("q6_k", 2), ("q5_k", 1), ("q4_k", 9),
+                                 ("q6_k", 9), ("q4_0", 6), ("q5_k", 8)])
 def test_matvec_longest_row(gq, orc, t, B):
     """K = 2^22 with 37 rows (two and a bit workgroups of rows on every path):
-    batch 1/2 on the dot-product path, 5 and 9 on the matrix cores."""
+    batch 1/2 on the dot-product path, 5..9 on the matrix cores."""
     N = 37
     g = synth.rng(0x67510009, ("q4_0", "q4_k", "q6_k", "q5_k").index(t) * 10 + B)
     W = synth.weight(t, g, N, KMAX)

@@ -131,9 +131,10 @@ def test_matvec_id_single_expert_equals_matvec(gq, t):
     y, _ = run_id(gq, t, ex, E, N, K, ids, dev(x), False)
     eb = N * K // QK[t] * BB[t]
     W3 = dev(ex.reshape(-1)[3 * eb:4 * eb])
-    # gq_matvec with 4 vectors at a time uses the same 4-vector kernel
-    for tok0 in range(0, T, 4):
-        xs = x[tok0:tok0 + 4]
+    # gq_matvec with 1 or 2 vectors runs the dot-product path, whose columns
+    # match its 4-vector kernel's bit for bit
+    for tok0 in range(0, T, 2):
+        xs = x[tok0:tok0 + 2]
         yy = torch.empty(xs.shape[0], N, device="cuda")
         gq.gq_matvec(t, W3, N, K, dev(xs), yy)
         torch.cuda.synchronize()

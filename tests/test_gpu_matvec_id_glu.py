@@ -1,0 +1,223 @@
+"""GPU parity of gq_matvec_id_glu (routed gate and up products with the
+activation and product between them, one launch) against the CPU oracle.
+
+Bar, per slot (t, j) and row n, with g, u the oracle's exact routed products
+and S_g, S_u their sums sum_k |w x| (the routed-product bar is 1e-3 S):
+  |h - act(g) u| <= 1.2e-3 S_g |u| + 1e-3 S_u |act(g)| + 1.2e-6 S_g S_u + 4e-6 |h|
+(1.2 bounds |act'| for both activations; the last term covers fp32 exp/tanh
+and the product), plus 2^-8 |h| for bf16 outputs -- the bar of the dense
+gated unit, applied to the routed products.
+
+The MoE layer test then runs the whole routed feed-forward block on the
+device (route, gated unit, weighted down projection) and checks the layer
+output against the oracle's layer, with the gated unit's bound carried through
+the down projection: sum_j |r_j| sum_k |w_down[n][k]| bound_h[t][j][k]."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_quantized_weight_q4_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TYPES = ("q4_0", "q4_k", "q6_k", "q5_k")
+BB = {"q4_0": 18, "q4_k": 144, "q6_k": 210, "q5_k": 176}
+QK = {"q4_0": 32, "q4_k": 256, "q6_k": 256, "q5_k": 256}
+
+
+@pytest.fixture(autouse=True)
+def _name_the_case(request):
+    print("\n[gpu case] %s" % request.node.nodeid, flush=True)
+    sys.stdout.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def gq():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_quantized_weight_q4_amd as g
+    return g
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def make_x(g, shape, xdt):
+    x = synth.normal_f32(g, shape)
+    if xdt == "bf16":
+        bits = synth.bf16_bits(x)
+        return synth.bf16_to_f32(bits), dev(bits.view(np.int16)).view(torch.bfloat16)
+    return x, dev(x)
+
+
+def run_glu_id(gq, t, gate, up, E, N, K, ids, x_t, act, hdt, ws_bytes=None):
+    T, k = ids.shape
+    ws = torch.empty(ws_bytes or gq.MATVEC_ID_GLU_WS_BYTES, dtype=torch.uint8, device="cuda")
+    ws.fill_(0xAB)  # contents need no initialisation
+    h = torch.full((T, k, N), float("nan"), device="cuda", dtype=torch.float32 if hdt == "f32" else torch.bfloat16)
+    gq.gq_matvec_id_glu(t, dev(gate), dev(up), E, N, K, dev(ids), x_t, act, h, ws)
+    torch.cuda.synchronize()
+    return h, ws
+
+
+def glu_ref(orc, t, gate, up, E, N, K, ids, x, act, hdt):
+    """(act(g) u, its per-element bound) from the oracle's routed products."""
+    g, sg = orc.matvec_id(t, gate, E, N, K, ids, x, False)
+    u, su = orc.matvec_id(t, up, E, N, K, ids, x, False)
+    ref = orc.glu(g, u, act)
+    ag = orc.glu(g, np.ones_like(g), act)
+    bound = 1.2e-3 * sg * np.abs(u) + 1e-3 * su * np.abs(ag) + 1.2e-6 * sg * su + 4e-6 * np.abs(ref)
+    if hdt == "bf16":
+        bound = bound + 2.0 ** -8 * np.abs(ref)
+    return ref, bound
+
+
+def check(h, ref, bound, what):
+    h = np.asarray(h, np.float64)
+    assert np.all(np.isfinite(h)), what
+    err = np.abs(h - ref)
+    bad = err > bound
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError("%s: %d outside the bound, first %s: h=%r ref=%r bound=%r" % (
+            what, bad.sum(), i, h[i], ref[i], bound[i]))
+    pos = bound > 0
+    return float(np.max(err[pos] / bound[pos])) if pos.any() else 0.0
+
+
+@pytest.mark.parametrize("t", TYPES)
+@pytest.mark.parametrize("xdt,hdt", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")])
+def test_glu_id_shapes(gq, orc, t, xdt, hdt):
+    """Ragged row counts (several row tiles and a partial one), groups of one to
+    several slots per expert, both activations."""
+    worst = 0.0
+    g = synth.rng(0x67510009, 10 * TYPES.index(t) + ["f32", "bf16"].index(xdt) + 2 * ["f32", "bf16"].index(hdt))
+    cases = ((5, 37, 512, 3, 2), (16, 130, 1024, 6, 4), (9, 64, 2048, 16, 3), (4, 200, 256, 5, 4))
+    for ci, (E, N, K, T, k) in enumerate(cases):
+        gate = synth.weight(t, g, E * N, K)
+        up = synth.weight(t, g, E * N, K)
+        ids = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        x, x_t = make_x(g, (T, K), xdt)
+        act = ("silu", "gelu_tanh")[ci % 2]
+        h, ws = run_glu_id(gq, t, gate, up, E, N, K, ids, x_t, act, hdt)
+        ref, bound = glu_ref(orc, t, gate, up, E, N, K, ids, x, act, hdt)
+        worst = max(worst, check(h.float().cpu().numpy(), ref, bound,
+                                 "%s E=%d N=%d K=%d T=%d k=%d %s %s->%s" % (t, E, N, K, T, k, act, xdt, hdt)))
+        assert gq.gq_matvec_id_check(ws) == 0
+    print("worst error / bound = %.4f" % worst)
+
+
+def test_glu_id_repeated_experts_and_determinism(gq, orc):
+    """Skewed routing (most slots to two experts, so long runs split into many
+    groups); repeated calls are bit-identical."""
+    g = synth.rng(0x67510009, 100)
+    E, N, K, T, k = 32, 72, 768, 64, 4
+    gate = synth.weight("q4_k", g, E * N, K)
+    up = synth.weight("q4_k", g, E * N, K)
+    ids = np.where(g.random((T, k)) < 0.7, g.integers(0, 2, (T, k)), g.integers(0, E, (T, k))).astype(np.int32)
+    x, x_t = make_x(g, (T, K), "f32")
+    h1, _ = run_glu_id(gq, "q4_k", gate, up, E, N, K, ids, x_t, "silu", "f32")
+    h2, _ = run_glu_id(gq, "q4_k", gate, up, E, N, K, ids, x_t, "silu", "f32")
+    h1 = h1.cpu().numpy()
+    assert np.array_equal(h1.view(np.uint32), h2.cpu().numpy().view(np.uint32))
+    ref, bound = glu_ref(orc, "q4_k", gate, up, E, N, K, ids, x, "silu", "f32")
+    check(h1, ref, bound, "skewed")
+
+
+def test_glu_id_bad_ids_counted_and_zero(gq, orc):
+    g = synth.rng(0x67510009, 101)
+    E, N, K, T, k = 8, 40, 512, 4, 3
+    gate = synth.weight("q4_k", g, E * N, K)
+    up = synth.weight("q4_k", g, E * N, K)
+    ids = g.integers(0, E, (T, k)).astype(np.int32)
+    ids[0, 1] = E
+    ids[2, 0] = -1
+    ids[3, 2] = 1 << 30
+    x, x_t = make_x(g, (T, K), "f32")
+    for hdt in ("f32", "bf16"):
+        h, ws = run_glu_id(gq, "q4_k", gate, up, E, N, K, ids, x_t, "gelu_tanh", hdt)
+        assert gq.gq_matvec_id_check(ws) == 3
+        h = h.float().cpu().numpy()
+        assert np.all(h[0, 1] == 0) and np.all(h[2, 0] == 0) and np.all(h[3, 2] == 0)
+        ref, bound = glu_ref(orc, "q4_k", gate, up, E, N, K, ids, x, "gelu_tanh", hdt)
+        check(h, ref, bound, "bad ids " + hdt)
+
+
+def test_glu_id_edge_cases(gq):
+    e = torch.empty(0, dtype=torch.uint8, device="cuda")
+    ids = torch.zeros((2, 2), dtype=torch.int32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    # K == 0: every h row is act(0) * 0 = 0
+    h = torch.full((2, 2, 9), float("nan"), device="cuda")
+    gq.gq_matvec_id_glu("q4_0", e, e, 3, 9, 0, ids, torch.empty(2, 0, device="cuda"), "silu", h, ws)
+    torch.cuda.synchronize()
+    assert torch.all(h == 0)
+    # no tokens, N == 0: no-ops that write nothing
+    h2 = torch.full((1, 2, 4), 2.0, device="cuda")
+    w = torch.empty(144 * 4, dtype=torch.uint8, device="cuda")
+    gq.gq_matvec_id_glu("q4_k", w, w, 2, 4, 256, ids[:0], torch.zeros(0, 256, device="cuda"), "silu", h2, ws)
+    gq.gq_matvec_id_glu("q4_k", w, w, 2, 0, 256, ids[:1], torch.zeros(1, 256, device="cuda"), "silu", h2[:, :, :0],
+                        ws)
+    torch.cuda.synchronize()
+    assert torch.all(h2 == 2.0)
+    with pytest.raises(gq.GqError, match="workspace"):
+        gq.gq_matvec_id_glu("q4_k", w, w, 2, 4, 256, ids, torch.zeros(2, 256, device="cuda"), "silu", h, ws[:255])
+
+
+@pytest.mark.parametrize("hdt", ["f32", "bf16"])
+def test_moe_layer_route_glu_down(gq, orc, hdt):
+    """128 experts, hidden 2816, expert FFN 704 (Q4_0); 8 tokens routed top-8
+    on the device; gated unit (SiLU) in one launch; weighted down projection
+    on its h.  Each step is checked against the oracle's step on the oracle's
+    own inputs; the layer output against the oracle's layer."""
+    E, H, F, T, k = 128, 2816, 704, 8, 8
+    g = synth.rng(0x67510004, 0)
+    logits = synth.router_logits(g, T, E)
+    ids_t = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    rw_t = torch.empty((T, k), device="cuda")
+    gq.gq_route_topk(dev(logits), k, ids_t, rw_t)
+    ids, rw64 = orc.route_topk(logits, k)
+    assert np.array_equal(ids_t.cpu().numpy(), ids)
+    rw = rw_t.cpu().numpy()
+    assert np.abs(rw - rw64).max() <= (k + 8) * 2.0 ** -24
+    x = synth.normal_f32(g, (T, H))
+    gate = synth.weight("q4_0", synth.rng(0x67510004, 1), E * F, H)
+    up = synth.weight("q4_0", synth.rng(0x67510004, 2), E * F, H)
+    down = synth.weight("q4_0", synth.rng(0x67510004, 3), E * H, F)
+
+    ws = torch.empty(gq.gq_matvec_id_workspace(E, T, k, H), dtype=torch.uint8, device="cuda")
+    h = torch.empty((T, k, F), device="cuda", dtype=torch.float32 if hdt == "f32" else torch.bfloat16)
+    gq.gq_matvec_id_glu("q4_0", dev(gate), dev(up), E, F, H, ids_t, dev(x), "silu", h, ws)
+    y = torch.full((T, H), float("nan"), device="cuda")
+    gq.gq_matvec_id("q4_0", dev(down), E, H, F, ids_t, h, True, y, ws, rw_t)
+    torch.cuda.synchronize()
+
+    h_ref, h_bound = glu_ref(orc, "q4_0", gate, up, E, F, H, ids, x, "silu", hdt)
+    r = check(h.float().cpu().numpy(), h_ref, h_bound, "gated unit " + hdt)
+    print("gated unit worst err/bound %.4f" % r)
+
+    h32 = h_ref.astype(np.float32)
+    y_ref, sa = orc.matvec_id("q4_0", down, E, H, F, ids, h32, True, rw)
+    # the gated unit's error (and the fp32 rounding of the oracle's h) carried
+    # through the down projection: sum_j |r_j| sum_k |w[n][k]| dh[t][j][k]
+    dh = h_bound + np.abs(h_ref - h32)
+    eb = H * F // QK["q4_0"] * BB["q4_0"]
+    carry = np.zeros((T, H))
+    for e in np.unique(ids):
+        Wa = np.abs(orc.dequant("q4_0", down.reshape(-1)[e * eb:(e + 1) * eb]).astype(np.float64).reshape(H, F))
+        for t_ in range(T):
+            for j in range(k):
+                if ids[t_, j] == e:
+                    carry[t_] += abs(float(rw[t_, j])) * (Wa @ dh[t_, j])
+    yv = y.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(yv))
+    err = np.abs(yv - y_ref)
+    bound = 1e-3 * sa + carry
+    assert not (err > bound).any(), "layer output: %d outside the bound" % (err > bound).sum()
+    print("layer output worst err/bound %.4f" % float(np.max(err / bound)))
