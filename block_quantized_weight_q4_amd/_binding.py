@@ -127,9 +127,6 @@ def gq_matvec_id(t, experts: torch.Tensor, n_experts: int, N: int, K: int, ids: 
     return y
 
 
-MATVEC_ID_GLU_WS_BYTES = 256
-
-
 def gq_matvec_id_glu(t, experts_gate: torch.Tensor, experts_up: torch.Tensor, n_experts: int, N: int, K: int,
                      ids: torch.Tensor, x: torch.Tensor, act: str, h: torch.Tensor, ws: torch.Tensor,
                      stream=None) -> torch.Tensor:

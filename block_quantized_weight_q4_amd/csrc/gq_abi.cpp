@@ -172,7 +172,7 @@ gq_status gq_matvec_id_glu(gq_type t, const void* experts_gate, const void* expe
     if (!aligned16(ids) || !aligned16(h) || !aligned16(ws) ||
         (K > 0 && (!aligned16(experts_gate) || !aligned16(experts_up) || !aligned16(x))))
         return GQ_ERR_ALIGN;
-    if (ws_bytes < GQ_MATVEC_ID_GLU_WS_BYTES) return GQ_ERR_WORKSPACE;
+    if (ws_bytes < gqk_matvec_id_ws_bytes(n_experts, n_tokens, top_k, N)) return GQ_ERR_WORKSPACE;
     try {
         return from_hip(gqk_matvec_id_glu(t, experts_gate, experts_up, n_experts, N, K, ids, n_tokens, top_k, x,
                                           x_dtype, act, h, h_dtype, ws, stream));

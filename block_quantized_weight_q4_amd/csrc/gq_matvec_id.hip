@@ -4,20 +4,18 @@
 // the routed 4-bit experts of the Architecture section of "Show HN: Gemma 4
 // 26B-A4B at up to 100+ tokens/s on a 16 GB Mac").
 //
-// One or two launches on the caller's stream, no host synchronisation:
-//  1. k_experts: one workgroup per (group, row tile).  The slots
-//     s = t*top_k + j are ordered by expert id and each expert's slots are
-//     cut into groups of at most CH; every workgroup derives that grouping
-//     from the ids itself (a histogram and a scan in LDS) and keeps the group
-//     whose index is its own.  It then
-//     runs the shared decode product on that expert's rows with the group's
-//     activation vectors (gathered by slot), writing one output row per slot.
-//     Workgroups past the number of groups exit after the grouping (the grid
+// Two or three launches on the caller's stream, no host synchronisation:
+//  1. k_plan (one workgroup): the slots s = t*top_k + j are ordered by expert
+//     id and each expert's slots are cut into groups of at most CH; the group
+//     table (expert, slot count, slots) goes to the workspace, with the group
+//     and invalid-id counts in its header.  Ids outside [0, n_experts) are
+//     left out, counted, and their output rows zeroed.
+//  2. k_experts: one workgroup per (group, row tile) reads its table entry
+//     and runs the shared decode product on that expert's rows with the
+//     group's activation vectors (gathered by slot), writing one output row
+//     per slot.  Workgroups past the number of groups exit at once (the grid
 //     is sized for the worst case, because the host never reads the ids).
-//     Ids outside [0, n_experts) are left out; workgroup (0, 0) counts them
-//     into the workspace header and the group-0 workgroups zero the per-slot
-//     output rows of such slots.
-//  2. k_combine (route_w given): y[t][n] = sum_j route_w[t][j] * slot[t][j][n],
+//  3. k_combine (route_w given): y[t][n] = sum_j route_w[t][j] * slot[t][j][n],
 //     j in increasing order.
 // The gated unit of a routed feed-forward block (gate and up stacks, the
 // activation between them) is the same k_experts launch in its GLU form: one
@@ -32,11 +30,20 @@ namespace {
 
 constexpr int CH = 4;           // slots per group = vectors per product workgroup
 constexpr int MAX_SLOTS = 1024; // n_tokens * top_k
-constexpr int MAX_EXPERTS_LDS = 1024;  // experts counted with an LDS histogram
 
+// One group of the table: expert e, nb <= CH slots in slot order.
+struct alignas(32) Entry {
+    int e, nb, sel[CH], pad[2];
+    // slot i for a runtime i, by selects (an indexed private array would live
+    // in scratch memory)
+    __device__ int slot(int i) const { return i == 0 ? sel[0] : i == 1 ? sel[1] : i == 2 ? sel[2] : sel[3]; }
+};
+
+// Workspace: header (int [0] = invalid ids, [1] = groups), the group table,
+// the per-slot outputs of a weighted product.
 struct WsLayout {
     int S, Gmax;
-    size_t off_out, total;
+    size_t off_plan, off_out, total;
 };
 
 WsLayout layout(int n_experts, int n_tokens, int top_k, int64_t N) {
@@ -44,9 +51,89 @@ WsLayout layout(int n_experts, int n_tokens, int top_k, int64_t N) {
     L.S = n_tokens * top_k;
     const int distinct = L.S < n_experts ? L.S : n_experts;
     L.Gmax = distinct + L.S / CH + 1;
-    L.off_out = 256;
+    L.off_plan = 256;
+    L.off_out = L.off_plan + ((size_t)L.Gmax * sizeof(Entry) + 255) / 256 * 256;
     L.total = L.off_out + 4 * (size_t)L.S * (size_t)N;
     return L;
+}
+
+// ---------------------------------------------------------------- plan ----
+// rank = position of a slot among the slots of its expert in slot order;
+// slot s belongs to group first[e_s] + rank_s / CH, where first[e] counts the
+// groups of the experts below e: the group heads (rank % CH == 0) with a
+// smaller expert id.  out (if given): the [S][N] outputs whose rows of
+// invalid slots are zeroed (fp32, or bf16 when out_bf16).
+__global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ ids, int S, int n_experts,
+                                                   int* __restrict__ hdr, Entry* __restrict__ plan,
+                                                   void* __restrict__ out, int64_t N, int out_bf16) {
+    __shared__ int4 key4[MAX_SLOTS / 4];
+    __shared__ int4 head4[MAX_SLOTS / 4];  // expert id of a group head, INT_MAX otherwise
+    __shared__ int rank[MAX_SLOTS], cnt[MAX_SLOTS];
+    __shared__ int n_bad, n_grp;
+    int* key = reinterpret_cast<int*>(key4);
+    int* head = reinterpret_cast<int*>(head4);
+    const int tid = threadIdx.x;
+    const int S4 = (S + 3) >> 2;
+    if (tid == 0) {
+        n_bad = 0;
+        n_grp = 0;
+    }
+    for (int s = tid; s < 4 * S4; s += NTHREADS) {
+        const int e = s < S ? ids[s] : -2;
+        key[s] = s >= S ? -2 : ((e >= 0 && e < n_experts) ? e : -1);  // -2: padding
+        head[s] = 0x7fffffff;
+    }
+    __syncthreads();
+    int bad = 0;
+    for (int s = tid; s < S; s += NTHREADS) {
+        const int e = key[s];
+        int r = 0, c = 0;
+        for (int j4 = 0; j4 < S4; ++j4) {
+            const int4 k = key4[j4];
+            const int j = 4 * j4;
+            c += (k.x == e) + (k.y == e) + (k.z == e) + (k.w == e);
+            r += ((k.x == e) & (j < s)) + ((k.y == e) & (j + 1 < s)) + ((k.z == e) & (j + 2 < s)) +
+                 ((k.w == e) & (j + 3 < s));
+        }
+        rank[s] = r;
+        cnt[s] = c;
+        if (e < 0) ++bad;
+        else if (r % CH == 0) head[s] = e;
+    }
+    if (bad) atomicAdd(&n_bad, bad);
+    __syncthreads();
+    int heads = 0;
+    for (int s = tid; s < S; s += NTHREADS) {
+        const int e = key[s];
+        if (e < 0) continue;
+        int before = 0;
+        for (int j4 = 0; j4 < S4; ++j4) {
+            const int4 h = head4[j4];
+            before += (h.x < e) + (h.y < e) + (h.z < e) + (h.w < e);
+        }
+        const int r = rank[s];
+        Entry& en = plan[before + r / CH];
+        en.sel[r % CH] = s;
+        if (r % CH == 0) {
+            en.e = e;
+            en.nb = cnt[s] - r < CH ? cnt[s] - r : CH;
+            ++heads;
+        }
+    }
+    if (heads) atomicAdd(&n_grp, heads);
+    __syncthreads();
+    if (tid == 0) {
+        hdr[0] = n_bad;
+        hdr[1] = n_grp;
+    }
+    if (out && n_bad)
+        for (int s = 0; s < S; ++s)
+            if (key[s] < 0)
+                for (int64_t n = tid; n < N; n += NTHREADS) {
+                    const int64_t o = (int64_t)s * N + n;
+                    if (out_bf16) static_cast<uint16_t*>(out)[o] = 0;
+                    else static_cast<float*>(out)[o] = 0.f;
+                }
 }
 
 // ------------------------------------------------------------- product ----
@@ -59,112 +146,18 @@ template <int TYPE, int XT, int D, bool RING, bool GLU>
 __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict__ experts,
                                                       const uint8_t* __restrict__ experts_up, int64_t expert_bytes,
                                                       int64_t N, int64_t K, const uint8_t* __restrict__ x,
-                                                      int x_per_slot, int top_k, const int32_t* __restrict__ ids,
-                                                      int S, int n_experts, int* __restrict__ ws_hdr,
-                                                      void* __restrict__ out, int out_bf16, int act, int LPR,
-                                                      int tile_units) {
+                                                      int x_per_slot, int top_k, const int* __restrict__ ws_hdr,
+                                                      const Entry* __restrict__ plan, void* __restrict__ out,
+                                                      int out_bf16, int act, int LPR, int tile_units) {
     extern __shared__ __align__(16) uint8_t lds[];
-    // Grouping.  rank = position of a slot among the slots of its expert in
-    // slot order; first[e] = number of groups of the experts before e (a scan
-    // of ceil(count / CH) over the experts, counts from an LDS histogram).
-    // Slot s belongs to group first[e_s] + rank_s / CH.  Every workgroup must
-    // derive exactly the same grouping, so nothing here depends on timing.
-    // More than MAX_EXPERTS_LDS experts: first[] by direct counting.
-    __shared__ int4 key4[MAX_SLOTS / 4];
-    __shared__ int rank[MAX_SLOTS];
-    __shared__ int cnt[MAX_EXPERTS_LDS + 1];
-    __shared__ int part[NTHREADS];
-    __shared__ int sel[CH];
-    __shared__ int n_sel, n_bad;
     const int tid = threadIdx.x, g = blockIdx.x;
-    const bool small_e = n_experts <= MAX_EXPERTS_LDS;
-    int* key = reinterpret_cast<int*>(key4);
-    const int S4 = (S + 3) >> 2;
-    if (tid == 0) {
-        n_sel = 0;
-        n_bad = 0;
-    }
-    if (small_e)
-        for (int e = tid; e < n_experts; e += NTHREADS) cnt[e] = 0;
-    for (int s = tid; s < 4 * S4; s += NTHREADS) {
-        const int e = s < S ? ids[s] : -2;
-        key[s] = s >= S ? -2 : ((e >= 0 && e < n_experts) ? e : -1);  // -2: padding
-    }
-    __syncthreads();
-    int bad = 0;
-    for (int s = tid; s < S; s += NTHREADS) {
-        const int e = key[s];
-        int r = 0;
-        for (int j4 = 0; 4 * j4 < s; ++j4) {
-            const int4 k = key4[j4];
-            const int j = 4 * j4;
-            r += (k.x == e) + ((k.y == e) & (j + 1 < s)) + ((k.z == e) & (j + 2 < s)) + ((k.w == e) & (j + 3 < s));
-        }
-        rank[s] = r;
-        if (e < 0) ++bad;
-        else if (small_e) atomicAdd(&cnt[e], 1);
-    }
-    if (bad) atomicAdd(&n_bad, bad);
-    __syncthreads();
-    if (small_e) {
-        // exclusive scan of ceil(cnt / CH) over the experts: each thread a
-        // contiguous run of experts, then a scan of the 256 run totals
-        const int per = (n_experts + NTHREADS - 1) / NTHREADS;
-        const int lo = tid * per, hi = lo + per < n_experts ? lo + per : n_experts;
-        int sum = 0;
-        for (int e = lo; e < hi; ++e) sum += (cnt[e] + CH - 1) / CH;
-        part[tid] = sum;
-        __syncthreads();
-        for (int off = 1; off < NTHREADS; off <<= 1) {
-            const int v = tid >= off ? part[tid - off] : 0;
-            __syncthreads();
-            part[tid] += v;
-            __syncthreads();
-        }
-        int run = part[tid] - sum;
-        for (int e = lo; e < hi; ++e) {
-            const int c = (cnt[e] + CH - 1) / CH;
-            cnt[e] = run;  // now: groups before expert e
-            run += c;
-        }
-        __syncthreads();
-    }
-    for (int s = tid; s < S; s += NTHREADS) {
-        const int e = key[s];
-        if (e < 0) continue;
-        int before;
-        if (small_e) {
-            before = cnt[e];
-        } else {
-            // groups of experts ordered before e: one head slot (rank % CH == 0) each
-            before = 0;
-            for (int j = 0; j < S; ++j) before += (key[j] >= 0) & (key[j] < e) & (rank[j] % CH == 0);
-        }
-        if (before + rank[s] / CH == g) {
-            sel[rank[s] % CH] = s;
-            atomicAdd(&n_sel, 1);
-        }
-    }
-    __syncthreads();
+    // the table entry and the group count, loaded together
+    const int n_groups = ws_hdr[1];
+    const Entry en = plan[g < n_groups ? g : 0];
+    if (g >= n_groups) return;
+    const int nb = en.nb, e = en.e;
     const int64_t rpw = (int64_t)(GLU ? 2 : NTHREADS >> 6) * (64 / LPR);
     const int64_t rowA = (int64_t)blockIdx.y * rpw;
-    if (g == 0) {
-        if (blockIdx.y == 0 && tid == 0) ws_hdr[0] = n_bad;
-        // out-of-range slots give zero rows (this workgroup's row range)
-        if (n_bad) {
-            const int64_t rows = N - rowA < rpw ? N - rowA : rpw;
-            for (int s = 0; s < S; ++s)
-                if (key[s] < 0)
-                    for (int64_t n = tid; n < rows; n += NTHREADS) {
-                        const int64_t o = (int64_t)s * N + rowA + n;
-                        if (out_bf16) static_cast<uint16_t*>(out)[o] = 0;
-                        else static_cast<float*>(out)[o] = 0.f;
-                    }
-        }
-    }
-    const int nb = n_sel;
-    if (nb == 0) return;
-    const int e = key[sel[0]];
     // the group's vector and output pointers live in LDS: the staging picks
     // them by a loop index, which a private copy would turn into scratch
     // memory accesses
@@ -172,7 +165,7 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
     __shared__ YDst yd;
     if (tid < 8) {
         const int esz = XT == 0 ? 4 : 2;
-        const int slot = sel[tid < nb ? tid : 0];
+        const int slot = en.slot(tid < nb ? tid : 0);
         const int64_t xrow = x_per_slot ? slot : slot / top_k;
         xs.p[tid] = x + xrow * K * esz;
         yd.p[tid] = static_cast<float*>(out) + (int64_t)slot * N;
@@ -198,7 +191,7 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
             const int b = i / rows, r = i - b * rows;
             if (r >= nr) continue;
             const float v = act_fn(act, gu[0][b][r]) * gu[1][b][r];
-            const int64_t o = (int64_t)sel[b] * N + rowA + r;
+            const int64_t o = (int64_t)en.slot(b) * N + rowA + r;
             if (out_bf16) static_cast<uint16_t*>(out)[o] = f2bf(v);
             else static_cast<float*>(out)[o] = v;
         }
@@ -231,8 +224,10 @@ struct Job {
     int x_per_slot, top_k, n_experts;
     const int32_t* ids;
     int* ws_hdr;
+    Entry* plan;
     void* out;
     int out_bf16, act;
+    bool zero_bad;  // invalid slots' output rows are the caller's (zero them)
 };
 
 template <int TYPE, int XT, int D, bool RING = false>
@@ -246,12 +241,12 @@ hipError_t launch_experts_d(const Plan& p, const WsLayout& L, const Job& j, hipS
     const dim3 grid((unsigned)L.Gmax, (unsigned)gy);
     if (glu)
         hipLaunchKernelGGL((k_experts<TYPE, XT, D, RING, true>), grid, dim3(NTHREADS), p.lds, s, j.experts, j.up,
-                           expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.ids, L.S, j.n_experts, j.ws_hdr,
-                           j.out, j.out_bf16, j.act, p.LPR, p.tile_units);
+                           expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.ws_hdr, j.plan, j.out, j.out_bf16,
+                           j.act, p.LPR, p.tile_units);
     else
         hipLaunchKernelGGL((k_experts<TYPE, XT, D, RING, false>), grid, dim3(NTHREADS), p.lds, s, j.experts, j.up,
-                           expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.ids, L.S, j.n_experts, j.ws_hdr,
-                           j.out, 0, 0, p.LPR, p.tile_units);
+                           expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.ws_hdr, j.plan, j.out, 0, 0, p.LPR,
+                           p.tile_units);
     return hipGetLastError();
 }
 
@@ -283,6 +278,13 @@ hipError_t launch_experts_x(const WsLayout& L, const Job& j, int x_dtype, hipStr
 }
 
 hipError_t launch_type(int type, const WsLayout& L, const Job& j, int x_dtype, hipStream_t s) {
+    // the group table first; zeroed rows for invalid ids where the product
+    // writes its outputs straight to the caller's buffer
+    void* zero_out = j.zero_bad ? j.out : nullptr;
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(NTHREADS), 0, s, j.ids, L.S, j.n_experts, j.ws_hdr, j.plan, zero_out,
+                       j.N, j.out_bf16);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (type == T_Q4_0) return launch_experts_x<T_Q4_0>(L, j, x_dtype, s);
     if (type == T_Q4_K) return launch_experts_x<T_Q4_K>(L, j, x_dtype, s);
     if (type == T_Q5_K) return launch_experts_x<T_Q5_K>(L, j, x_dtype, s);
@@ -304,8 +306,9 @@ hipError_t gqk_matvec_id(int type, const void* experts, int n_experts, int64_t N
     int* hdr = reinterpret_cast<int*>(w);
     // per-slot outputs: straight into y when there is no routing combine
     float* out = route_w ? reinterpret_cast<float*>(w + L.off_out) : y;
+    Entry* plan = reinterpret_cast<Entry*>(w + L.off_plan);
     const Job j{static_cast<const uint8_t*>(experts), nullptr, N, K, static_cast<const uint8_t*>(x), x_per_slot,
-                top_k, n_experts, ids, hdr, out, 0, 0};
+                top_k, n_experts, ids, hdr, plan, out, 0, 0, route_w == nullptr};
     const hipError_t e = launch_type(type, L, j, x_dtype, s);
     if (e != hipSuccess || !route_w) return e;
     const unsigned nx = (unsigned)((N + 255) / 256);
@@ -319,9 +322,10 @@ hipError_t gqk_matvec_id_glu(int type, const void* experts_gate, const void* exp
                              int act, void* h, int h_dtype, void* ws, hipStream_t s) {
     const WsLayout L = layout(n_experts, n_tokens, top_k, N);
     if (L.S > MAX_SLOTS) return hipErrorInvalidValue;
+    uint8_t* w = static_cast<uint8_t*>(ws);
     const Job j{static_cast<const uint8_t*>(experts_gate), static_cast<const uint8_t*>(experts_up), N, K,
-                static_cast<const uint8_t*>(x), 0, top_k, n_experts, ids, static_cast<int*>(ws), h,
-                h_dtype == DT_BF16 ? 1 : 0, act};
+                static_cast<const uint8_t*>(x), 0, top_k, n_experts, ids, reinterpret_cast<int*>(w),
+                reinterpret_cast<Entry*>(w + L.off_plan), h, h_dtype == DT_BF16 ? 1 : 0, act, true};
     return launch_type(type, L, j, x_dtype, s);
 }
 

@@ -151,7 +151,9 @@ gq_status gq_matvec_glu(gq_type t, const void* W_gate, const void* W_up, int64_t
                         gq_dtype x_dtype, int32_t batch, gq_act act, void* h, gq_dtype h_dtype,
                         hipStream_t stream);
 
-/* Workspace bytes needed by gq_matvec_id for these sizes (host only). */
+/* Workspace bytes needed by gq_matvec_id and gq_matvec_id_glu for these sizes
+ * (host only): a header, the table of expert groups and, for a weighted
+ * product, the per-slot outputs. */
 gq_status gq_matvec_id_workspace(int32_t n_experts, int32_t n_tokens, int32_t top_k, int64_t N,
                                  size_t* bytes);
 
@@ -179,10 +181,6 @@ gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_
                        gq_dtype x_dtype, int32_t x_per_slot, const float* route_w, float* y,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes gq_matvec_id_glu needs (any gq_matvec_id_workspace size is
- * at least this). */
-#define GQ_MATVEC_ID_GLU_WS_BYTES 256
-
 /* Routed gated unit: the gate and up products of a routed feed-forward block
  * and the activation between them, in one launch (the routed 4-bit experts of
  * the Architecture section of the Gemma 4 26B-A4B Show HN page; the
@@ -196,7 +194,8 @@ gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_
  * vectors a down projection takes as gq_matvec_id's x with x_per_slot == 1.
  * Each distinct expert's rows of both stacks are read once for all its slots.
  * act as for gq_matvec_glu.  ws: device workspace of at least
- * GQ_MATVEC_ID_GLU_WS_BYTES bytes, no initialisation needed; an id outside
+ * gq_matvec_id_workspace bytes for (n_experts, n_tokens, top_k, N), no
+ * initialisation needed; an id outside
  * [0, n_experts) gives its slot a zero row of h and is counted in ws (see
  * gq_matvec_id_check).  Shapes and limits as gq_matvec_id; n_tokens == 0 or
  * N == 0 is a no-op.  Accuracy: g and u as gq_matvec_id, act and the product

@@ -209,7 +209,7 @@ def test_matvec_glu_validation(lib):
 def test_matvec_id_glu_validation(lib):
     f = lib.gq_matvec_id_glu
     # (type, gate, up, n_experts, N, K, ids, n_tokens, top_k, x, x_dtype, act, h, h_dtype, ws, ws_bytes, stream)
-    ok = [2, A, A, 128, 704, 2816, A, 8, 8, A, 0, 0, A, 0, A, 256, None]
+    ok = [2, A, A, 128, 704, 2816, A, 8, 8, A, 0, 0, A, 0, A, 1 << 30, None]
 
     def call(**kw):
         a = list(ok)
@@ -231,6 +231,8 @@ def test_matvec_id_glu_validation(lib):
         assert call(**{"a%d" % i: None}) == GQ_ERR_NULL, i
     for i in (1, 2, 6, 9, 12, 14):
         assert call(**{"a%d" % i: MIS}) == GQ_ERR_ALIGN, i
-    assert call(a15=255) == GQ_ERR_WORKSPACE
+    need = ctypes.c_size_t()
+    assert lib.gq_matvec_id_workspace(128, 8, 8, 704, ctypes.byref(need)) == GQ_OK
+    assert call(a15=need.value - 1) == GQ_ERR_WORKSPACE
     assert call(a7=0, a1=None, a2=None, a6=None, a9=None, a12=None, a14=None) == GQ_OK  # no tokens: no-op
     assert call(a4=0) == GQ_OK  # N == 0: no-op

@@ -56,9 +56,9 @@ def make_x(g, shape, xdt):
     return x, dev(x)
 
 
-def run_glu_id(gq, t, gate, up, E, N, K, ids, x_t, act, hdt, ws_bytes=None):
+def run_glu_id(gq, t, gate, up, E, N, K, ids, x_t, act, hdt):
     T, k = ids.shape
-    ws = torch.empty(ws_bytes or gq.MATVEC_ID_GLU_WS_BYTES, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(gq.gq_matvec_id_workspace(E, T, k, N), dtype=torch.uint8, device="cuda")
     ws.fill_(0xAB)  # contents need no initialisation
     h = torch.full((T, k, N), float("nan"), device="cuda", dtype=torch.float32 if hdt == "f32" else torch.bfloat16)
     gq.gq_matvec_id_glu(t, dev(gate), dev(up), E, N, K, dev(ids), x_t, act, h, ws)
@@ -152,7 +152,7 @@ def test_glu_id_bad_ids_counted_and_zero(gq, orc):
 def test_glu_id_edge_cases(gq):
     e = torch.empty(0, dtype=torch.uint8, device="cuda")
     ids = torch.zeros((2, 2), dtype=torch.int32, device="cuda")
-    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(gq.gq_matvec_id_workspace(3, 2, 2, 9), dtype=torch.uint8, device="cuda")
     # K == 0: every h row is act(0) * 0 = 0
     h = torch.full((2, 2, 9), float("nan"), device="cuda")
     gq.gq_matvec_id_glu("q4_0", e, e, 3, 9, 0, ids, torch.empty(2, 0, device="cuda"), "silu", h, ws)
@@ -166,8 +166,11 @@ def test_glu_id_edge_cases(gq):
                         ws)
     torch.cuda.synchronize()
     assert torch.all(h2 == 2.0)
+    need = gq.gq_matvec_id_workspace(2, 2, 2, 4)
+    assert ws.numel() >= need
     with pytest.raises(gq.GqError, match="workspace"):
-        gq.gq_matvec_id_glu("q4_k", w, w, 2, 4, 256, ids, torch.zeros(2, 256, device="cuda"), "silu", h, ws[:255])
+        gq.gq_matvec_id_glu("q4_k", w, w, 2, 4, 256, ids, torch.zeros(2, 256, device="cuda"), "silu", h,
+                            ws[:need - 16])
 
 
 @pytest.mark.parametrize("hdt", ["f32", "bf16"])
