@@ -521,7 +521,7 @@ def bench_context(torch, gq, synth, dev, stream, t_):
 
     ms = Timer(torch, p4, stream).time(10) / len(cp4)
     res["moe_q4_0_128x_h2816_f704_t8_top8"] = {
-        "launches": "route_topk, gate, up, down (weighted)",
+        "launches": "route_topk, gate, up, down (weighted); each routed call = group plan + product",
         "us_per_layer": round(ms * 1e3, 2), "distinct_experts": distinct, "packed_bytes_read": read_bytes,
         "GBps": round(read_bytes / (ms * 1e-3) / 1e9, 1),
         "tokens_per_s_equiv_30_layers": round(T / (30 * ms * 1e-3), 1)}
@@ -538,7 +538,7 @@ def bench_context(torch, gq, synth, dev, stream, t_):
 
     ms = Timer(torch, p5, stream).time(10) / len(cp4)
     res["moe_q4_0_128x_h2816_f704_t8_top8_fused_glu"] = {
-        "launches": "route_topk, gate|up + SiLU (bf16 h), down (weighted)",
+        "launches": "route_topk, gate|up + SiLU (bf16 h), down (weighted); each routed call = group plan + product",
         "us_per_layer": round(ms * 1e3, 2), "distinct_experts": distinct, "packed_bytes_read": read_bytes,
         "GBps": round(read_bytes / (ms * 1e-3) / 1e9, 1),
         "tokens_per_s_equiv_30_layers": round(T / (30 * ms * 1e-3), 1)}
