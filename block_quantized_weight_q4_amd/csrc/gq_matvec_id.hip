@@ -60,24 +60,33 @@ WsLayout layout(int n_experts, int n_tokens, int top_k, int64_t N) {
 // ---------------------------------------------------------------- plan ----
 // rank = position of a slot among the slots of its expert in slot order;
 // slot s belongs to group first[e_s] + rank_s / CH, where first[e] counts the
-// groups of the experts below e: the group heads (rank % CH == 0) with a
-// smaller expert id.  out (if given): the [S][N] outputs whose rows of
-// invalid slots are zeroed (fp32, or bf16 when out_bf16).
+// groups of the experts below e (an LDS histogram of the slots per expert and
+// a scan of ceil(count / CH) over the experts; with more than
+// MAX_EXPERTS_LDS experts, the group heads -- rank % CH == 0 -- with a smaller
+// expert id, counted directly).  out (if given): the [S][N] outputs whose rows
+// of invalid slots are zeroed (fp32, or bf16 when out_bf16).
+constexpr int MAX_EXPERTS_LDS = 1024;
+
 __global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ ids, int S, int n_experts,
                                                    int* __restrict__ hdr, Entry* __restrict__ plan,
                                                    void* __restrict__ out, int64_t N, int out_bf16) {
     __shared__ int4 key4[MAX_SLOTS / 4];
     __shared__ int4 head4[MAX_SLOTS / 4];  // expert id of a group head, INT_MAX otherwise
-    __shared__ int rank[MAX_SLOTS], cnt[MAX_SLOTS];
+    __shared__ int rank[MAX_SLOTS];
+    __shared__ int cnt[MAX_EXPERTS_LDS];   // slots per expert, then groups before it
+    __shared__ int part[NTHREADS];
     __shared__ int n_bad, n_grp;
     int* key = reinterpret_cast<int*>(key4);
     int* head = reinterpret_cast<int*>(head4);
     const int tid = threadIdx.x;
     const int S4 = (S + 3) >> 2;
+    const bool small_e = n_experts <= MAX_EXPERTS_LDS;
     if (tid == 0) {
         n_bad = 0;
         n_grp = 0;
     }
+    if (small_e)
+        for (int e = tid; e < n_experts; e += NTHREADS) cnt[e] = 0;
     for (int s = tid; s < 4 * S4; s += NTHREADS) {
         const int e = s < S ? ids[s] : -2;
         key[s] = s >= S ? -2 : ((e >= 0 && e < n_experts) ? e : -1);  // -2: padding
@@ -87,36 +96,67 @@ __global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ i
     int bad = 0;
     for (int s = tid; s < S; s += NTHREADS) {
         const int e = key[s];
-        int r = 0, c = 0;
-        for (int j4 = 0; j4 < S4; ++j4) {
+        int r = 0;
+        for (int j4 = 0; 4 * j4 < s; ++j4) {
             const int4 k = key4[j4];
             const int j = 4 * j4;
-            c += (k.x == e) + (k.y == e) + (k.z == e) + (k.w == e);
-            r += ((k.x == e) & (j < s)) + ((k.y == e) & (j + 1 < s)) + ((k.z == e) & (j + 2 < s)) +
-                 ((k.w == e) & (j + 3 < s));
+            r += (k.x == e) + ((k.y == e) & (j + 1 < s)) + ((k.z == e) & (j + 2 < s)) + ((k.w == e) & (j + 3 < s));
         }
         rank[s] = r;
-        cnt[s] = c;
         if (e < 0) ++bad;
-        else if (r % CH == 0) head[s] = e;
+        else {
+            if (small_e) atomicAdd(&cnt[e], 1);
+            if (r % CH == 0) head[s] = e;
+        }
     }
     if (bad) atomicAdd(&n_bad, bad);
     __syncthreads();
+    if (small_e) {
+        // exclusive scan of ceil(cnt / CH) over the experts: each thread a
+        // contiguous run of experts, then a scan of the run totals
+        const int per = (n_experts + NTHREADS - 1) / NTHREADS;
+        const int lo = tid * per, hi = lo + per < n_experts ? lo + per : n_experts;
+        int sum = 0;
+        for (int e = lo; e < hi; ++e) sum += (cnt[e] + CH - 1) / CH;
+        part[tid] = sum;
+        __syncthreads();
+        for (int off = 1; off < NTHREADS; off <<= 1) {
+            const int v = tid >= off ? part[tid - off] : 0;
+            __syncthreads();
+            part[tid] += v;
+            __syncthreads();
+        }
+        int run = part[tid] - sum;
+        for (int e = lo; e < hi; ++e) {
+            const int c = cnt[e];
+            cnt[e] = run | (c << 16);  // groups before e (low half), slot count (high half)
+            run += (c + CH - 1) / CH;
+        }
+        __syncthreads();
+    }
     int heads = 0;
     for (int s = tid; s < S; s += NTHREADS) {
         const int e = key[s];
         if (e < 0) continue;
-        int before = 0;
-        for (int j4 = 0; j4 < S4; ++j4) {
-            const int4 h = head4[j4];
-            before += (h.x < e) + (h.y < e) + (h.z < e) + (h.w < e);
+        int before, count;
+        if (small_e) {
+            before = cnt[e] & 0xffff;
+            count = cnt[e] >> 16;
+        } else {
+            before = 0;
+            count = 0;
+            for (int j4 = 0; j4 < S4; ++j4) {
+                const int4 h = head4[j4], k = key4[j4];
+                before += (h.x < e) + (h.y < e) + (h.z < e) + (h.w < e);
+                count += (k.x == e) + (k.y == e) + (k.z == e) + (k.w == e);
+            }
         }
         const int r = rank[s];
         Entry& en = plan[before + r / CH];
         en.sel[r % CH] = s;
         if (r % CH == 0) {
             en.e = e;
-            en.nb = cnt[s] - r < CH ? cnt[s] - r : CH;
+            en.nb = count - r < CH ? count - r : CH;
             ++heads;
         }
     }

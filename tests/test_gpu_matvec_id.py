@@ -179,3 +179,26 @@ def test_matvec_id_many_slots_one_expert_and_determinism(gq, orc):
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
     yref, sa = orc.matvec_id("q4_k", ex, E, N, K, ids, x, False, rw)
     check_bound(y1, yref, sa, "skewed")
+
+
+@pytest.mark.parametrize("E", [64, 1500])
+def test_matvec_id_max_slots_and_many_experts(gq, orc, E):
+    """1024 slots (128 tokens, top 8; the largest call) and, with 1500 experts,
+    the group table built without the per-expert histogram."""
+    g = synth.rng(0x67510004, 30 + E)
+    N, K, T, k = 40, 256, 128, 8
+    if E > 1024:
+        T, k = 24, 6
+    ex = synth.weight("q4_k", g, E * N, K)
+    ids = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    if E <= 1024:
+        ids[::3] = ids[0]  # many tokens on the same experts: long runs split into groups
+    x = synth.normal_f32(g, (T, K))
+    y, ws = run_id(gq, "q4_k", ex, E, N, K, ids, dev(x), False)
+    yref, sa = orc.matvec_id("q4_k", ex, E, N, K, ids, x, False)
+    check_bound(y, yref, sa, "E=%d S=%d per slot" % (E, T * k))
+    assert gq.gq_matvec_id_check(ws) == 0
+    rw = g.random((T, k)).astype(np.float32)
+    y, _ = run_id(gq, "q4_k", ex, E, N, K, ids, dev(x), False, rw)
+    yref, sa = orc.matvec_id("q4_k", ex, E, N, K, ids, x, False, rw)
+    check_bound(y, yref, sa, "E=%d S=%d routed" % (E, T * k))

@@ -224,3 +224,18 @@ def test_moe_layer_route_glu_down(gq, orc, hdt):
     bound = 1e-3 * sa + carry
     assert not (err > bound).any(), "layer output: %d outside the bound" % (err > bound).sum()
     print("layer output worst err/bound %.4f" % float(np.max(err / bound)))
+
+
+def test_glu_id_max_slots(gq, orc):
+    """1024 slots (128 tokens, top 8), skewed so that runs span many groups."""
+    g = synth.rng(0x67510009, 102)
+    E, N, K, T, k = 48, 36, 512, 128, 8
+    gate = synth.weight("q4_0", g, E * N, K)
+    up = synth.weight("q4_0", g, E * N, K)
+    ids = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids[::2, :4] = np.arange(4)
+    x, x_t = make_x(g, (T, K), "bf16")
+    h, ws = run_glu_id(gq, "q4_0", gate, up, E, N, K, ids, x_t, "silu", "bf16")
+    ref, bound = glu_ref(orc, "q4_0", gate, up, E, N, K, ids, x, "silu", "bf16")
+    check(h.float().cpu().numpy(), ref, bound, "S=1024")
+    assert gq.gq_matvec_id_check(ws) == 0
