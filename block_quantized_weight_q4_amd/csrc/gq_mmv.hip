@@ -562,13 +562,25 @@ __global__ __launch_bounds__(64 * WMAX) void k_mmv(const uint8_t* __restrict__ W
     };
 #pragma unroll
     for (int j = 0; j < P; ++j) issue(j, j);
-    for (int i = 0; i < n; i += P) {
+    // Whole rounds of P steps in straight-line code, so that the wait before
+    // each slot is exact (a conditional slot in the loop body merges load
+    // counts from several paths into a wait for all loads), then the last
+    // partial round.  The refill of slot j goes out right after slot j is
+    // consumed (left to itself the scheduler sinks it behind the next slot's
+    // work, and the wait for that slot would then cover it too).
+    int i = 0;
+    for (; i + P <= n; i += P) {
 #pragma unroll
         for (int j = 0; j < P; ++j) {
-            if (i + j < n) F::template compute<XT, R>(wr[j], xr[j], g, acc);
+            F::template compute<XT, R>(wr[j], xr[j], g, acc);
+            __builtin_amdgcn_sched_barrier(0);
             issue(j, i + j + P);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+#pragma unroll
+    for (int j = 0; j < P - 1; ++j)
+        if (i + j < n) F::template compute<XT, R>(wr[j], xr[j], g, acc);
 
     if (nw > 1) {
         if (wave > 0)
@@ -598,7 +610,7 @@ hipError_t launch_r(const uint8_t* W, int64_t N, int64_t K, const uint8_t* x, in
                     hipStream_t s) {
     // steps in flight: enough to cover the memory latency within the
     // register budget of two wavefronts per SIMD (256 registers)
-    constexpr int P = R == 1 && XT == 1 ? 3 : 2;
+    constexpr int P = R == 1 && XT == 1 && TYPE != T_Q5_K ? 3 : 2;
     const int64_t groups = (N + 16 * R - 1) / (16 * R);
     if (groups > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_mmv<TYPE, XT, R, P>), dim3((unsigned)groups), dim3(64 * nw), 0, s, W, N, K, x, batch, y);
@@ -621,10 +633,10 @@ hipError_t launch(const uint8_t* W, int64_t N, int64_t K, const uint8_t* x, int 
         return groups * nw;
     };
     int nw;
-    // four tiles fit the register budget with bf16 activations and the
-    // 32-weight sub-blocks; fp32 (hi and lo operands) and Q6_K (16 operands
-    // per step) take at most two
-    if constexpr (XT == 1 && TYPE != T_Q6_K)
+    // four tiles fit the register budget with bf16 activations and Q4_0 /
+    // Q4_K; fp32 (hi and lo operands), Q5_K (its fifth-bit plane) and Q6_K
+    // (16 operands per step) take at most two
+    if constexpr (XT == 1 && (TYPE == T_Q4_0 || TYPE == T_Q4_K))
         if (waves(4, nw) >= 1024) return launch_r<TYPE, XT, 4>(W, N, K, x, batch, y, nw, s);
     if (waves(2, nw) >= 1024) return launch_r<TYPE, XT, 2>(W, N, K, x, batch, y, nw, s);
     waves(1, nw);
