@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline only (no context workloads)")
+    ap.add_argument("--context-only", action="store_true",
+                    help="only the context workloads (one JSON line of them; for kernel traces)")
     ap.add_argument("--pmc-pass", action="store_true", help="run the dominant kernel 8x and one copy kernel")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--stats-summary", nargs=2, metavar=("DIR", "OUT"))
@@ -244,6 +246,10 @@ def main():
 
     def t_(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if args.context_only:
+        print(json.dumps({"context": bench_context(torch, gq, synth, dev, stream, t_)}), flush=True)
+        return
 
     # ------------------------------------------------ headline: dense layer
     mats = {name: synth.weight("q4_k", synth.rng(0x67510002, i), N, K) for i, (name, N, K) in enumerate(DENSE)}

@@ -74,7 +74,6 @@ __global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ i
     __shared__ int4 head4[MAX_SLOTS / 4];  // expert id of a group head, INT_MAX otherwise
     __shared__ int rank[MAX_SLOTS];
     __shared__ int cnt[MAX_EXPERTS_LDS];   // slots per expert, then groups before it
-    __shared__ int part[NTHREADS];
     __shared__ int n_bad, n_grp;
     int* key = reinterpret_cast<int*>(key4);
     int* head = reinterpret_cast<int*>(head4);
@@ -112,25 +111,26 @@ __global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ i
     if (bad) atomicAdd(&n_bad, bad);
     __syncthreads();
     if (small_e) {
-        // exclusive scan of ceil(cnt / CH) over the experts: each thread a
-        // contiguous run of experts, then a scan of the run totals
-        const int per = (n_experts + NTHREADS - 1) / NTHREADS;
-        const int lo = tid * per, hi = lo + per < n_experts ? lo + per : n_experts;
-        int sum = 0;
-        for (int e = lo; e < hi; ++e) sum += (cnt[e] + CH - 1) / CH;
-        part[tid] = sum;
-        __syncthreads();
-        for (int off = 1; off < NTHREADS; off <<= 1) {
-            const int v = tid >= off ? part[tid - off] : 0;
-            __syncthreads();
-            part[tid] += v;
-            __syncthreads();
-        }
-        int run = part[tid] - sum;
-        for (int e = lo; e < hi; ++e) {
-            const int c = cnt[e];
-            cnt[e] = run | (c << 16);  // groups before e (low half), slot count (high half)
-            run += (c + CH - 1) / CH;
+        // exclusive scan of ceil(cnt / CH) over the experts by wavefront 0:
+        // each lane a contiguous run of experts, then a shuffle scan of the
+        // 64 run totals (no barrier inside)
+        if (tid < 64) {
+            const int per = (n_experts + 63) / 64;
+            const int lo = tid * per, hi = lo + per < n_experts ? lo + per : n_experts;
+            int sum = 0;
+            for (int e = lo; e < hi; ++e) sum += (cnt[e] + CH - 1) / CH;
+            int incl = sum;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int v = __shfl_up(incl, off, 64);
+                if (tid >= off) incl += v;
+            }
+            int run = incl - sum;
+            for (int e = lo; e < hi; ++e) {
+                const int c = cnt[e];
+                cnt[e] = run | (c << 16);  // groups before e (low half), slot count (high half)
+                run += (c + CH - 1) / CH;
+            }
         }
         __syncthreads();
     }
