@@ -15,7 +15,9 @@
 // (two per SIMD; the other formats) a 128 x 64 eighth as 4 x 2 blocks, so one
 // wavefront's MFMAs run while the other expands weights or waits on LDS.  K advances in
 // stages of BK = 64 inputs: one 32-byte slice of quants of a Q4_K super-block,
-// a quarter of a Q6_K super-block, or two Q4_0 blocks.
+// two Q4_0 blocks, or the two 32-input quarters of a Q6_K super-block half
+// whose low bits share 32 ql bytes (inputs 0-31 with 64-95, or 32-63 with
+// 96-127, of the half; X's columns are taken in the same order).
 //
 // Pipeline.  LDS holds two stage buffers.  While the MFMAs of stage s read
 // buffer s & 1, the same wavefronts write stage s+1 -- its X rows as loaded and
@@ -89,6 +91,8 @@ struct WF;
 // nibbles: 2c+1 = inputs 32..63) and the header.  w = (d sc) q - dmin m.
 template <>
 struct WF<T_Q4_K> {
+    // input index of the stage's 8-input chunk c (c = 0..7): contiguous
+    __device__ static uint32_t xin(int s, int c) { return (uint32_t)s * 64u + 8u * (uint32_t)c; }
     static constexpr int QK = 256, BB = 144;
     struct Regs {
         u32x4 h, q0, q1;
@@ -131,6 +135,8 @@ struct WF<T_Q4_K> {
 // 8j + i as its bit 4, input 32 + 8j + i (high nibble) bit 2c + 1.
 template <>
 struct WF<T_Q5_K> {
+    // input index of the stage's 8-input chunk c (c = 0..7): contiguous
+    __device__ static uint32_t xin(int s, int c) { return (uint32_t)s * 64u + 8u * (uint32_t)c; }
     static constexpr int QK = 256, BB = 176;
     struct Regs {
         u32x4 h, q0, q1, f0, f1;
@@ -167,6 +173,8 @@ struct WF<T_Q5_K> {
 // i, input i >= 16 the high nibble of byte i-16.  w = d (q - 8), exact in fp32.
 template <>
 struct WF<T_Q4_0> {
+    // input index of the stage's 8-input chunk c (c = 0..7): contiguous
+    __device__ static uint32_t xin(int s, int c) { return (uint32_t)s * 64u + 8u * (uint32_t)c; }
     static constexpr int QK = 32, BB = 18;
     struct Regs {
         u32x4 a, b;
@@ -208,23 +216,35 @@ struct WF<T_Q4_0> {
 template <>
 struct WF<T_Q6_K> {
     static constexpr int QK = 256, BB = 210;
+    // Stage s = (half h, part p) = ((s % 4) / 2, s % 2) of super-block s / 4:
+    // the quarters p and p + 2 of half h, whose low 4 bits are the low and
+    // high nibbles of the same 32 ql bytes 64h + 32p.. and whose high 2 bits
+    // are bits 2p.. and 2p+4.. of the 32 qh bytes 128 + 32h...  Stage input
+    // k < 32 is input 128h + 32p + k of the super-block, k >= 32 is input
+    // 128h + 64 + 32p + (k - 32): the product sums over k, so X's columns
+    // follow the same order (xin).
     struct Regs {
-        u32x4 l0, l1, l2, l3, h0, h1;
+        u32x4 l0, l1, h0, h1;
         uint32_t sc, d;
     };
     struct Scl {
-        float s[4];  // (jq, sh 0), (jq, sh 1), (jq + 1, sh 0), (jq + 1, sh 1)
+        float s[4];  // the stage's four 16-input scales: quarter p (two), quarter p + 2 (two)
     };
+    __device__ static uint32_t xin(int s, int c) {
+        const uint32_t c4 = (uint32_t)(s & 3);
+        return (uint32_t)(s >> 2) * 256u + 128u * (c4 >> 1) + 32u * (c4 & 1u) + 8u * (uint32_t)c + (c >= 4 ? 32u : 0u);
+    }
     __device__ static void load(Rsrc wr, uint32_t woff, int s, bool ok, bool, Regs& r) {
-        const int c = s & 3, h = c >> 1;
+        const uint32_t c4 = (uint32_t)(s & 3), h = c4 >> 1, p = c4 & 1u;
         const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * BB : 0x80000000u;
-        r.l0 = bld16(wr, bo + 64 * h);
-        r.l1 = bld16(wr, bo + 64 * h + 16);
-        r.l2 = bld16(wr, bo + 64 * h + 32);
-        r.l3 = bld16(wr, bo + 64 * h + 48);
+        r.l0 = bld16(wr, bo + 64 * h + 32 * p);
+        r.l1 = bld16(wr, bo + 64 * h + 32 * p + 16);
         r.h0 = bld16(wr, bo + 128 + 32 * h);
         r.h1 = bld16(wr, bo + 128 + 32 * h + 16);
-        r.sc = __builtin_amdgcn_raw_buffer_load_b32(wr, (int)(bo + 192 + 8 * h + 4 * (c & 1)), 0, 0);
+        // scales 8h + 2p, +1 (quarter p) and 8h + 4 + 2p, +1 (quarter p + 2)
+        const uint32_t sa = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 192 + 8 * h + 2 * p), 0, 0);
+        const uint32_t sb = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 196 + 8 * h + 2 * p), 0, 0);
+        r.sc = sa | (sb << 16);
         r.d = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 208), 0, 0);
     }
     __device__ static Scl scales(const Regs& r, int) {
@@ -234,16 +254,22 @@ struct WF<T_Q6_K> {
         for (int i = 0; i < 4; ++i) o.s[i] = d * (float)(int)(int8_t)((r.sc >> (8 * i)) & 0xffu);
         return o;
     }
+    // slice j: ql / qh bytes 8j..8j+7 of the stage's 32; lo = their low
+    // nibbles with qh bits 2p (quarter p), hi = high nibbles with qh bits
+    // 2p + 4 (quarter p + 2); w = (d sc) q - 32 (d sc)
     __device__ static void expand(const Regs& r, const Scl& sc, int s, int j, u32x4& lo, u32x4& hi) {
-        const uint32_t sh = 4u * (uint32_t)(s & 1);  // nibble shift; qh bits 2jq = sh, 2(jq+1) = sh + 2
-        const u32x4 la = j < 2 ? r.l0 : r.l1, lb = j < 2 ? r.l2 : r.l3, hq = j < 2 ? r.h0 : r.h1;
-        const int k = 2 * (j & 1), i = j >> 1;  // inputs 8j.. lie in sub-block i of each quarter
-        const uint32_t a0 = ((la[k] >> sh) & 0x0F0F0F0Fu) | (((hq[k] >> sh) & 0x03030303u) << 4);
-        const uint32_t a1 = ((la[k + 1] >> sh) & 0x0F0F0F0Fu) | (((hq[k + 1] >> sh) & 0x03030303u) << 4);
-        const uint32_t b0 = ((lb[k] >> sh) & 0x0F0F0F0Fu) | (((hq[k] >> (sh + 2)) & 0x03030303u) << 4);
-        const uint32_t b1 = ((lb[k + 1] >> sh) & 0x0F0F0F0Fu) | (((hq[k + 1] >> (sh + 2)) & 0x03030303u) << 4);
-        lo = expand_bytes(a0, a1, sc.s[i], 32.0f * sc.s[i]);
-        hi = expand_bytes(b0, b1, sc.s[2 + i], 32.0f * sc.s[2 + i]);
+        const uint32_t sh = 2u * (uint32_t)(s & 1);
+        const u32x4 lq = j < 2 ? r.l0 : r.l1, hq = j < 2 ? r.h0 : r.h1;
+        const int k = 2 * (j & 1), i = j >> 1;  // bytes 8j.. lie in 16-input sub-block i of each quarter
+        const uint32_t a0 = (lq[k] & 0x0F0F0F0Fu) | (((hq[k] >> sh) & 0x03030303u) << 4);
+        const uint32_t a1 = (lq[k + 1] & 0x0F0F0F0Fu) | (((hq[k + 1] >> sh) & 0x03030303u) << 4);
+        const uint32_t b0 = ((lq[k] >> 4) & 0x0F0F0F0Fu) | (((hq[k] >> (sh + 4)) & 0x03030303u) << 4);
+        const uint32_t b1 = ((lq[k + 1] >> 4) & 0x0F0F0F0Fu) | (((hq[k + 1] >> (sh + 4)) & 0x03030303u) << 4);
+        // selects, not an indexed array: j may be a runtime value, and an
+        // indexed private array would live in scratch memory
+        const float s_lo = i ? sc.s[1] : sc.s[0], s_hi = i ? sc.s[3] : sc.s[2];
+        lo = expand_bytes(a0, a1, s_lo, 32.0f * s_lo);
+        hi = expand_bytes(b0, b1, s_hi, 32.0f * s_hi);
     }
 };
 
@@ -289,7 +315,7 @@ __global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W
     const Rsrc wr = make_rsrc(W + n0 * (int64_t)row_bytes, (uint32_t)rows_w * row_bytes);
     const int xrow = tid >> 3, xchunk = tid & 7;
     const uint32_t xstride = (uint32_t)(32 * ldx * 2);
-    const uint32_t xoff = (uint32_t)xrow * (uint32_t)(ldx * 2) + 16 * xchunk, woff = (uint32_t)tid * row_bytes;
+    const uint32_t xoff = (uint32_t)xrow * (uint32_t)(ldx * 2), woff = (uint32_t)tid * row_bytes;
 
     // a stage past the last loads zeros without touching memory (offset past
     // the buffers), so every load is unconditional and the load-counter waits
@@ -298,7 +324,7 @@ __global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W
         const bool ok = s < s1;
         // inputs past K (the second half of a Q4_0 row's last stage) read as zeros
         const bool xok = ok && (TYPE != T_Q4_0 || (int64_t)s * BK + 8 * xchunk < K);
-        const uint32_t xo = xok ? xoff + (uint32_t)s * (BK * 2) : 0x80000000u;
+        const uint32_t xo = xok ? xoff + 2u * F::xin(s, xchunk) : 0x80000000u;
 #pragma unroll
         for (int i = 0; i < 8; ++i) r.x[i] = bld16(xr, xok ? xo + (uint32_t)i * xstride : xo);
         F::load(wr, woff, s, ok, (int64_t)s * BK + 32 < K, r.w);
@@ -444,14 +470,14 @@ __global__ __launch_bounds__(512, 1) void k_matmul8(const uint8_t* __restrict__ 
     const Rsrc wr = make_rsrc(W + n0 * (int64_t)row_bytes, (uint32_t)rows_w * row_bytes);
     const int xrow = tid >> 3, xchunk = tid & 7;
     const uint32_t xstride = (uint32_t)(64 * ldx * 2);
-    const uint32_t xoff = (uint32_t)xrow * (uint32_t)(ldx * 2) + 16 * xchunk;
+    const uint32_t xoff = (uint32_t)xrow * (uint32_t)(ldx * 2);
     const int wrow = tid & 255, whalf = wave >> 2;
     const uint32_t woff = (uint32_t)wrow * row_bytes;
 
     auto load_stage = [&](int s, SR8& r) {
         const bool ok = s < s1;
         const bool xok = ok && (TYPE != T_Q4_0 || (int64_t)s * BK + 8 * xchunk < K);
-        const uint32_t xo = xok ? xoff + (uint32_t)s * (BK * 2) : 0x80000000u;
+        const uint32_t xo = xok ? xoff + 2u * F::xin(s, xchunk) : 0x80000000u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) r.x[i] = bld16(xr, xok ? xo + (uint32_t)i * xstride : xo);
         F::load(wr, woff, s, ok, (int64_t)s * BK + 32 < K, r.w);
