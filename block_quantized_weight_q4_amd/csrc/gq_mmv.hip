@@ -623,9 +623,13 @@ hipError_t launch(const uint8_t* W, int64_t N, int64_t K, const uint8_t* x, int 
     const int64_t tiles = (N + 15) / 16;
     const int64_t steps = (K / F::QK + F::BPS - 1) / F::BPS;
     // Row tiles per wavefront R (each activation fragment serves R tiles) and
-    // wavefronts per workgroup (splitting K): the largest R whose launch still
-    // holds >= 1024 wavefronts, each workgroup doubling its wavefronts while
-    // the launch holds < 2048 and each keeps >= 2 steps.
+    // wavefronts per workgroup (splitting K): R = 2 if its launch still holds
+    // >= 1024 wavefronts, else 1, each workgroup doubling its wavefronts while
+    // the launch holds < 2048 and each keeps >= 2 steps.  (Four tiles per
+    // wavefront, which bf16 Q4_0 / Q4_K activations fit in two wavefronts'
+    // registers per SIMD, measured 5-33% slower from 5 to 12 vectors -- half
+    // the wavefronts where rows are few -- and at most 1% faster at 16; one
+    // tile, 0-40% slower.)
     auto waves = [&](int R, int& nw) {
         const int64_t groups = (tiles + R - 1) / R;
         nw = 1;
@@ -633,11 +637,6 @@ hipError_t launch(const uint8_t* W, int64_t N, int64_t K, const uint8_t* x, int 
         return groups * nw;
     };
     int nw;
-    // four tiles fit the register budget with bf16 activations and Q4_0 /
-    // Q4_K; fp32 (hi and lo operands), Q5_K (its fifth-bit plane) and Q6_K
-    // (16 operands per step) take at most two
-    if constexpr (XT == 1 && (TYPE == T_Q4_0 || TYPE == T_Q4_K))
-        if (waves(4, nw) >= 1024) return launch_r<TYPE, XT, 4>(W, N, K, x, batch, y, nw, s);
     if (waves(2, nw) >= 1024) return launch_r<TYPE, XT, 2>(W, N, K, x, batch, y, nw, s);
     waves(1, nw);
     return launch_r<TYPE, XT, 1>(W, N, K, x, batch, y, nw, s);
