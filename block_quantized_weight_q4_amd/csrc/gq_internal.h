@@ -5,6 +5,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// Compute units of the current device (queried once per device).
+int gqk_cu_count();
+
 // All launchers assume their arguments were validated by the ABI layer.
 hipError_t gqk_dequant(int type, const void* blocks, int64_t n_blocks, void* out, int out_dtype,
                        hipStream_t s);
@@ -24,7 +27,8 @@ hipError_t gqk_matvec_id(int type, const void* experts, int n_experts, int64_t N
                          const int32_t* ids, int n_tokens, int top_k, const void* x, int x_dtype,
                          int x_per_slot, const float* route_w, float* y, void* ws, hipStream_t s);
 // Routed gated unit: h[t][j][n] = act(gate_e[n] . x_t) * (up_e[n] . x_t), e = ids[t][j];
-// ws needs only its 256-byte header (the bad-id count).
+// ws has the layout of gqk_matvec_id_ws_bytes (header and group table; the
+// per-slot output area is not used).
 hipError_t gqk_matvec_id_glu(int type, const void* experts_gate, const void* experts_up, int n_experts, int64_t N,
                              int64_t K, const int32_t* ids, int n_tokens, int top_k, const void* x, int x_dtype,
                              int act, void* h, int h_dtype, void* ws, hipStream_t s);

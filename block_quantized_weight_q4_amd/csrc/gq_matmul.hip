@@ -29,6 +29,8 @@
 //
 // Rows of X past M and of W past N, and inputs past K, are read as zeros
 // (buffer loads beyond the resource's span); their outputs are never stored.
+#include <atomic>
+
 #include "gq_device.h"
 #include "gq_internal.h"
 
@@ -580,18 +582,6 @@ __global__ __launch_bounds__(256) void k_zero_tiles(float* __restrict__ Y, int64
     }
 }
 
-int cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 template <int TYPE>
 hipError_t launch(const void* W, int64_t N, int64_t K, const void* X, int64_t M, int64_t ldx, float* Y, int64_t ldy,
                   hipStream_t s) {
@@ -599,7 +589,7 @@ hipError_t launch(const void* W, int64_t N, int64_t K, const void* X, int64_t M,
     const int64_t tiles = gn * gm;
     if (tiles > 0x3fffffff) return hipErrorInvalidValue;
     // one workgroup per CU (the LDS holds one): split a short last round
-    const int cus = cu_count();
+    const int cus = gqk_cu_count();
     const int64_t tail = tiles % cus;
     const int S = (int)((K + BK - 1) / BK);
     const bool split = tiles > cus && tail > 0 && tail <= cus / 2 && S >= 4;
@@ -632,6 +622,18 @@ hipError_t launch(const void* W, int64_t N, int64_t K, const void* X, int64_t M,
 }
 
 }  // namespace
+
+int gqk_cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 hipError_t gqk_matmul(int type, const void* W, int64_t N, int64_t K, const void* X, int x_dtype, int64_t M,
                       int64_t ldx, float* Y, int64_t ldy, hipStream_t s) {
