@@ -556,11 +556,11 @@ struct YDst {
     float* p[8];
 };
 
-// Most units per lane in one straight-line pass (larger K tiles use the ring),
-// and how many of them are in flight before the first is taken.
+// Most units per lane in one straight-line pass (larger K tiles use the ring,
+// whose depth each launcher picks), and how many of them are in flight before
+// the first is taken.
 constexpr int D_MAX = 6;
 constexpr int PREFETCH = 3;
-constexpr int D_RING = 4;
 
 // The whole decode product for one workgroup: rows [rowA, rowA + wcount * SR)
 // of the packed matrix W (N rows, K inputs) against nb <= BMAX staged vectors;
@@ -726,7 +726,7 @@ inline Plan plan_for(int64_t N, int64_t K, int nb, int64_t rows_in_flight = -1, 
     }
     const int T = (p.tile_units + p.LPR - 1) / p.LPR;
     p.ring = T > D_MAX;
-    p.D = p.ring ? D_RING : T;
+    p.D = p.ring ? 0 : T;  // ring depth: chosen by the launcher
     const int SR = 64 / p.LPR;
     p.grid = (N + 4 * (int64_t)SR - 1) / (4 * (int64_t)SR);
     p.lds = per_unit * p.tile_units;
