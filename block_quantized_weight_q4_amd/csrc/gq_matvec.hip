@@ -25,7 +25,7 @@ __global__ __launch_bounds__(64 * WGW) void k_matvec(const uint8_t* __restrict__
                                                      XSrc xs, int nb, YDst yd, int LPR, int tile_units) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int64_t rpw = (int64_t)WGW * (64 / LPR);
-    gemv_workgroup<TYPE, XT, BMAX, D, RING, 64 * WGW>(W, N, K, (int64_t)blockIdx.x * rpw, xs, nb, yd, LPR, tile_units, lds,
+    gemv_workgroup<TYPE, XT, BMAX, D, RING, 64 * WGW, 1>(W, N, K, (int64_t)blockIdx.x * rpw, xs, nb, yd, LPR, tile_units, lds,
                                             (int)(threadIdx.x >> 6), WGW);
 }
 
