@@ -14,12 +14,12 @@ using namespace gqd;
 
 namespace {
 
-// WGW wavefronts per workgroup: 4, or 8 for batch-1 products whose 8-wave
-// grid holds 150..256 workgroups -- twice the rows then share each staged
-// activation tile and the staging has twice the threads, while every
-// workgroup still gets a CU of its own (measured: the 2560-row projections of
-// the hidden-2560 layer gain 10-20%; grids of 64-128 workgroups lose, since
-// fewer CUs then pull the weights).
+// WGW wavefronts per workgroup: 4, or 8 for products whose 8-wave grid holds
+// 150..256 workgroups -- twice the rows then share each staged activation
+// tile and the staging has twice the threads, while every workgroup still
+// gets a CU of its own (measured: the 2560-row projections of the hidden-2560
+// layer gain 10-20% at 1 vector and 9-11% at 2; grids of 64-128 workgroups
+// lose, since fewer CUs then pull the weights).
 template <int TYPE, int XT, int BMAX, int D, bool RING, int WGW>
 __global__ __launch_bounds__(64 * WGW) void k_matvec(const uint8_t* __restrict__ W, int64_t N, int64_t K,
                                                      XSrc xs, int nb, YDst yd, int LPR, int tile_units) {
@@ -70,7 +70,7 @@ hipError_t launch_b(const uint8_t* W, int64_t N, int64_t K, const XSrc& xs, int 
     using F = Fmt<TYPE>;
     const Plan p = plan_for<F>(N, K, nb);
     if (p.grid > 0x7fffffff) return hipErrorInvalidValue;
-    if constexpr (BMAX == 1) {
+    {
         const int64_t rows8 = 8 * (int64_t)(64 / p.LPR);
         const int64_t g8 = (N + rows8 - 1) / rows8;
         if (g8 >= 150 && g8 <= 256) return launch_w<TYPE, XT, BMAX, 8>(p, W, N, K, xs, nb, y, s);
