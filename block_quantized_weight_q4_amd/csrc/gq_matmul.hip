@@ -388,12 +388,13 @@ __global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W
             store_slice(s + 1, nxt, sc, cur ^ 1, ks);
             // one k step = one scheduling region: each MFMA is followed by a
             // few VALU instructions of the expansion and the LDS traffic, so
-            // they issue while the matrix core is busy
+            // they issue while the matrix core is busy (5 VALU per MFMA
+            // measured 2% faster for Q6_K than 3, 4, 6 or 8)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 if (ks < 3 && i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
                 if ((i & 3) == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
             }
             __builtin_amdgcn_sched_barrier(0);
