@@ -627,10 +627,11 @@ hipError_t launch(const uint8_t* W, int64_t N, int64_t K, const uint8_t* x, int 
     // Row tiles per wavefront R (each activation fragment serves R tiles) and
     // wavefronts per workgroup (splitting K): R = 2 if its launch still holds
     // >= 1024 wavefronts, else 1, each workgroup doubling its wavefronts while
-    // the launch holds < 4096 and each keeps >= 1 step (>= 2 measured up to
-    // 7% slower on short-K matrices; with one step in flight per wavefront,
-    // 2048 instead of 4096 is 1-2% slower on the large matrices, 8192 no
-    // faster).  (Four tiles per
+    // the launch holds < 2048 and each keeps >= 1 step, or while it holds
+    // < 4096 and each keeps >= 4 steps (>= 2 steps below 2048 measured up to
+    // 7% slower on short-K matrices; going on to 4096 is 1-2% faster on the
+    // large matrices but 47% slower on 19456 x 2560 at 8 fp32 vectors, where
+    // each wavefront would keep 1-2 of its 10 steps; 8192 no faster).  (Four tiles per
     // wavefront, which bf16 Q4_0 / Q4_K activations fit in two wavefronts'
     // registers per SIMD, measured 5-33% slower from 5 to 12 vectors -- half
     // the wavefronts where rows are few -- and at most 1% faster at 16; one
@@ -638,7 +639,8 @@ hipError_t launch(const uint8_t* W, int64_t N, int64_t K, const uint8_t* x, int 
     auto waves = [&](int R, int& nw) {
         const int64_t groups = (tiles + R - 1) / R;
         nw = 1;
-        while (nw < WMAX && groups * nw < 4096 && steps >= 2 * nw) nw *= 2;
+        while (nw < WMAX && ((groups * nw < 2048 && steps >= 2 * nw) || (groups * nw < 4096 && steps >= 8 * nw)))
+            nw *= 2;
         return groups * nw;
     };
     int nw;
