@@ -67,6 +67,13 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c, false);
 }
 
+// (a.lo - b.lo, a.hi - b.hi) of two fp16 pairs: one packed fp16 add with the
+// second operand negated.  Exact where both are integers of at most 11
+// significant bits whose difference is too (the weight-minus-zero-point step).
+__device__ __forceinline__ uint32_t sub_h2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, a) - __builtin_bit_cast(half2v, b));
+}
+
 // Two fp32 -> fp16 (round to nearest even), packed lo | hi << 16.
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
     half2v h = {(_Float16)lo, (_Float16)hi};

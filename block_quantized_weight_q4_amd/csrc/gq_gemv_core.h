@@ -16,23 +16,28 @@
 // load instructions is fixed at compile time (the load counter waits stay
 // exact) while no byte is fetched twice or needlessly.
 //
-// Arithmetic.  A weight quant q (4 or 6 bits) is turned into the fp16 value
-// 1024 + q (or 1024 + 16 q for a high nibble) by OR-ing it into the mantissa of
-// 1024 -- two weights per 32-bit register with one AND-OR.  Activations are
-// staged once per workgroup in LDS as fp16 pairs that match that register
-// order, each group of 32 inputs scaled by a power of two 2^e so that its
-// largest magnitude lies in [2^14, 2^15) (the scaling is exact; only the fp16
-// rounding of the scaled value, at most 2^-11 relative, is inexact).  One
-// v_dot2_f32_f16 then adds two weight-activation products into an fp32
-// accumulator.  Per sub-block the format's scale (and min) are applied once:
+// Arithmetic.  Every weight reaches the fp16 dot instructions as the exact
+// fp16 value of q - z (z = the format's zero point), so every product is exact
+// and the fp32 sums carry nothing that only cancels later:
+//   Q4_0, Q6_K:  q is OR-ed into the mantissa of 1024 (1024 + q, or 1024 + 16 q
+//                for a high nibble) and 1024 + z (1024 + 16 z) is subtracted
+//                with one packed fp16 add per two weights -- exact, the
+//                result is a small integer;
+//   Q4_K, Q5_K:  z = 0 and the masked quant bits are used as they are: the fp16
+//                subnormal q * 2^-24 (16 q * 2^-24 for a high nibble), exact,
+//                with the 2^24 folded into the block scale.
+// Activations are staged once per workgroup in LDS as fp16 pairs that match
+// the register order of the weights, each group of 32 inputs scaled by a power
+// of two 2^e so that its largest magnitude lies in [2^14, 2^15) (the scaling is
+// exact; only the fp16 rounding of the scaled value, at most 2^-11 relative, is
+// inexact).  One v_dot2_f32_f16 then adds two weight-activation products into
+// an fp32 accumulator.  Per sub-block the format's scale (and min) are applied
+// once:
 //   Q4_0:  d * 2^-e * ( S_lo + S_hi / 16 )
-//   Q4_K:  d*sc * 2^-e * S - dmin*m * sum(x)
+//   Q4_K:  d*2^24*sc * 2^-e * S - dmin*m * sum(x)
 //   Q6_K:  d*sc * 2^-e * S          (S / 16 for the high-nibble groups)
-// where S is the integer-weighted dot product.  The constant 1024 (and the
-// format's zero point 8 or 32) is removed by subtracting a correction that the
-// staging step computes with exactly the same dot2 sequence applied to the
-// zero-point's fp16 pattern, so a sub-block whose quants all equal the zero
-// point contributes exactly zero.
+// where S is the dot product of the integers q - z with the staged values.
+// A sub-block whose quants all equal the zero point has S == 0 exactly.
 #pragma once
 
 #include "gq_device.h"
@@ -77,6 +82,7 @@ struct Fmt;
 template <>
 struct Fmt<T_Q4_0> {
     static constexpr int QK = 32, BB = 18, UW = 32, UPB = 1, NA = 2, NP = 8, NF = 1, NQ = NA * NP / 4;
+    static constexpr int KIND = 0;  // staged factors: {2^-e, -, -, -}
     struct Raw {
         uint32_t d;
         u32x4 q;
@@ -100,19 +106,21 @@ struct Fmt<T_Q4_0> {
         unit = g;
         a = r;
     }
+    // q - 8 (16 (q - 8) for the high nibbles) as exact fp16 pairs
     __device__ static void pairs(const Raw& r, int a, uint32_t magic, uint32_t P[NP]) {
         const uint32_t mask = a == 0 ? 0x000F000Fu : 0x00F000F0u;
+        const uint32_t z = zero_pattern(a);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             uint32_t w = r.q[k];
-            P[2 * k] = (w & mask) | magic;
-            P[2 * k + 1] = ((w >> 8) & mask) | magic;
+            P[2 * k] = sub_h2((w & mask) | magic, z);
+            P[2 * k + 1] = sub_h2(((w >> 8) & mask) | magic, z);
         }
     }
     __device__ static Scl scales(const Raw& r, const Lane&) { return Scl{h2f(r.d)}; }
-    // dacc[a] = accumulator - correction; f[0] = {corr0, corr1, 2^-e, 0}
+    // dacc[a] = dot product of run a; f[0] = {2^-e, -, -, -}
     __device__ static float contrib(const Scl& s, const float dacc[NA], const f32x4 f[NF]) {
-        return (s.d * f[0].z) * __builtin_fmaf(0.0625f, dacc[1], dacc[0]);
+        return (s.d * f[0].x) * __builtin_fmaf(0.0625f, dacc[1], dacc[0]);
     }
 };
 
@@ -121,7 +129,8 @@ struct Fmt<T_Q4_0> {
 // sub-blocks 2c and 2c+1) plus the block's 16-byte header.
 template <>
 struct Fmt<T_Q4_K> {
-    static constexpr int QK = 256, BB = 144, UW = 64, UPB = 4, NA = 2, NP = 16, NF = 2, NQ = NA * NP / 4;
+    static constexpr int QK = 256, BB = 144, UW = 64, UPB = 4, NA = 2, NP = 16, NF = 1, NQ = NA * NP / 4;
+    static constexpr int KIND = 1;  // staged factors: {2^-eL, 2^-eH, sum xL, sum xH}
     struct Raw {
         u32x4 h, q0, q1;
     };
@@ -143,7 +152,6 @@ struct Fmt<T_Q4_K> {
     struct Scl {
         float dsL, dsH, dmL, dmH;
     };
-    __device__ static uint32_t zero_pattern(int) { return MAGIC; }
     __device__ static Raw load(Rsrc rs, uint32_t boff, const Lane& ln) {
         Raw r;
         r.h = bld16(rs, boff);
@@ -156,13 +164,14 @@ struct Fmt<T_Q4_K> {
         unit = g >> 1;
         a = g & 1;
     }
-    __device__ static void pairs(const Raw& r, int a, uint32_t magic, uint32_t P[NP]) {
+    // q (16 q for the high nibbles) as exact fp16 subnormals, times 2^-24
+    __device__ static void pairs(const Raw& r, int a, uint32_t, uint32_t P[NP]) {
         const uint32_t mask = a == 0 ? 0x000F000Fu : 0x00F000F0u;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             uint32_t w = k < 4 ? r.q0[k] : r.q1[k - 4];
-            P[2 * k] = (w & mask) | magic;
-            P[2 * k + 1] = ((w >> 8) & mask) | magic;
+            P[2 * k] = w & mask;
+            P[2 * k + 1] = (w >> 8) & mask;
         }
     }
     // 6-bit (scale, min) of sub-blocks s = 2c, 2c+1 (j = s & 3 over the 12
@@ -177,7 +186,8 @@ struct Fmt<T_Q4_K> {
         const uint32_t lo = C & 0x3F3F3F3Fu;
         const uint32_t hi = ((C >> 2) & 0x30303030u) | (A & 0x00000F0Fu) | ((A >> 4) & 0x0F0F0000u);
         const uint32_t v = ln.low ? lo : hi;
-        const float d = h2f(r.h.x & 0xffffu), dmin = h2f(r.h.x >> 16);
+        // d * 2^24 undoes the subnormal encoding of the quants (exact)
+        const float d = h2f(r.h.x & 0xffffu) * 16777216.0f, dmin = h2f(r.h.x >> 16);
         Scl s;
         s.dsL = d * (float)(v & 0xffu);
         s.dsH = (d * 0.0625f) * (float)((v >> 8) & 0xffu);
@@ -185,21 +195,21 @@ struct Fmt<T_Q4_K> {
         s.dmH = dmin * (float)(v >> 24);
         return s;
     }
-    // f[0] = {corrL, corrH, 2^-eL, 2^-eH}; f[1] = {sum xL, sum xH, 0, 0}
+    // f[0] = {2^-eL, 2^-eH, sum xL, sum xH}
     __device__ static float contrib(const Scl& s, const float dacc[NA], const f32x4 f[NF]) {
-        float v = (s.dsL * f[0].z) * dacc[0];
-        v = __builtin_fmaf(s.dsH * f[0].w, dacc[1], v);
-        v = __builtin_fmaf(-s.dmL, f[1].x, v);
-        return __builtin_fmaf(-s.dmH, f[1].y, v);
+        float v = (s.dsL * f[0].x) * dacc[0];
+        v = __builtin_fmaf(s.dsH * f[0].y, dacc[1], v);
+        v = __builtin_fmaf(-s.dmL, f[0].z, v);
+        return __builtin_fmaf(-s.dmH, f[0].w, v);
     }
 };
 
 // ---------------------------------------------------------------- Q5_K ----
 // Q4_K with a plane of fifth bits (32 bytes at 16; the quants move to 48).
-// Unit c as for Q4_K; the pair of sub-block 2c (low nibbles, value 1024 + q)
+// Unit c as for Q4_K; the pair of sub-block 2c (low nibbles, subnormal q)
 // takes bit 2c of the plane byte as its bit 4, the pair of 2c+1 (high nibbles
-// in place, 1024 + 16 q) takes bit 2c+1 as its bit 8: one rotate and one
-// and-or per pair.
+// in place, 16 q) takes bit 2c+1 as its bit 8: one rotate and one and-or per
+// pair.
 template <>
 struct Fmt<T_Q5_K> : Fmt<T_Q4_K> {
     static constexpr int BB = 176;
@@ -226,7 +236,7 @@ struct Fmt<T_Q5_K> : Fmt<T_Q4_K> {
         r.rhi = ln.rhi;
         return r;
     }
-    __device__ static void pairs(const Raw& r, int a, uint32_t magic, uint32_t P[NP]) {
+    __device__ static void pairs(const Raw& r, int a, uint32_t, uint32_t P[NP]) {
         const uint32_t mask = a == 0 ? 0x000F000Fu : 0x00F000F0u;
         const uint32_t fm = a == 0 ? 0x00100010u : 0x01000100u;
         const uint32_t rot = a == 0 ? r.rlo : r.rhi;
@@ -234,8 +244,8 @@ struct Fmt<T_Q5_K> : Fmt<T_Q4_K> {
         for (int k = 0; k < 8; ++k) {
             const uint32_t w = k < 4 ? r.q0[k] : r.q1[k - 4];
             const uint32_t f = k < 4 ? r.f0[k] : r.f1[k - 4];
-            P[2 * k] = ((w & mask) | magic) | (__builtin_amdgcn_alignbit(f, f, rot) & fm);
-            P[2 * k + 1] = (((w >> 8) & mask) | magic) | (__builtin_amdgcn_alignbit(f, f, rot + 8u) & fm);
+            P[2 * k] = (w & mask) | (__builtin_amdgcn_alignbit(f, f, rot) & fm);
+            P[2 * k + 1] = ((w >> 8) & mask) | (__builtin_amdgcn_alignbit(f, f, rot + 8u) & fm);
         }
     }
 };
@@ -246,7 +256,8 @@ struct Fmt<T_Q5_K> : Fmt<T_Q4_K> {
 // sub-blocks).  Accumulator g.
 template <>
 struct Fmt<T_Q6_K> {
-    static constexpr int QK = 256, BB = 210, UW = 64, UPB = 4, NA = 4, NP = 8, NF = 2, NQ = NA * NP / 4;
+    static constexpr int QK = 256, BB = 210, UW = 64, UPB = 4, NA = 4, NP = 8, NF = 1, NQ = NA * NP / 4;
+    static constexpr int KIND = 2;  // staged factors: {2^-e of groups 0..3}
     struct Raw {
         u32x4 la, lb, qh;
         u32x2 sc;
@@ -295,7 +306,7 @@ struct Fmt<T_Q6_K> {
                 else if (g == 1) v = ((H << 2) & 0x00300030u) | (Bq & 0x000F000Fu);
                 else if (g == 2) v = ((H << 4) & 0x03000300u) | (A & 0x00F000F0u);
                 else v = ((H << 2) & 0x03000300u) | (Bq & 0x00F000F0u);
-                P[2 * k + j] = v | magic;
+                P[2 * k + j] = sub_h2(v | magic, zero_pattern(g));
             }
         }
     }
@@ -309,12 +320,12 @@ struct Fmt<T_Q6_K> {
         s.ds[3] = d16 * (float)(int)(int8_t)(r.sc.y >> (sh + 16));
         return s;
     }
-    // f[0] = corrections of groups 0..3; f[1] = 2^-e of groups 0..3
+    // f[0] = 2^-e of groups 0..3
     __device__ static float contrib(const Scl& s, const float dacc[NA], const f32x4 f[NF]) {
-        float v = (s.ds[0] * f[1].x) * dacc[0];
-        v = __builtin_fmaf(s.ds[1] * f[1].y, dacc[1], v);
-        v = __builtin_fmaf(s.ds[2] * f[1].z, dacc[2], v);
-        return __builtin_fmaf(s.ds[3] * f[1].w, dacc[3], v);
+        float v = (s.ds[0] * f[0].x) * dacc[0];
+        v = __builtin_fmaf(s.ds[1] * f[0].y, dacc[1], v);
+        v = __builtin_fmaf(s.ds[2] * f[0].z, dacc[2], v);
+        return __builtin_fmaf(s.ds[3] * f[0].w, dacc[3], v);
     }
 };
 
@@ -377,7 +388,7 @@ __device__ __forceinline__ int group_exp(uint32_t mbits) {
 }
 
 // Staged activations of one K tile, unit-major: the record of (unit u,
-// vector b) is NQ fp16-pair quads followed by NF factor vectors, 16 B each, at
+// vector b) is NQ fp16-pair quads followed by NF (= 1) factor vector, 16 B each, at
 // 16-byte slot (u * RS + b * (NQ + NF)).  The unit stride RS is odd (in 16-B
 // slots), so the lanes of a wave, which read consecutive units, hit distinct
 // LDS banks; all reads of one record share a base address.
@@ -396,9 +407,8 @@ struct TileLds {
     __device__ u32x4* rec(int u, int b) const { return base + u * RS + b * NREC; }
 };
 
-// One run (16 or 32 consecutive inputs starting at group element `off`) of an
-// already-scaled group -> fp16 pairs in unpack order, its zero-point
-// correction, and its factors.
+// One run (16 or 32 consecutive inputs) of an already-scaled group -> fp16
+// pairs in unpack order, and the run's factors.
 template <class F>
 __device__ __forceinline__ void stage_write_run(const TileLds<F>& L, int b, int u, int a, const float* r, int e) {
     uint32_t P[F::NP];
@@ -411,29 +421,19 @@ __device__ __forceinline__ void stage_write_run(const TileLds<F>& L, int b, int 
 #pragma unroll
     for (int qd = 0; qd < F::NP / 4; ++qd)
         rp[a * (F::NP / 4) + qd] = u32x4{P[4 * qd], P[4 * qd + 1], P[4 * qd + 2], P[4 * qd + 3]};
-    const uint32_t z = F::zero_pattern(a);
-    float corr = 0.f;
-#pragma unroll
-    for (int n = 0; n < F::NP; ++n) corr = dot2(z, P[n], corr);
     float sc = __builtin_ldexpf(1.0f, -e);
     float* f0 = reinterpret_cast<float*>(rp + F::NQ);
-    float* f1 = reinterpret_cast<float*>(rp + F::NQ + F::NF - 1);
-    if (F::NA == 2 && F::NF == 1) {  // Q4_0: {corr0, corr1, 2^-e, 0}
-        f0[a] = corr;
-        if (a == 0) f0[2] = sc;
-        else f0[3] = 0.f;
-    } else if (F::NA == 2) {         // Q4_K: {corrL, corrH, sL, sH}, {sum xL, sum xH, 0, 0}
+    if constexpr (F::KIND == 0) {  // Q4_0: {2^-e, 0, 0, 0} (both runs share e)
+        if (a == 0) *reinterpret_cast<f32x4*>(f0) = f32x4{sc, 0.f, 0.f, 0.f};
+    } else if constexpr (F::KIND == 1) {  // Q4_K: {sL, sH, sum xL, sum xH}
         // sum of the run's fp16 values (dot2 against ones), times 2^-e
         float sx = 0.f;
 #pragma unroll
         for (int n = 0; n < F::NP; ++n) sx = dot2(0x3C003C00u, P[n], sx);
-        f0[a] = corr;
-        f0[2 + a] = sc;
-        f1[a] = sx * sc;
-        f1[2 + a] = 0.f;
-    } else {                         // Q6_K: {corr0..3}, {s0..3}
-        f0[a] = corr;
-        f1[a] = sc;
+        f0[a] = sc;
+        f0[2 + a] = sx * sc;
+    } else {  // Q6_K: {s0..3}
+        f0[a] = sc;
     }
 }
 
@@ -536,7 +536,7 @@ __device__ __forceinline__ void unit_math(const TileLds<F>& L, const typename F:
             for (int qd = 0; qd < F::NP / 4; ++qd)
 #pragma unroll
                 for (int n4 = 0; n4 < 4; ++n4) s = dot2(P[a][4 * qd + n4], xq[qd][n4], s);
-            dacc[a] = s - f[0][a];
+            dacc[a] = s;
         }
         const float c = F::contrib(sc, dacc, f);
         acc[b] += valid ? c : 0.f;

@@ -13,17 +13,21 @@
 // v_mfma_f32_16x16x32_bf16 (Q4_0, Q4_K, Q5_K: one MFMA per 32-weight
 // sub-block) or v_mfma_f32_16x16x16_bf16 (Q6_K: one per 16-weight sub-block):
 //   A (16 x K) = the activations, vector t in row t (rows >= batch read zeros),
-//   B (K x 16) = the weights of a tile's 16 rows, expanded in registers to
-//                the exact bf16 values 128 + q (OR-ing q into bf16 128.0),
+//   B (K x 16) = the weights of a tile's 16 rows as the exact bf16 values of
+//                c (q - z), z the format's zero point and c a power of two
+//                (16 for Q4_0 and Q4_K's high nibbles, 4 for Q6_K, else 1):
+//                the quant bits are placed in the bytes of a register (with
+//                the zero point removed by flipping the sign bit of c q where
+//                z = 128 / c), each byte converted to fp32 (unsigned, or
+//                sign-extended) and two fp32 packed into a bf16 pair -- every
+//                step exact,
 //   C lane l, register r = output (vector 4 (l/16) + r, row l % 16).
-// With acc = A B and az = A Z (the same MFMA against the constant Z = 128 +
-// the format's zero point, i.e. the operand of a sub-block whose quants all sit
-// on the zero point), a sub-block adds s (acc - az) to the output, s = d * sc
-// its scale; Q4_K / Q5_K also subtract dmin m (az / 128).  Every product in
-// the MFMAs is exact (8-bit by 8-bit significands) and the sums are fp32; a
-// sub-block whose quants all equal the zero point gives acc == az bit for bit
-// and so contributes exactly zero.  az depends on the activations only, so
-// the R tiles of a wavefront share it (and the A operand).
+// A sub-block adds (s / c) acc to the output, s = d * sc its scale; Q4_K /
+// Q5_K also subtract dmin m sum(x), with sum(x) from one MFMA against ones
+// that the R tiles of a wavefront share.  Every product in the MFMAs is exact
+// (8-bit by 8-bit significands) and the sums are fp32, so the error is
+// relative to sum |w x|; a sub-block whose quants all equal the zero point
+// contributes exactly zero.
 // fp32 activations enter as x = hi + lo with hi the bf16 truncation of x and
 // lo the bf16 rounding of the exact remainder (|x - hi - lo| <= 2^-17 |x|),
 // two MFMAs each.
@@ -52,10 +56,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WMAX = 8;                   // wavefronts per workgroup
-constexpr uint32_t BMAG = 0x43004300u;    // bf16 pair (128, 128)
-constexpr uint32_t M4 = 0x000F000Fu;
-// byte permutes [b0, 0, b1, 0] and [b2, 0, b3, 0] of one dword
-constexpr uint32_t SEL01 = 0x0C010C00u, SEL23 = 0x0C030C02u;
+constexpr uint32_t BONE = 0x3F803F80u;    // bf16 pair (1, 1)
+constexpr uint32_t LO4 = 0x0F0F0F0Fu, HI4 = 0xF0F0F0F0u, SIGN8 = 0x80808080u;
 
 __device__ __forceinline__ f32x4 mma32(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -66,17 +68,23 @@ __device__ __forceinline__ f32x4 mma16(const u32x2& a, const u32x2& b, const f32
                                                      0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t perm(uint32_t w, uint32_t sel) { return __builtin_amdgcn_perm(w, w, sel); }
-
-// bf16 pair (128 + low nibble of byte 0, 128 + low nibble of byte 2)
-__device__ __forceinline__ uint32_t nib_lo(uint32_t t) { return (t & M4) | BMAG; }
-__device__ __forceinline__ uint32_t nib_hi(uint32_t t) { return ((t >> 4) & M4) | BMAG; }
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     const bf16x2 v = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, v);
 }
+
+// The four bytes of w as exact bf16 values, in two pairs (bytes 0, 1 and 2,
+// 3): unsigned (v_cvt_f32_ubyteN) or sign-extended (SDWA byte select).
+__device__ __forceinline__ u32x2 bytes_u(uint32_t w) {
+    return u32x2{pk_bf16((float)(w & 0xffu), (float)((w >> 8) & 0xffu)),
+                 pk_bf16((float)((w >> 16) & 0xffu), (float)(w >> 24))};
+}
+__device__ __forceinline__ u32x2 bytes_s(uint32_t w) {
+    return u32x2{pk_bf16((float)(int8_t)w, (float)(int8_t)(w >> 8)),
+                 pk_bf16((float)(int8_t)(w >> 16), (float)(int8_t)(w >> 24))};
+}
+__device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a.x, a.y, b.x, b.y}; }
 
 // Two fp32 (bit patterns) -> bf16 pairs hi = truncation, lo = RN of x - hi.
 __device__ __forceinline__ uint32_t split_hi(uint32_t e0, uint32_t e1) {
@@ -224,15 +232,15 @@ struct AO4<0> {
     __device__ f32x4 mm(const u32x2& b) const { return mma16(lo, b, mma16(hi, b, f32x4{0.f, 0.f, 0.f, 0.f})); }
 };
 
-// y += s (acc - az)
-__device__ __forceinline__ void add_sub_block(f32x4& y, float s, const f32x4& acc, const f32x4& az) {
+// y += s acc
+__device__ __forceinline__ void add_sub_block(f32x4& y, float s, const f32x4& acc) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) y[r] = __builtin_fmaf(s, acc[r] - az[r], y[r]);
+    for (int r = 0; r < 4; ++r) y[r] = __builtin_fmaf(s, acc[r], y[r]);
 }
-// y += s (acc - az) - m az   (m = dmin * min / 128)
-__device__ __forceinline__ void add_sub_block_min(f32x4& y, float s, float m, const f32x4& acc, const f32x4& az) {
+// y += s acc - m sx   (sx = sum of the sub-block's activations, m = dmin * min)
+__device__ __forceinline__ void add_sub_block_min(f32x4& y, float s, float m, const f32x4& acc, const f32x4& sx) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) y[r] = __builtin_fmaf(-m, az[r], __builtin_fmaf(s, acc[r] - az[r], y[r]));
+    for (int r = 0; r < 4; ++r) y[r] = __builtin_fmaf(-m, sx[r], __builtin_fmaf(s, acc[r], y[r]));
 }
 
 // ------------------------------------------------------------- formats ----
@@ -246,8 +254,9 @@ __device__ __forceinline__ void add_sub_block_min(f32x4& y, float s, float m, co
 // chunk c = bytes 32c..32c+31 holds weight 64c + j (low nibble, sub-block 2c)
 // and 64c + 32 + j (high nibble, sub-block 2c + 1).  Group g loads quant bytes
 // 16g.. of chunks (0, 1) and (2, 3); after pair_swap its k-slots j = 0..7 of
-// sub-block s are weights 32 s + off(g) + j.  w = d sc q - dmin m: s = d sc,
-// Z = 128, and the min term dmin m sum x with sum x = az / 128.
+// sub-block s are weights 32 s + off(g) + j.  w = d sc q - dmin m: the low
+// nibbles enter as q (c = 1), the high ones in place as 16 q (c = 16), and the
+// min term is dmin m sum x.
 template <int TYPE>
 struct MF;
 
@@ -282,7 +291,7 @@ struct MF<T_Q4_K> {
         uint32_t sc0, sc1, m0, m1;
         __device__ explicit Scl(const u32x4& h) {
             d = h2f(h.x & 0xffffu);
-            dm = h2f(h.x >> 16) * 0.0078125f;  // dmin / 128 (exact)
+            dm = h2f(h.x >> 16);
             sc0 = h.y & 0x3F3F3F3Fu;
             m0 = h.z & 0x3F3F3F3Fu;
             sc1 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
@@ -297,24 +306,27 @@ struct MF<T_Q4_K> {
             return dm * (float)((v >> (8 * (sb & 3))) & 0xffu);
         }
     };
-    // weight operands of chunk c from the swapped quant registers (plus, for
-    // Q5_K, the fifth bits: bit sb of plane byte off(g) + j for k-slot j)
+    // weight operands of chunk c from the swapped quant registers: k-slot j of
+    // sub-block 2c is the low nibble of byte j of (q0, q1), of 2c + 1 the high
+    // nibble.  Q4_K: bl = q, bh = 16 q.  Q5_K (FIFTH): bit 2c (2c + 1) of plane
+    // byte j is bit 4 of the low (high) quant, bl = q, bh = q.
     template <bool FIFTH>
     __device__ static void chunk_ops(const W& w, int c, const u32x2& f, u32x4& bl, u32x4& bh) {
         const uint32_t q0 = c == 0 ? w.qa.x : c == 1 ? w.qa.z : c == 2 ? w.qb.x : w.qb.z;
         const uint32_t q1 = c == 0 ? w.qa.y : c == 1 ? w.qa.w : c == 2 ? w.qb.y : w.qb.w;
-        const uint32_t t0 = perm(q0, SEL01), t1 = perm(q0, SEL23), t2 = perm(q1, SEL01), t3 = perm(q1, SEL23);
-        bl = u32x4{nib_lo(t0), nib_lo(t1), nib_lo(t2), nib_lo(t3)};
-        bh = u32x4{nib_hi(t0), nib_hi(t1), nib_hi(t2), nib_hi(t3)};
+        uint32_t l0 = q0 & LO4, l1 = q1 & LO4, h0, h1;
         if constexpr (FIFTH) {
-            const uint32_t u[4] = {perm(f.x, SEL01), perm(f.x, SEL23), perm(f.y, SEL01), perm(f.y, SEL23)};
             const uint32_t sl = 2u * (uint32_t)c, sh = sl + 1u;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                bl[i] |= ((u[i] >> sl) & 0x00010001u) << 4;
-                bh[i] |= ((u[i] >> sh) & 0x00010001u) << 4;
-            }
+            l0 |= ((f.x >> sl) & 0x01010101u) << 4;
+            l1 |= ((f.y >> sl) & 0x01010101u) << 4;
+            h0 = ((q0 >> 4) & LO4) | (((f.x >> sh) & 0x01010101u) << 4);
+            h1 = ((q1 >> 4) & LO4) | (((f.y >> sh) & 0x01010101u) << 4);
+        } else {
+            h0 = q0 & HI4;
+            h1 = q1 & HI4;
         }
+        bl = cat(bytes_u(l0), bytes_u(l1));
+        bh = cat(bytes_u(h0), bytes_u(h1));
     }
     template <int XT, int R, bool FIFTH = false>
     __device__ static void compute_k(W (&w)[R], const X<XT>& x, const u32x2 (&f)[R], f32x4 (&y)[R]) {
@@ -323,18 +335,19 @@ struct MF<T_Q4_K> {
             pair_swap(w[t].qa);
             pair_swap(w[t].qb);
         }
-        const u32x4 zz = {BMAG, BMAG, BMAG, BMAG};
+        const u32x4 ones = {BONE, BONE, BONE, BONE};
+        constexpr float hs = FIFTH ? 1.0f : 0.0625f;  // 1 / c of the high nibbles
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const AO8<XT> al(x.a[2 * c]), ah(x.a[2 * c + 1]);
-            const f32x4 azl = al.mm(zz), azh = ah.mm(zz);
+            const f32x4 sxl = al.mm(ones), sxh = ah.mm(ones);
 #pragma unroll
             for (int t = 0; t < R; ++t) {
                 u32x4 bl, bh;
                 chunk_ops<FIFTH>(w[t], c, f[t], bl, bh);
                 const Scl sc(w[t].h);
-                add_sub_block_min(y[t], sc.s(2 * c), sc.m(2 * c), al.mm(bl), azl);
-                add_sub_block_min(y[t], sc.s(2 * c + 1), sc.m(2 * c + 1), ah.mm(bh), azh);
+                add_sub_block_min(y[t], sc.s(2 * c), sc.m(2 * c), al.mm(bl), sxl);
+                add_sub_block_min(y[t], hs * sc.s(2 * c + 1), sc.m(2 * c + 1), ah.mm(bh), sxh);
             }
         }
     }
@@ -348,8 +361,7 @@ struct MF<T_Q4_K> {
 };
 
 // Q5_K: the Q4_K header, a 32-byte plane of fifth bits at 16 (bit s of byte
-// j: weight 32 s + j), the quants at 48.  Operands 128 + q, q <= 31, stay
-// exact in bf16.
+// j: weight 32 s + j), the quants at 48.  Operands q <= 31, exact in bf16.
 template <>
 struct MF<T_Q5_K> : MF<T_Q4_K> {
     static constexpr int BB = 176, QOFF = 48;
@@ -379,7 +391,8 @@ struct MF<T_Q5_K> : MF<T_Q4_K> {
 // weight j in its low nibble and 16 + j in its high one).  Group g loads block
 // g's quants; after transpose4 its dword j holds bytes 4g..4g+3 of block j:
 // k-slots 0..3 = weights 4g..4g+3, 4..7 = weights 16 + 4g..16 + 4g + 3.
-// w = d (q - 8): s = d, Z = 128 + 8.
+// w = d (q - 8): the operand is 16 (q - 8), the byte 16 q with its sign bit
+// flipped, read sign-extended (c = 16).
 template <>
 struct MF<T_Q4_0> {
     static constexpr int QK = 32, BB = 18, BPS = 4;
@@ -415,17 +428,15 @@ struct MF<T_Q4_0> {
             transpose4(w[t].q);
             gather4(w[t].d, d[t]);
         }
-        const u32x4 zz = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const AO8<XT> a(x.a[j]);
-            const f32x4 az = a.mm(zz);
 #pragma unroll
             for (int t = 0; t < R; ++t) {
                 const uint32_t q = w[t].q[j];
-                const uint32_t t0 = perm(q, SEL01), t1 = perm(q, SEL23);
-                const u32x4 b = {nib_lo(t0), nib_lo(t1), nib_hi(t0), nib_hi(t1)};
-                add_sub_block(y[t], h2f(d[t][j]), a.mm(b), az);
+                // 16 (low nibble - 8), then 16 (high nibble - 8)
+                const u32x4 b = cat(bytes_s(((q << 4) & HI4) ^ SIGN8), bytes_s((q & HI4) ^ SIGN8));
+                add_sub_block(y[t], h2f(d[t][j]) * 0.0625f, a.mm(b));
             }
         }
     }
@@ -438,8 +449,9 @@ struct MF<T_Q4_0> {
 // 16-byte piece g of ql[0..63], ql[64..127] and qh; after transpose4 its dword
 // j of each holds bytes 16 j + 4 g .. 16 j + 4 g + 3, so for sub-block
 // (h, q4, a = l / 16) its k-slots i = 0..3 are l = 16 a + 4 g + i: ql dword
-// 2 (q4 & 1) + a of half h, qh dword 2 h + a.  w = d sc (q - 32): s = d sc,
-// Z = 128 + 32.
+// 2 (q4 & 1) + a of half h, qh dword 2 h + a.  w = d sc (q - 32): the
+// operand is 4 (q - 32), the byte 4 q with its sign bit flipped, read
+// sign-extended (c = 4).
 template <>
 struct MF<T_Q6_K> {
     static constexpr int QK = 256, BB = 210, BPS = 1;
@@ -473,23 +485,20 @@ struct MF<T_Q6_K> {
             transpose4(w[t].l1);
             transpose4(w[t].qh);
         }
-        const u32x2 zz = {0x43204320u, 0x43204320u};
 #pragma unroll
         for (int sb = 0; sb < 16; ++sb) {
             const int h = sb >> 3, q4 = (sb >> 1) & 3, a = sb & 1;
             const AO4<XT> ao(x.a[sb]);
-            const f32x4 az = ao.mm(zz);
 #pragma unroll
             for (int t = 0; t < R; ++t) {
                 const uint32_t L = (h ? w[t].l1 : w[t].l0)[2 * (q4 & 1) + a];
                 const uint32_t H = w[t].qh[2 * h + a];
-                const uint32_t t0 = perm(L, SEL01), t1 = perm(L, SEL23);
-                const uint32_t u0 = perm(H, SEL01), u1 = perm(H, SEL23);
                 const int ns = 4 * (q4 >> 1), hs = 2 * q4;
-                const u32x2 b = {((t0 >> ns) & M4) | (((u0 >> hs) & 0x00030003u) << 4) | BMAG,
-                                 ((t1 >> ns) & M4) | (((u1 >> hs) & 0x00030003u) << 4) | BMAG};
+                // byte i = 4 q of k-slot i with its sign bit flipped: 4 (q - 32)
+                const uint32_t q = ((L >> ns) & LO4) | (((H >> hs) & 0x03030303u) << 4);
+                const u32x2 b = bytes_s((q << 2) ^ SIGN8);
                 const float s = h2f(w[t].d) * (float)(int)(int8_t)(w[t].sc[sb >> 2] >> (8 * (sb & 3)));
-                add_sub_block(y[t], s, ao.mm(b), az);
+                add_sub_block(y[t], s * 0.25f, ao.mm(b));
             }
         }
     }

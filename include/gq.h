@@ -116,17 +116,22 @@ gq_status gq_dequant(gq_type t, const void* blocks, int64_t n_blocks, void* out,
  * Two paths compute it: batch >= 5, Q4_0 / Q4_K / Q5_K at batch 4 with
  * N <= 4 K and at batch 3 with 4 N <= 5 K run on the matrix cores (the
  * measured crossovers); the rest on the packed fp16 dot instructions.
- * Accuracy, dot path: activations enter as fp16 after an exact power-of-two
- * scaling per 32 inputs (relative rounding <= 2^-11), weights as the exact
- * fp16 values 1024 + q, sums are fp32.  Matrix-core path: bf16 activations
- * enter exactly, fp32 ones as a bf16 pair hi + lo (relative error <= 2^-17),
- * weights as the exact bf16 values 128 + q, sums are fp32.  Either way the
- * result is within 1e-3 * sum_k |w[n][k] * x[b][k]| of the exact product
- * unless that sum is tiny next to the magnitudes the fp32 sums carry (d * sc *
- * 1024 (dot) or 160 (matrix cores) * sum |x| per sub-block), e.g. rows whose
- * quants nearly all sit at the zero point; a sub-block whose quants all equal
- * the zero point contributes exactly zero.  Each vector's result depends on
- * that vector and on N, K alone (bit for bit) within one path. */
+ * Accuracy.  Every weight enters the arithmetic as the exact value of q - z
+ * (z its format's zero point) times a power of two, so every product is exact
+ * and nothing in the fp32 sums cancels later.  Dot path: activations enter as
+ * fp16 after an exact power-of-two scaling per 32 inputs (relative rounding
+ * <= 2^-11).  Matrix-core path: bf16 activations enter exactly, fp32 ones as a
+ * bf16 pair hi + lo (relative error <= 2^-17).  Sums are fp32.  The result is
+ * within 1e-3 * sum_k |w[n][k] * x[b][k]| of the exact product, and a
+ * sub-block whose quants all equal the zero point contributes exactly zero.
+ * For Q4_K / Q5_K the min term dmin * m * sum(x) is taken once per 32-weight
+ * sub-block, so there the same bound holds with sum |w x| replaced by
+ * d * sc * sum q |x| + dmin * m * sum |x| over each sub-block -- the same
+ * quantity unless d * sc * q and dmin * m nearly cancel for most weights of a
+ * sub-block.  On the dot path, a group of 32 activations whose magnitudes
+ * span more than 2^28 loses its smallest elements to fp16 subnormals.  Each
+ * vector's result depends on that vector and on N, K alone (bit for bit)
+ * within one path. */
 gq_status gq_matvec(gq_type t, const void* W, int64_t N, int64_t K, const void* x,
                     gq_dtype x_dtype, int32_t batch, float* y, hipStream_t stream);
 
