@@ -1,8 +1,12 @@
 """Benchmark of the packed-weight products on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu-baseline]
+    python bench.py --context-only        (the context workloads alone, for kernel traces)
+    python bench.py --floor-only          (the stream-read kernel at the headline's byte counts)
     python bench.py --pmc-pass            (the dominant kernel + a copy kernel, for rocprofv3 --pmc)
+    python bench.py --prefill-pass        (the Q4_K prefill product alone, for rocprofv3 --pmc)
     python bench.py --traffic-summary FETCH_DIR WRITE_DIR   (writes profiles/<kernel>_traffic.txt)
+    python bench.py --mfma-summary DIR                      (writes profiles/<prefill>_mfma_counters.txt)
     python bench.py --stats-summary DIR OUT.txt             (rocprofv3 --stats CSV -> text summary)
 
 The step (the headline workload) is one decoder layer of Q4_K products at
@@ -10,28 +14,39 @@ batch 1, hidden 2560: q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up
 9728x2560, down 2560x9728 -- 56,770,560 packed bytes.  q|k|v and gate|up read
 the same activation vector and are issued as one launch each over their
 row-concatenated weights (a loader stores them that way), so a step is four
-dependent launches: qkv, o, gate|up, down.  Weights rotate over >= 1 GiB of
-distinct copies so each step streams from HBM, not from the 256 MB last-level
-cache; inputs are resident in HBM before the timed region.  The steps are
-captured once in a HIP graph that walks every copy; the timed region replays
-it, bracketed by device synchronisation and HIP events on the launch stream.
+dependent launches: qkv, o, gate|up, down.  The launches are the list
+block_quantized_weight_q4_amd.workloads.HEADLINE, which the parity tests walk
+too.  Weights rotate over >= 1 GiB of distinct copies so each step streams
+from HBM, not from the 256 MB last-level cache; inputs are resident in HBM
+before the timed region.  The steps are captured once in a HIP graph that
+walks every copy; the timed region replays it at least 5 times (more when
+--steps asks for more steps), each replay between its own HIP events on the
+launch stream, bracketed by device synchronisation.
 
-One JSON line: value = packed-weight GB/s of the whole step; roofline = the
-dominant kernel (gate|up, 28,016,640 B per launch) timed over back-to-back
-launches of it alone; cpu_baseline = the CPU oracle on the same layer; plus
-the prefill product's TFLOP/s and the other workloads as context.
+One JSON line: value = packed-weight GB/s of the whole step (total bytes of
+all timed steps / total time), with the median and minimum per replay;
+`launches` = each of the four launches alone, against the time of a plain
+streaming read of the same number of bytes (libgqfloor.so, measured in the
+same run); roofline = the dominant kernel (gate|up, 28,016,640 B per launch)
+timed over back-to-back launches of it alone; cpu_baseline = the CPU oracle on
+the same layer, on all the host cores the process may use (one thread per
+core, over row ranges) and on one; plus the prefill products' TFLOP/s and the
+other workloads as context.
 
 roofline.traffic is the HBM bytes per launch of that kernel from two
 rocprofv3 --pmc runs of `--pmc-pass` (FETCH_SIZE, then WRITE_SIZE), each
 scaled by the factor that makes the same counter read right for a plain copy
-kernel of known size.  The summary file records a hash of the kernel's
-sources; when the sources have changed since, traffic is reported as null.
+kernel of known size.  prefill.mfma_busy comes from one rocprofv3 --pmc run of
+`--prefill-pass`.  Each summary file records a hash of the kernel's sources;
+when the sources have changed since, the figure is reported as null.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -42,13 +57,14 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from block_quantized_weight_q4_amd import workloads as WL  # noqa: E402
+
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "packed-weight GB/s (% of HBM peak), Q4_K GEMV batch 1; prefill TFLOP/s"
 ROTATE_BYTES = 1 << 30
-
-DENSE = [("q", 4096, 2560), ("k", 1024, 2560), ("v", 1024, 2560), ("o", 2560, 4096),
-         ("gate", 9728, 2560), ("up", 9728, 2560), ("down", 2560, 9728)]
+MIN_REPS = 5
+CSRC = os.path.join(ROOT, "block_quantized_weight_q4_amd", "csrc")
 
 
 def parse():
@@ -60,26 +76,33 @@ def parse():
     ap.add_argument("--quick", action="store_true", help="headline only (no context workloads)")
     ap.add_argument("--context-only", action="store_true",
                     help="only the context workloads (one JSON line of them; for kernel traces)")
+    ap.add_argument("--floor-only", action="store_true", help="only the stream-read kernel at the headline sizes")
     ap.add_argument("--pmc-pass", action="store_true", help="run the dominant kernel 8x and one copy kernel")
+    ap.add_argument("--prefill-pass", action="store_true", help="run the Q4_K prefill product a few times")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--mfma-summary", metavar="DIR")
     ap.add_argument("--stats-summary", nargs=2, metavar=("DIR", "OUT"))
     return ap.parse_args()
 
 
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 # ------------------------------------------------------------ traffic
-GU_N, GU_K = 19456, 2560
+DOM = WL.DOMINANT
 GU_KERNEL = "k_matvec<2, 0, 1"          # Q4_K, fp32 activations, batch 1
 COPY_BYTES = 64 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "matvec_q4k_gateup_19456x2560_b1_traffic.txt")
 KERNEL_SOURCES = ["gq_device.h", "gq_gemv_core.h", "gq_matvec.hip"]
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "block_quantized_weight_q4_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+PREFILL = WL.TIMED_MATMUL[0]
+MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_q4k_3015x17408x5120_mfma_counters.txt")
+MFMA_SOURCES = ["gq_device.h", "gq_matmul.hip"]
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16"]
 
 
 def pmc_pass():
@@ -88,14 +111,13 @@ def pmc_pass():
     64 MiB written, the calibration for the byte counters."""
     import torch
     import block_quantized_weight_q4_amd as gq
-    from block_quantized_weight_q4_amd import synth
     dev = torch.device("cuda:0")
-    W = synth.weight("q4_k", synth.rng(0x67510002, 4), GU_N, GU_K)
+    W = DOM.weight()
     Ws = [torch.from_numpy(W).to(dev) for _ in range(8)]
-    x = torch.from_numpy(synth.normal_f32(synth.rng(0x67510002, 100), (1, GU_K))).to(dev)
-    y = torch.empty(1, GU_N, device=dev)
+    x = torch.from_numpy(DOM.x()).to(dev)
+    y = torch.empty(1, DOM.N, device=dev)
     for w in Ws:
-        gq.gq_matvec("q4_k", w, GU_N, GU_K, x, y)
+        gq.gq_matvec(DOM.t, w, DOM.N, DOM.K, x, y)
     torch.cuda.synchronize()
     src = torch.empty(COPY_BYTES // 4, device=dev).normal_()
     dst = torch.empty_like(src)
@@ -105,7 +127,23 @@ def pmc_pass():
     print("pmc pass done", flush=True)
 
 
-def _counter_means(d: str) -> dict:
+def prefill_pass():
+    """The Q4_K prefill product 5 times (the counters of each dispatch are
+    averaged by the summary)."""
+    import torch
+    import block_quantized_weight_q4_amd as gq
+    dev = torch.device("cuda:0")
+    L = PREFILL
+    W = torch.from_numpy(L.weight()).to(dev)
+    X = torch.from_numpy(L.x_bf16_bits().view(np.int16)).to(dev).view(torch.bfloat16)
+    Y = torch.empty(L.M, L.N, device=dev)
+    for _ in range(5):
+        gq.gq_matmul(L.t, W, L.N, L.K, X, Y)
+    torch.cuda.synchronize()
+    print("prefill pass done", flush=True)
+
+
+def _counter_means(d: str) -> tuple[dict, dict]:
     import csv
     import glob
     vals = {}
@@ -120,6 +158,7 @@ def _counter_means(d: str) -> dict:
 def traffic_summary(fetch_dir: str, write_dir: str):
     out_lines = []
     per = {}
+    kname = ""
     for d, ctr in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         means, counts = _counter_means(d)
         mv = [k for k in means if k[1] == ctr and GU_KERNEL in k[0]]
@@ -133,11 +172,11 @@ def traffic_summary(fetch_dir: str, write_dir: str):
                          "moved -> scale %.4f -> %.0f bytes per launch"
                          % (ctr, kib_mv, counts[mv[0]], kib_cp, COPY_BYTES // 1024, factor, kib_mv * factor * 1024))
     traffic = sum(v[0] * v[2] * 1024 for v in per.values())
-    algo = GU_N * (GU_K // 256) * 144
+    algo = DOM.N * (DOM.K // 256) * 144
     text = ["# HBM traffic of the Q4_K gate|up product (19456 x 2560, batch 1, fp32 x)",
             "",
             "kernel: %s (Q4_K, fp32 activations, batch 1)" % kname.split("(unsigned")[0].replace("void ", ""),
-            "source_sha256: %s" % kernel_source_hash(),
+            "source_sha256: %s" % source_hash(KERNEL_SOURCES),
             "commands (from the repository root, on the GPU host):",
             "  timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -- python3 bench.py --pmc-pass",
             "  timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -- python3 bench.py --pmc-pass",
@@ -145,26 +184,56 @@ def traffic_summary(fetch_dir: str, write_dir: str):
             ""] + out_lines + [
             "",
             "traffic_bytes_per_launch: %.0f" % traffic,
-            "algorithmic_bytes_per_launch: %d (packed weights) + %d (x) + %d (y)" % (algo, GU_K * 4, GU_N * 4),
-            "traffic / algorithmic: %.4f" % (traffic / (algo + GU_K * 4 + GU_N * 4))]
+            "algorithmic_bytes_per_launch: %d (packed weights) + %d (x) + %d (y)" % (algo, DOM.K * 4, DOM.N * 4),
+            "traffic / algorithmic: %.4f" % (traffic / (algo + DOM.K * 4 + DOM.N * 4))]
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         f.write("\n".join(text) + "\n")
     print("\n".join(text))
 
 
-def read_traffic():
-    """traffic_bytes_per_launch from the committed summary, or None when the
-    kernel sources changed since it was taken (or there is none)."""
+def mfma_summary(d: str):
+    """MFMA busy cycles of the prefill kernel against the cycles its CUs were
+    busy: utilisation = SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES (both
+    summed over the CUs; per CU the matrix core is counted busy for each
+    cycle any of its MFMA pipelines works)."""
+    means, counts = _counter_means(d)
+    ks = sorted({k[0] for k in means if "k_matmul" in k[0]})
+    assert len(ks) >= 1, ks
+    kname = ks[0]
+    v = {c: means.get((kname, c)) for c in MFMA_COUNTERS}
+    n = counts.get((kname, MFMA_COUNTERS[0]), 0)
+    util = v["SQ_VALU_MFMA_BUSY_CYCLES"] / v["SQ_BUSY_CU_CYCLES"] if v["SQ_BUSY_CU_CYCLES"] else float("nan")
+    text = ["# MFMA counters of the Q4_K prefill product (%d x %d x %d, bf16 activations)" % (PREFILL.M, PREFILL.N,
+                                                                                           PREFILL.K),
+            "",
+            "kernel: %s" % kname.split("(")[0].replace("void ", ""),
+            "source_sha256: %s" % source_hash(MFMA_SOURCES),
+            "command (from the repository root, on the GPU host):",
+            "  timeout -s KILL 60 rocprofv3 --pmc %s --output-format csv -d <DIR> -- python3 bench.py --prefill-pass"
+            % " ".join(MFMA_COUNTERS),
+            "  python bench.py --mfma-summary <DIR>",
+            "",
+            "dispatches averaged: %d" % n] + ["%s: %.6g" % (c, v[c]) for c in MFMA_COUNTERS] + [
+            "",
+            "mfma_busy_fraction: %.4f   (SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES)" % util]
+    with open(MFMA_FILE, "w") as f:
+        f.write("\n".join(text) + "\n")
+    print("\n".join(text))
+
+
+def read_summary(path: str, key: str, sources) -> float | None:
+    """A figure from a committed summary, or None when the kernel sources
+    changed since it was taken (or there is none)."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None
     m = re.search(r"source_sha256: (\w+)", text)
-    t = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    if not m or not t or m.group(1) != kernel_source_hash():
+    t = re.search(key + r": ([0-9.eE+-]+)", text)
+    if not m or not t or m.group(1) != source_hash(sources):
         return None
-    return int(t.group(1))
+    return float(t.group(1))
 
 
 def stats_summary(d: str, out: str):
@@ -193,6 +262,7 @@ def stats_summary(d: str, out: str):
     print("\n".join(lines))
 
 
+# ------------------------------------------------------------ timing
 class Timer:
     """Capture a list of launches once in a HIP graph; replay and time it."""
 
@@ -205,38 +275,96 @@ class Timer:
             fn()
         torch.cuda.synchronize()
 
-    def time(self, reps: int, warm: int = 2) -> float:
-        """Mean ms per replay over `reps` replays."""
+    def replays(self, reps: int, warm: int = 2) -> list[float]:
+        """ms of each of `reps` back-to-back replays (events between them on
+        the launch stream, no host synchronisation until the last)."""
         torch = self.torch
         for _ in range(warm):
             self.graph.replay()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(self.stream)
-        for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(self.stream)
+        for i in range(reps):
             self.graph.replay()
-        b.record(self.stream)
+            ev[i + 1].record(self.stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+    def time(self, reps: int, warm: int = 2) -> float:
+        """Mean ms per replay over `reps` replays."""
+        r = self.replays(reps, warm)
+        return sum(r) / len(r)
 
 
+def n_copies(nbytes: int) -> int:
+    return max(2, -(-ROTATE_BYTES // nbytes))
+
+
+class Floor:
+    """The plain streaming read (libgqfloor.so) at a given byte count, over
+    rotated buffers like the products it is compared with."""
+
+    def __init__(self, torch, stream):
+        path = os.path.join(ROOT, "block_quantized_weight_q4_amd", "libgqfloor.so")
+        if not os.path.exists(path):
+            raise RuntimeError("libgqfloor.so is not built (python -m block_quantized_weight_q4_amd.build)")
+        self.lib = ctypes.CDLL(path)
+        self.lib.gqf_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                             ctypes.c_void_p]
+        self.lib.gqf_stream_read.restype = ctypes.c_int
+        self.torch, self.stream = torch, stream
+        self.sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def us(self, nbytes: int, reps: int = MIN_REPS) -> float:
+        torch = self.torch
+        nb = (nbytes + 15) // 16 * 16
+        bufs = [torch.full((nb,), 1, dtype=torch.uint8, device="cuda") for _ in range(n_copies(nb))]
+        threads = 512 if nb >= (20 << 20) else 256
+
+        def run():
+            for b in bufs:
+                rc = self.lib.gqf_stream_read(b.data_ptr(), nb, self.sink.data_ptr(), threads, self.stream.cuda_stream)
+                if rc:
+                    raise RuntimeError("gqf_stream_read failed: %d" % rc)
+
+        r = Timer(torch, run, self.stream).replays(reps)
+        del bufs
+        torch.cuda.empty_cache()
+        return float(np.median(r)) * 1e3 / n_copies(nb)
+
+
+def floor_only(torch, stream):
+    fl = Floor(torch, stream)
+    out = {}
+    for L in WL.HEADLINE:
+        nb = L.N * (L.K // 256) * 144
+        out[L.name] = {"bytes": nb, "floor_us": round(fl.us(nb), 3)}
+        print("floor %s %d B: %.3f us" % (L.name, nb, out[L.name]["floor_us"]), flush=True)
+    lb = WL.layer_bytes("dense")
+    out["layer_as_one_read"] = {"bytes": lb, "floor_us": round(fl.us(lb), 3)}
+    print(json.dumps({"stream_floor": out}))
+
+
+# ------------------------------------------------------------ main
 def main():
     args = parse()
     if args.traffic_summary:
         return traffic_summary(*args.traffic_summary)
+    if args.mfma_summary:
+        return mfma_summary(args.mfma_summary)
     if args.stats_summary:
         return stats_summary(*args.stats_summary)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the products shard by "
               "output rows across GPUs).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-
     if args.pmc_pass:
         return pmc_pass()
+    if args.prefill_pass:
+        return prefill_pass()
 
     import torch
     import block_quantized_weight_q4_amd as gq
-    from block_quantized_weight_q4_amd import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -247,102 +375,105 @@ def main():
     def t_(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+    if args.floor_only:
+        return floor_only(torch, stream)
     if args.context_only:
-        print(json.dumps({"context": bench_context(torch, gq, synth, dev, stream, t_)}), flush=True)
+        print(json.dumps({"context": bench_context(torch, gq, dev, stream, t_)}), flush=True)
         return
 
     # ------------------------------------------------ headline: dense layer
-    mats = {name: synth.weight("q4_k", synth.rng(0x67510002, i), N, K) for i, (name, N, K) in enumerate(DENSE)}
-    host = {"qkv": np.concatenate([mats["q"], mats["k"], mats["v"]]), "o": mats["o"],
-            "gu": np.concatenate([mats["gate"], mats["up"]]), "down": mats["down"]}
-    shapes = {"qkv": (6144, 2560), "o": (2560, 4096), "gu": (19456, 2560), "down": (2560, 9728)}
-    layer_bytes = sum(m.nbytes for m in mats.values())
-    n_copies = max(2, -(-ROTATE_BYTES // layer_bytes))
-    copies = [{k: t_(v) for k, v in host.items()} for _ in range(n_copies)]
-    g = synth.rng(0x67510002, 100)
-    xs = {k: t_(synth.normal_f32(g, (1, K))) for k, (N, K) in shapes.items()}
-    ys = {k: torch.empty(1, N, device=dev) for k, (N, K) in shapes.items()}
+    launches = WL.HEADLINE
+    host = {L.name: L.weight() for L in launches}
+    layer_bytes = WL.layer_bytes("dense")
+    assert layer_bytes == sum(w.nbytes for w in host.values())
+    nc = n_copies(layer_bytes)
+    copies = [{k: t_(v) for k, v in host.items()} for _ in range(nc)]
+    xs = {L.name: t_(L.x()) for L in launches}
+    ys = {L.name: torch.empty(1, L.N, device=dev) for L in launches}
 
     def layer_pass():
         for c in copies:
-            for k in ("qkv", "o", "gu", "down"):
-                n, kk = shapes[k]
-                gq.gq_matvec("q4_k", c[k], n, kk, xs[k], ys[k], stream)
+            for L in launches:
+                gq.gq_matvec(L.t, c[L.name], L.N, L.K, xs[L.name], ys[L.name], stream)
 
     tl = Timer(torch, layer_pass, stream)
-    reps = max(1, args.steps // n_copies)
-    tl.time(max(1, args.warmup // n_copies))
-    ms_pass = tl.time(reps)
-    steps = reps * n_copies
-    ms_step = ms_pass / n_copies
+    reps = max(MIN_REPS, math.ceil(args.steps / nc))
+    warm = max(2, math.ceil(args.warmup / nc))
+    torch.cuda.synchronize()
+    rep_ms = tl.replays(reps, warm)
+    torch.cuda.synchronize()
+    steps = reps * nc
+    ms_step = sum(rep_ms) / steps
+    per_rep = sorted(r / nc for r in rep_ms)
     value = layer_bytes / (ms_step * 1e-3) / 1e9
+    del tl
+
+    # each launch alone, back to back over the copies, and the stream floor
+    # of its byte count
+    fl = Floor(torch, stream)
+    per_launch = {}
+    for L in launches:
+        def one(L=L):
+            for c in copies:
+                gq.gq_matvec(L.t, c[L.name], L.N, L.K, xs[L.name], ys[L.name], stream)
+
+        r = sorted(v / nc * 1e3 for v in Timer(torch, one, stream).replays(MIN_REPS))
+        nb = host[L.name].nbytes
+        f_us = fl.us(nb)
+        per_launch[L.name] = {"shape": "%dx%d" % (L.N, L.K), "bytes": nb, "us_median": round(r[len(r) // 2], 3),
+                              "us_min": round(r[0], 3), "floor_us": round(f_us, 3),
+                              "pct_of_floor": round(100.0 * f_us / r[len(r) // 2], 1),
+                              "pct_hbm_peak": round(100.0 * nb / (r[len(r) // 2] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+    floor_sum = sum(v["floor_us"] for v in per_launch.values())
+    peak_read = fl.us(1 << 29, reps=3)
+    read_peak_gbs = (1 << 29) / (peak_read * 1e-6) / 1e9
 
     # dominant kernel: gate|up alone, back to back over the copies
+    gu_us = per_launch[DOM.name]["us_median"]
+    gu_mean_ms = None
+
     def gu_pass():
         for c in copies:
-            gq.gq_matvec("q4_k", c["gu"], 19456, 2560, xs["gu"], ys["gu"], stream)
+            gq.gq_matvec(DOM.t, c[DOM.name], DOM.N, DOM.K, xs[DOM.name], ys[DOM.name], stream)
 
     tg = Timer(torch, gu_pass, stream)
-    gu_ms = tg.time(max(2, reps)) / n_copies
-    gu_bytes = host["gu"].nbytes
-    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
-    del tl, tg, copies
+    gu_mean_ms = tg.time(max(MIN_REPS, reps)) / nc
+    gu_bytes = host[DOM.name].nbytes
+    gu_gbs = gu_bytes / (gu_mean_ms * 1e-3) / 1e9
+    del tg, copies
     torch.cuda.empty_cache()
 
-    context = {}
-    # ------------------------------------------------ prefill product
-    M, N5, K5 = 3015, 17408, 5120
-    W5 = t_(synth.weight("q4_k", synth.rng(0x67510005, 0), N5, K5))
-    X5 = t_(synth.bf16_bits(synth.normal_f32(synth.rng(0x67510005, 1), (M, K5))).view(np.int16)).view(torch.bfloat16)
-    Y5 = torch.empty(M, N5, device=dev)
-    tp = Timer(torch, lambda: gq.gq_matmul("q4_k", W5, N5, K5, X5, Y5, stream), stream)
-    # the matrix cores reach their sustained clock only after some tens of
-    # milliseconds of this load: replay well past that before timing
-    ms_mm = tp.time(30, warm=60)
-    flops = 2.0 * M * N5 * K5
-    prefill = {"workload": "q4_k_prefill_3015x17408x5120_bf16", "ms": round(ms_mm, 4),
-               "TFLOPs": round(flops / (ms_mm * 1e-3) / 1e12, 2),
-               "frac_bf16_dense_peak": round(flops / (ms_mm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-               "tokens_per_s": round(M / (ms_mm * 1e-3), 1)}
-    del tp, W5, X5, Y5
-    torch.cuda.empty_cache()
-    # the same prefill length through the other formats of a Q4_K_M layer:
-    # the Q6_K down projection (5120 x 17408) and a Q4_0 matrix of the c5 shape
+    # ------------------------------------------------ prefill products
+    prefill = None
     others = {}
-    for t5, N6, K6 in (("q6_k", 5120, 17408), ("q4_0", 17408, 5120)):
-        W6 = t_(synth.weight(t5, synth.rng(0x67510005, 2), N6, K6))
-        X6 = t_(synth.bf16_bits(synth.normal_f32(synth.rng(0x67510005, 3), (M, K6))).view(np.int16)).view(
-            torch.bfloat16)
-        Y6 = torch.empty(M, N6, device=dev)
-        tp = Timer(torch, lambda: gq.gq_matmul(t5, W6, N6, K6, X6, Y6, stream), stream)
-        ms6 = tp.time(20, warm=40)
-        others["%s_prefill_%dx%dx%d_bf16" % (t5, M, N6, K6)] = {
-            "ms": round(ms6, 4), "TFLOPs": round(2.0 * M * N6 * K6 / (ms6 * 1e-3) / 1e12, 2)}
-        del tp, W6, X6, Y6
+    for L in WL.TIMED_MATMUL:
+        W5 = t_(L.weight())
+        X5 = t_(L.x_bf16_bits().view(np.int16)).view(torch.bfloat16)
+        Y5 = torch.empty(L.M, L.N, device=dev)
+        tp = Timer(torch, lambda: gq.gq_matmul(L.t, W5, L.N, L.K, X5, Y5, stream), stream)
+        # the matrix cores reach their sustained clock only after some tens of
+        # milliseconds of this load: replay well past that before timing
+        r = sorted(tp.replays(30, warm=60))
+        ms_mm = float(np.median(r))
+        flops = 2.0 * L.M * L.N * L.K
+        tf = flops / (ms_mm * 1e-3) / 1e12
+        if L is PREFILL:
+            prefill = {"workload": "q4_k_prefill_%dx%dx%d_bf16" % (L.M, L.N, L.K), "ms": round(ms_mm, 4),
+                       "ms_min": round(r[0], 4), "TFLOPs": round(tf, 2),
+                       "frac_bf16_dense_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                       "mfma_busy_fraction": read_summary(MFMA_FILE, "mfma_busy_fraction", MFMA_SOURCES),
+                       "tokens_per_s": round(L.M / (ms_mm * 1e-3), 1)}
+        else:
+            others["%s_prefill_%dx%dx%d_bf16" % (L.t, L.M, L.N, L.K)] = {"ms": round(ms_mm, 4),
+                                                                         "TFLOPs": round(tf, 2)}
+        del tp, W5, X5, Y5
         torch.cuda.empty_cache()
     prefill["other_formats"] = others
 
-    if not args.quick:
-        context = bench_context(torch, gq, synth, dev, stream, t_)
+    context = {} if args.quick else bench_context(torch, gq, dev, stream, t_)
 
     # ------------------------------------------------ CPU oracle on the host
-    cpu = None
-    if not args.no_cpu_baseline:
-        from oracle import oracle as orc
-        xh = {2560: xs["qkv"].cpu().numpy(), 4096: xs["o"].cpu().numpy(), 9728: xs["down"].cpu().numpy()}
-        tc = time.perf_counter()
-        nrep = 0
-        while True:
-            for name, N, K in DENSE:
-                orc.matvec("q4_k", mats[name], N, K, xh[K])
-            nrep += 1
-            if time.perf_counter() - tc > 10.0 or nrep >= 30:
-                break
-        dt = (time.perf_counter() - tc) / nrep
-        cpu = {"value": round(layer_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": "the whole 7-projection Q4_K layer at batch 1 (56,770,560 packed bytes), %d "
-                         "repetition(s) on one host thread (plain C: fp32 dequant + fp64 dot), %.3f s per layer"
-                         % (nrep, dt)}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(launches, host, xs)
 
     out = {
         "metric": METRIC,
@@ -352,6 +483,9 @@ def main():
         "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_median": round(per_rep[len(per_rep) // 2], 5),
+        "ms_per_step_min": round(per_rep[0], 5),
+        "timed_replays": reps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -363,15 +497,23 @@ def main():
             "launches_per_step": "qkv 6144x2560, o, gate|up 19456x2560, down (HIP graph)",
             "batch": 1,
             "packed_bytes_per_step": layer_bytes,
-            "weight_copies_rotated": n_copies,
+            "weight_copies_rotated": nc,
             "activations": "fp32 N(0,1)",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "pct_of_measured_read_peak": round(100.0 * value / read_peak_gbs, 2),
         "tokens_per_s_equiv": round(value / 2.74, 1),
+        "launches": per_launch,
+        "stream_floor": {"kernel": "k_stream_read (one 16-byte load per work-item, libgqfloor.so)",
+                         "sum_of_launch_floors_us": round(floor_sum, 3),
+                         "pct_of_floor": round(100.0 * floor_sum / (ms_step * 1e3), 1),
+                         "read_peak_GBs_512MiB": round(read_peak_gbs, 1)},
         "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": read_summary(TRAFFIC_FILE, "traffic_bytes_per_launch", KERNEL_SOURCES),
                      "kernel": "k_matvec<Q4_K, fp32, batch 1> gate|up 19456x2560",
-                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_ms * 1e3, 3)},
+                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_mean_ms * 1e3, 3),
+                     "median_launch_us": gu_us},
         "cpu_baseline": cpu,
         "prefill": prefill,
         "context": context,
@@ -379,177 +521,188 @@ def main():
     print(json.dumps(out))
 
 
-def bench_context(torch, gq, synth, dev, stream, t_):
+def cpu_info() -> tuple[str, int, int]:
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return model, os.cpu_count() or 1, usable
+
+
+def cpu_baseline(launches, host, xs):
+    """The oracle (plain C: fp32 dequant, fp64 dot) over the headline layer on
+    the host: once on one thread, once with one thread per usable core (at
+    most 16, the host share of one GPU) over row ranges of each projection
+    (ctypes releases the interpreter lock during the call)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import oracle as orc
+    model, nproc, usable = cpu_info()
+    threads = max(1, min(16, usable))
+    xh = {L.name: xs[L.name].cpu().numpy() for L in launches}
+    nbytes = sum(host[L.name].nbytes for L in launches)
+
+    def layer(pool, parts):
+        futs = []
+        for L in launches:
+            step = -(-L.N // parts)
+            for r0 in range(0, L.N, step):
+                futs.append(pool.submit(orc.matvec, L.t, host[L.name], L.N, L.K, xh[L.name],
+                                        (r0, min(L.N, r0 + step))))
+        for f in futs:
+            f.result()
+
+    res = {}
+    for n in (1, threads):
+        with ThreadPoolExecutor(n) as pool:
+            tc = time.perf_counter()
+            nrep = 0
+            while True:
+                layer(pool, n)
+                nrep += 1
+                if time.perf_counter() - tc > 8.0 or nrep >= 200:
+                    break
+            res[n] = ((time.perf_counter() - tc) / nrep, nrep)
+    dt, nrep = res[threads]
+    dt1, nrep1 = res[1]
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole 7-projection Q4_K layer at batch 1 (%d packed bytes) as the four launches' row "
+                      "ranges split over %d threads, %d repetition(s), %.4f s per layer (plain C: fp32 dequant + "
+                      "fp64 dot)" % (nbytes, threads, nrep, dt),
+            "single_thread": {"value": round(nbytes / dt1 / 1e9, 4), "s_per_layer": round(dt1, 4),
+                              "repetitions": nrep1},
+            "host": {"cpu_model": model, "nproc": nproc, "usable_cores": usable}}
+
+
+def bench_context(torch, gq, dev, stream, t_):
     """The other workloads, each timed the same way (graph of back-to-back
-    launches over rotated copies)."""
+    launches over rotated copies), built from the same launch lists the
+    parity tests check."""
     res = {}
 
-    def rotated(make, nbytes):
-        return [make() for _ in range(max(2, -(-ROTATE_BYTES // nbytes)))]
+    def x_dev(L):
+        x = L.x()
+        if L.xdt == "bf16":
+            from block_quantized_weight_q4_amd import synth
+            return t_(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16)
+        return t_(x)
 
-    # Q4_0 2048x2048, batch 1
-    w1 = synth.weight("q4_0", synth.rng(0x67510001, 0), 2048, 2048)
-    c1 = [t_(w1) for _ in range(max(2, -(-(256 << 20) // w1.nbytes)))]
-    x1 = t_(synth.normal_f32(synth.rng(0x67510001, 1), (1, 2048)))
-    y1 = torch.empty(1, 2048, device=dev)
+    def time_launches(group, reps):
+        """Mean us per pass of `group` (launches in order) over rotated copies."""
+        host = {L.name: L.weight() for L in group}
+        nb = sum(w.nbytes for w in host.values())
+        cps = [{k: t_(v) for k, v in host.items()} for _ in range(n_copies(nb))]
+        xs = {L.name: x_dev(L) for L in group}
+        ys = {L.name: torch.empty(L.batch, L.N, device=dev) for L in group}
 
-    def p1():
-        for c in c1:
-            gq.gq_matvec("q4_0", c, 2048, 2048, x1, y1, stream)
+        def run():
+            for c in cps:
+                for L in group:
+                    gq.gq_matvec(L.t, c[L.name], L.N, L.K, xs[L.name], ys[L.name], stream)
 
-    ms = Timer(torch, p1, stream).time(20) / len(c1)
-    res["q4_0_2048x2048_b1"] = {"us": round(ms * 1e3, 3), "GBps": round(w1.nbytes / (ms * 1e-3) / 1e9, 1)}
-    del c1
+        ms = float(np.median(Timer(torch, run, stream).replays(reps))) / len(cps)
+        del cps
+        torch.cuda.empty_cache()
+        return ms * 1e3, nb
 
-    # Q5_K (the Q5_K_M variant's main type) at the hidden-5120 gate shape, batch 1 and 8, bf16
-    w5 = synth.weight("q5_k", synth.rng(0x67510007, 0), 17408, 5120)
-    c5 = [t_(w5) for _ in range(max(2, -(-ROTATE_BYTES // w5.nbytes)))]
-    for B in (1, 8):
-        x5 = t_(synth.bf16_bits(synth.normal_f32(synth.rng(0x67510007, B), (B, 5120))).view(np.int16)).view(
-            torch.bfloat16)
-        y5 = torch.empty(B, 17408, device=dev)
-
-        def p5():
-            for c in c5:
-                gq.gq_matvec("q5_k", c, 17408, 5120, x5, y5, stream)
-
-        ms = Timer(torch, p5, stream).time(10) / len(c5)
-        res["q5_k_17408x5120_bf16_b%d" % B] = {"us": round(ms * 1e3, 3),
-                                               "GBps": round(w5.nbytes / (ms * 1e-3) / 1e9, 1)}
-    del c5
-    torch.cuda.empty_cache()
+    by_wl = {}
+    for L in WL.TIMED_MATVEC:
+        by_wl.setdefault((L.workload, L.batch), []).append(L)
+    for (wl, B), group in by_wl.items():
+        if group == WL.HEADLINE:
+            continue  # the headline
+        us, nb = time_launches(group, MIN_REPS)
+        entry = {"launches": ", ".join("%s %dx%d" % (L.name, L.N, L.K) if L.name != "w" else "%dx%d" % (L.N, L.K)
+                                       for L in group),
+                 "us": round(us, 2), "GBps": round(nb / (us * 1e-6) / 1e9, 1)}
+        if len(group) > 1:
+            entry["tokens_per_s_equiv"] = round(B / (us * 1e-6), 1)
+        name = wl if wl.endswith("_b%d" % B) else "%s_b%d" % (wl, B)
+        res["%s_%s" % (name, group[0].xdt)] = entry
 
     # dense layer at batch 1 with the fused gated unit: qkv, o, then
     # h = silu(gate x) * (up x) in one launch feeding the down projection
-    mats = {name: synth.weight("q4_k", synth.rng(0x67510002, i), N, K) for i, (name, N, K) in enumerate(DENSE)}
-    lb = sum(m.nbytes for m in mats.values())
-    qkv = np.concatenate([mats["q"], mats["k"], mats["v"]])
-    cpf = [{"qkv": t_(qkv), "o": t_(mats["o"]), "gate": t_(mats["gate"]), "up": t_(mats["up"]),
-            "down": t_(mats["down"])} for _ in range(max(2, -(-ROTATE_BYTES // lb)))]
-    gx = synth.rng(0x67510002, 100)
-    xq = t_(synth.normal_f32(gx, (1, 2560)))
-    xo = t_(synth.normal_f32(gx, (1, 4096)))
-    xf = t_(synth.normal_f32(gx, (1, 2560)))
-    yq, yo = torch.empty(1, 6144, device=dev), torch.empty(1, 2560, device=dev)
-    hf, yd = torch.empty(1, 9728, device=dev), torch.empty(1, 2560, device=dev)
+    G = WL.TIMED_GLU[0]
+    qkv, o, _, down = WL.HEADLINE
+    wq, wo, wd = qkv.weight(), o.weight(), down.weight()
+    wg, wu = G.weights()
+    lb = WL.layer_bytes("dense")
+    cpf = [{"qkv": t_(wq), "o": t_(wo), "gate": t_(wg), "up": t_(wu), "down": t_(wd)} for _ in range(n_copies(lb))]
+    xq, xo, xf = t_(qkv.x()), t_(o.x()), t_(G.x())
+    yq, yo = torch.empty(1, qkv.N, device=dev), torch.empty(1, o.N, device=dev)
+    hf, yd = torch.empty(1, G.N, device=dev), torch.empty(1, down.N, device=dev)
 
     def pf():
         for c in cpf:
-            gq.gq_matvec("q4_k", c["qkv"], 6144, 2560, xq, yq, stream)
-            gq.gq_matvec("q4_k", c["o"], 2560, 4096, xo, yo, stream)
-            gq.gq_matvec_glu("q4_k", c["gate"], c["up"], 9728, 2560, xf, "silu", hf, stream)
-            gq.gq_matvec("q4_k", c["down"], 2560, 9728, hf, yd, stream)
+            gq.gq_matvec("q4_k", c["qkv"], qkv.N, qkv.K, xq, yq, stream)
+            gq.gq_matvec("q4_k", c["o"], o.N, o.K, xo, yo, stream)
+            gq.gq_matvec_glu(G.t, c["gate"], c["up"], G.N, G.K, xf, G.act, hf, stream)
+            gq.gq_matvec("q4_k", c["down"], down.N, down.K, hf, yd, stream)
 
-    ms = Timer(torch, pf, stream).time(20) / len(cpf)
-    res["q4_k_dense_layer_b1_fused_glu"] = {
-        "launches": "qkv, o, silu(gate)*up, down(h)", "us_per_layer": round(ms * 1e3, 2),
-        "GBps": round(lb / (ms * 1e-3) / 1e9, 1)}
+    ms = float(np.median(Timer(torch, pf, stream).replays(MIN_REPS))) / len(cpf)
+    res["dense_b1_fused_glu_f32"] = {"launches": "qkv, o, silu(gate)*up, down(h)", "us": round(ms * 1e3, 2),
+                                     "GBps": round(lb / (ms * 1e-3) / 1e9, 1)}
     del cpf
     torch.cuda.empty_cache()
 
-    # dense layer at batch 4
-    mats = {name: synth.weight("q4_k", synth.rng(0x67510002, i), N, K) for i, (name, N, K) in enumerate(DENSE)}
-    host = {"qkv": (np.concatenate([mats["q"], mats["k"], mats["v"]]), 6144, 2560), "o": (mats["o"], 2560, 4096),
-            "gu": (np.concatenate([mats["gate"], mats["up"]]), 19456, 2560), "down": (mats["down"], 2560, 9728)}
-    lb = sum(m.nbytes for m in mats.values())
-    cp = [{k: t_(v[0]) for k, v in host.items()} for _ in range(max(2, -(-ROTATE_BYTES // lb)))]
-    x4 = {k: t_(synth.normal_f32(synth.rng(0x67510002, 200), (4, v[2]))) for k, v in host.items()}
-    y4 = {k: torch.empty(4, v[1], device=dev) for k, v in host.items()}
-
-    def p2():
-        for c in cp:
-            for k, v in host.items():
-                gq.gq_matvec("q4_k", c[k], v[1], v[2], x4[k], y4[k], stream)
-
-    ms = Timer(torch, p2, stream).time(5) / len(cp)
-    res["q4_k_dense_layer_b4"] = {"us_per_layer": round(ms * 1e3, 2), "GBps": round(lb / (ms * 1e-3) / 1e9, 1),
-                                  "tokens_per_s_equiv": round(4 * lb / (ms * 1e-3) / 1e9 / 2.74, 1)}
-    del cp
-    torch.cuda.empty_cache()
-
-    # mixed Q4_K / Q6_K layer, hidden 5120, FFN 17408, bf16 activations
-    specs = [("qk", "q4_k", [("q", 5120), ("k", 1024)], 5120), ("v", "q6_k", [("v", 1024)], 5120),
-             ("o", "q4_k", [("o", 5120)], 5120), ("gu", "q4_k", [("gate", 17408), ("up", 17408)], 5120),
-             ("down", "q6_k", [("down", 5120)], 17408)]
-    idx = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6}
-    hw = {}
-    lb3 = 0
-    for name, t, parts, K in specs:
-        arrs = [synth.weight(t, synth.rng(0x67510003, idx[p]), n, K) for p, n in parts]
-        hw[name] = (np.concatenate(arrs), t, sum(n for _, n in parts), K)
-        lb3 += sum(a.nbytes for a in arrs)
-    cp3 = [{k: t_(v[0]) for k, v in hw.items()} for _ in range(max(2, -(-ROTATE_BYTES // lb3)))]
-    for B in (1, 2, 8, 16):
-        xb = {k: t_(synth.bf16_bits(synth.normal_f32(synth.rng(0x67510003, 300 + B), (B, v[3]))).view(np.int16))
-              .view(torch.bfloat16) for k, v in hw.items()}
-        yb = {k: torch.empty(B, v[2], device=dev) for k, v in hw.items()}
-
-        def p3():
-            for c in cp3:
-                for k, v in hw.items():
-                    gq.gq_matvec(v[1], c[k], v[2], v[3], xb[k], yb[k], stream)
-
-        ms = Timer(torch, p3, stream).time(5) / len(cp3)
-        res["mixed_layer_h5120_bf16_b%d" % B] = {"us_per_layer": round(ms * 1e3, 2),
-                                                 "GBps": round(lb3 / (ms * 1e-3) / 1e9, 1),
-                                                 "tokens_per_s_equiv": round(B / (ms * 1e-3), 1)}
-    del cp3
-    torch.cuda.empty_cache()
-
-    # MoE routed experts: 128 experts, hidden 2816, FFN 704, 8 tokens top-8
-    E, H, F, T, k = 128, 2816, 704, 8, 8
-    g = synth.rng(0x67510004, 0)
-    logits = synth.router_logits(g, T, E)
-    lg_t = t_(logits)
-    ids_t = torch.empty((T, k), dtype=torch.int32, device=dev)
-    rw_t = torch.empty((T, k), device=dev)
-    gq.gq_route_topk(lg_t, k, ids_t, rw_t, stream)
+    # routed experts
+    m = WL.MOE
+    lg_t = t_(m.logits())
+    ids_t = torch.empty((m.T, m.k), dtype=torch.int32, device=dev)
+    rw_t = torch.empty((m.T, m.k), device=dev)
+    gq.gq_route_topk(lg_t, m.k, ids_t, rw_t, stream)
     stream.synchronize()
     distinct = len(np.unique(ids_t.cpu().numpy()))
-    ex = {"gate": synth.weight("q4_0", synth.rng(0x67510004, 1), E * F, H),
-          "up": synth.weight("q4_0", synth.rng(0x67510004, 2), E * F, H),
-          "down": synth.weight("q4_0", synth.rng(0x67510004, 3), E * H, F)}
+    ex = m.experts()
     layer_all = sum(v.nbytes for v in ex.values())
-    read_bytes = layer_all // E * distinct
-    cp4 = [{kk: t_(v) for kk, v in ex.items()} for _ in range(max(2, -(-ROTATE_BYTES // layer_all)))]
-    x4 = t_(synth.normal_f32(g, (T, H)))
-    h4 = t_(synth.normal_f32(g, (T, k, F)))
-    yg = torch.empty(T, k, F, device=dev)
-    yu = torch.empty(T, k, F, device=dev)
-    yd = torch.empty(T, H, device=dev)
-    wsz = max(gq.gq_matvec_id_workspace(E, T, k, F), gq.gq_matvec_id_workspace(E, T, k, H))
+    read_bytes = layer_all // m.E * distinct
+    cp4 = [{kk: t_(v) for kk, v in ex.items()} for _ in range(n_copies(layer_all))]
+    x4 = t_(m.x())
+    h4 = t_(m.h())
+    yg = torch.empty(m.T, m.k, m.F, device=dev)
+    yu = torch.empty(m.T, m.k, m.F, device=dev)
+    yd = torch.empty(m.T, m.H, device=dev)
+    wsz = max(gq.gq_matvec_id_workspace(m.E, m.T, m.k, m.F), gq.gq_matvec_id_workspace(m.E, m.T, m.k, m.H))
     ws = [torch.empty(wsz, dtype=torch.uint8, device=dev) for _ in range(3)]
 
     def p4():
         for c in cp4:
-            gq.gq_route_topk(lg_t, k, ids_t, rw_t, stream)
-            gq.gq_matvec_id("q4_0", c["gate"], E, F, H, ids_t, x4, False, yg, ws[0], None, stream)
-            gq.gq_matvec_id("q4_0", c["up"], E, F, H, ids_t, x4, False, yu, ws[1], None, stream)
-            gq.gq_matvec_id("q4_0", c["down"], E, H, F, ids_t, h4, True, yd, ws[2], rw_t, stream)
+            gq.gq_route_topk(lg_t, m.k, ids_t, rw_t, stream)
+            gq.gq_matvec_id(m.t, c["gate"], m.E, m.F, m.H, ids_t, x4, False, yg, ws[0], None, stream)
+            gq.gq_matvec_id(m.t, c["up"], m.E, m.F, m.H, ids_t, x4, False, yu, ws[1], None, stream)
+            gq.gq_matvec_id(m.t, c["down"], m.E, m.H, m.F, ids_t, h4, True, yd, ws[2], rw_t, stream)
 
-    ms = Timer(torch, p4, stream).time(10) / len(cp4)
+    ms = float(np.median(Timer(torch, p4, stream).replays(MIN_REPS))) / len(cp4)
     res["moe_q4_0_128x_h2816_f704_t8_top8"] = {
-        "launches": "route_topk, gate, up, down (weighted); each routed call = group plan + product",
+        "launches": "route_topk, gate, up, down (weighted)",
         "us_per_layer": round(ms * 1e3, 2), "distinct_experts": distinct, "packed_bytes_read": read_bytes,
         "GBps": round(read_bytes / (ms * 1e-3) / 1e9, 1),
-        "tokens_per_s_equiv_30_layers": round(T / (30 * ms * 1e-3), 1)}
+        "tokens_per_s_equiv_30_layers": round(m.T / (30 * ms * 1e-3), 1)}
 
     # the same layer with the routed gated unit in one launch; h (bf16) feeds
     # the down projection directly
-    hb = torch.empty((T, k, F), device=dev, dtype=torch.bfloat16)
+    hb = torch.empty((m.T, m.k, m.F), device=dev, dtype=torch.bfloat16)
 
     def p5():
         for c in cp4:
-            gq.gq_route_topk(lg_t, k, ids_t, rw_t, stream)
-            gq.gq_matvec_id_glu("q4_0", c["gate"], c["up"], E, F, H, ids_t, x4, "silu", hb, ws[0], stream)
-            gq.gq_matvec_id("q4_0", c["down"], E, H, F, ids_t, hb, True, yd, ws[2], rw_t, stream)
+            gq.gq_route_topk(lg_t, m.k, ids_t, rw_t, stream)
+            gq.gq_matvec_id_glu(m.t, c["gate"], c["up"], m.E, m.F, m.H, ids_t, x4, "silu", hb, ws[0], stream)
+            gq.gq_matvec_id(m.t, c["down"], m.E, m.H, m.F, ids_t, hb, True, yd, ws[2], rw_t, stream)
 
-    ms = Timer(torch, p5, stream).time(10) / len(cp4)
+    ms = float(np.median(Timer(torch, p5, stream).replays(MIN_REPS))) / len(cp4)
     res["moe_q4_0_128x_h2816_f704_t8_top8_fused_glu"] = {
-        "launches": "route_topk, gate|up + SiLU (bf16 h), down (weighted); each routed call = group plan + product",
+        "launches": "route_topk, gate|up + SiLU (bf16 h), down (weighted)",
         "us_per_layer": round(ms * 1e3, 2), "distinct_experts": distinct, "packed_bytes_read": read_bytes,
         "GBps": round(read_bytes / (ms * 1e-3) / 1e9, 1),
-        "tokens_per_s_equiv_30_layers": round(T / (30 * ms * 1e-3), 1)}
+        "tokens_per_s_equiv_30_layers": round(m.T / (30 * ms * 1e-3), 1)}
     del cp4
     torch.cuda.empty_cache()
     return res

@@ -3,9 +3,11 @@
     python -m block_quantized_weight_q4_amd.build
 
 Every HIP/C++ source under csrc/ is compiled in parallel into _build/ and
-linked into block_quantized_weight_q4_amd/libgq.so.  The build always
-recompiles (it is the "does it build" check), using an atomic rename so a
-loaded copy is never overwritten in place.
+linked into block_quantized_weight_q4_amd/libgq.so; floor/gq_floor.hip (the
+plain streaming read the benchmark reports against, not part of the C ABI)
+becomes libgqfloor.so.  The build always recompiles (it is the "does it
+build" check), using an atomic rename so a loaded copy is never overwritten
+in place.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libgq.so")
+FLOOR_SRC = os.path.join(PKG, "floor", "gq_floor.hip")
+FLOOR_OUT = os.path.join(PKG, "libgqfloor.so")
 BUILD = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -43,20 +47,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp%d" % os.getpid()
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = min(len(srcs) + 1, max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        floor_obj = ex.submit(_compile, FLOOR_SRC)
+        objs = list(ex.map(_compile, srcs))
+        _link([floor_obj.result()], FLOOR_OUT)
+    _link(objs, OUT)
     if verbose:
-        print("built", OUT)
+        print("built", OUT, "and", FLOOR_OUT)
     return OUT
 
 

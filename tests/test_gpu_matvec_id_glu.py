@@ -168,8 +168,9 @@ def test_glu_id_edge_cases(gq):
     assert torch.all(h2 == 2.0)
     need = gq.gq_matvec_id_workspace(2, 2, 2, 4)
     assert ws.numel() >= need
+    w8 = torch.empty(144 * 8, dtype=torch.uint8, device="cuda")  # both experts' 4 rows
     with pytest.raises(gq.GqError, match="workspace"):
-        gq.gq_matvec_id_glu("q4_k", w, w, 2, 4, 256, ids, torch.zeros(2, 256, device="cuda"), "silu", h,
+        gq.gq_matvec_id_glu("q4_k", w8, w8, 2, 4, 256, ids, torch.zeros(2, 256, device="cuda"), "silu", h,
                             ws[:need - 16])
 
 
