@@ -212,12 +212,19 @@ def _workspace(ws: torch.Tensor) -> None:
     _contig("ws", ws)
 
 
-def gq_matvec_id(t, experts: torch.Tensor, n_experts: int, N: int, K: int, ids: torch.Tensor, x: torch.Tensor,
+def gq_matvec_id(t, experts: torch.Tensor, n_experts: int, N: int, K: int, ids, x: torch.Tensor,
                  x_per_slot: bool, y: torch.Tensor, ws: torch.Tensor, route_w: torch.Tensor | None = None,
                  stream=None) -> torch.Tensor:
     """Routed product; x [n_tokens][K] (or [n_tokens][top_k][K] per slot), y
-    [n_tokens][top_k][N] (or [n_tokens][N] weighted by route_w [n_tokens][top_k])."""
-    n_tokens, top_k = _ids(ids)
+    [n_tokens][top_k][N] (or [n_tokens][N] weighted by route_w [n_tokens][top_k]).
+    ids may be a (n_tokens, top_k) tuple instead of a tensor for a weighted
+    product: the group table the previous routed call left in ws is reused."""
+    reuse = isinstance(ids, tuple)
+    if reuse:
+        n_tokens, top_k = ids
+        _need(route_w is not None, "reusing the group table needs route_w (a weighted product)")
+    else:
+        n_tokens, top_k = _ids(ids)
     _tensor("x", x, _ACT)
     _tensor("y", y, _F32)
     if route_w is not None:
@@ -233,8 +240,9 @@ def gq_matvec_id(t, experts: torch.Tensor, n_experts: int, N: int, K: int, ids: 
     _need(x.numel() == slots * K, "x must hold %d x %d elements" % (slots, K))
     want_y = n_tokens * N * (1 if route_w is not None else top_k)
     _need(y.numel() >= want_y, "y holds %d elements, fewer than %d" % (y.numel(), want_y))
-    _on_gpu(experts=experts, ids=ids, x=x, y=y, ws=ws, route_w=route_w)
-    _check("gq_matvec_id", _lib.gq_matvec_id(_type(t), _ptr(experts), n_experts, N, K, _ptr(ids), n_tokens, top_k,
+    _on_gpu(experts=experts, ids=None if reuse else ids, x=x, y=y, ws=ws, route_w=route_w)
+    _check("gq_matvec_id", _lib.gq_matvec_id(_type(t), _ptr(experts), n_experts, N, K,
+                                             None if reuse else _ptr(ids), n_tokens, top_k,
                                              _ptr(x), _DTYPES[x.dtype], 1 if x_per_slot else 0, _ptr(route_w),
                                              _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return y

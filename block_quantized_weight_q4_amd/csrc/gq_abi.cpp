@@ -140,8 +140,10 @@ gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_
         (K > 0 && N > 0 && (int64_t)n_experts > MAX_ELEMS / (N * K)))
         return GQ_ERR_SHAPE;
     if (n_tokens == 0 || N == 0) return GQ_OK;
-    if (!ids || !y || !ws || (K > 0 && (!experts || !x))) return GQ_ERR_NULL;
-    if (!aligned16(ids) || !aligned16(y) || !aligned16(ws) || (route_w && !aligned16(route_w)) ||
+    // ids may be NULL only for a weighted product (it then reuses the group
+    // table already in ws)
+    if ((!ids && !route_w) || !y || !ws || (K > 0 && (!experts || !x))) return GQ_ERR_NULL;
+    if ((ids && !aligned16(ids)) || !aligned16(y) || !aligned16(ws) || (route_w && !aligned16(route_w)) ||
         (K > 0 && (!aligned16(experts) || !aligned16(x))))
         return GQ_ERR_ALIGN;
     if (ws_bytes < gqk_matvec_id_ws_bytes(n_experts, n_tokens, top_k, N)) return GQ_ERR_WORKSPACE;

@@ -4,17 +4,23 @@
 // the routed 4-bit experts of the Architecture section of "Show HN: Gemma 4
 // 26B-A4B at up to 100+ tokens/s on a 16 GB Mac").
 //
-// Two or three launches on the caller's stream, no host synchronisation:
+// Up to three launches on the caller's stream, no host synchronisation:
 //  1. k_plan (one workgroup): the slots s = t*top_k + j are ordered by expert
 //     id and each expert's slots are cut into groups of at most CH; the group
 //     table (expert, slot count, slots) goes to the workspace, with the group
-//     and invalid-id counts in its header.  Ids outside [0, n_experts) are
-//     left out, counted, and their output rows zeroed.
+//     and invalid-id counts in its header and each slot's expert (-1 for an
+//     invalid id).  Ids outside [0, n_experts) are left out, counted, and
+//     their output rows zeroed.  A weighted product called without ids reuses
+//     the table an earlier call left in the workspace (the gated unit and the
+//     down projection of one layer route the same ids) and skips this launch.
 //  2. k_experts: one workgroup per (group, row tile) reads its table entry
 //     and runs the shared decode product on that expert's rows with the
 //     group's activation vectors (gathered by slot), writing one output row
 //     per slot.  Workgroups past the number of groups exit at once (the grid
 //     is sized for the worst case, because the host never reads the ids).
+//     The K tile is chosen by each workgroup from its group's slot count, so a
+//     group of one or two slots stages as many inputs at a time as the LDS
+//     budget allows for that count.
 //  3. k_combine (route_w given): y[t][n] = sum_j route_w[t][j] * slot[t][j][n],
 //     j in increasing order.
 // The gated unit of a routed feed-forward block (gate and up stacks, the
@@ -28,22 +34,23 @@ using namespace gqd;
 
 namespace {
 
-constexpr int CH = 4;           // slots per group = vectors per product workgroup
+constexpr int CH = 8;           // slots per group = vectors per product workgroup
 constexpr int MAX_SLOTS = 1024; // n_tokens * top_k
 
-// One group of the table: expert e, nb <= CH slots in slot order.
-struct alignas(32) Entry {
-    int e, nb, sel[CH], pad[2];
-    // slot i for a runtime i, by selects (an indexed private array would live
-    // in scratch memory)
-    __device__ int slot(int i) const { return i == 0 ? sel[0] : i == 1 ? sel[1] : i == 2 ? sel[2] : sel[3]; }
+// One group of the table: expert e, nb <= CH slots in slot order.  Kernels
+// read an entry through a pointer (a private copy indexed by a runtime slot
+// number would live in scratch memory).
+struct alignas(64) Entry {
+    int e, nb, sel[CH];
 };
 
-// Workspace: header (int [0] = invalid ids, [1] = groups), the group table,
-// the per-slot outputs of a weighted product.
+// Workspace: header (int [0] = invalid ids, [1] = groups), each slot's expert
+// (-1 for an invalid id), the group table, the per-slot outputs of a weighted
+// product.  Everything before the outputs depends on n_experts and the slot
+// count only, so calls with different N find the same table.
 struct WsLayout {
     int S, Gmax;
-    size_t off_plan, off_out, total;
+    size_t off_slot, off_plan, off_out, total;
 };
 
 WsLayout layout(int n_experts, int n_tokens, int top_k, int64_t N) {
@@ -51,7 +58,8 @@ WsLayout layout(int n_experts, int n_tokens, int top_k, int64_t N) {
     L.S = n_tokens * top_k;
     const int distinct = L.S < n_experts ? L.S : n_experts;
     L.Gmax = distinct + L.S / CH + 1;
-    L.off_plan = 256;
+    L.off_slot = 256;
+    L.off_plan = L.off_slot + ((size_t)L.S * 4 + 255) / 256 * 256;
     L.off_out = L.off_plan + ((size_t)L.Gmax * sizeof(Entry) + 255) / 256 * 256;
     L.total = L.off_out + 4 * (size_t)L.S * (size_t)N;
     return L;
@@ -68,8 +76,9 @@ WsLayout layout(int n_experts, int n_tokens, int top_k, int64_t N) {
 constexpr int MAX_EXPERTS_LDS = 1024;
 
 __global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ ids, int S, int n_experts,
-                                                   int* __restrict__ hdr, Entry* __restrict__ plan,
-                                                   void* __restrict__ out, int64_t N, int out_bf16) {
+                                                   int* __restrict__ hdr, int* __restrict__ slot_e,
+                                                   Entry* __restrict__ plan, void* __restrict__ out, int64_t N,
+                                                   int out_bf16) {
     __shared__ int4 key4[MAX_SLOTS / 4];
     __shared__ int4 head4[MAX_SLOTS / 4];  // expert id of a group head, INT_MAX otherwise
     __shared__ int rank[MAX_SLOTS];
@@ -95,6 +104,7 @@ __global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ i
     int bad = 0;
     for (int s = tid; s < S; s += NTHREADS) {
         const int e = key[s];
+        slot_e[s] = e;
         int r = 0;
         for (int j4 = 0; 4 * j4 < s; ++j4) {
             const int4 k = key4[j4];
@@ -177,6 +187,22 @@ __global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ i
 }
 
 // ------------------------------------------------------------- product ----
+// K tile (units) of a workgroup whose group has nb slots: as many units as
+// the LDS budget allows for nb vectors, a multiple of LPR, balanced over the
+// tiles -- the same rule as the dense product's launch plan, so the lanes sum
+// their units in the same order whatever the tile (tiles hold whole multiples
+// of LPR units).
+template <class F>
+__host__ __device__ inline int tile_for(int64_t units, int nb, int LPR) {
+    const int64_t per_unit = (int64_t)16 * TileLds<F>::unit_stride(nb);
+    int64_t max_units = (int64_t)(LDS_BUDGET / per_unit) / LPR * LPR;
+    if (max_units < LPR) max_units = LPR;
+    if (units <= max_units) return (int)(units > 0 ? units : 1);
+    const int64_t n_tiles = (units + max_units - 1) / max_units;
+    const int64_t tu = (units + n_tiles - 1) / n_tiles;
+    return (int)((tu + LPR - 1) / LPR * LPR);
+}
+
 // GLU: the gated unit of the routed feed-forward block instead of one
 // product.  experts is then the gate stack and experts_up the up stack; a
 // workgroup covers 2 SR rows, wavefronts 0, 1 computing the gate rows and
@@ -188,14 +214,16 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
                                                       int64_t N, int64_t K, const uint8_t* __restrict__ x,
                                                       int x_per_slot, int top_k, const int* __restrict__ ws_hdr,
                                                       const Entry* __restrict__ plan, void* __restrict__ out,
-                                                      int out_bf16, int act, int LPR, int tile_units) {
+                                                      int out_bf16, int act, int LPR) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x, g = blockIdx.x;
-    // the table entry and the group count, loaded together
+    // the group count and this workgroup's entry, loaded together (the grid
+    // has one column per table entry, so plan[g] exists even when unused)
     const int n_groups = ws_hdr[1];
-    const Entry en = plan[g < n_groups ? g : 0];
+    const Entry* en = plan + g;
+    const int nb = en->nb, e = en->e;
     if (g >= n_groups) return;
-    const int nb = en.nb, e = en.e;
+    const int tile_units = tile_for<Fmt<TYPE>>(K / Fmt<TYPE>::UW, nb, LPR);
     const int64_t rpw = (int64_t)(GLU ? 2 : NTHREADS >> 6) * (64 / LPR);
     const int64_t rowA = (int64_t)blockIdx.y * rpw;
     // the group's vector and output pointers live in LDS: the staging picks
@@ -205,7 +233,7 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
     __shared__ YDst yd;
     if (tid < 8) {
         const int esz = XT == 0 ? 4 : 2;
-        const int slot = en.slot(tid < nb ? tid : 0);
+        const int slot = en->sel[tid < nb ? tid : 0];
         const int64_t xrow = x_per_slot ? slot : slot / top_k;
         xs.p[tid] = x + xrow * K * esz;
         yd.p[tid] = static_cast<float*>(out) + (int64_t)slot * N;
@@ -231,7 +259,7 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
             const int b = i / rows, r = i - b * rows;
             if (r >= nr) continue;
             const float v = act_fn(act, gu[0][b][r]) * gu[1][b][r];
-            const int64_t o = (int64_t)en.slot(b) * N + rowA + r;
+            const int64_t o = (int64_t)en->sel[b] * N + rowA + r;
             if (out_bf16) static_cast<uint16_t*>(out)[o] = f2bf(v);
             else static_cast<float*>(out)[o] = v;
         }
@@ -239,16 +267,17 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
 }
 
 // ------------------------------------------------------------- combine ----
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ slot_out, const int32_t* __restrict__ ids,
-                                                 const float* __restrict__ route_w, int n_experts, int top_k,
-                                                 int64_t N, float* __restrict__ y) {
+// y[t][n] = sum_j route_w[t][j] * slot[t][j][n] over the valid slots, j in
+// increasing order (slot_e: each slot's expert from the table, -1 if invalid).
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ slot_out, const int* __restrict__ slot_e,
+                                                 const float* __restrict__ route_w, int top_k, int64_t N,
+                                                 float* __restrict__ y) {
     const int t = blockIdx.y;
     const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (n >= N) return;
     float acc = 0.f;
     for (int j = 0; j < top_k; ++j) {
-        int e = ids[t * top_k + j];
-        if (e < 0 || e >= n_experts) continue;
+        if (slot_e[t * top_k + j] < 0) continue;
         acc = __builtin_fmaf(route_w[t * top_k + j], slot_out[((int64_t)t * top_k + j) * N + n], acc);
     }
     y[(int64_t)t * N + n] = acc;
@@ -262,8 +291,9 @@ struct Job {
     int64_t N, K;
     const uint8_t* x;
     int x_per_slot, top_k, n_experts;
-    const int32_t* ids;
+    const int32_t* ids;  // nullptr: the table in the workspace is reused
     int* ws_hdr;
+    int* slot_e;
     Entry* plan;
     void* out;
     int out_bf16, act;
@@ -282,11 +312,10 @@ hipError_t launch_experts_d(const Plan& p, const WsLayout& L, const Job& j, hipS
     if (glu)
         hipLaunchKernelGGL((k_experts<TYPE, XT, D, RING, true>), grid, dim3(NTHREADS), p.lds, s, j.experts, j.up,
                            expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.ws_hdr, j.plan, j.out, j.out_bf16,
-                           j.act, p.LPR, p.tile_units);
+                           j.act, p.LPR);
     else
         hipLaunchKernelGGL((k_experts<TYPE, XT, D, RING, false>), grid, dim3(NTHREADS), p.lds, s, j.experts, j.up,
-                           expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.ws_hdr, j.plan, j.out, 0, 0, p.LPR,
-                           p.tile_units);
+                           expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.ws_hdr, j.plan, j.out, 0, 0, p.LPR);
     return hipGetLastError();
 }
 
@@ -296,7 +325,20 @@ hipError_t launch_experts(const WsLayout& L, const Job& j, hipStream_t s) {
     // the launch covers the rows of up to min(S, n_experts) experts (twice
     // as many for the gated unit)
     const int64_t distinct = L.S < j.n_experts ? L.S : j.n_experts;
-    const Plan p = plan_for<F>(j.N, j.K, CH, (j.up ? 2 : 1) * j.N * distinct, 4);
+    Plan p = plan_for<F>(j.N, j.K, CH, (j.up ? 2 : 1) * j.N * distinct, 4);
+    // each workgroup picks its K tile from its slot count (tile_for): the
+    // LDS is sized for the largest of those tiles, and the units per lane of
+    // the largest tile (one slot) decide between the straight-line form and
+    // the ring
+    const int64_t units = j.K / F::UW;
+    p.lds = 0;
+    for (int nb = 1; nb <= CH; ++nb) {
+        const size_t b = (size_t)16 * TileLds<F>::unit_stride(nb) * (size_t)tile_for<F>(units, nb, p.LPR);
+        p.lds = b > p.lds ? b : p.lds;
+    }
+    const int T1 = (tile_for<F>(units, 1, p.LPR) + p.LPR - 1) / p.LPR;
+    p.ring = T1 > D_MAX;
+    p.D = p.ring ? 0 : T1;
 #define GQ_LAUNCH(DD, RR) launch_experts_d<TYPE, XT, DD, RR>(p, L, j, s)
     // two units per lane in flight (measured against 1 and 4: the gated MoE
     // product 2.5% faster than with 4, the rest equal)
@@ -322,11 +364,13 @@ hipError_t launch_experts_x(const WsLayout& L, const Job& j, int x_dtype, hipStr
 hipError_t launch_type(int type, const WsLayout& L, const Job& j, int x_dtype, hipStream_t s) {
     // the group table first; zeroed rows for invalid ids where the product
     // writes its outputs straight to the caller's buffer
-    void* zero_out = j.zero_bad ? j.out : nullptr;
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(NTHREADS), 0, s, j.ids, L.S, j.n_experts, j.ws_hdr, j.plan, zero_out,
-                       j.N, j.out_bf16);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (j.ids) {
+        void* zero_out = j.zero_bad ? j.out : nullptr;
+        hipLaunchKernelGGL(k_plan, dim3(1), dim3(NTHREADS), 0, s, j.ids, L.S, j.n_experts, j.ws_hdr, j.slot_e, j.plan,
+                           zero_out, j.N, j.out_bf16);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (type == T_Q4_0) return launch_experts_x<T_Q4_0>(L, j, x_dtype, s);
     if (type == T_Q4_K) return launch_experts_x<T_Q4_K>(L, j, x_dtype, s);
     if (type == T_Q5_K) return launch_experts_x<T_Q5_K>(L, j, x_dtype, s);
@@ -349,13 +393,13 @@ hipError_t gqk_matvec_id(int type, const void* experts, int n_experts, int64_t N
     // per-slot outputs: straight into y when there is no routing combine
     float* out = route_w ? reinterpret_cast<float*>(w + L.off_out) : y;
     Entry* plan = reinterpret_cast<Entry*>(w + L.off_plan);
+    int* slot_e = reinterpret_cast<int*>(w + L.off_slot);
     const Job j{static_cast<const uint8_t*>(experts), nullptr, N, K, static_cast<const uint8_t*>(x), x_per_slot,
-                top_k, n_experts, ids, hdr, plan, out, 0, 0, route_w == nullptr};
+                top_k, n_experts, ids, hdr, slot_e, plan, out, 0, 0, route_w == nullptr};
     const hipError_t e = launch_type(type, L, j, x_dtype, s);
     if (e != hipSuccess || !route_w) return e;
     const unsigned nx = (unsigned)((N + 255) / 256);
-    hipLaunchKernelGGL(k_combine, dim3(nx, (unsigned)n_tokens), dim3(256), 0, s, out, ids, route_w, n_experts,
-                       top_k, N, y);
+    hipLaunchKernelGGL(k_combine, dim3(nx, (unsigned)n_tokens), dim3(256), 0, s, out, slot_e, route_w, top_k, N, y);
     return hipGetLastError();
 }
 
@@ -367,7 +411,8 @@ hipError_t gqk_matvec_id_glu(int type, const void* experts_gate, const void* exp
     uint8_t* w = static_cast<uint8_t*>(ws);
     const Job j{static_cast<const uint8_t*>(experts_gate), static_cast<const uint8_t*>(experts_up), N, K,
                 static_cast<const uint8_t*>(x), 0, top_k, n_experts, ids, reinterpret_cast<int*>(w),
-                reinterpret_cast<Entry*>(w + L.off_plan), h, h_dtype == DT_BF16 ? 1 : 0, act, true};
+                reinterpret_cast<int*>(w + L.off_slot), reinterpret_cast<Entry*>(w + L.off_plan), h,
+                h_dtype == DT_BF16 ? 1 : 0, act, true};
     return launch_type(type, L, j, x_dtype, s);
 }
 

@@ -174,13 +174,23 @@ gq_status gq_matvec_id_workspace(int32_t n_experts, int32_t n_tokens, int32_t to
  *   route_w != NULL (fp32 [n_tokens][top_k], device): y is [n_tokens][N],
  *       y[t][n] = sum_j route_w[t][j] * (sum_k w_{ids[t][j]}[n][k] * x_{t,j}[k]),
  *       summed over j in increasing order.
- * Each distinct expert's rows are read once for all the (token, slot) pairs
- * routed to it.  ws: device workspace of at least gq_matvec_id_workspace
- * bytes; its contents need no initialisation.  An id outside [0, n_experts)
- * makes its slot contribute zero and is counted in ws (see
- * gq_matvec_id_check).  1 <= top_k <= n_experts, n_tokens * top_k <= 1024,
- * x_dtype GQ_F32 or GQ_BF16, K limited as for gq_matvec.  Accuracy as gq_matvec (for route_w != NULL the
- * bound is 1e-3 * sum_j |route_w[t][j]| * sum_k |w * x|). */
+ * The (token, slot) pairs routed to one expert are taken in groups of up to
+ * 8, and each group reads the expert's rows once: an expert that receives at
+ * most 8 of the call's slots (every expert of an 8-token top-8 step; an
+ * 8-token block reads about 29 experts per layer in the Show HN page's
+ * "Speculative decoding" section) is read once for all of them.
+ * ws: device workspace of at least gq_matvec_id_workspace bytes; its contents
+ * need no initialisation.  Each call leaves in ws the table of groups it
+ * built from ids.  With route_w != NULL, ids may be NULL: the call then uses
+ * the table left in ws by the previous routed call (gq_matvec_id or
+ * gq_matvec_id_glu) made with the same ws, n_experts, n_tokens, top_k and
+ * ids -- the down projection of a layer reusing its gated unit's table -- and
+ * builds none; ws must also be large enough for this call's N.  An id
+ * outside [0, n_experts) makes its slot contribute zero and is counted in ws
+ * (see gq_matvec_id_check).  1 <= top_k <= n_experts, n_tokens * top_k <=
+ * 1024, x_dtype GQ_F32 or GQ_BF16, K limited as for gq_matvec.  Accuracy as
+ * gq_matvec (for route_w != NULL the bound is 1e-3 * sum_j |route_w[t][j]| *
+ * sum_k |w * x|). */
 gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_t N, int64_t K,
                        const int32_t* ids, int32_t n_tokens, int32_t top_k, const void* x,
                        gq_dtype x_dtype, int32_t x_per_slot, const float* route_w, float* y,
@@ -197,7 +207,8 @@ gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_
  *   h[t][j][n] = act(sum_k gate_e[n][k] x_t[k]) * (sum_k up_e[n][k] x_t[k]),
  * h: [n_tokens][top_k][N] of h_dtype (GQ_F32 or GQ_BF16) -- the per-slot
  * vectors a down projection takes as gq_matvec_id's x with x_per_slot == 1.
- * Each distinct expert's rows of both stacks are read once for all its slots.
+ * Each expert's rows of both stacks are read once per group of up to 8 of its
+ * slots (so once for all of them when it receives at most 8).
  * act as for gq_matvec_glu.  ws: device workspace of at least
  * gq_matvec_id_workspace bytes for (n_experts, n_tokens, top_k, N), no
  * initialisation needed; an id outside

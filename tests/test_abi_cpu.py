@@ -127,7 +127,9 @@ def test_matvec_id_validation(lib):
     assert call(E=0) == GQ_ERR_SHAPE
     assert call(per=2) == GQ_ERR_SHAPE
     assert call(T=129) == GQ_ERR_SHAPE  # 129 * 8 > 1024 slots
-    assert call(ids=None) == GQ_ERR_NULL
+    assert call(ids=None) == GQ_ERR_NULL  # ids may be NULL only with route_w
+    assert call(ids=None, rw=A, wsb=0) == GQ_ERR_WORKSPACE  # accepted up to the workspace check
+    assert call(ids=MIS) == GQ_ERR_ALIGN
     assert call(ws=None) == GQ_ERR_NULL
     assert call(y=MIS) == GQ_ERR_ALIGN
     assert call(rw=MIS) == GQ_ERR_ALIGN

@@ -119,7 +119,7 @@ def test_matvec_id_shapes(gq, orc, t, xdt):
 
 @pytest.mark.parametrize("t", ["q4_0", "q4_k"])
 def test_matvec_id_single_expert_equals_matvec(gq, t):
-    """Every slot routed to one expert (groups of 4 slots, several groups):
+    """Every slot routed to one expert (groups of up to 8 slots, two groups):
     each output row equals gq_matvec of that expert on the same vector, bit for
     bit (at this size both launches take the same lanes per row, which fixes
     the summation order)."""
@@ -202,3 +202,66 @@ def test_matvec_id_max_slots_and_many_experts(gq, orc, E):
     y, _ = run_id(gq, "q4_k", ex, E, N, K, ids, dev(x), False, rw)
     yref, sa = orc.matvec_id("q4_k", ex, E, N, K, ids, x, False, rw)
     check_bound(y, yref, sa, "E=%d S=%d routed" % (E, T * k))
+
+
+def test_matvec_id_reused_table(gq, orc):
+    """A weighted product called without ids uses the group table the
+    previous routed call left in the same workspace (invalid ids included):
+    its result equals a call that builds the table itself, bit for bit, and the
+    invalid-id count is still the table's."""
+    g = synth.rng(0x67510004, 40)
+    E, N, K, T, k = 12, 48, 512, 5, 3
+    ex = synth.weight("q4_k", g, E * N, K)
+    exd = synth.weight("q4_k", g, E * K, 512)  # down-like: K rows of 512 inputs per expert
+    ids = g.integers(0, E, (T, k)).astype(np.int32)
+    ids[1, 2] = E + 5
+    x = synth.normal_f32(g, (T, K))
+    h = synth.normal_f32(g, (T, k, 512))
+    rw = g.random((T, k)).astype(np.float32)
+    ids_t, rw_t = dev(ids), dev(rw)
+    ws = torch.empty(max(gq.gq_matvec_id_workspace(E, T, k, N), gq.gq_matvec_id_workspace(E, T, k, K)),
+                     dtype=torch.uint8, device="cuda")
+    y0 = torch.full((T, k, N), float("nan"), device="cuda")
+    gq.gq_matvec_id("q4_k", dev(ex), E, N, K, ids_t, dev(x), False, y0, ws)  # builds the table
+    yr = torch.full((T, K), float("nan"), device="cuda")
+    gq.gq_matvec_id("q4_k", dev(exd), E, K, 512, (T, k), dev(h), True, yr, ws, rw_t)  # reuses it
+    torch.cuda.synchronize()
+    assert gq.gq_matvec_id_check(ws) == 1
+    yf = torch.full((T, K), float("nan"), device="cuda")
+    gq.gq_matvec_id("q4_k", dev(exd), E, K, 512, ids_t, dev(h), True, yf, ws, rw_t)
+    torch.cuda.synchronize()
+    assert torch.equal(yr.view(torch.int32), yf.view(torch.int32))
+    yref, sa = orc.matvec_id("q4_k", exd, E, K, 512, ids, h, True, rw)
+    check_bound(yr.cpu().numpy(), yref, sa, "reused table")
+
+
+def test_moe_64_tokens_top8(gq, orc):
+    """The routed-expert shapes (128 Q4_0 experts, hidden 2816, FFN 704) at 64
+    tokens routed top-8 on the device: 512 slots, about 4 per expert, so
+    several experts receive more than the 4 slots one group held before; every
+    expert is read once per group of up to 8 of its slots (the printed count of
+    expert reads against the distinct experts)."""
+    E, H, F, T, k = 128, 2816, 704, 64, 8
+    g = synth.rng(0x67510004, 64)
+    logits = synth.router_logits(g, T, E)
+    ids_t = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    rw_t = torch.empty((T, k), device="cuda")
+    gq.gq_route_topk(dev(logits), k, ids_t, rw_t)
+    torch.cuda.synchronize()
+    ids, _ = orc.route_topk(logits, k)
+    assert np.array_equal(ids_t.cpu().numpy(), ids)
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    reads = int(np.sum((counts + 7) // 8))
+    print("distinct experts %d, max slots per expert %d, expert reads %d (groups of 4 would read %d)"
+          % (int(np.sum(counts > 0)), int(counts.max()), reads, int(np.sum((counts + 3) // 4))))
+    x = synth.normal_f32(g, (T, H))
+    gate = synth.weight("q4_0", synth.rng(0x67510004, 1), E * F, H)
+    y, ws = run_id(gq, "q4_0", gate, E, F, H, ids, dev(x), False)
+    yref, sa = orc.matvec_id("q4_0", gate, E, F, H, ids, x, False)
+    check_bound(y, yref, sa, "gate, 64 tokens")
+    rw = rw_t.cpu().numpy()
+    h = synth.normal_f32(g, (T, k, F))
+    down = synth.weight("q4_0", synth.rng(0x67510004, 3), E * H, F)
+    y, _ = run_id(gq, "q4_0", down, E, H, F, ids, dev(h), True, rw)
+    yref, sa = orc.matvec_id("q4_0", down, E, H, F, ids, h, True, rw)
+    check_bound(y, yref, sa, "down, 64 tokens")

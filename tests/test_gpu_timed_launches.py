@@ -109,9 +109,14 @@ def test_timed_moe_layer(gq, orc):
     hbits = hb.view(torch.int16).cpu().numpy().view(np.uint16)
     hf = synth.bf16_to_f32(hbits)
     assert np.all(np.isfinite(hf))
+    # the down projection as timed: it reuses the group table the gated call
+    # left in ws; the result equals a call that builds its own, bit for bit
     y = torch.full((m.T, m.H), float("nan"), device="cuda")
-    gq.gq_matvec_id(m.t, dev(ex["down"]), m.E, m.H, m.F, ids_t, hb, True, y, ws, rw_t)
+    gq.gq_matvec_id(m.t, dev(ex["down"]), m.E, m.H, m.F, (m.T, m.k), hb, True, y, ws, rw_t)
+    y2 = torch.full((m.T, m.H), float("nan"), device="cuda")
+    gq.gq_matvec_id(m.t, dev(ex["down"]), m.E, m.H, m.F, ids_t, hb, True, y2, ws, rw_t)
     torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
     yref, sa = orc.matvec_id(m.t, ex["down"], m.E, m.H, m.F, ids, hf, True, rw)
     check_bound(y.cpu().numpy(), yref, sa, "down (bf16 h of the routed gated unit)")
 
