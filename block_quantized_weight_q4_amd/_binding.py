@@ -36,13 +36,14 @@ _lib.gq_matvec.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I32, P, P
 _lib.gq_matvec_id_workspace.argtypes = [I32, I32, I32, I64, ctypes.POINTER(SZ)]
 _lib.gq_matvec_id.argtypes = [ctypes.c_int, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, I32, P, P, P, SZ, P]
 _lib.gq_matvec_id_check.argtypes = [P, P, ctypes.POINTER(I32)]
+_lib.gq_matvec_id_noalloc.argtypes = [ctypes.c_int, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, I32, P, P, P]
 _lib.gq_matmul.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I64, I64, P, I64, P]
 _lib.gq_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
 _lib.gq_matvec_glu.argtypes = [ctypes.c_int, P, P, I64, I64, P, ctypes.c_int, I32, ctypes.c_int, P, ctypes.c_int, P]
 _lib.gq_matvec_id_glu.argtypes = [ctypes.c_int, P, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, ctypes.c_int, P,
                                   ctypes.c_int, P, SZ, P]
 ACTS = {"silu": 0, "gelu_tanh": 1}
-for _f in ("gq_block_info", "gq_dequant", "gq_matvec", "gq_matvec_id_workspace", "gq_matvec_id",
+for _f in ("gq_block_info", "gq_dequant", "gq_matvec", "gq_matvec_id_workspace", "gq_matvec_id", "gq_matvec_id_noalloc",
            "gq_matvec_id_check", "gq_matmul", "gq_route_topk", "gq_matvec_glu", "gq_matvec_id_glu"):
     getattr(_lib, _f).restype = ctypes.c_int
 
@@ -245,6 +246,38 @@ def gq_matvec_id(t, experts: torch.Tensor, n_experts: int, N: int, K: int, ids, 
                                              None if reuse else _ptr(ids), n_tokens, top_k,
                                              _ptr(x), _DTYPES[x.dtype], 1 if x_per_slot else 0, _ptr(route_w),
                                              _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return y
+
+
+def gq_matvec_id_noalloc(t, experts: torch.Tensor, n_experts: int, N: int, K: int, ids, x: torch.Tensor,
+                         x_per_slot: bool, y: torch.Tensor, route_w: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """gq_matvec_id with the library's own per-GPU workspace (no allocation;
+    ids may be a (n_tokens, top_k) tuple for a weighted product to reuse the
+    previous call's group table)."""
+    reuse = isinstance(ids, tuple)
+    if reuse:
+        n_tokens, top_k = ids
+        _need(route_w is not None, "reusing the group table needs route_w (a weighted product)")
+    else:
+        n_tokens, top_k = _ids(ids)
+    _tensor("x", x, _ACT)
+    _tensor("y", y, _F32)
+    if route_w is not None:
+        _tensor("route_w", route_w, _F32)
+        _contig("route_w", route_w)
+        _need(route_w.numel() >= n_tokens * top_k, "route_w must hold n_tokens * top_k elements")
+    _weights("experts", experts, t, max(n_experts, 0) * N if n_tokens and N else 0, K)
+    _contig("x", x)
+    _contig("y", y)
+    slots = n_tokens * (top_k if x_per_slot else 1)
+    _need(x.numel() == slots * K, "x must hold %d x %d elements" % (slots, K))
+    want_y = n_tokens * N * (1 if route_w is not None else top_k)
+    _need(y.numel() >= want_y, "y holds %d elements, fewer than %d" % (y.numel(), want_y))
+    _on_gpu(experts=experts, ids=None if reuse else ids, x=x, y=y, route_w=route_w)
+    _check("gq_matvec_id_noalloc", _lib.gq_matvec_id_noalloc(
+        _type(t), _ptr(experts), n_experts, N, K, None if reuse else _ptr(ids), n_tokens, top_k, _ptr(x),
+        _DTYPES[x.dtype], 1 if x_per_slot else 0, _ptr(route_w), _ptr(y), _stream(stream)))
     return y
 
 

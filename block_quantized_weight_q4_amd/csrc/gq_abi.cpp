@@ -155,6 +155,32 @@ gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_
     }
 }
 
+gq_status gq_matvec_id_noalloc(gq_type t, const void* experts, int32_t n_experts, int64_t N, int64_t K,
+                               const int32_t* ids, int32_t n_tokens, int32_t top_k, const void* x,
+                               gq_dtype x_dtype, int32_t x_per_slot, const float* route_w, float* y,
+                               hipStream_t stream) {
+    if (!known_type(t)) return GQ_ERR_TYPE;
+    if (x_dtype != GQ_F32 && x_dtype != GQ_BF16) return GQ_ERR_DTYPE;
+    if (n_experts < 1 || n_tokens < 0 || top_k < 1 || top_k > n_experts || N < 0 || K < 0 ||
+        K % qk_of(t) != 0 || (x_per_slot != 0 && x_per_slot != 1) || (int64_t)n_tokens * top_k > 1024)
+        return GQ_ERR_SHAPE;
+    if (N > MAX_ELEMS || K > MAX_K_DECODE || (K > 0 && N > MAX_ELEMS / K) ||
+        (K > 0 && N > 0 && (int64_t)n_experts > MAX_ELEMS / (N * K)))
+        return GQ_ERR_SHAPE;
+    if (n_tokens == 0 || N == 0) return GQ_OK;
+    if ((!ids && !route_w) || !y || (K > 0 && (!experts || !x))) return GQ_ERR_NULL;
+    if ((ids && !aligned16(ids)) || !aligned16(y) || (route_w && !aligned16(route_w)) ||
+        (K > 0 && (!aligned16(experts) || !aligned16(x))))
+        return GQ_ERR_ALIGN;
+    if (gqk_matvec_id_ws_bytes(n_experts, n_tokens, top_k, N) > GQK_NOALLOC_WS_BYTES) return GQ_ERR_WORKSPACE;
+    try {
+        return from_hip(gqk_matvec_id_noalloc(t, experts, n_experts, N, K, ids, n_tokens, top_k, x, x_dtype,
+                                              x_per_slot, route_w, y, stream));
+    } catch (...) {
+        return GQ_ERR_LAUNCH;
+    }
+}
+
 gq_status gq_matvec_id_glu(gq_type t, const void* experts_gate, const void* experts_up, int32_t n_experts, int64_t N,
                            int64_t K, const int32_t* ids, int32_t n_tokens, int32_t top_k, const void* x,
                            gq_dtype x_dtype, gq_act act, void* h, gq_dtype h_dtype, void* ws, size_t ws_bytes,

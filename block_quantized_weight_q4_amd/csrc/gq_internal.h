@@ -33,6 +33,12 @@ hipError_t gqk_matvec_id_glu(int type, const void* experts_gate, const void* exp
                              int64_t K, const int32_t* ids, int n_tokens, int top_k, const void* x, int x_dtype,
                              int act, void* h, int h_dtype, void* ws, hipStream_t s);
 hipError_t gqk_matvec_id_bad_count(const void* ws, hipStream_t s, int32_t* n_bad);
+// gqk_matvec_id with the workspace in a per-device array of the library
+// (GQK_NOALLOC_WS_BYTES; larger requests fail with hipErrorInvalidValue).
+constexpr size_t GQK_NOALLOC_WS_BYTES = (size_t)8 << 20;
+hipError_t gqk_matvec_id_noalloc(int type, const void* experts, int n_experts, int64_t N, int64_t K,
+                                 const int32_t* ids, int n_tokens, int top_k, const void* x, int x_dtype,
+                                 int x_per_slot, const float* route_w, float* y, hipStream_t s);
 
 hipError_t gqk_matmul(int type, const void* W, int64_t N, int64_t K, const void* X, int x_dtype,
                       int64_t M, int64_t ldx, float* Y, int64_t ldy, hipStream_t s);

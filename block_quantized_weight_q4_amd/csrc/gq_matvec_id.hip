@@ -27,10 +27,18 @@
 // activation between them) is the same k_experts launch in its GLU form: one
 // launch writes h[t][j][n] = act(gate_e[n] . x_t) * (up_e[n] . x_t), e =
 // ids[t][j], which the down projection then takes as its per-slot vectors.
+#include <mutex>
+
 #include "gq_gemv_core.h"
 #include "gq_internal.h"
 
 using namespace gqd;
+
+// Workspace of gq_matvec_id_noalloc: one per device, held until the process
+// ends.  Host code never uses this name as an address (on the host it is only
+// a stand-in for the symbol); the device address of each GPU's copy comes
+// from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[GQK_NOALLOC_WS_BYTES];
 
 namespace {
 
@@ -414,6 +422,42 @@ hipError_t gqk_matvec_id_glu(int type, const void* experts_gate, const void* exp
                 reinterpret_cast<int*>(w + L.off_slot), reinterpret_cast<Entry*>(w + L.off_plan), h,
                 h_dtype == DT_BF16 ? 1 : 0, act, true};
     return launch_type(type, L, j, x_dtype, s);
+}
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];  // device address of `scratch` on each device
+
+hipError_t scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t gqk_matvec_id_noalloc(int type, const void* experts, int n_experts, int64_t N, int64_t K,
+                                 const int32_t* ids, int n_tokens, int top_k, const void* x, int x_dtype,
+                                 int x_per_slot, const float* route_w, float* y, hipStream_t s) {
+    if (gqk_matvec_id_ws_bytes(n_experts, n_tokens, top_k, N) > GQK_NOALLOC_WS_BYTES) return hipErrorInvalidValue;
+    void* ws = nullptr;
+    const hipError_t e = scratch_of_current_device(&ws);
+    if (e != hipSuccess) return e;
+    // the table, its header and the per-slot outputs are all written by the
+    // call itself: nothing in the array has to start at zero
+    return gqk_matvec_id(type, experts, n_experts, N, K, ids, n_tokens, top_k, x, x_dtype, x_per_slot, route_w, y,
+                         ws, s);
 }
 
 hipError_t gqk_matvec_id_bad_count(const void* ws, hipStream_t s, int32_t* n_bad) {

@@ -196,6 +196,26 @@ gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_
                        gq_dtype x_dtype, int32_t x_per_slot, const float* route_w, float* y,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* gq_matvec_id without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The call allocates nothing: its workspace is an
+ * array inside the library, one per GPU, of GQ_NOALLOC_WS_BYTES (8 MiB), held
+ * from the first call on that GPU until the process ends.  Arguments,
+ * results, limits and accuracy are those of gq_matvec_id with
+ * ws = that array; a call whose gq_matvec_id_workspace(n_experts, n_tokens,
+ * top_k, N) exceeds GQ_NOALLOC_WS_BYTES returns GQ_ERR_WORKSPACE and launches
+ * nothing (e.g. 64 slots allow N up to about 32,000).  Every call on a GPU
+ * uses that GPU's one array, which keeps the last call's contents: ids may
+ * be NULL (with route_w) to reuse the group table of the previous call of
+ * this function on the same GPU, and calls that overlap on one GPU (other
+ * streams, other threads) race with each other -- serialise them.  Invalid
+ * ids are handled as by gq_matvec_id but their count cannot be read back. */
+#define GQ_NOALLOC_WS_BYTES ((size_t)8 << 20)
+gq_status gq_matvec_id_noalloc(gq_type t, const void* experts, int32_t n_experts, int64_t N, int64_t K,
+                               const int32_t* ids, int32_t n_tokens, int32_t top_k, const void* x,
+                               gq_dtype x_dtype, int32_t x_per_slot, const float* route_w, float* y,
+                               hipStream_t stream);
+
 /* Routed gated unit: the gate and up products of a routed feed-forward block
  * and the activation between them, in one launch (the routed 4-bit experts of
  * the Architecture section of the Gemma 4 26B-A4B Show HN page; the

@@ -29,6 +29,7 @@ def lib(gq_lib_path):
     L.gq_matvec_id_workspace.argtypes = [I32, I32, I32, I64, ctypes.POINTER(SZ)]
     L.gq_matvec_id.argtypes = [ctypes.c_int, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, I32, P, P, P, SZ, P]
     L.gq_matvec_id_check.argtypes = [P, P, ctypes.POINTER(I32)]
+    L.gq_matvec_id_noalloc.argtypes = [ctypes.c_int, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, I32, P, P, P]
     L.gq_matmul.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I64, I64, P, I64, P]
     L.gq_block_info.argtypes = [ctypes.c_int, ctypes.POINTER(I32), ctypes.POINTER(I32)]
     L.gq_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
@@ -46,7 +47,7 @@ def declared_functions() -> list[str]:
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -238,3 +239,32 @@ def test_matvec_id_glu_validation(lib):
     assert call(a15=need.value - 1) == GQ_ERR_WORKSPACE
     assert call(a7=0, a1=None, a2=None, a6=None, a9=None, a12=None, a14=None) == GQ_OK  # no tokens: no-op
     assert call(a4=0) == GQ_OK  # N == 0: no-op
+
+
+def test_matvec_id_noalloc_validation(lib):
+    """The no-allocation routed product validates like gq_matvec_id and refuses
+    a call whose workspace would exceed its per-GPU array (8 MiB), all on the
+    host, before any HIP call."""
+    f = lib.gq_matvec_id_noalloc
+    args = [1, A, 128, 704, 2816, A, 8, 8, A, 0, 0, None, A, None]
+    names = ["t", "ex", "E", "N", "K", "ids", "T", "k", "x", "xd", "per", "rw", "y", "s"]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(t=5) == GQ_ERR_TYPE
+    assert call(xd=2) == GQ_ERR_DTYPE
+    assert call(K=2817) == GQ_ERR_SHAPE
+    assert call(T=129) == GQ_ERR_SHAPE
+    assert call(ids=None) == GQ_ERR_NULL
+    assert call(y=None) == GQ_ERR_NULL
+    assert call(y=MIS) == GQ_ERR_ALIGN
+    assert call(ids=MIS) == GQ_ERR_ALIGN
+    # 1024 slots of N = 2816: 11.5 MB of per-slot outputs for a weighted call
+    assert call(T=128, rw=A, N=2816, K=704) == GQ_ERR_WORKSPACE
+    sz = ctypes.c_size_t()
+    assert lib.gq_matvec_id_workspace(128, 128, 8, 2816, ctypes.byref(sz)) == GQ_OK and sz.value > 8 << 20
+    assert call(T=0) == GQ_OK  # no tokens: no-op
