@@ -39,12 +39,14 @@ _lib.gq_matvec_id_check.argtypes = [P, P, ctypes.POINTER(I32)]
 _lib.gq_matvec_id_noalloc.argtypes = [ctypes.c_int, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, I32, P, P, P]
 _lib.gq_matmul.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I64, I64, P, I64, P]
 _lib.gq_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
+_lib.gq_route_topk_plan.argtypes = [P, I32, I32, I32, P, P, P, SZ, P]
 _lib.gq_matvec_glu.argtypes = [ctypes.c_int, P, P, I64, I64, P, ctypes.c_int, I32, ctypes.c_int, P, ctypes.c_int, P]
 _lib.gq_matvec_id_glu.argtypes = [ctypes.c_int, P, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, ctypes.c_int, P,
                                   ctypes.c_int, P, SZ, P]
 ACTS = {"silu": 0, "gelu_tanh": 1}
 for _f in ("gq_block_info", "gq_dequant", "gq_matvec", "gq_matvec_id_workspace", "gq_matvec_id", "gq_matvec_id_noalloc",
-           "gq_matvec_id_check", "gq_matmul", "gq_route_topk", "gq_matvec_glu", "gq_matvec_id_glu"):
+           "gq_matvec_id_check", "gq_matmul", "gq_route_topk", "gq_route_topk_plan", "gq_matvec_glu",
+           "gq_matvec_id_glu"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -219,13 +221,9 @@ def gq_matvec_id(t, experts: torch.Tensor, n_experts: int, N: int, K: int, ids, 
     """Routed product; x [n_tokens][K] (or [n_tokens][top_k][K] per slot), y
     [n_tokens][top_k][N] (or [n_tokens][N] weighted by route_w [n_tokens][top_k]).
     ids may be a (n_tokens, top_k) tuple instead of a tensor for a weighted
-    product: the group table the previous routed call left in ws is reused."""
+    product: the group table already in ws is used (ids NULL in the C call)."""
     reuse = isinstance(ids, tuple)
-    if reuse:
-        n_tokens, top_k = ids
-        _need(route_w is not None, "reusing the group table needs route_w (a weighted product)")
-    else:
-        n_tokens, top_k = _ids(ids)
+    n_tokens, top_k = ids if reuse else _ids(ids)
     _tensor("x", x, _ACT)
     _tensor("y", y, _F32)
     if route_w is not None:
@@ -256,11 +254,7 @@ def gq_matvec_id_noalloc(t, experts: torch.Tensor, n_experts: int, N: int, K: in
     ids may be a (n_tokens, top_k) tuple for a weighted product to reuse the
     previous call's group table)."""
     reuse = isinstance(ids, tuple)
-    if reuse:
-        n_tokens, top_k = ids
-        _need(route_w is not None, "reusing the group table needs route_w (a weighted product)")
-    else:
-        n_tokens, top_k = _ids(ids)
+    n_tokens, top_k = ids if reuse else _ids(ids)
     _tensor("x", x, _ACT)
     _tensor("y", y, _F32)
     if route_w is not None:
@@ -284,8 +278,10 @@ def gq_matvec_id_noalloc(t, experts: torch.Tensor, n_experts: int, N: int, K: in
 def gq_matvec_id_glu(t, experts_gate: torch.Tensor, experts_up: torch.Tensor, n_experts: int, N: int, K: int,
                      ids: torch.Tensor, x: torch.Tensor, act: str, h: torch.Tensor, ws: torch.Tensor,
                      stream=None) -> torch.Tensor:
-    """h[t][j][n] = act(gate_e[n] . x[t]) * (up_e[n] . x[t]) with e = ids[t][j]; h [n_tokens][top_k][N]."""
-    n_tokens, top_k = _ids(ids)
+    """h[t][j][n] = act(gate_e[n] . x[t]) * (up_e[n] . x[t]) with e = ids[t][j]; h [n_tokens][top_k][N].
+    ids may be a (n_tokens, top_k) tuple: the group table already in ws is used."""
+    reuse = isinstance(ids, tuple)
+    n_tokens, top_k = ids if reuse else _ids(ids)
     _tensor("x", x, _ACT)
     _tensor("h", h, _ACT)
     _need(act in ACTS, "act must be one of %s" % sorted(ACTS))
@@ -297,9 +293,9 @@ def gq_matvec_id_glu(t, experts_gate: torch.Tensor, experts_up: torch.Tensor, n_
     _contig("h", h)
     _need(x.numel() == n_tokens * K, "x must hold n_tokens x K = %d x %d elements" % (n_tokens, K))
     _need(h.numel() >= n_tokens * top_k * N, "h holds %d elements, fewer than n_tokens * top_k * N" % h.numel())
-    _on_gpu(experts_gate=experts_gate, experts_up=experts_up, ids=ids, x=x, h=h, ws=ws)
+    _on_gpu(experts_gate=experts_gate, experts_up=experts_up, ids=None if reuse else ids, x=x, h=h, ws=ws)
     _check("gq_matvec_id_glu", _lib.gq_matvec_id_glu(_type(t), _ptr(experts_gate), _ptr(experts_up), n_experts, N,
-                                                     K, _ptr(ids), n_tokens, top_k, _ptr(x), _DTYPES[x.dtype],
+                                                     K, None if reuse else _ptr(ids), n_tokens, top_k, _ptr(x), _DTYPES[x.dtype],
                                                      ACTS[act], _ptr(h), _DTYPES[h.dtype], _ptr(ws),
                                                      ws.numel() * ws.element_size(), _stream(stream)))
     return h
@@ -348,6 +344,26 @@ def gq_route_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor, weights: 
     _on_gpu(logits=logits, ids=ids, weights=weights)
     _check("gq_route_topk", _lib.gq_route_topk(_ptr(logits), n_tokens, n_experts, top_k, _ptr(ids),
                                                _ptr(weights), _stream(stream)))
+    return ids, weights
+
+
+def gq_route_topk_plan(logits: torch.Tensor, top_k: int, ids: torch.Tensor, weights: torch.Tensor, ws: torch.Tensor,
+                       stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """gq_route_topk plus the routed products' group table in ws (so that the
+    products can take ids as a (n_tokens, top_k) tuple)."""
+    _tensor("logits", logits, _F32)
+    _tensor("ids", ids, _I32)
+    _tensor("weights", weights, _F32)
+    _need(logits.dim() == 2, "logits must be [n_tokens][n_experts]")
+    n_tokens, n_experts = logits.shape
+    _need(ids.numel() == n_tokens * top_k and weights.numel() == n_tokens * top_k,
+          "ids / weights must hold n_tokens * top_k elements")
+    for name, v in (("logits", logits), ("ids", ids), ("weights", weights)):
+        _contig(name, v)
+    _workspace(ws)
+    _on_gpu(logits=logits, ids=ids, weights=weights, ws=ws)
+    _check("gq_route_topk_plan", _lib.gq_route_topk_plan(_ptr(logits), n_tokens, n_experts, top_k, _ptr(ids),
+                                                         _ptr(weights), _ptr(ws), ws.numel(), _stream(stream)))
     return ids, weights
 
 

@@ -140,9 +140,8 @@ gq_status gq_matvec_id(gq_type t, const void* experts, int32_t n_experts, int64_
         (K > 0 && N > 0 && (int64_t)n_experts > MAX_ELEMS / (N * K)))
         return GQ_ERR_SHAPE;
     if (n_tokens == 0 || N == 0) return GQ_OK;
-    // ids may be NULL only for a weighted product (it then reuses the group
-    // table already in ws)
-    if ((!ids && !route_w) || !y || !ws || (K > 0 && (!experts || !x))) return GQ_ERR_NULL;
+    // ids may be NULL: the group table already in ws is then used
+    if (!y || !ws || (K > 0 && (!experts || !x))) return GQ_ERR_NULL;
     if ((ids && !aligned16(ids)) || !aligned16(y) || !aligned16(ws) || (route_w && !aligned16(route_w)) ||
         (K > 0 && (!aligned16(experts) || !aligned16(x))))
         return GQ_ERR_ALIGN;
@@ -168,7 +167,7 @@ gq_status gq_matvec_id_noalloc(gq_type t, const void* experts, int32_t n_experts
         (K > 0 && N > 0 && (int64_t)n_experts > MAX_ELEMS / (N * K)))
         return GQ_ERR_SHAPE;
     if (n_tokens == 0 || N == 0) return GQ_OK;
-    if ((!ids && !route_w) || !y || (K > 0 && (!experts || !x))) return GQ_ERR_NULL;
+    if (!y || (K > 0 && (!experts || !x))) return GQ_ERR_NULL;
     if ((ids && !aligned16(ids)) || !aligned16(y) || (route_w && !aligned16(route_w)) ||
         (K > 0 && (!aligned16(experts) || !aligned16(x))))
         return GQ_ERR_ALIGN;
@@ -196,8 +195,8 @@ gq_status gq_matvec_id_glu(gq_type t, const void* experts_gate, const void* expe
         return GQ_ERR_SHAPE;
     if (act != GQ_ACT_SILU && act != GQ_ACT_GELU_TANH) return GQ_ERR_UNSUPPORTED;
     if (n_tokens == 0 || N == 0) return GQ_OK;
-    if (!ids || !h || !ws || (K > 0 && (!experts_gate || !experts_up || !x))) return GQ_ERR_NULL;
-    if (!aligned16(ids) || !aligned16(h) || !aligned16(ws) ||
+    if (!h || !ws || (K > 0 && (!experts_gate || !experts_up || !x))) return GQ_ERR_NULL;
+    if ((ids && !aligned16(ids)) || !aligned16(h) || !aligned16(ws) ||
         (K > 0 && (!aligned16(experts_gate) || !aligned16(experts_up) || !aligned16(x))))
         return GQ_ERR_ALIGN;
     if (ws_bytes < gqk_matvec_id_ws_bytes(n_experts, n_tokens, top_k, N)) return GQ_ERR_WORKSPACE;
@@ -214,6 +213,23 @@ gq_status gq_matvec_id_check(const void* ws, hipStream_t stream, int32_t* n_bad_
     if (!aligned16(ws)) return GQ_ERR_ALIGN;
     try {
         return from_hip(gqk_matvec_id_bad_count(ws, stream, n_bad_ids));
+    } catch (...) {
+        return GQ_ERR_LAUNCH;
+    }
+}
+
+gq_status gq_route_topk_plan(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t top_k, int32_t* ids,
+                             float* weights, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (n_tokens < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts || (int64_t)n_tokens * top_k > 1024)
+        return GQ_ERR_SHAPE;
+    if ((int64_t)n_tokens * n_experts > MAX_ELEMS) return GQ_ERR_SHAPE;
+    if (n_experts > 4096 || top_k > 64) return GQ_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return GQ_OK;
+    if (!logits || !ids || !weights || !ws) return GQ_ERR_NULL;
+    if (!aligned16(logits) || !aligned16(ids) || !aligned16(weights) || !aligned16(ws)) return GQ_ERR_ALIGN;
+    if (ws_bytes < gqk_matvec_id_ws_bytes(n_experts, n_tokens, top_k, 0)) return GQ_ERR_WORKSPACE;
+    try {
+        return from_hip(gqk_route_topk_plan(logits, n_tokens, n_experts, top_k, ids, weights, ws, stream));
     } catch (...) {
         return GQ_ERR_LAUNCH;
     }

@@ -45,3 +45,6 @@ hipError_t gqk_matmul(int type, const void* W, int64_t N, int64_t K, const void*
 
 hipError_t gqk_route_topk(const float* logits, int n_tokens, int n_experts, int top_k, int32_t* ids, float* w,
                           hipStream_t s);
+// Routing plus the routed products' group table in ws (gq_matvec_id.hip).
+hipError_t gqk_route_topk_plan(const float* logits, int n_tokens, int n_experts, int top_k, int32_t* ids, float* w,
+                               void* ws, hipStream_t s);

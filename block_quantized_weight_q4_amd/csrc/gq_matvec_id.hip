@@ -31,6 +31,7 @@
 
 #include "gq_gemv_core.h"
 #include "gq_internal.h"
+#include "gq_route_core.h"
 
 using namespace gqd;
 
@@ -83,10 +84,10 @@ WsLayout layout(int n_experts, int n_tokens, int top_k, int64_t N) {
 // of invalid slots are zeroed (fp32, or bf16 when out_bf16).
 constexpr int MAX_EXPERTS_LDS = 1024;
 
-__global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ ids, int S, int n_experts,
-                                                   int* __restrict__ hdr, int* __restrict__ slot_e,
-                                                   Entry* __restrict__ plan, void* __restrict__ out, int64_t N,
-                                                   int out_bf16) {
+template <int NT>
+__device__ __forceinline__ void plan_body(const int32_t* ids, int S, int n_experts, int* __restrict__ hdr,
+                                          int* __restrict__ slot_e, Entry* __restrict__ plan, void* __restrict__ out,
+                                          int64_t N, int out_bf16) {
     __shared__ int4 key4[MAX_SLOTS / 4];
     __shared__ int4 head4[MAX_SLOTS / 4];  // expert id of a group head, INT_MAX otherwise
     __shared__ int rank[MAX_SLOTS];
@@ -102,15 +103,15 @@ __global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ i
         n_grp = 0;
     }
     if (small_e)
-        for (int e = tid; e < n_experts; e += NTHREADS) cnt[e] = 0;
-    for (int s = tid; s < 4 * S4; s += NTHREADS) {
+        for (int e = tid; e < n_experts; e += NT) cnt[e] = 0;
+    for (int s = tid; s < 4 * S4; s += NT) {
         const int e = s < S ? ids[s] : -2;
         key[s] = s >= S ? -2 : ((e >= 0 && e < n_experts) ? e : -1);  // -2: padding
         head[s] = 0x7fffffff;
     }
     __syncthreads();
     int bad = 0;
-    for (int s = tid; s < S; s += NTHREADS) {
+    for (int s = tid; s < S; s += NT) {
         const int e = key[s];
         slot_e[s] = e;
         int r = 0;
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ i
         __syncthreads();
     }
     int heads = 0;
-    for (int s = tid; s < S; s += NTHREADS) {
+    for (int s = tid; s < S; s += NT) {
         const int e = key[s];
         if (e < 0) continue;
         int before, count;
@@ -187,11 +188,45 @@ __global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ i
     if (out && n_bad)
         for (int s = 0; s < S; ++s)
             if (key[s] < 0)
-                for (int64_t n = tid; n < N; n += NTHREADS) {
+                for (int64_t n = tid; n < N; n += NT) {
                     const int64_t o = (int64_t)s * N + n;
                     if (out_bf16) static_cast<uint16_t*>(out)[o] = 0;
                     else static_cast<float*>(out)[o] = 0.f;
                 }
+}
+
+__global__ __launch_bounds__(NTHREADS) void k_plan(const int32_t* __restrict__ ids, int S, int n_experts,
+                                                   int* __restrict__ hdr, int* __restrict__ slot_e,
+                                                   Entry* __restrict__ plan, void* __restrict__ out, int64_t N,
+                                                   int out_bf16) {
+    plan_body<NTHREADS>(ids, S, n_experts, hdr, slot_e, plan, out, N, out_bf16);
+}
+
+// Routing and the table in one launch (one workgroup): wave w routes tokens
+// w, w + RW, ... (the step of gq_route_topk), writing ids and weights and the
+// ids into LDS; the table is then built from those.
+constexpr int RW = 16;  // waves of the routing workgroup
+
+template <int NI>
+__global__ __launch_bounds__(64 * RW) void k_route_plan(const float* __restrict__ logits, int n_tokens, int n_experts,
+                                                       int top_k, int32_t* __restrict__ ids,
+                                                       float* __restrict__ weights, int* __restrict__ hdr,
+                                                       int* __restrict__ slot_e, Entry* __restrict__ plan) {
+    __shared__ int lids[MAX_SLOTS];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    for (int t = wave; t < n_tokens; t += RW) {
+        int id;
+        float w;
+        gqr::route_token<NI>(logits + (int64_t)t * n_experts, n_experts, top_k, lane, id, w);
+        if (lane < top_k) {
+            ids[(int64_t)t * top_k + lane] = id;
+            weights[(int64_t)t * top_k + lane] = w;
+            lids[t * top_k + lane] = id;
+        }
+    }
+    __syncthreads();
+    plan_body<64 * RW>(lids, n_tokens * top_k, n_experts, hdr, slot_e, plan, nullptr, 0, 0);
 }
 
 // ------------------------------------------------------------- product ----
@@ -220,16 +255,19 @@ template <int TYPE, int XT, int D, bool RING, bool GLU>
 __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict__ experts,
                                                       const uint8_t* __restrict__ experts_up, int64_t expert_bytes,
                                                       int64_t N, int64_t K, const uint8_t* __restrict__ x,
-                                                      int x_per_slot, int top_k, const int* __restrict__ ws_hdr,
-                                                      const Entry* __restrict__ plan, void* __restrict__ out,
-                                                      int out_bf16, int act, int LPR) {
+                                                      int x_per_slot, int top_k, int n_experts, int S,
+                                                      const int* __restrict__ ws_hdr, const Entry* __restrict__ plan,
+                                                      void* __restrict__ out, int out_bf16, int act, int LPR) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x, g = blockIdx.x;
     // the group count and this workgroup's entry, loaded together (the grid
     // has one column per table entry, so plan[g] exists even when unused)
     const int n_groups = ws_hdr[1];
     const Entry* en = plan + g;
-    const int nb = en->nb, e = en->e;
+    // fields clamped to their ranges: a workspace that holds no table (a
+    // caller's mistake when ids are not given) then gives wrong numbers but
+    // no access outside the experts, the activations or the outputs
+    const int nb = min(max(en->nb, 0), CH), e = min(max(en->e, 0), n_experts - 1);
     if (g >= n_groups) return;
     const int tile_units = tile_for<Fmt<TYPE>>(K / Fmt<TYPE>::UW, nb, LPR);
     const int64_t rpw = (int64_t)(GLU ? 2 : NTHREADS >> 6) * (64 / LPR);
@@ -241,7 +279,7 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
     __shared__ YDst yd;
     if (tid < 8) {
         const int esz = XT == 0 ? 4 : 2;
-        const int slot = en->sel[tid < nb ? tid : 0];
+        const int slot = min(max(en->sel[tid < nb ? tid : 0], 0), S - 1);
         const int64_t xrow = x_per_slot ? slot : slot / top_k;
         xs.p[tid] = x + xrow * K * esz;
         yd.p[tid] = static_cast<float*>(out) + (int64_t)slot * N;
@@ -267,7 +305,7 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
             const int b = i / rows, r = i - b * rows;
             if (r >= nr) continue;
             const float v = act_fn(act, gu[0][b][r]) * gu[1][b][r];
-            const int64_t o = (int64_t)en->sel[b] * N + rowA + r;
+            const int64_t o = (int64_t)min(max(en->sel[b], 0), S - 1) * N + rowA + r;
             if (out_bf16) static_cast<uint16_t*>(out)[o] = f2bf(v);
             else static_cast<float*>(out)[o] = v;
         }
@@ -319,11 +357,12 @@ hipError_t launch_experts_d(const Plan& p, const WsLayout& L, const Job& j, hipS
     const dim3 grid((unsigned)L.Gmax, (unsigned)gy);
     if (glu)
         hipLaunchKernelGGL((k_experts<TYPE, XT, D, RING, true>), grid, dim3(NTHREADS), p.lds, s, j.experts, j.up,
-                           expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.ws_hdr, j.plan, j.out, j.out_bf16,
-                           j.act, p.LPR);
+                           expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.n_experts, L.S, j.ws_hdr, j.plan,
+                           j.out, j.out_bf16, j.act, p.LPR);
     else
         hipLaunchKernelGGL((k_experts<TYPE, XT, D, RING, false>), grid, dim3(NTHREADS), p.lds, s, j.experts, j.up,
-                           expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.ws_hdr, j.plan, j.out, 0, 0, p.LPR);
+                           expert_bytes, j.N, j.K, j.x, j.x_per_slot, j.top_k, j.n_experts, L.S, j.ws_hdr, j.plan,
+                           j.out, 0, 0, p.LPR);
     return hipGetLastError();
 }
 
@@ -385,7 +424,31 @@ hipError_t launch_type(int type, const WsLayout& L, const Job& j, int x_dtype, h
     return launch_experts_x<T_Q6_K>(L, j, x_dtype, s);
 }
 
+template <int NI>
+hipError_t launch_route_plan(const float* logits, int n_tokens, int n_experts, int top_k, int32_t* ids, float* w,
+                             void* ws, hipStream_t s) {
+    const WsLayout L = layout(n_experts, n_tokens, top_k, 0);
+    uint8_t* b = static_cast<uint8_t*>(ws);
+    hipLaunchKernelGGL(k_route_plan<NI>, dim3(1), dim3(64 * RW), 0, s, logits, n_tokens, n_experts, top_k, ids, w,
+                       reinterpret_cast<int*>(b), reinterpret_cast<int*>(b + L.off_slot),
+                       reinterpret_cast<Entry*>(b + L.off_plan));
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t gqk_route_topk_plan(const float* logits, int n_tokens, int n_experts, int top_k, int32_t* ids, float* w,
+                               void* ws, hipStream_t s) {
+    if (n_tokens * top_k > MAX_SLOTS) return hipErrorInvalidValue;
+    const int ni = (n_experts + 63) / 64;
+    if (ni <= 1) return launch_route_plan<1>(logits, n_tokens, n_experts, top_k, ids, w, ws, s);
+    if (ni <= 2) return launch_route_plan<2>(logits, n_tokens, n_experts, top_k, ids, w, ws, s);
+    if (ni <= 4) return launch_route_plan<4>(logits, n_tokens, n_experts, top_k, ids, w, ws, s);
+    if (ni <= 8) return launch_route_plan<8>(logits, n_tokens, n_experts, top_k, ids, w, ws, s);
+    if (ni <= 16) return launch_route_plan<16>(logits, n_tokens, n_experts, top_k, ids, w, ws, s);
+    if (ni <= 32) return launch_route_plan<32>(logits, n_tokens, n_experts, top_k, ids, w, ws, s);
+    return launch_route_plan<64>(logits, n_tokens, n_experts, top_k, ids, w, ws, s);
+}
 
 size_t gqk_matvec_id_ws_bytes(int n_experts, int n_tokens, int top_k, int64_t N) {
     return layout(n_experts, n_tokens, top_k, N).total;

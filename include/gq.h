@@ -180,14 +180,17 @@ gq_status gq_matvec_id_workspace(int32_t n_experts, int32_t n_tokens, int32_t to
  * 8-token block reads about 29 experts per layer in the Show HN page's
  * "Speculative decoding" section) is read once for all of them.
  * ws: device workspace of at least gq_matvec_id_workspace bytes; its contents
- * need no initialisation.  Each call leaves in ws the table of groups it
- * built from ids.  With route_w != NULL, ids may be NULL: the call then uses
- * the table left in ws by the previous routed call (gq_matvec_id or
- * gq_matvec_id_glu) made with the same ws, n_experts, n_tokens, top_k and
- * ids -- the down projection of a layer reusing its gated unit's table -- and
- * builds none; ws must also be large enough for this call's N.  An id
- * outside [0, n_experts) makes its slot contribute zero and is counted in ws
- * (see gq_matvec_id_check).  1 <= top_k <= n_experts, n_tokens * top_k <=
+ * need no initialisation.  Each call given ids leaves in ws the table of
+ * groups it built from them.  ids may be NULL: the call then uses the table
+ * already in ws -- left by gq_route_topk_plan or by the previous routed call
+ * (gq_matvec_id or gq_matvec_id_glu) made with the same ws, n_experts,
+ * n_tokens, top_k and ids -- and builds none, so that the products of one
+ * layer share one table; ws must still be large enough for this call's N.
+ * (Table fields are clamped to their ranges, so a workspace that holds no
+ * table gives wrong values but no access out of bounds.)  An id outside
+ * [0, n_experts) makes its slot contribute zero and is counted in ws (see
+ * gq_matvec_id_check); with ids == NULL, the output rows of such slots are
+ * left as they were (a weighted product still leaves them out).  1 <= top_k <= n_experts, n_tokens * top_k <=
  * 1024, x_dtype GQ_F32 or GQ_BF16, K limited as for gq_matvec.  Accuracy as
  * gq_matvec (for route_w != NULL the bound is 1e-3 * sum_j |route_w[t][j]| *
  * sum_k |w * x|). */
@@ -233,7 +236,8 @@ gq_status gq_matvec_id_noalloc(gq_type t, const void* experts, int32_t n_experts
  * gq_matvec_id_workspace bytes for (n_experts, n_tokens, top_k, N), no
  * initialisation needed; an id outside
  * [0, n_experts) gives its slot a zero row of h and is counted in ws (see
- * gq_matvec_id_check).  Shapes and limits as gq_matvec_id; n_tokens == 0 or
+ * gq_matvec_id_check).  ids may be NULL to use the table already in ws, as
+ * for gq_matvec_id.  Shapes and limits as gq_matvec_id; n_tokens == 0 or
  * N == 0 is a no-op.  Accuracy: g and u as gq_matvec_id, act and the product
  * as gq_matvec_glu. */
 gq_status gq_matvec_id_glu(gq_type t, const void* experts_gate, const void* experts_up, int32_t n_experts,
@@ -264,6 +268,17 @@ gq_status gq_matvec_id_check(const void* ws, hipStream_t stream, int32_t* n_bad_
  * the largest selected logit is infinite. */
 gq_status gq_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t top_k,
                         int32_t* ids, float* weights, hipStream_t stream);
+
+/* gq_route_topk and the routed products' table of expert groups in one
+ * launch: ids and weights exactly as gq_route_topk computes them, and in ws
+ * the table that gq_matvec_id / gq_matvec_id_glu would build from those ids,
+ * so that the products of the layer can all be called with ids == NULL (the
+ * topk kernel row of "GGUF in transformers" feeding its routed-expert
+ * product).  ws: at least gq_matvec_id_workspace(n_experts, n_tokens, top_k,
+ * N) bytes for the largest N of the products that will use it (0 for the
+ * table alone).  n_tokens * top_k <= 1024; other limits as gq_route_topk. */
+gq_status gq_route_topk_plan(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                             int32_t* ids, float* weights, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Prefill product Y[m][n] = sum_k X[m][k] * w[n][k] for 0 <= m < M, 0 <= n < N.
  * X: [M][ldx] of x_dtype (row stride ldx >= K elements); Y: [M][ldy] fp32

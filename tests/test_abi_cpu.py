@@ -33,6 +33,7 @@ def lib(gq_lib_path):
     L.gq_matmul.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I64, I64, P, I64, P]
     L.gq_block_info.argtypes = [ctypes.c_int, ctypes.POINTER(I32), ctypes.POINTER(I32)]
     L.gq_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
+    L.gq_route_topk_plan.argtypes = [P, I32, I32, I32, P, P, P, SZ, P]
     L.gq_matvec_glu.argtypes = [ctypes.c_int, P, P, I64, I64, P, ctypes.c_int, I32, ctypes.c_int, P, ctypes.c_int, P]
     L.gq_matvec_id_glu.argtypes = [ctypes.c_int, P, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, ctypes.c_int, P,
                                    ctypes.c_int, P, SZ, P]
@@ -47,7 +48,7 @@ def declared_functions() -> list[str]:
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -128,8 +129,9 @@ def test_matvec_id_validation(lib):
     assert call(E=0) == GQ_ERR_SHAPE
     assert call(per=2) == GQ_ERR_SHAPE
     assert call(T=129) == GQ_ERR_SHAPE  # 129 * 8 > 1024 slots
-    assert call(ids=None) == GQ_ERR_NULL  # ids may be NULL only with route_w
-    assert call(ids=None, rw=A, wsb=0) == GQ_ERR_WORKSPACE  # accepted up to the workspace check
+    # ids may be NULL (the table in ws is used): accepted up to the workspace check
+    assert call(ids=None, wsb=0) == GQ_ERR_WORKSPACE
+    assert call(ids=None, rw=A, wsb=0) == GQ_ERR_WORKSPACE
     assert call(ids=MIS) == GQ_ERR_ALIGN
     assert call(ws=None) == GQ_ERR_NULL
     assert call(y=MIS) == GQ_ERR_ALIGN
@@ -230,8 +232,9 @@ def test_matvec_id_glu_validation(lib):
     assert call(a7=129) == GQ_ERR_SHAPE  # 129 * 8 slots > 1024
     assert call(a5=(1 << 22) + 256) == GQ_ERR_SHAPE
     assert call(a11=2) == GQ_ERR_UNSUPPORTED  # unknown activation
-    for i in (1, 2, 6, 9, 12, 14):
+    for i in (1, 2, 9, 12, 14):
         assert call(**{"a%d" % i: None}) == GQ_ERR_NULL, i
+    assert call(a6=None, a15=0) == GQ_ERR_WORKSPACE  # NULL ids (the table in ws is used) pass validation
     for i in (1, 2, 6, 9, 12, 14):
         assert call(**{"a%d" % i: MIS}) == GQ_ERR_ALIGN, i
     need = ctypes.c_size_t()
@@ -259,7 +262,7 @@ def test_matvec_id_noalloc_validation(lib):
     assert call(xd=2) == GQ_ERR_DTYPE
     assert call(K=2817) == GQ_ERR_SHAPE
     assert call(T=129) == GQ_ERR_SHAPE
-    assert call(ids=None) == GQ_ERR_NULL
+    assert call(ids=None, y=None) == GQ_ERR_NULL
     assert call(y=None) == GQ_ERR_NULL
     assert call(y=MIS) == GQ_ERR_ALIGN
     assert call(ids=MIS) == GQ_ERR_ALIGN
@@ -268,3 +271,27 @@ def test_matvec_id_noalloc_validation(lib):
     sz = ctypes.c_size_t()
     assert lib.gq_matvec_id_workspace(128, 128, 8, 2816, ctypes.byref(sz)) == GQ_OK and sz.value > 8 << 20
     assert call(T=0) == GQ_OK  # no tokens: no-op
+
+
+def test_route_topk_plan_validation(lib):
+    f = lib.gq_route_topk_plan
+    sz = ctypes.c_size_t()
+    assert lib.gq_matvec_id_workspace(128, 8, 8, 0, ctypes.byref(sz)) == GQ_OK
+    need = sz.value
+    ok = [A, 8, 128, 8, A, A, A, need, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a3=0) == GQ_ERR_SHAPE
+    assert call(a3=129) == GQ_ERR_SHAPE      # top_k > n_experts
+    assert call(a1=129) == GQ_ERR_SHAPE      # 129 * 8 slots > 1024
+    assert call(a2=5000, a1=1) == GQ_ERR_UNSUPPORTED
+    for i in (0, 4, 5, 6):
+        assert call(**{"a%d" % i: None}) == GQ_ERR_NULL, i
+        assert call(**{"a%d" % i: MIS}) == GQ_ERR_ALIGN, i
+    assert call(a7=need - 1) == GQ_ERR_WORKSPACE
+    assert call(a1=0, a0=None, a4=None, a5=None, a6=None) == GQ_OK  # no tokens: no-op

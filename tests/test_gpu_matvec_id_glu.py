@@ -240,3 +240,52 @@ def test_glu_id_max_slots(gq, orc):
     ref, bound = glu_ref(orc, "q4_0", gate, up, E, N, K, ids, x, "silu", "bf16")
     check(h.float().cpu().numpy(), ref, bound, "S=1024")
     assert gq.gq_matvec_id_check(ws) == 0
+
+
+@pytest.mark.parametrize("T", [8, 64])
+def test_route_topk_plan_feeds_the_layer(gq, orc, T):
+    """gq_route_topk_plan: ids and weights bit-identical to gq_route_topk's, and
+    a table in ws that the gated unit and the weighted down projection use
+    without ids, giving their results with ids bit for bit; the products of
+    the tableless calls are also within the oracle's bounds."""
+    E, H, F, k = 128, 2816, 704, 8
+    g = synth.rng(0x67510004, 500 + T)
+    logits = dev(synth.router_logits(g, T, E))
+    ids_a = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    rw_a = torch.empty((T, k), device="cuda")
+    gq.gq_route_topk(logits, k, ids_a, rw_a)
+    ws = torch.empty(gq.gq_matvec_id_workspace(E, T, k, H), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xCD)
+    ids_b = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    rw_b = torch.full((T, k), float("nan"), device="cuda")
+    gq.gq_route_topk_plan(logits, k, ids_b, rw_b, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids_a, ids_b)
+    assert torch.equal(rw_a.view(torch.int32), rw_b.view(torch.int32))
+    x = dev(synth.normal_f32(g, (T, H)))
+    gate = dev(synth.weight("q4_0", synth.rng(0x67510004, 1), E * F, H))
+    up = dev(synth.weight("q4_0", synth.rng(0x67510004, 2), E * F, H))
+    down = dev(synth.weight("q4_0", synth.rng(0x67510004, 3), E * H, F))
+    # tableless calls on the routed table
+    h = torch.full((T, k, F), float("nan"), device="cuda", dtype=torch.bfloat16)
+    gq.gq_matvec_id_glu("q4_0", gate, up, E, F, H, (T, k), x, "silu", h, ws)
+    y = torch.full((T, H), float("nan"), device="cuda")
+    gq.gq_matvec_id("q4_0", down, E, H, F, (T, k), h, True, y, ws, rw_b)
+    yg = torch.full((T, k, F), float("nan"), device="cuda")
+    gq.gq_matvec_id("q4_0", gate, E, F, H, (T, k), x, False, yg, ws)
+    # the same calls building their own tables
+    ws2 = torch.empty_like(ws)
+    h2 = torch.full((T, k, F), float("nan"), device="cuda", dtype=torch.bfloat16)
+    gq.gq_matvec_id_glu("q4_0", gate, up, E, F, H, ids_a, x, "silu", h2, ws2)
+    y2 = torch.full((T, H), float("nan"), device="cuda")
+    gq.gq_matvec_id("q4_0", down, E, H, F, ids_a, h2, True, y2, ws2, rw_a)
+    yg2 = torch.full((T, k, F), float("nan"), device="cuda")
+    gq.gq_matvec_id("q4_0", gate, E, F, H, ids_a, x, False, yg2, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(h.view(torch.int16), h2.view(torch.int16))
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    assert torch.equal(yg.view(torch.int32), yg2.view(torch.int32))
+    ids = ids_a.cpu().numpy()
+    yref, sa = orc.matvec_id("q4_0", gate.cpu().numpy(), E, F, H, ids, x.cpu().numpy(), False)
+    err = np.abs(yg.cpu().numpy().astype(np.float64) - yref)
+    assert np.all(err <= 1e-3 * sa)
