@@ -8,6 +8,8 @@
     python bench.py --traffic-summary FETCH_DIR WRITE_DIR   (writes profiles/<kernel>_traffic.txt)
     python bench.py --mfma-summary DIR                      (writes profiles/<prefill>_mfma_counters.txt)
     python bench.py --stats-summary DIR OUT.txt             (rocprofv3 --stats CSV -> text summary)
+    python bench.py --abba LIB_A LIB_B [--rounds R] [--workload headline|moe|prefill]
+                                          (two builds of libgq.so compared A-B-B-A in fresh processes)
 
 The step (the headline workload) is one decoder layer of Q4_K products at
 batch 1, hidden 2560: q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up
@@ -82,6 +84,10 @@ def parse():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--mfma-summary", metavar="DIR")
     ap.add_argument("--stats-summary", nargs=2, metavar=("DIR", "OUT"))
+    ap.add_argument("--abba", nargs=2, metavar=("LIB_A", "LIB_B"))
+    ap.add_argument("--rounds", type=int, default=4, help="A-B-B-A blocks for --abba")
+    ap.add_argument("--workload", default="headline", help="workload --abba / --measure-only time")
+    ap.add_argument("--measure-only", action="store_true", help="time --workload alone (one JSON line)")
     return ap.parse_args()
 
 
@@ -354,6 +360,8 @@ def main():
         return mfma_summary(args.mfma_summary)
     if args.stats_summary:
         return stats_summary(*args.stats_summary)
+    if args.abba:
+        return abba(*args.abba, rounds=args.rounds, workload=args.workload)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the products shard by "
               "output rows across GPUs).  Run with --gpus 1.", file=sys.stderr)
@@ -377,6 +385,10 @@ def main():
 
     if args.floor_only:
         return floor_only(torch, stream)
+    if args.measure_only:
+        print(json.dumps({"workload": args.workload,
+                          "ms_per_step": measure(torch, gq, dev, stream, t_, args.workload)}), flush=True)
+        return
     if args.context_only:
         print(json.dumps({"context": bench_context(torch, gq, dev, stream, t_)}), flush=True)
         return
@@ -519,6 +531,95 @@ def main():
         "context": context,
     }
     print(json.dumps(out))
+
+
+def measure(torch, gq, dev, stream, t_, workload: str) -> float:
+    """ms per step of one workload, timed as in the full run (median of the
+    replays; the headline and MoE layers over rotated weight copies)."""
+    if workload == "headline":
+        launches = WL.HEADLINE
+        host = {L.name: L.weight() for L in launches}
+        nc = n_copies(WL.layer_bytes("dense"))
+        cps = [{k: t_(v) for k, v in host.items()} for _ in range(nc)]
+        xs = {L.name: t_(L.x()) for L in launches}
+        ys = {L.name: torch.empty(1, L.N, device=dev) for L in launches}
+
+        def run():
+            for c in cps:
+                for L in launches:
+                    gq.gq_matvec(L.t, c[L.name], L.N, L.K, xs[L.name], ys[L.name], stream)
+
+        return float(np.median(Timer(torch, run, stream).replays(2 * MIN_REPS))) / nc
+    if workload == "moe":
+        m = WL.MOE
+        ex = m.experts()
+        nb = sum(v.nbytes for v in ex.values())
+        cps = [{k: t_(v) for k, v in ex.items()} for _ in range(n_copies(nb))]
+        lg, x4 = t_(m.logits()), t_(m.x())
+        ids = torch.empty((m.T, m.k), dtype=torch.int32, device=dev)
+        rw = torch.empty((m.T, m.k), device=dev)
+        hb = torch.empty((m.T, m.k, m.F), device=dev, dtype=torch.bfloat16)
+        yd = torch.empty(m.T, m.H, device=dev)
+        ws = torch.empty(gq.gq_matvec_id_workspace(m.E, m.T, m.k, m.H), dtype=torch.uint8, device=dev)
+
+        def run():
+            for c in cps:
+                gq.gq_route_topk_plan(lg, m.k, ids, rw, ws, stream)
+                gq.gq_matvec_id_glu(m.t, c["gate"], c["up"], m.E, m.F, m.H, (m.T, m.k), x4, "silu", hb, ws, stream)
+                gq.gq_matvec_id(m.t, c["down"], m.E, m.H, m.F, (m.T, m.k), hb, True, yd, ws, rw, stream)
+
+        return float(np.median(Timer(torch, run, stream).replays(2 * MIN_REPS))) / len(cps)
+    if workload == "prefill":
+        L = PREFILL
+        W5, X5 = t_(L.weight()), t_(L.x_bf16_bits().view(np.int16)).view(torch.bfloat16)
+        Y5 = torch.empty(L.M, L.N, device=dev)
+        return float(np.median(Timer(torch, lambda: gq.gq_matmul(L.t, W5, L.N, L.K, X5, Y5, stream),
+                                     stream).replays(30, warm=60)))
+    raise SystemExit("unknown workload %r (headline, moe, prefill)" % workload)
+
+
+def abba(lib_a: str, lib_b: str, rounds: int, workload: str):
+    """Compare two builds of libgq.so on one workload: `rounds` blocks of
+    A, B, B, A, each run a fresh process (bench.py --measure-only with
+    GQ_LIBGQ naming the build).  Reports the time ratio B / A with a 95%
+    confidence interval over the blocks and the noise floor, the largest
+    relative difference between two runs of the same build; a change is only
+    called faster or slower when the interval excludes 1 and the ratio is
+    further from 1 than that floor."""
+    import subprocess
+    libs = {"A": os.path.abspath(lib_a), "B": os.path.abspath(lib_b)}
+    runs = {"A": [], "B": []}
+    blocks = []
+    for r in range(rounds):
+        blk = {"A": [], "B": []}
+        for which in "ABBA":
+            env = dict(os.environ, GQ_LIBGQ=libs[which])
+            out = subprocess.run([sys.executable, os.path.abspath(__file__), "--measure-only", "--workload", workload],
+                                 env=env, capture_output=True, text=True, timeout=600)
+            if out.returncode != 0:
+                raise SystemExit("run %s failed:\n%s" % (which, out.stderr[-2000:]))
+            ms = json.loads(out.stdout.strip().splitlines()[-1])["ms_per_step"]
+            runs[which].append(ms)
+            blk[which].append(ms)
+            print("block %d %s: %.5f ms" % (r, which, ms), file=sys.stderr, flush=True)
+        blocks.append(sum(blk["B"]) / sum(blk["A"]))
+    ratio = sum(runs["B"]) / sum(runs["A"])
+    n = len(blocks)
+    mean = sum(blocks) / n
+    sd = (sum((b - mean) ** 2 for b in blocks) / (n - 1)) ** 0.5 if n > 1 else float("nan")
+    t975 = {1: 12.706, 2: 4.303, 3: 3.182, 4: 2.776, 5: 2.571, 6: 2.447, 7: 2.365, 8: 2.306, 9: 2.262}.get(n - 1, 2.0)
+    half = t975 * sd / n ** 0.5
+    noise = max((max(v) - min(v)) / (sum(v) / len(v)) for v in runs.values())
+    if mean + half < 1 and 1 - ratio > noise:
+        verdict = "B faster"
+    elif mean - half > 1 and ratio - 1 > noise:
+        verdict = "B slower"
+    else:
+        verdict = "no difference beyond the noise"
+    print(json.dumps({"workload": workload, "lib_a": libs["A"], "lib_b": libs["B"], "blocks": n,
+                      "ms_a": runs["A"], "ms_b": runs["B"], "ratio_b_over_a": round(ratio, 4),
+                      "ci95": [round(mean - half, 4), round(mean + half, 4)], "noise_floor": round(noise, 4),
+                      "verdict": verdict}))
 
 
 def cpu_info() -> tuple[str, int, int]:

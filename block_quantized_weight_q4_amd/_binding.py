@@ -14,7 +14,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_PKG, "libgq.so")
+# GQ_LIBGQ names another build of the library (bench.py --abba compares two
+# builds in alternating fresh processes this way)
+lib_path = os.environ.get("GQ_LIBGQ") or os.path.join(_PKG, "libgq.so")
 
 if not os.path.exists(lib_path):
     raise ImportError(
@@ -36,10 +38,13 @@ _lib.gq_matvec.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I32, P, P
 _lib.gq_matvec_id_workspace.argtypes = [I32, I32, I32, I64, ctypes.POINTER(SZ)]
 _lib.gq_matvec_id.argtypes = [ctypes.c_int, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, I32, P, P, P, SZ, P]
 _lib.gq_matvec_id_check.argtypes = [P, P, ctypes.POINTER(I32)]
-_lib.gq_matvec_id_noalloc.argtypes = [ctypes.c_int, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, I32, P, P, P]
+if hasattr(_lib, "gq_matvec_id_noalloc"):  # (older builds, compared by bench.py --abba, lack the newer calls)
+    _lib.gq_matvec_id_noalloc.argtypes = [ctypes.c_int, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, I32, P, P,
+                                          P]
 _lib.gq_matmul.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I64, I64, P, I64, P]
 _lib.gq_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
-_lib.gq_route_topk_plan.argtypes = [P, I32, I32, I32, P, P, P, SZ, P]
+if hasattr(_lib, "gq_route_topk_plan"):
+    _lib.gq_route_topk_plan.argtypes = [P, I32, I32, I32, P, P, P, SZ, P]
 _lib.gq_matvec_glu.argtypes = [ctypes.c_int, P, P, I64, I64, P, ctypes.c_int, I32, ctypes.c_int, P, ctypes.c_int, P]
 _lib.gq_matvec_id_glu.argtypes = [ctypes.c_int, P, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, ctypes.c_int, P,
                                   ctypes.c_int, P, SZ, P]
@@ -47,7 +52,8 @@ ACTS = {"silu": 0, "gelu_tanh": 1}
 for _f in ("gq_block_info", "gq_dequant", "gq_matvec", "gq_matvec_id_workspace", "gq_matvec_id", "gq_matvec_id_noalloc",
            "gq_matvec_id_check", "gq_matmul", "gq_route_topk", "gq_route_topk_plan", "gq_matvec_glu",
            "gq_matvec_id_glu"):
-    getattr(_lib, _f).restype = ctypes.c_int
+    if hasattr(_lib, _f):
+        getattr(_lib, _f).restype = ctypes.c_int
 
 
 class GqError(RuntimeError):
