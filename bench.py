@@ -198,22 +198,35 @@ def traffic_summary(fetch_dir: str, write_dir: str):
     print("\n".join(text))
 
 
+def _short_kernel_name(name: str) -> str:
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    return name.split("(")[0]
+
+
 def mfma_summary(d: str):
-    """MFMA busy cycles of the prefill kernel against the cycles its CUs were
-    busy: utilisation = SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES (both
-    summed over the CUs; per CU the matrix core is counted busy for each
-    cycle any of its MFMA pipelines works)."""
+    """Matrix-core utilisation of the prefill kernel from one counter pass.
+
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over every SIMD of the chip (it equals
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops / 1024 flops per SIMD cycle, the
+    bf16 rate of one SIMD), and GRBM_GUI_ACTIVE over the 8 XCDs.  The cycles
+    the matrix cores could have worked are therefore
+    GRBM_GUI_ACTIVE / 8 x 1024 SIMDs, and the utilisation is the ratio.  It is
+    counted in the clock the chip ran at, which under this load is below the
+    2.4 GHz of the published peak; the time the kernel takes gives that clock."""
     means, counts = _counter_means(d)
     ks = sorted({k[0] for k in means if "k_matmul" in k[0]})
     assert len(ks) >= 1, ks
     kname = ks[0]
     v = {c: means.get((kname, c)) for c in MFMA_COUNTERS}
     n = counts.get((kname, MFMA_COUNTERS[0]), 0)
-    util = v["SQ_VALU_MFMA_BUSY_CYCLES"] / v["SQ_BUSY_CU_CYCLES"] if v["SQ_BUSY_CU_CYCLES"] else float("nan")
+    xcds, simds = 8, 1024
+    cycles = v["GRBM_GUI_ACTIVE"] / xcds
+    util = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * simds) if cycles else float("nan")
+    flops = v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
     text = ["# MFMA counters of the Q4_K prefill product (%d x %d x %d, bf16 activations)" % (PREFILL.M, PREFILL.N,
                                                                                            PREFILL.K),
             "",
-            "kernel: %s" % kname.split("(")[0].replace("void ", ""),
+            "kernel: %s" % _short_kernel_name(kname),
             "source_sha256: %s" % source_hash(MFMA_SOURCES),
             "command (from the repository root, on the GPU host):",
             "  timeout -s KILL 60 rocprofv3 --pmc %s --output-format csv -d <DIR> -- python3 bench.py --prefill-pass"
@@ -222,7 +235,10 @@ def mfma_summary(d: str):
             "",
             "dispatches averaged: %d" % n] + ["%s: %.6g" % (c, v[c]) for c in MFMA_COUNTERS] + [
             "",
-            "mfma_busy_fraction: %.4f   (SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES)" % util]
+            "MFMA flops per dispatch (MOPS x 512): %.4g (2 x M x N x K with M padded to whole 256-row tiles: %.4g)"
+            % (flops, 2.0 * -(-PREFILL.M // 256) * 256 * PREFILL.N * PREFILL.K),
+            "kernel cycles (GRBM_GUI_ACTIVE / %d XCDs): %.4g" % (xcds, cycles),
+            "mfma_busy_fraction: %.4f   (SQ_VALU_MFMA_BUSY_CYCLES / (kernel cycles x %d SIMDs))" % (util, simds)]
     with open(MFMA_FILE, "w") as f:
         f.write("\n".join(text) + "\n")
     print("\n".join(text))
