@@ -443,38 +443,61 @@ __global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W
 namespace {
 
 // 8-wavefront variant: wavefront (wm, wn) = (wave / 4, wave % 4) owns a
-// 128 x 64 quarter-column of the 256 x 256 tile (4 x 2 blocks of 32x32x16
-// MFMAs, 128 accumulators), so two wavefronts share each SIMD.
-template <int TYPE>
-__global__ __launch_bounds__(512, 1) void k_matmul8(const uint8_t* __restrict__ W, int64_t N, int64_t K,
-                                                    const uint16_t* __restrict__ X, int64_t M, int64_t ldx,
-                                                    float* __restrict__ Y, int64_t ldy, int gn, int n_full,
-                                                    int s_split) {
+// 128 x (NT / 4) part of the 256 x NT tile (4 x NT/128 blocks of 32x32x16
+// MFMAs), so two wavefronts share each SIMD.  NT = 256 for whole tiles.
+// NT = 128 runs the tiles of a last, partial round as quarters: workgroup
+// n_full + q takes N half (q / 2) % 2 and K half q % 2 of tile n_full + q / 4
+// and adds its partial tile into Y (zeroed there beforehand), so that round
+// takes about a quarter of a whole tile's time instead of half.  Both kinds
+// of workgroup are one launch, so the quarters start on the CUs that the
+// whole tiles free.
+template <int TYPE, int NT>
+__device__ __forceinline__ void matmul8_tile(const uint8_t* __restrict__ W, int64_t N, int64_t K,
+                                             const uint16_t* __restrict__ X, int64_t M, int64_t ldx,
+                                             float* __restrict__ Y, int64_t ldy, int gn, int n_full, int s_split,
+                                             int wg) {
     using F = WF<TYPE>;
     struct SR8 {
         u32x4 x[4];
         typename F::Regs w;
     };
+    constexpr int JB = NT / 128;                  // 32-column blocks per wavefront
+    constexpr int TBUF = (BM + NT) * ROWB;        // one stage buffer: X rows then W rows
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int S = (int)((K + BK - 1) / BK);
-    const int wg = (int)blockIdx.x;
-    const bool split = wg >= n_full;
-    const int tile = split ? n_full + ((wg - n_full) >> 1) : wg;
-    const int s0 = split && ((wg - n_full) & 1) ? s_split : 0;
-    const int s1 = split && !((wg - n_full) & 1) ? s_split : S;
-    const int64_t n0 = (int64_t)(tile % gn) * BN, m0 = (int64_t)(tile / gn) * BM;
+    bool split;
+    int tile, s0, s1;
+    int64_t n0;
+    if constexpr (NT == 256) {
+        split = wg >= n_full;
+        tile = split ? n_full + ((wg - n_full) >> 1) : wg;
+        s0 = split && ((wg - n_full) & 1) ? s_split : 0;
+        s1 = split && !((wg - n_full) & 1) ? s_split : S;
+        n0 = (int64_t)(tile % gn) * BN;
+    } else {
+        const int q = wg - n_full;
+        split = true;
+        tile = n_full + (q >> 2);
+        s0 = (q & 1) ? s_split : 0;
+        s1 = (q & 1) ? S : s_split;
+        n0 = (int64_t)(tile % gn) * BN + NT * ((q >> 1) & 1);
+        if (n0 >= N) return;  // the second half of a last, narrow column of tiles: nothing to compute
+    }
+    const int64_t m0 = (int64_t)(tile / gn) * BM;
     const uint32_t row_bytes = (uint32_t)((K / F::QK) * F::BB);
 
-    const int64_t rows_x = M - m0 < BM ? M - m0 : BM, rows_w = N - n0 < BN ? N - n0 : BN;
+    const int64_t rows_x = M - m0 < BM ? M - m0 : BM, rows_w = N - n0 < NT ? N - n0 : NT;
     const Rsrc xr = make_rsrc(X + m0 * ldx, (uint32_t)(rows_x * ldx * 2));
     const Rsrc wr = make_rsrc(W + n0 * (int64_t)row_bytes, (uint32_t)rows_w * row_bytes);
     const int xrow = tid >> 3, xchunk = tid & 7;
     const uint32_t xstride = (uint32_t)(64 * ldx * 2);
     const uint32_t xoff = (uint32_t)xrow * (uint32_t)(ldx * 2);
-    const int wrow = tid & 255, whalf = wave >> 2;
+    // W: thread tid expands row tid % NT; with NT = 256 wavefronts 0-3 take
+    // slices 0, 1 and 4-7 slices 2, 3; with NT = 128 slice tid / 128
+    const int wrow = tid & (NT - 1), wpart = NT == 256 ? wave >> 2 : tid >> 7;
     const uint32_t woff = (uint32_t)wrow * row_bytes;
 
     auto load_stage = [&](int s, SR8& r) {
@@ -486,45 +509,53 @@ __global__ __launch_bounds__(512, 1) void k_matmul8(const uint8_t* __restrict__ 
         F::load(wr, woff, s, ok, (int64_t)s * BK + 32 < K, r.w);
     };
     auto store_x = [&](const SR8& r, int buf, int i) {
-        uint8_t* xs = lds + buf * BUF + (xrow + 64 * i) * ROWB + 16 * xchunk;
+        uint8_t* xs = lds + buf * TBUF + (xrow + 64 * i) * ROWB + 16 * xchunk;
         *reinterpret_cast<u32x4*>(xs) = r.x[i];
     };
     auto store_w = [&](int s, const SR8& r, const typename F::Scl& sc, int buf, int j) {
-        uint8_t* ws = lds + buf * BUF + BM * ROWB + wrow * ROWB;
+        uint8_t* ws = lds + buf * TBUF + BM * ROWB + wrow * ROWB;
         u32x4 lo, hi;
         F::expand(r.w, sc, s, j, lo, hi);
         reinterpret_cast<u32x4*>(ws)[j] = lo;
         reinterpret_cast<u32x4*>(ws + 64)[j] = hi;
     };
+    // the stage's W slices this thread writes while k step ks runs
+    auto store_w_at = [&](int ks, int s, const SR8& r, const typename F::Scl& sc, int buf) {
+        if constexpr (NT == 256) {
+            if ((ks & 1) == 0) store_w(s, r, sc, buf, 2 * wpart + (ks >> 1));
+        } else {
+            if (ks == 0) store_w(s, r, sc, buf, wpart);
+        }
+    };
 
-    f32x16 acc[4][2];
+    f32x16 acc[4][JB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < JB; ++j) acc[i][j] = f32x16{};
 
     const int fr = lane & 31, fk = 8 * (lane >> 5);
     const uint32_t a_base = (uint32_t)((wm * 128 + fr) * ROWB + fk * 2);
-    const uint32_t b_base = (uint32_t)(BM * ROWB + (wn * 64 + fr) * ROWB + fk * 2);
+    const uint32_t b_base = (uint32_t)(BM * ROWB + (wn * 32 * JB + fr) * ROWB + fk * 2);
 
     auto stage_body = [&](int s, SR8& nxt) {
         const int cur = (s - s0) & 1;
-        const uint8_t* buf = lds + cur * BUF;
+        const uint8_t* buf = lds + cur * TBUF;
         const typename F::Scl sc = F::scales(nxt.w, s + 1);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 a[4], b[2];
+            bf16x8 a[4], b[JB];
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(buf + a_base + i * 32 * ROWB + ks * 32);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const bf16x8*>(buf + b_base + j * 32 * ROWB + ks * 32);
+            for (int j = 0; j < JB; ++j) b[j] = *reinterpret_cast<const bf16x8*>(buf + b_base + j * 32 * ROWB + ks * 32);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < JB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
             store_x(nxt, cur ^ 1, ks);
-            if ((ks & 1) == 0) store_w(s + 1, nxt, sc, cur ^ 1, 2 * whalf + (ks >> 1));
+            store_w_at(ks, s + 1, nxt, sc, cur ^ 1);
         }
         load_stage(s + 3, nxt);
         lds_barrier();
@@ -537,8 +568,8 @@ __global__ __launch_bounds__(512, 1) void k_matmul8(const uint8_t* __restrict__ 
         const typename F::Scl sc0 = F::scales(r0.w, s0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) store_x(r0, 0, i);
-        store_w(s0, r0, sc0, 0, 2 * whalf);
-        store_w(s0, r0, sc0, 0, 2 * whalf + 1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) store_w_at(ks, s0, r0, sc0, 0);
         load_stage(s0 + 2, r0);
         lds_barrier();
     }
@@ -549,8 +580,8 @@ __global__ __launch_bounds__(512, 1) void k_matmul8(const uint8_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t n = n0 + wn * 64 + 32 * j + (lane & 31);
+        for (int j = 0; j < JB; ++j) {
+            const int64_t n = n0 + wn * 32 * JB + 32 * j + (lane & 31);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -561,6 +592,18 @@ __global__ __launch_bounds__(512, 1) void k_matmul8(const uint8_t* __restrict__ 
             }
         }
     }
+}
+
+template <int TYPE>
+__global__ __launch_bounds__(512, 1) void k_matmul8(const uint8_t* __restrict__ W, int64_t N, int64_t K,
+                                                    const uint16_t* __restrict__ X, int64_t M, int64_t ldx,
+                                                    float* __restrict__ Y, int64_t ldy, int gn, int n_full,
+                                                    int s_split, int quarters) {
+    const int wg = (int)blockIdx.x;
+    if (quarters && wg >= n_full)
+        matmul8_tile<TYPE, 128>(W, N, K, X, M, ldx, Y, ldy, gn, n_full, s_split, wg);
+    else
+        matmul8_tile<TYPE, 256>(W, N, K, X, M, ldx, Y, ldy, gn, n_full, s_split, wg);
 }
 
 // Zeroes the output tiles from n_full on (clipped to M x N) before their two
@@ -589,14 +632,18 @@ hipError_t launch(const void* W, int64_t N, int64_t K, const void* X, int64_t M,
     const int64_t gn = (N + BN - 1) / BN, gm = (M + BM - 1) / BM;
     const int64_t tiles = gn * gm;
     if (tiles > 0x3fffffff) return hipErrorInvalidValue;
-    // one workgroup per CU (the LDS holds one): split a short last round
+    // one workgroup per CU (the LDS holds one).  A last round that would
+    // fill only part of the GPU runs its tiles as K halves (two workgroups
+    // per tile) or, for the 8-wavefront kernel when four per tile still fit
+    // in one round, as N and K quarters.
     const int cus = gqk_cu_count();
     const int64_t tail = tiles % cus;
     const int S = (int)((K + BK - 1) / BK);
-    const bool split = tiles > cus && tail > 0 && tail <= cus / 2 && S >= 4;
-    const int n_full = (int)(split ? tiles - tail : tiles);
-    const int64_t grid = split ? n_full + 2 * tail : tiles;
-    if (split) {
+    const bool part = tiles > cus && tail > 0 && S >= 4;
+    const bool quarters = TYPE != T_Q6_K && part && 4 * tail <= cus;
+    const bool halves = !quarters && part && tail <= cus / 2;
+    const int n_full = (int)(part && (quarters || halves) ? tiles - tail : tiles);
+    if (n_full < tiles) {
         hipLaunchKernelGGL(k_zero_tiles, dim3(BM / 4, (unsigned)tail), dim3(256), 0, s, Y, ldy, M, N, (int)gn, n_full);
         hipError_t e0 = hipGetLastError();
         if (e0 != hipSuccess) return e0;
@@ -605,13 +652,15 @@ hipError_t launch(const void* W, int64_t N, int64_t K, const void* X, int64_t M,
     // eight wavefronts (two per SIMD) where the format's registers allow
     // it; Q6_K's larger stage registers keep the four-wavefront kernel
     if constexpr (TYPE != T_Q6_K) {
+        const int64_t grid = halves ? n_full + 2 * tail : quarters ? n_full + 4 * tail : tiles;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul8<TYPE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k_matmul8<TYPE>, dim3((unsigned)grid), dim3(512), LDS_BYTES, s,
                            static_cast<const uint8_t*>(W), N, K, static_cast<const uint16_t*>(X), M, ldx, Y, ldy,
-                           (int)gn, n_full, S / 2);
+                           (int)gn, n_full, S / 2, quarters ? 1 : 0);
     } else {
+        const int64_t grid = halves ? n_full + 2 * tail : tiles;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul<TYPE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;

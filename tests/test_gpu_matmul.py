@@ -150,3 +150,40 @@ def test_matmul_tail_round_split_along_k(gq, orc, t):
     check_bound(Y[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, sa, "rows")
     refc, sac = orc.matmul_cols(t, W, N, K, xf, cols)
     check_bound(Y[:, torch.from_numpy(cols).cuda()].cpu().numpy(), refc, sac, "cols")
+
+
+@pytest.mark.parametrize("t,rem,K", [("q4_k", 100, 1024), ("q4_k", 200, 1024), ("q5_k", 100, 1024),
+                                     ("q4_0", 200, 1056), ("q6_k", 100, 1024)])
+def test_matmul_last_round_in_quarters(gq, orc, t, rem, K):
+    """M = 300 rows (two rows of tiles) and N chosen so that the tile count is
+    the CU count plus 4: the last round holds 4 tiles, which the 8-wavefront
+    kernel runs as N and K quarters (Q6_K as K halves).  The last column of
+    tiles is rem < 256 wide, so its second N quarter is empty (rem <= 128) or
+    partial.  Y is NaN-filled: every output must be written; two calls give
+    the same bits; sampled rows and columns of the last tiles against the
+    oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert cus % 2 == 0, cus
+    M, gn = 300, cus // 2 + 2
+    N = (gn - 1) * 256 + rem
+    g = synth.rng(0x67510005, 900 + rem + K + ("q4_k", "q6_k", "q4_0", "q5_k").index(t))
+    W = synth.weight(t, g, N, K)
+    xf, X = make_X(g, M, K)
+    Wd = dev(W)
+    Y = torch.full((M, N), float("nan"), device="cuda")
+    gq.gq_matmul(t, Wd, N, K, X, Y)
+    Y2 = torch.full((M, N), float("nan"), device="cuda")
+    gq.gq_matmul(t, Wd, N, K, X, Y2)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Y).all())
+    assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32))
+    s = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], s.choice(np.arange(257, M - 1), 8, replace=False)]))
+    last = (gn - 4) * 256  # first column of the last round's tiles
+    cols = np.unique(np.concatenate([[0, last - 1, last, N - 1, N - rem, N - rem + 127],
+                                     s.choice(np.arange(last + 1, N - 1), 10, replace=False)]))
+    cols = cols[cols < N]
+    ref, sa = orc.matmul_rows(t, W, N, K, xf, rows)
+    check_bound(Y[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, sa, "rows")
+    refc, sac = orc.matmul_cols(t, W, N, K, xf, cols)
+    check_bound(Y[:, torch.from_numpy(cols).cuda()].cpu().numpy(), refc, sac, "cols")
