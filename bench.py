@@ -318,6 +318,22 @@ class Timer:
         return sum(r) / len(r)
 
 
+def eager_ms(torch, fn, stream, reps: int = 30, warm: int = 60) -> list[float]:
+    """ms of each of `reps` back-to-back eager calls of fn on `stream` (events
+    between them), for library calls that are not captured in a graph."""
+    with torch.cuda.stream(stream):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            fn()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+
 def n_copies(nbytes: int) -> int:
     return max(2, -(-ROTATE_BYTES // nbytes))
 
@@ -491,6 +507,26 @@ def main():
                        "frac_bf16_dense_peak": round(tf / BF16_PEAK_TFLOPS, 4),
                        "mfma_busy_fraction": read_summary(MFMA_FILE, "mfma_busy_fraction", MFMA_SOURCES),
                        "tokens_per_s": round(L.M / (ms_mm * 1e-3), 1)}
+            # context: the same product with all-zero activations (the time
+            # depends on the data when the chip runs at its power limit), and
+            # the vendor's plain bf16 GEMM (torch.matmul -> hipBLASLt, weights
+            # already dense bf16, bf16 output) at this shape
+            X0 = torch.zeros_like(X5)
+            t0 = Timer(torch, lambda: gq.gq_matmul(L.t, W5, L.N, L.K, X0, Y5, stream), stream)
+            ms_zero = float(np.median(t0.replays(30, warm=60)))
+            del t0, X0
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(WL.S_PREFILL + 1000)
+            WT = torch.randn(L.K, L.N, device=dev, generator=gen).to(torch.bfloat16).contiguous()
+            ms_blas = float(np.median(eager_ms(torch, lambda: torch.matmul(X5, WT), stream)))
+            del WT
+            prefill["context"] = {
+                "ms_with_zero_activations": round(ms_zero, 4),
+                "vendor_bf16_gemm": {"what": "torch.matmul(X bf16 [M,K], W^T bf16 [K,N]) -> bf16 (hipBLASLt), "
+                                             "random weights, eager, median of 30 after 60 warm-up calls",
+                                     "ms": round(ms_blas, 4),
+                                     "TFLOPs": round(flops / (ms_blas * 1e-3) / 1e12, 2),
+                                     "fused_q4_k_over_vendor_bf16": round(ms_blas / ms_mm, 4)}}
         else:
             others["%s_prefill_%dx%dx%d_bf16" % (L.t, L.M, L.N, L.K)] = {"ms": round(ms_mm, 4),
                                                                          "TFLOPs": round(tf, 2)}
@@ -585,13 +621,15 @@ def measure(torch, gq, dev, stream, t_, workload: str) -> float:
                 gq.gq_matvec_id(m.t, c["down"], m.E, m.H, m.F, (m.T, m.k), hb, True, yd, ws, rw, stream)
 
         return float(np.median(Timer(torch, run, stream).replays(2 * MIN_REPS))) / len(cps)
-    if workload == "prefill":
-        L = PREFILL
+    if workload.startswith("prefill"):
+        # "prefill" is the Q4_K product; "prefill:q6_k" / "prefill:q4_0" the others
+        fmt = workload.split(":")[1] if ":" in workload else PREFILL.t
+        L = next(m for m in WL.TIMED_MATMUL if m.t == fmt)
         W5, X5 = t_(L.weight()), t_(L.x_bf16_bits().view(np.int16)).view(torch.bfloat16)
         Y5 = torch.empty(L.M, L.N, device=dev)
         return float(np.median(Timer(torch, lambda: gq.gq_matmul(L.t, W5, L.N, L.K, X5, Y5, stream),
                                      stream).replays(30, warm=60)))
-    raise SystemExit("unknown workload %r (headline, moe, prefill)" % workload)
+    raise SystemExit("unknown workload %r (headline, moe, prefill, prefill:q6_k, prefill:q4_0)" % workload)
 
 
 def abba(lib_a: str, lib_b: str, rounds: int, workload: str):
