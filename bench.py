@@ -80,6 +80,10 @@ def parse():
                     help="only the context workloads (one JSON line of them; for kernel traces)")
     ap.add_argument("--floor-only", action="store_true", help="only the stream-read kernel at the headline sizes")
     ap.add_argument("--pmc-pass", action="store_true", help="run the dominant kernel 8x and one copy kernel")
+    ap.add_argument("--pmc-moe-pass", metavar="META_JSON",
+                    help="run the fused MoE layer (8 and 64 tokens, 3 times each) and one copy kernel; "
+                         "writes each layer's routing facts to META_JSON")
+    ap.add_argument("--moe-traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "META_JSON"))
     ap.add_argument("--prefill-pass", action="store_true", help="run the Q4_K prefill product a few times")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--mfma-summary", metavar="DIR")
@@ -107,6 +111,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "matvec_q4k_gateup_19456x2560_b1_t
 KERNEL_SOURCES = ["gq_device.h", "gq_gemv_core.h", "gq_matvec.hip"]
 PREFILL = WL.TIMED_MATMUL[0]
 MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_q4k_3015x17408x5120_mfma_counters.txt")
+MOE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_q4_0_128x_h2816_f704_top8_traffic.txt")
+MOE_SOURCES = ["gq_device.h", "gq_gemv_core.h", "gq_route_core.h", "gq_matvec_id.hip"]
 MFMA_SOURCES = ["gq_device.h", "gq_matmul.hip"]
 MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16"]
 
@@ -131,6 +137,111 @@ def pmc_pass():
     torch.add(src, 0.0, out=dst)
     torch.cuda.synchronize()
     print("pmc pass done", flush=True)
+
+
+def pmc_moe_pass(meta_path: str):
+    """The fused MoE layer (router + group table, gated unit, weighted down
+    product on that table) on one copy of the experts, 3 times at 8 tokens and
+    3 times at 64 tokens (top 8 of 128), then the copy kernel of pmc_pass.
+    meta_path gets, per layer in launch order, the token count, the distinct
+    experts the router chose, the group count of the table and the bytes of
+    one expert matrix, for --moe-traffic-summary."""
+    import torch
+    import block_quantized_weight_q4_amd as gq
+    dev = torch.device("cuda:0")
+    base = WL.MOE
+    ex = {k: torch.from_numpy(v).to(dev) for k, v in base.experts().items()}
+    meta = []
+    for T in (8, 64):
+        m = WL.MoeLayer(T=T)
+        lg = torch.from_numpy(m.logits()).to(dev)
+        x = torch.from_numpy(m.x()).to(dev)
+        ids = torch.empty((T, m.k), dtype=torch.int32, device=dev)
+        rw = torch.empty((T, m.k), device=dev)
+        hb = torch.empty((T, m.k, m.F), device=dev, dtype=torch.bfloat16)
+        yd = torch.empty(T, m.H, device=dev)
+        ws = torch.zeros(gq.gq_matvec_id_workspace(m.E, T, m.k, m.H), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            gq.gq_route_topk_plan(lg, m.k, ids, rw, ws)
+            gq.gq_matvec_id_glu(m.t, ex["gate"], ex["up"], m.E, m.F, m.H, (T, m.k), x, "silu", hb, ws)
+            gq.gq_matvec_id(m.t, ex["down"], m.E, m.H, m.F, (T, m.k), hb, True, yd, ws, rw)
+            torch.cuda.synchronize()
+            hdr = ws[:8].view(torch.int32).cpu().numpy()
+            distinct = int(np.unique(ids.cpu().numpy()).size)
+            meta.append({"tokens": T, "top_k": m.k, "experts": m.E, "distinct_experts": distinct,
+                         "groups": int(hdr[1]), "invalid_ids": int(hdr[0]),
+                         "expert_matrix_bytes": int(ex["down"].numel() // m.E)})
+    src = torch.empty(COPY_BYTES // 4, device=dev).normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    with open(meta_path, "w") as f:
+        json.dump(meta, f)
+    print("moe pmc pass done", flush=True)
+
+
+def moe_traffic_summary(fetch_dir: str, write_dir: str, meta_path: str):
+    """HBM bytes of each fused MoE layer of --pmc-moe-pass (the sum over its
+    router, gated-unit and down-product dispatches, FETCH_SIZE and WRITE_SIZE
+    scaled by the copy kernel's calibration) against the bytes of the expert
+    matrices it had to read: once per distinct expert, and once per group of
+    the table (an expert with more than 8 slots is read once per 8)."""
+    import csv
+    import glob
+    meta = json.load(open(meta_path))
+    per_ctr = {}
+    for d, ctr in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        runs = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True),
+                      key=os.path.getmtime)
+        rows = [r for r in csv.DictReader(open(runs[-1])) if r["Counter_Name"] == ctr]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        cp = [float(r["Counter_Value"]) for r in rows
+              if "vectorized_elementwise_kernel" in r["Kernel_Name"] and "add" in r["Kernel_Name"].lower()]
+        assert len(cp) == 1, cp
+        factor = (COPY_BYTES / 1024.0) / cp[0]
+        layers, cur = [], None
+        for r in rows:
+            name = r["Kernel_Name"]
+            if "k_route_plan" in name:
+                cur = []
+                layers.append(cur)
+            if cur is not None and ("k_route_plan" in name or "k_experts" in name):
+                cur.append(float(r["Counter_Value"]) * 1024.0 * factor)
+        assert len(layers) == len(meta) and all(len(l) == 3 for l in layers), (len(layers), [len(l) for l in layers])
+        per_ctr[ctr] = (layers, factor)
+    out = ["# HBM traffic of the fused MoE layer (128 Q4_0 experts, hidden 2816, FFN 704, top 8) at 8 and 64 tokens",
+           "",
+           "kernels: k_route_plan (router + group table), k_experts GLU form (gate|up + SiLU, bf16 h),",
+           "k_experts weighted down product on the same table; one copy of the experts, so every layer",
+           "reads its experts from HBM or the last-level cache, not from L2 (4 MB per XCD)",
+           "source_sha256: %s" % source_hash(MOE_SOURCES),
+           "commands (from the repository root, on the GPU host):",
+           "  timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -- python3 bench.py "
+           "--pmc-moe-pass <DIR>/meta_fetch.json",
+           "  timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -- python3 bench.py "
+           "--pmc-moe-pass <DIR>/meta_write.json",
+           "  python bench.py --moe-traffic-summary <FETCH_DIR> <WRITE_DIR> <DIR>/meta_fetch.json",
+           "",
+           "calibration (copy kernel of %d MiB): FETCH_SIZE x %.3f, WRITE_SIZE x %.3f"
+           % (COPY_BYTES >> 20, per_ctr["FETCH_SIZE"][1], per_ctr["WRITE_SIZE"][1]),
+           "",
+           "%-7s %9s %7s %14s %14s %14s %9s %9s" % ("tokens", "distinct", "groups", "read_bytes", "distinct_bytes",
+                                                     "group_bytes", "read/dist", "read/grp")]
+    for i, m in enumerate(meta):
+        fetch = sum(per_ctr["FETCH_SIZE"][0][i])
+        mb = m["expert_matrix_bytes"]
+        dist_b = 3 * mb * m["distinct_experts"]
+        grp_b = 3 * mb * m["groups"]
+        out.append("%-7d %9d %7d %14.0f %14d %14d %9.4f %9.4f" % (m["tokens"], m["distinct_experts"], m["groups"],
+                                                                  fetch, dist_b, grp_b, fetch / dist_b,
+                                                                  fetch / grp_b))
+    out += ["", "read_bytes: FETCH_SIZE of the layer's three dispatches (weights, activations, logits, the table);",
+            "written bytes per layer (WRITE_SIZE): " + ", ".join(
+                "%.0f" % sum(l) for l in per_ctr["WRITE_SIZE"][0])]
+    with open(MOE_TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
 
 
 def prefill_pass():
@@ -400,6 +511,10 @@ def main():
         sys.exit(2)
     if args.pmc_pass:
         return pmc_pass()
+    if args.pmc_moe_pass:
+        return pmc_moe_pass(args.pmc_moe_pass)
+    if args.moe_traffic_summary:
+        return moe_traffic_summary(*args.moe_traffic_summary)
     if args.prefill_pass:
         return prefill_pass()
 
