@@ -717,8 +717,9 @@ def measure(torch, gq, dev, stream, t_, workload: str) -> float:
                     gq.gq_matvec(L.t, c[L.name], L.N, L.K, xs[L.name], ys[L.name], stream)
 
         return float(np.median(Timer(torch, run, stream).replays(2 * MIN_REPS))) / nc
-    if workload == "moe":
-        m = WL.MOE
+    if workload in ("moe", "moe:64"):
+        # the fused MoE layer at 8 tokens ("moe", the context workload) or 64
+        m = WL.MOE if workload == "moe" else WL.MoeLayer(T=64)
         ex = m.experts()
         nb = sum(v.nbytes for v in ex.values())
         cps = [{k: t_(v) for k, v in ex.items()} for _ in range(n_copies(nb))]
@@ -744,7 +745,7 @@ def measure(torch, gq, dev, stream, t_, workload: str) -> float:
         Y5 = torch.empty(L.M, L.N, device=dev)
         return float(np.median(Timer(torch, lambda: gq.gq_matmul(L.t, W5, L.N, L.K, X5, Y5, stream),
                                      stream).replays(30, warm=60)))
-    raise SystemExit("unknown workload %r (headline, moe, prefill, prefill:q6_k, prefill:q4_0)" % workload)
+    raise SystemExit("unknown workload %r (headline, moe, moe:64, prefill, prefill:q6_k, prefill:q4_0)" % workload)
 
 
 def abba(lib_a: str, lib_b: str, rounds: int, workload: str):

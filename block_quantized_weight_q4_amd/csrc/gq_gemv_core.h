@@ -466,7 +466,9 @@ __device__ __forceinline__ void stage_group(const TileLds<F>& L, int b, int g, c
 // issues the weight loads, so the in-order load counter lets staging start as
 // soon as the activations arrive.  stage_finish does the arithmetic, the
 // remaining groups (loop over vectors is wave-uniform, so the vector pointer
-// stays a scalar) and ends with an LDS barrier.
+// stays a scalar) and ends with an LDS barrier.  With XPF it loads each next
+// group while staging the current one; without, one group at a time, which
+// frees a group's registers (32 for fp32 activations) for occupancy.
 template <class F, int XT>
 __device__ __forceinline__ void stage_issue(const XSrc& xs, int64_t k0, const TileLds<F>& L, XRaw<XT>& in) {
     // every thread loads (threads past the groups reload group 0): an
@@ -476,7 +478,7 @@ __device__ __forceinline__ void stage_issue(const XSrc& xs, int64_t k0, const Ti
     load_group<XT>(xs.p[0], k0 + 32 * g, in);
 }
 
-template <class F, int XT, int NT>
+template <class F, int XT, int NT, bool XPF = true>
 __device__ __forceinline__ void stage_finish(const XSrc& xs, int64_t k0, const TileLds<F>& L,
                                              const XRaw<XT>& first) {
     const int G = L.U * F::UW / 32;
@@ -487,6 +489,15 @@ __device__ __forceinline__ void stage_finish(const XSrc& xs, int64_t k0, const T
     const int items = L.nb * rounds;
     if (items == 1) {
         if (tid < G) stage_group<F, XT>(L, 0, tid, first);
+    } else if constexpr (!XPF) {
+        if (tid < G) stage_group<F, XT>(L, 0, tid, first);
+#pragma unroll 1
+        for (int i = 1; i < items; ++i) {
+            const int g = tid + nthreads * (i % rounds);
+            XRaw<XT> cur;
+            load_group<XT>(xs.at(i / rounds), k0 + 32 * (g < G ? g : 0), cur);
+            if (g < G) stage_group<F, XT>(L, i / rounds, g, cur);
+        }
     } else {
         // the next item's activations are loaded while this one is staged; the
         // load is unconditional (the last item reloads itself) so that the
@@ -575,7 +586,7 @@ constexpr int PREFETCH = 3;
 // around the activation staging and each later one as an earlier unit is
 // taken, all in straight-line code (units past the tile load as zeros).  With
 // RING a ring keeps D units per lane in flight over any number of units.
-template <int TYPE, int XT, int BMAX, int D, bool RING, int NT = NTHREADS, int PF = PREFETCH>
+template <int TYPE, int XT, int BMAX, int D, bool RING, int NT = NTHREADS, int PF = PREFETCH, bool XPF = true>
 __device__ __forceinline__ void gemv_workgroup(const uint8_t* __restrict__ W, int64_t N, int64_t K, int64_t rowA,
                                                const XSrc& xs, int nb, const YDst& yd, int LPR, int tile_units,
                                                uint8_t* lds, int wslot, int wcount) {
@@ -622,7 +633,7 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t* __restrict__ W, in
         Raw ring[D];
         ring[0] = F::load(rs, off_of(0), ln);
         __builtin_amdgcn_sched_barrier(0);
-        stage_finish<F, XT, NT>(xs, u0 * F::UW, L, xin);
+        stage_finish<F, XT, NT, XPF>(xs, u0 * F::UW, L, xin);
 #pragma unroll
         for (int t = 1; t < P; ++t) ring[t] = F::load(rs, off_of(t), ln);
         if constexpr (!RING) {
