@@ -465,10 +465,14 @@ __device__ __forceinline__ void stage_group(const TileLds<F>& L, int b, int g, c
 // stage_issue loads this thread's first group (vector 0); the caller then
 // issues the weight loads, so the in-order load counter lets staging start as
 // soon as the activations arrive.  stage_finish does the arithmetic, the
-// remaining groups (loop over vectors is wave-uniform, so the vector pointer
-// stays a scalar) and ends with an LDS barrier.  With XPF it loads each next
-// group while staging the current one; without, one group at a time, which
-// frees a group's registers (32 for fp32 activations) for occupancy.
+// remaining groups one at a time (loop over vectors is wave-uniform, so the
+// vector pointer stays a scalar) and ends with an LDS barrier.  Loading the
+// next group while staging one held a second group's registers (32 for fp32
+// activations) through the whole kernel: without it the batch-1 products
+// drop from 143-146 to 114-116 registers and the routed ones from 142 to 115
+// (4 wavefronts per SIMD instead of 3); measured 0-3% faster (dense layer at
+// 4 vectors 55.6 -> 54.0 us, fused MoE layer 1.8%), nowhere slower beyond
+// the noise.
 template <class F, int XT>
 __device__ __forceinline__ void stage_issue(const XSrc& xs, int64_t k0, const TileLds<F>& L, XRaw<XT>& in) {
     // every thread loads (threads past the groups reload group 0): an
@@ -478,7 +482,7 @@ __device__ __forceinline__ void stage_issue(const XSrc& xs, int64_t k0, const Ti
     load_group<XT>(xs.p[0], k0 + 32 * g, in);
 }
 
-template <class F, int XT, int NT, bool XPF = true>
+template <class F, int XT, int NT>
 __device__ __forceinline__ void stage_finish(const XSrc& xs, int64_t k0, const TileLds<F>& L,
                                              const XRaw<XT>& first) {
     const int G = L.U * F::UW / 32;
@@ -487,32 +491,15 @@ __device__ __forceinline__ void stage_finish(const XSrc& xs, int64_t k0, const T
     // work items: (vector b, round r) -> group tid + nthreads r of vector b
     const int rounds = (G + nthreads - 1) / nthreads;
     const int items = L.nb * rounds;
-    if (items == 1) {
-        if (tid < G) stage_group<F, XT>(L, 0, tid, first);
-    } else if constexpr (!XPF) {
-        if (tid < G) stage_group<F, XT>(L, 0, tid, first);
+    if (tid < G) stage_group<F, XT>(L, 0, tid, first);
+    // the later items' loads are unconditional (threads past the groups
+    // reload group 0) so that the load-counter waits stay exact
 #pragma unroll 1
-        for (int i = 1; i < items; ++i) {
-            const int g = tid + nthreads * (i % rounds);
-            XRaw<XT> cur;
-            load_group<XT>(xs.at(i / rounds), k0 + 32 * (g < G ? g : 0), cur);
-            if (g < G) stage_group<F, XT>(L, i / rounds, g, cur);
-        }
-    } else {
-        // the next item's activations are loaded while this one is staged; the
-        // load is unconditional (the last item reloads itself) so that the
-        // load-counter wait stays exact
-        XRaw<XT> cur = first;
-#pragma unroll 1
-        for (int i = 0; i < items; ++i) {
-            const int in = i + 1 < items ? i + 1 : i;
-            const int gn = tid + nthreads * (in % rounds);
-            XRaw<XT> nxt;
-            load_group<XT>(xs.at(in / rounds), k0 + 32 * (gn < G ? gn : 0), nxt);
-            const int g = tid + nthreads * (i % rounds);
-            if (g < G) stage_group<F, XT>(L, i / rounds, g, cur);
-            cur = nxt;
-        }
+    for (int i = 1; i < items; ++i) {
+        const int g = tid + nthreads * (i % rounds);
+        XRaw<XT> cur;
+        load_group<XT>(xs.at(i / rounds), k0 + 32 * (g < G ? g : 0), cur);
+        if (g < G) stage_group<F, XT>(L, i / rounds, g, cur);
     }
     lds_barrier();
 }
@@ -586,7 +573,7 @@ constexpr int PREFETCH = 3;
 // around the activation staging and each later one as an earlier unit is
 // taken, all in straight-line code (units past the tile load as zeros).  With
 // RING a ring keeps D units per lane in flight over any number of units.
-template <int TYPE, int XT, int BMAX, int D, bool RING, int NT = NTHREADS, int PF = PREFETCH, bool XPF = true>
+template <int TYPE, int XT, int BMAX, int D, bool RING, int NT = NTHREADS, int PF = PREFETCH>
 __device__ __forceinline__ void gemv_workgroup(const uint8_t* __restrict__ W, int64_t N, int64_t K, int64_t rowA,
                                                const XSrc& xs, int nb, const YDst& yd, int LPR, int tile_units,
                                                uint8_t* lds, int wslot, int wcount) {
@@ -633,7 +620,7 @@ __device__ __forceinline__ void gemv_workgroup(const uint8_t* __restrict__ W, in
         Raw ring[D];
         ring[0] = F::load(rs, off_of(0), ln);
         __builtin_amdgcn_sched_barrier(0);
-        stage_finish<F, XT, NT, XPF>(xs, u0 * F::UW, L, xin);
+        stage_finish<F, XT, NT>(xs, u0 * F::UW, L, xin);
 #pragma unroll
         for (int t = 1; t < P; ++t) ring[t] = F::load(rs, off_of(t), ln);
         if constexpr (!RING) {

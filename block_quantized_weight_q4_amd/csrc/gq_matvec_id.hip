@@ -44,11 +44,6 @@ static __device__ __align__(256) uint8_t scratch[GQK_NOALLOC_WS_BYTES];
 namespace {
 
 constexpr int CH = 8;           // slots per group = vectors per product workgroup
-// the product workgroups stage their vectors one 32-input group at a time
-// (no load of the next group while staging one): the registers that frees
-// give 4 wavefronts per SIMD instead of 3 with fp32 activations (fused MoE
-// layer, 8 tokens: 92.4 -> 90.9 us)
-constexpr bool XPF_ROUTED = false;
 constexpr int MAX_SLOTS = 1024; // n_tokens * top_k
 
 // One group of the table: expert e, nb <= CH slots in slot order.  Kernels
@@ -291,9 +286,8 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
     }
     __syncthreads();
     if constexpr (!GLU) {
-        gemv_workgroup<TYPE, XT, 8, D, RING, NTHREADS, PREFETCH, XPF_ROUTED>(
-            experts + (int64_t)e * expert_bytes, N, K, rowA, xs, nb, yd, LPR, tile_units, lds,
-            (int)(threadIdx.x >> 6), NTHREADS >> 6);
+        gemv_workgroup<TYPE, XT, 8, D, RING>(experts + (int64_t)e * expert_bytes, N, K, rowA, xs, nb, yd, LPR,
+                                              tile_units, lds, (int)(threadIdx.x >> 6), NTHREADS >> 6);
     } else {
         // [gate | up][vector][row in tile]; 2 SR <= 32 rows (LPR >= 4)
         __shared__ float gu[2][CH][32];
@@ -303,8 +297,7 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
 #pragma unroll
         for (int b = 0; b < 8; ++b) yp.p[b] = &gu[half][b < CH ? b : 0][0];
         const uint8_t* W = (half ? experts_up : experts) + (int64_t)e * expert_bytes + rowA * row_bytes;
-        gemv_workgroup<TYPE, XT, 8, D, RING, NTHREADS, PREFETCH, XPF_ROUTED>(W, N - rowA, K, 0, xs, nb, yp, LPR,
-                                                                           tile_units, lds, wave & 1, 2);
+        gemv_workgroup<TYPE, XT, 8, D, RING>(W, N - rowA, K, 0, xs, nb, yp, LPR, tile_units, lds, wave & 1, 2);
         __syncthreads();
         const int rows = (int)rpw;
         const int64_t nr = N - rowA < rpw ? N - rowA : rpw;
