@@ -12,20 +12,23 @@
 // Tiling.  A workgroup owns a BM x BN = 256 x 256 tile of Y.  With 4
 // wavefronts (one per SIMD; Q6_K) wavefront (wm, wn) owns a 128 x 128 quarter
 // as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators); with 8
-// (two per SIMD; the other formats) a 128 x 64 eighth as 4 x 2 blocks, so one
-// wavefront's MFMAs run while the other expands weights or waits on LDS.  K advances in
-// stages of BK = 64 inputs: one 32-byte slice of quants of a Q4_K super-block,
-// two Q4_0 blocks, or the two 32-input quarters of a Q6_K super-block half
-// whose low bits share 32 ql bytes (inputs 0-31 with 64-95, or 32-63 with
-// 96-127, of the half; X's columns are taken in the same order).
+// (two per SIMD; the other formats) a 128 x 64 eighth as 8 x 4 blocks of
+// v_mfma_f32_16x16x32_bf16 (128 accumulators), so one wavefront's MFMAs run
+// while the other expands weights or waits on LDS.  K advances in stages of
+// BK = 64 inputs: one 32-byte slice of quants of a Q4_K super-block, two Q4_0
+// blocks, or the two 32-input quarters of a Q6_K super-block half whose low
+// bits share 32 ql bytes (inputs 0-31 with 64-95, or 32-63 with 96-127, of the
+// half; X's columns are taken in the same order).
 //
 // Pipeline.  LDS holds two stage buffers.  While the MFMAs of stage s read
-// buffer s & 1, the same wavefronts write stage s+1 -- its X rows as loaded and
-// its W rows expanded to bf16 (the format's fp32 weight, one rounding to
-// nearest even) -- into the other buffer, in four slices placed between the
-// four 16-deep k steps; then they issue the global loads of stage s+3 into the
-// registers just freed (two register sets alternate, so a load has more than a
-// stage of MFMA work to arrive).  One LDS-only barrier per stage.
+// buffer s & 1, the same wavefronts fill the other buffer with stage s+1: its
+// W rows expanded to bf16 (the format's fp32 weight, one rounding to nearest
+// even) in slices placed between the k steps, from global loads issued two
+// stages ahead into two alternating register sets; its X rows (4 wavefronts)
+// stored from registers the same way, or (8 wavefronts) copied by the
+// global-to-LDS form of the buffer load, issued at the start of stage s and
+// waited for before its end -- no registers and no LDS stores for X.  One
+// LDS-only barrier per stage.
 //
 // Rows of X past M and of W past N, and inputs past K, are read as zeros
 // (buffer loads beyond the resource's span); their outputs are never stored.
@@ -46,8 +49,20 @@ constexpr int LDX = BK + 8;                   // bf16 per LDS row (+16 B pad: co
 constexpr int ROWB = LDX * 2;                 // bytes per LDS row
 constexpr int BUF = (BM + BN) * ROWB;         // one stage buffer: X rows then W rows
 constexpr int LDS_BYTES = 2 * BUF;            // 147,456 B
+// 8-wavefront kernel: X rows unpadded (128 B, chunks XOR-swizzled), W rows padded
+constexpr int XROWS_BYTES = BM * 128;
+constexpr int LDS8_BYTES = 2 * (XROWS_BYTES + BN * ROWB);  // 139,264 B
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((address_space(3))) void* LdsPtr;
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and
+// lgkmcnt at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -96,6 +111,7 @@ struct WF<T_Q4_K> {
     // input index of the stage's 8-input chunk c (c = 0..7): contiguous
     __device__ static uint32_t xin(int s, int c) { return (uint32_t)s * 64u + 8u * (uint32_t)c; }
     static constexpr int QK = 256, BB = 144;
+    static constexpr int NLOADS = 2;  // load instructions per stage of load_part
     struct Regs {
         u32x4 h, q0, q1;
     };
@@ -130,6 +146,18 @@ struct WF<T_Q4_K> {
         lo = expand_bytes(w0 & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, sc.dsL, sc.dmL);
         hi = expand_bytes((w0 >> 4) & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu, sc.dsH, sc.dmH);
     }
+    // a thread that expands only slices 2 part, 2 part + 1 loads only their
+    // 16 quant bytes (into q0)
+    __device__ static void load_part(Rsrc wr, uint32_t woff, int s, bool ok, bool, int part, Regs& r) {
+        const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * BB : 0x80000000u;
+        r.h = bld16(wr, bo);
+        r.q0 = bld16(wr, bo + 16 + 32 * (s & 3) + 16 * part);
+    }
+    __device__ static void expand_part(const Regs& r, const Scl& sc, int s, int j, u32x4& lo, u32x4& hi) {
+        Regs t = r;
+        t.q1 = r.q0;
+        expand(t, sc, s, j, lo, hi);
+    }
 };
 
 // Q5_K: Q4_K with a 32-byte plane of fifth bits at 16 (quants at 48): input
@@ -140,6 +168,7 @@ struct WF<T_Q5_K> {
     // input index of the stage's 8-input chunk c (c = 0..7): contiguous
     __device__ static uint32_t xin(int s, int c) { return (uint32_t)s * 64u + 8u * (uint32_t)c; }
     static constexpr int QK = 256, BB = 176;
+    static constexpr int NLOADS = 3;
     struct Regs {
         u32x4 h, q0, q1, f0, f1;
     };
@@ -156,6 +185,18 @@ struct WF<T_Q5_K> {
         WF<T_Q4_K>::Regs h4;
         h4.h = r.h;
         return WF<T_Q4_K>::scales(h4, s);
+    }
+    __device__ static void load_part(Rsrc wr, uint32_t woff, int s, bool ok, bool, int part, Regs& r) {
+        const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * BB : 0x80000000u;
+        r.h = bld16(wr, bo);
+        r.q0 = bld16(wr, bo + 48 + 32 * (s & 3) + 16 * part);
+        r.f0 = bld16(wr, bo + 16 + 16 * part);
+    }
+    __device__ static void expand_part(const Regs& r, const Scl& sc, int s, int j, u32x4& lo, u32x4& hi) {
+        Regs t = r;
+        t.q1 = r.q0;
+        t.f1 = r.f0;
+        expand(t, sc, s, j, lo, hi);
     }
     __device__ static void expand(const Regs& r, const Scl& sc, int s, int j, u32x4& lo, u32x4& hi) {
         const u32x4 q = j < 2 ? r.q0 : r.q1, f = j < 2 ? r.f0 : r.f1;
@@ -178,6 +219,7 @@ struct WF<T_Q4_0> {
     // input index of the stage's 8-input chunk c (c = 0..7): contiguous
     __device__ static uint32_t xin(int s, int c) { return (uint32_t)s * 64u + 8u * (uint32_t)c; }
     static constexpr int QK = 32, BB = 18;
+    static constexpr int NLOADS = 4;
     struct Regs {
         u32x4 a, b;
         uint32_t c;
@@ -207,6 +249,13 @@ struct WF<T_Q4_0> {
         const int k = 2 * (j & 1), sh = j < 2 ? 0 : 4;
         lo = expand_bytes((qa[k] >> sh) & 0x0F0F0F0Fu, (qa[k + 1] >> sh) & 0x0F0F0F0Fu, sc.dA, 8.0f * sc.dA);
         hi = expand_bytes((qb[k] >> sh) & 0x0F0F0F0Fu, (qb[k + 1] >> sh) & 0x0F0F0F0Fu, sc.dB, 8.0f * sc.dB);
+    }
+    // every slice needs both blocks' quant bytes: part loads load everything
+    __device__ static void load_part(Rsrc wr, uint32_t woff, int s, bool ok, bool full, int, Regs& r) {
+        load(wr, woff, s, ok, full, r);
+    }
+    __device__ static void expand_part(const Regs& r, const Scl& sc, int s, int j, u32x4& lo, u32x4& hi) {
+        expand(r, sc, s, j, lo, hi);
     }
 };
 
@@ -457,12 +506,9 @@ __device__ __forceinline__ void matmul8_tile(const uint8_t* __restrict__ W, int6
                                              float* __restrict__ Y, int64_t ldy, int gn, int n_full, int s_split,
                                              int wg) {
     using F = WF<TYPE>;
-    struct SR8 {
-        u32x4 x[4];
-        typename F::Regs w;
-    };
-    constexpr int JB = NT / 128;                  // 32-column blocks per wavefront
-    constexpr int TBUF = (BM + NT) * ROWB;        // one stage buffer: X rows then W rows
+    using SR8 = typename F::Regs;                 // one stage's bytes of this thread's W row
+    constexpr int JB = NT / 64;                   // 16-column blocks per wavefront
+    constexpr int TBUF = XROWS_BYTES + NT * ROWB; // one stage buffer: X rows (swizzled) then W rows
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -492,30 +538,33 @@ __device__ __forceinline__ void matmul8_tile(const uint8_t* __restrict__ W, int6
     const int64_t rows_x = M - m0 < BM ? M - m0 : BM, rows_w = N - n0 < NT ? N - n0 : NT;
     const Rsrc xr = make_rsrc(X + m0 * ldx, (uint32_t)(rows_x * ldx * 2));
     const Rsrc wr = make_rsrc(W + n0 * (int64_t)row_bytes, (uint32_t)rows_w * row_bytes);
-    const int xrow = tid >> 3, xchunk = tid & 7;
-    const uint32_t xstride = (uint32_t)(64 * ldx * 2);
-    const uint32_t xoff = (uint32_t)xrow * (uint32_t)(ldx * 2);
+    // X: wavefront w moves rows 32 w + 8 t + lane / 8 (t = 0..3) straight into
+    // LDS; lane's 16 bytes land at position lane % 8 of its row, which holds
+    // the row's 8-input chunk (lane % 8) ^ (row % 8)
+    const int drow = 32 * wave + (lane >> 3), dchunk = (lane & 7) ^ (drow & 7);
+    const uint32_t dsrc = (uint32_t)drow * (uint32_t)(ldx * 2), dstep = (uint32_t)(8 * ldx * 2);
     // W: thread tid expands row tid % NT; with NT = 256 wavefronts 0-3 take
     // slices 0, 1 and 4-7 slices 2, 3; with NT = 128 slice tid / 128
     const int wrow = tid & (NT - 1), wpart = NT == 256 ? wave >> 2 : tid >> 7;
     const uint32_t woff = (uint32_t)wrow * row_bytes;
 
-    auto load_stage = [&](int s, SR8& r) {
-        const bool ok = s < s1;
-        const bool xok = ok && (TYPE != T_Q4_0 || (int64_t)s * BK + 8 * xchunk < K);
-        const uint32_t xo = xok ? xoff + 2u * F::xin(s, xchunk) : 0x80000000u;
+    // inputs past K (the second half of a Q4_0 row's last stage) read as zeros
+    auto dma_x = [&](int s, int buf) {
+        const bool ok = s < s1 && (TYPE != T_Q4_0 || (int64_t)s * BK + 8 * dchunk < K);
+        const uint32_t base = ok ? dsrc + 2u * F::xin(s, dchunk) : 0x80000000u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.x[i] = bld16(xr, xok ? xo + (uint32_t)i * xstride : xo);
-        F::load(wr, woff, s, ok, (int64_t)s * BK + 32 < K, r.w);
+        for (int t = 0; t < 4; ++t)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (LdsPtr)(lds + buf * TBUF + (32 * wave + 8 * t) * 128), 16,
+                                                     ok ? base + (uint32_t)t * dstep : base, 0, 0, 0);
     };
-    auto store_x = [&](const SR8& r, int buf, int i) {
-        uint8_t* xs = lds + buf * TBUF + (xrow + 64 * i) * ROWB + 16 * xchunk;
-        *reinterpret_cast<u32x4*>(xs) = r.x[i];
-    };
+    // the half of each stage's quant bytes this thread expands (slices
+    // 2 part, 2 part + 1)
+    const int part = NT == 256 ? wpart : wpart >> 1;
+    auto load_stage = [&](int s, SR8& r) { F::load_part(wr, woff, s, s < s1, (int64_t)s * BK + 32 < K, part, r); };
     auto store_w = [&](int s, const SR8& r, const typename F::Scl& sc, int buf, int j) {
-        uint8_t* ws = lds + buf * TBUF + BM * ROWB + wrow * ROWB;
+        uint8_t* ws = lds + buf * TBUF + XROWS_BYTES + wrow * ROWB;
         u32x4 lo, hi;
-        F::expand(r.w, sc, s, j, lo, hi);
+        F::expand_part(r, sc, s, j, lo, hi);
         reinterpret_cast<u32x4*>(ws)[j] = lo;
         reinterpret_cast<u32x4*>(ws + 64)[j] = hi;
     };
@@ -528,63 +577,88 @@ __device__ __forceinline__ void matmul8_tile(const uint8_t* __restrict__ W, int6
         }
     };
 
-    f32x16 acc[4][JB];
+    f32x4 acc[8][JB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < JB; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < JB; ++j) acc[i][j] = f32x4{};
 
-    const int fr = lane & 31, fk = 8 * (lane >> 5);
-    const uint32_t a_base = (uint32_t)((wm * 128 + fr) * ROWB + fk * 2);
-    const uint32_t b_base = (uint32_t)(BM * ROWB + (wn * 32 * JB + fr) * ROWB + fk * 2);
+    // fragment addresses (v_mfma_f32_16x16x32_bf16): A (X rows) lane l -> row
+    // 16 i + l%16, inputs 8 (l/16)..+7 of the 32-deep k step; B (W rows) the
+    // same with row 16 j + l%16 of the wavefront's columns
+    const int fr = lane & 15, fk = 8 * (lane >> 4);
+    const uint32_t a_base = (uint32_t)((wm * 128 + fr) * 128);
+    uint32_t a_sw[2];  // the chunk 4 kk + lane / 16 of X row (16 i + fr): row % 8 = fr % 8
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) a_sw[kk] = (uint32_t)(((4 * kk + (lane >> 4)) ^ (fr & 7)) << 4);
+    const uint32_t b_base = (uint32_t)(XROWS_BYTES + (wn * 16 * JB + fr) * ROWB + fk * 2);
 
     auto stage_body = [&](int s, SR8& nxt) {
         const int cur = (s - s0) & 1;
         const uint8_t* buf = lds + cur * TBUF;
-        const typename F::Scl sc = F::scales(nxt.w, s + 1);
+        // stage s+1's X rows go straight into the other buffer, free since
+        // the barrier that ended stage s-1
+        dma_x(s + 1, cur ^ 1);
+        const typename F::Scl sc = F::scales(nxt, s + 1);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 a[4], b[JB];
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 b[JB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(buf + a_base + i * 32 * ROWB + ks * 32);
+            for (int j = 0; j < JB; ++j) b[j] = *reinterpret_cast<const bf16x8*>(buf + b_base + j * 16 * ROWB + kk * 64);
+            // the X fragments in two halves of four row blocks: fewer live
+            // registers than all eight at once
 #pragma unroll
-            for (int j = 0; j < JB; ++j) b[j] = *reinterpret_cast<const bf16x8*>(buf + b_base + j * 32 * ROWB + ks * 32);
+            for (int ih = 0; ih < 2; ++ih) {
+                bf16x8 a[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i)
+                    a[i] = *reinterpret_cast<const bf16x8*>(buf + a_base + (4 * ih + i) * 16 * 128 + a_sw[kk]);
 #pragma unroll
-                for (int j = 0; j < JB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-            store_x(nxt, cur ^ 1, ks);
-            store_w_at(ks, s + 1, nxt, sc, cur ^ 1);
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < JB; ++j)
+                        acc[4 * ih + i][j] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[4 * ih + i][j], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) store_w_at(2 * kk + h, s + 1, nxt, sc, cur ^ 1);
         }
         load_stage(s + 3, nxt);
+        // the X rows of stage s+1 have landed: only the W loads of stage s+3,
+        // issued after them, may still be in flight
+        wait_vm<F::NLOADS>();
         lds_barrier();
     };
 
     SR8 r0, r1;
     if (s1 > s0) {
+        dma_x(s0, 0);
         load_stage(s0, r0);
         load_stage(s0 + 1, r1);
-        const typename F::Scl sc0 = F::scales(r0.w, s0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_x(r0, 0, i);
+        const typename F::Scl sc0 = F::scales(r0, s0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) store_w_at(ks, s0, r0, sc0, 0);
         load_stage(s0 + 2, r0);
+        // stage s0's X rows and W loads have landed; those of s0+1 and s0+2
+        // may be in flight
+        wait_vm<2 * F::NLOADS>();
         lds_barrier();
     }
     for (int s = s0; s < s1; s += 2) {
         stage_body(s, r1);
         stage_body(s + 1, r0);
     }
+    // C block (i, j): lane holds W row 16 j + lane%16 (column of Y) and X rows
+    // 16 i + 4 (lane/16) + r for register r
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
         for (int j = 0; j < JB; ++j) {
-            const int64_t n = n0 + wn * 32 * JB + 32 * j + (lane & 31);
+            const int64_t n = n0 + wn * 16 * JB + 16 * j + (lane & 15);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = m0 + wm * 128 + 16 * i + 4 * (lane >> 4) + r;
                 if (m < M && n < N) {
                     if (split) unsafeAtomicAdd(&Y[m * ldy + n], acc[i][j][r]);
                     else Y[m * ldy + n] = acc[i][j][r];
@@ -654,9 +728,9 @@ hipError_t launch(const void* W, int64_t N, int64_t K, const void* X, int64_t M,
     if constexpr (TYPE != T_Q6_K) {
         const int64_t grid = halves ? n_full + 2 * tail : quarters ? n_full + 4 * tail : tiles;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul8<TYPE>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS8_BYTES);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_matmul8<TYPE>, dim3((unsigned)grid), dim3(512), LDS_BYTES, s,
+        hipLaunchKernelGGL(k_matmul8<TYPE>, dim3((unsigned)grid), dim3(512), LDS8_BYTES, s,
                            static_cast<const uint8_t*>(W), N, K, static_cast<const uint16_t*>(X), M, ldx, Y, ldy,
                            (int)gn, n_full, S / 2, quarters ? 1 : 0);
     } else {
