@@ -1,5 +1,5 @@
 // gq_matmul.hip -- prefill product Y[m][n] = sum_k X[m][k] w[n][k] with Q4_0,
-// Q4_K or Q6_K weights and bf16 activations on the CDNA4 matrix cores (gfx950).
+// Q4_K, Q5_K or Q6_K weights and bf16 activations on the CDNA4 matrix cores (gfx950).
 //
 // The dequantise-then-matrix-engine step follows the prefill design of "Show
 // HN: Gemma 4 26B-A4B at up to 100+ tokens/s on a 16 GB Mac" (Architecture
@@ -9,26 +9,28 @@
 // Q4_K_M checkpoint ("GGUF in transformers", section on the GGUF format) mixes
 // Q4_K with Q6_K tensors, so a layer's prefill needs both.
 //
-// Tiling.  A workgroup owns a BM x BN = 256 x 256 tile of Y.  With 4
-// wavefronts (one per SIMD; Q6_K) wavefront (wm, wn) owns a 128 x 128 quarter
-// as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators); with 8
-// (two per SIMD; the other formats) a 128 x 64 eighth as 8 x 4 blocks of
-// v_mfma_f32_16x16x32_bf16 (128 accumulators), so one wavefront's MFMAs run
-// while the other expands weights or waits on LDS.  K advances in stages of
-// BK = 64 inputs: one 32-byte slice of quants of a Q4_K super-block, two Q4_0
-// blocks, or the two 32-input quarters of a Q6_K super-block half whose low
-// bits share 32 ql bytes (inputs 0-31 with 64-95, or 32-63 with 96-127, of the
-// half; X's columns are taken in the same order).
+// Tiling.  A workgroup of 8 wavefronts (two per SIMD) owns a BM x BN =
+// 256 x 256 tile of Y; wavefront (wm, wn) owns a 128 x 64 eighth as 8 x 4
+// blocks of v_mfma_f32_16x16x32_bf16 (128 fp32 accumulators), so one
+// wavefront's MFMAs run while the other expands weights or waits on LDS.  K
+// advances in stages of BK = 64 inputs: one 32-byte slice of quants of a Q4_K
+// super-block, two Q4_0 blocks, or the two 32-input quarters of a Q6_K
+// super-block half whose low bits share 32 ql bytes (inputs 0-31 with 64-95,
+// or 32-63 with 96-127, of the half; X's columns are taken in the same
+// order).  Each thread expands its W row's slices of a stage and loads only
+// the half of the stage's quant bytes those slices use.
 //
 // Pipeline.  LDS holds two stage buffers.  While the MFMAs of stage s read
-// buffer s & 1, the same wavefronts fill the other buffer with stage s+1: its
-// W rows expanded to bf16 (the format's fp32 weight, one rounding to nearest
+// buffer s & 1, the wavefronts fill the other buffer with stage s+1: its W
+// rows expanded to bf16 (the format's fp32 weight, one rounding to nearest
 // even) in slices placed between the k steps, from global loads issued two
-// stages ahead into two alternating register sets; its X rows (4 wavefronts)
-// stored from registers the same way, or (8 wavefronts) copied by the
-// global-to-LDS form of the buffer load, issued at the start of stage s and
-// waited for before its end -- no registers and no LDS stores for X.  One
-// LDS-only barrier per stage.
+// stages ahead into two alternating register sets, and its X rows copied by
+// the global-to-LDS form of the buffer load, issued at the start of stage s
+// and waited for before its end (no registers and no LDS stores for X).  One
+// LDS-only barrier per stage.  Measured against the earlier form of this
+// kernel (32x32x16 MFMAs, X through registers, whole slices loaded; Q6_K on a
+// 4-wavefront 128 x 128 variant): Q4_K 3015x17408x5120 3.0% faster, Q4_0
+// 2.2%, Q6_K 3015x5120x17408 6.4%.
 //
 // Rows of X past M and of W past N, and inputs past K, are read as zeros
 // (buffer loads beyond the resource's span); their outputs are never stored.
@@ -47,9 +49,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int LDX = BK + 8;                   // bf16 per LDS row (+16 B pad: conflict-free b128 reads)
 constexpr int ROWB = LDX * 2;                 // bytes per LDS row
-constexpr int BUF = (BM + BN) * ROWB;         // one stage buffer: X rows then W rows
-constexpr int LDS_BYTES = 2 * BUF;            // 147,456 B
-// 8-wavefront kernel: X rows unpadded (128 B, chunks XOR-swizzled), W rows padded
+// a stage buffer: X rows unpadded (128 B, 16-byte chunks XOR-swizzled), then
+// W rows padded (conflict-free b128 reads)
 constexpr int XROWS_BYTES = BM * 128;
 constexpr int LDS8_BYTES = 2 * (XROWS_BYTES + BN * ROWB);  // 139,264 B
 
@@ -96,10 +97,11 @@ __device__ __forceinline__ u32x4 expand_bytes(uint32_t w0, uint32_t w1, float s,
     return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])};
 }
 
-// Weight formats.  For one W row and stage s a format loads its bytes (Regs,
-// from the row's buffer offset woff; ok == false loads zeros), decodes the
-// stage's scales (Scl) and expands slice j (0..3): lo = stage inputs
-// 8j..8j+7, hi = 32+8j..32+8j+7, as bf16.
+// Weight formats.  For one W row and stage s a format loads the bytes that
+// slices 2 part and 2 part + 1 need (load_part into Regs, from the row's
+// buffer offset woff, NLOADS load instructions; ok == false loads zeros),
+// decodes the stage's scales (Scl) and expands slice j (0..3) of them
+// (expand_part): lo = stage inputs 8j..8j+7, hi = 32+8j..32+8j+7, as bf16.
 template <int TYPE>
 struct WF;
 
@@ -118,12 +120,6 @@ struct WF<T_Q4_K> {
     struct Scl {
         float dsL, dmL, dsH, dmH;
     };
-    __device__ static void load(Rsrc wr, uint32_t woff, int s, bool ok, bool, Regs& r) {
-        const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * BB : 0x80000000u;
-        r.h = bld16(wr, bo);
-        r.q0 = bld16(wr, bo + 16 + 32 * (s & 3));
-        r.q1 = bld16(wr, bo + 32 + 32 * (s & 3));
-    }
     // Selects rather than branches: the decode sits in the same scheduling
     // region as the MFMAs it is interleaved with.
     __device__ static Scl scales(const Regs& r, int s) {
@@ -173,14 +169,6 @@ struct WF<T_Q5_K> {
         u32x4 h, q0, q1, f0, f1;
     };
     using Scl = WF<T_Q4_K>::Scl;
-    __device__ static void load(Rsrc wr, uint32_t woff, int s, bool ok, bool, Regs& r) {
-        const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * BB : 0x80000000u;
-        r.h = bld16(wr, bo);
-        r.q0 = bld16(wr, bo + 48 + 32 * (s & 3));
-        r.q1 = bld16(wr, bo + 64 + 32 * (s & 3));
-        r.f0 = bld16(wr, bo + 16);
-        r.f1 = bld16(wr, bo + 32);
-    }
     __device__ static Scl scales(const Regs& r, int s) {
         WF<T_Q4_K>::Regs h4;
         h4.h = r.h;
@@ -285,19 +273,6 @@ struct WF<T_Q6_K> {
         const uint32_t c4 = (uint32_t)(s & 3);
         return (uint32_t)(s >> 2) * 256u + 128u * (c4 >> 1) + 32u * (c4 & 1u) + 8u * (uint32_t)c + (c >= 4 ? 32u : 0u);
     }
-    __device__ static void load(Rsrc wr, uint32_t woff, int s, bool ok, bool, Regs& r) {
-        const uint32_t c4 = (uint32_t)(s & 3), h = c4 >> 1, p = c4 & 1u;
-        const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * BB : 0x80000000u;
-        r.l0 = bld16(wr, bo + 64 * h + 32 * p);
-        r.l1 = bld16(wr, bo + 64 * h + 32 * p + 16);
-        r.h0 = bld16(wr, bo + 128 + 32 * h);
-        r.h1 = bld16(wr, bo + 128 + 32 * h + 16);
-        // scales 8h + 2p, +1 (quarter p) and 8h + 4 + 2p, +1 (quarter p + 2)
-        const uint32_t sa = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 192 + 8 * h + 2 * p), 0, 0);
-        const uint32_t sb = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 196 + 8 * h + 2 * p), 0, 0);
-        r.sc = sa | (sb << 16);
-        r.d = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 208), 0, 0);
-    }
     __device__ static Scl scales(const Regs& r, int) {
         const float d = h2f(r.d);
         Scl o;
@@ -322,178 +297,34 @@ struct WF<T_Q6_K> {
         lo = expand_bytes(a0, a1, s_lo, 32.0f * s_lo);
         hi = expand_bytes(b0, b1, s_hi, 32.0f * s_hi);
     }
-};
-
-// Global data of one stage for this thread: eight 16-byte chunks of X (one
-// from each of eight rows 32 apart) and the stage's bytes of its W row.
-template <int TYPE>
-struct StageRegs {
-    u32x4 x[8];
-    typename WF<TYPE>::Regs w;
+    // slices 2 part, 2 part + 1 use ql / qh bytes 16 part..16 part + 15 of
+    // the stage's 32 (into l0 / h0), the scales and d
+    static constexpr int NLOADS = 5;
+    __device__ static void load_part(Rsrc wr, uint32_t woff, int s, bool ok, bool, int part, Regs& r) {
+        const uint32_t c4 = (uint32_t)(s & 3), h = c4 >> 1, p = c4 & 1u;
+        const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * BB : 0x80000000u;
+        r.l0 = bld16(wr, bo + 64 * h + 32 * p + 16 * part);
+        r.h0 = bld16(wr, bo + 128 + 32 * h + 16 * part);
+        const uint32_t sa = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 192 + 8 * h + 2 * p), 0, 0);
+        const uint32_t sb = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 196 + 8 * h + 2 * p), 0, 0);
+        r.sc = sa | (sb << 16);
+        r.d = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 208), 0, 0);
+    }
+    __device__ static void expand_part(const Regs& r, const Scl& sc, int s, int j, u32x4& lo, u32x4& hi) {
+        Regs t = r;
+        t.l1 = r.l0;
+        t.h1 = r.h0;
+        expand(t, sc, s, j, lo, hi);
+    }
 };
 
 // Grid: one workgroup per output tile, tiles numbered n-tile fastest (gn of
-// them per row of tiles).  When the tile count leaves a last round that
-// would fill only part of the GPU, its tiles (those from n_full on) are each
-// split in two workgroups along K -- stages [0, s_split) and [s_split, S) --
-// that add their partial tiles into Y, which the launcher has zeroed there:
-// the tail round then takes half as long.  Two fp32 additions into zero give
-// the same bits in either order, so the result stays deterministic.
-template <int TYPE>
-__global__ __launch_bounds__(256, 1) void k_matmul(const uint8_t* __restrict__ W, int64_t N, int64_t K,
-                                                   const uint16_t* __restrict__ X, int64_t M, int64_t ldx,
-                                                   float* __restrict__ Y, int64_t ldy, int gn, int n_full,
-                                                   int s_split) {
-    using F = WF<TYPE>;
-    using SR = StageRegs<TYPE>;
-    extern __shared__ __align__(16) uint8_t lds[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int S = (int)((K + BK - 1) / BK);  // a Q4_0 row may end half way into a stage
-    const int wg = (int)blockIdx.x;
-    const bool split = wg >= n_full;
-    const int tile = split ? n_full + ((wg - n_full) >> 1) : wg;
-    const int s0 = split && ((wg - n_full) & 1) ? s_split : 0;
-    const int s1 = split && !((wg - n_full) & 1) ? s_split : S;
-    const int64_t n0 = (int64_t)(tile % gn) * BN, m0 = (int64_t)(tile / gn) * BM;
-    const uint32_t row_bytes = (uint32_t)((K / F::QK) * F::BB);
-
-    // X: thread tid stages 16-byte chunk tid % 8 of rows tid / 8 + 32 i
-    // (i = 0..7): eight lanes cover one row's 128 bytes, so every load
-    // instruction reads whole cache lines.  W: thread tid stages row n0 + tid.
-    const int64_t rows_x = M - m0 < BM ? M - m0 : BM, rows_w = N - n0 < BN ? N - n0 : BN;
-    const Rsrc xr = make_rsrc(X + m0 * ldx, (uint32_t)(rows_x * ldx * 2));
-    const Rsrc wr = make_rsrc(W + n0 * (int64_t)row_bytes, (uint32_t)rows_w * row_bytes);
-    const int xrow = tid >> 3, xchunk = tid & 7;
-    const uint32_t xstride = (uint32_t)(32 * ldx * 2);
-    const uint32_t xoff = (uint32_t)xrow * (uint32_t)(ldx * 2), woff = (uint32_t)tid * row_bytes;
-
-    // a stage past the last loads zeros without touching memory (offset past
-    // the buffers), so every load is unconditional and the load-counter waits
-    // stay exact
-    auto load_stage = [&](int s, SR& r) {
-        const bool ok = s < s1;
-        // inputs past K (the second half of a Q4_0 row's last stage) read as zeros
-        const bool xok = ok && (TYPE != T_Q4_0 || (int64_t)s * BK + 8 * xchunk < K);
-        const uint32_t xo = xok ? xoff + 2u * F::xin(s, xchunk) : 0x80000000u;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r.x[i] = bld16(xr, xok ? xo + (uint32_t)i * xstride : xo);
-        F::load(wr, woff, s, ok, (int64_t)s * BK + 32 < K, r.w);
-    };
-    // slice j (0..3) of the stage's LDS writes: X chunks 2j, 2j+1 and W quant
-    // bytes 8j..8j+7 expanded to k = 8j..8j+7 and 32+8j..32+8j+7
-    auto store_slice = [&](int s, const SR& r, const typename F::Scl& sc, int buf, int j) {
-        uint8_t* xs = lds + buf * BUF + xrow * ROWB + 16 * xchunk;
-        uint8_t* ws = lds + buf * BUF + BM * ROWB + tid * ROWB;
-        *reinterpret_cast<u32x4*>(xs + (2 * j) * 32 * ROWB) = r.x[2 * j];
-        *reinterpret_cast<u32x4*>(xs + (2 * j + 1) * 32 * ROWB) = r.x[2 * j + 1];
-        u32x4 lo, hi;
-        F::expand(r.w, sc, s, j, lo, hi);
-        reinterpret_cast<u32x4*>(ws)[j] = lo;
-        reinterpret_cast<u32x4*>(ws + 64)[j] = hi;
-    };
-
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-    // fragment addresses: A (X rows) lane l -> row 32*mi + l%32, k 8*(l/32);
-    // B (W rows) lane l -> row 32*ni + l%32, same k
-    const int fr = lane & 31, fk = 8 * (lane >> 5);
-    const uint32_t a_base = (uint32_t)((wm * 128 + fr) * ROWB + fk * 2);
-    const uint32_t b_base = (uint32_t)(BM * ROWB + (wn * 128 + fr) * ROWB + fk * 2);
-
-    // stage s's global data lives in register set s & 1; it is loaded two
-    // stages before its LDS writes, which happen during stage s-1's MFMAs
-    auto stage_body = [&](int s, SR& nxt) {
-        const int cur = (s - s0) & 1;
-        const uint8_t* buf = lds + cur * BUF;
-        // stage s+1's data arrived during the previous stage; past the last
-        // stage it is zeros, written to a buffer nobody reads
-        const typename F::Scl sc = F::scales(nxt.w, s + 1);
-        bf16x8 a[2][4], b[2][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            a[0][i] = *reinterpret_cast<const bf16x8*>(buf + a_base + i * 32 * ROWB);
-            b[0][i] = *reinterpret_cast<const bf16x8*>(buf + b_base + i * 32 * ROWB);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int p = ks & 1;
-            if (ks < 3) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    a[p ^ 1][i] = *reinterpret_cast<const bf16x8*>(buf + a_base + i * 32 * ROWB + (ks + 1) * 32);
-                    b[p ^ 1][i] = *reinterpret_cast<const bf16x8*>(buf + b_base + i * 32 * ROWB + (ks + 1) * 32);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[p][i], b[p][j], acc[i][j], 0, 0, 0);
-            store_slice(s + 1, nxt, sc, cur ^ 1, ks);
-            // one k step = one scheduling region: each MFMA is followed by a
-            // few VALU instructions of the expansion and the LDS traffic, so
-            // they issue while the matrix core is busy (5 VALU per MFMA
-            // measured 2% faster for Q6_K than 3, 4, 6 or 8)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                if (ks < 3 && i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
-                if ((i & 3) == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        load_stage(s + 3, nxt);
-        lds_barrier();
-    };
-
-    // an odd stage count runs one stage of zeros at the end
-    SR r0, r1;
-    if (s1 > s0) {
-        load_stage(s0, r0);
-        load_stage(s0 + 1, r1);
-        const typename F::Scl sc0 = F::scales(r0.w, s0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) store_slice(s0, r0, sc0, 0, j);
-        load_stage(s0 + 2, r0);
-        lds_barrier();
-    }
-    for (int s = s0; s < s1; s += 2) {
-        stage_body(s, r1);      // writes stage s+1 (set 1), then loads s+3 into set 1
-        stage_body(s + 1, r0);  // writes stage s+2 (set 0), then loads s+4 into set 0
-    }
-
-    // C block (i, j): lane holds W row 32*j + lane%32 (column of Y) and X rows
-    // 32*i + 8*(r/4) + 4*(lane/32) + r%4 for register r
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + wn * 128 + 32 * j + (lane & 31);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m < M && n < N) {
-                    if (split) unsafeAtomicAdd(&Y[m * ldy + n], acc[i][j][r]);
-                    else Y[m * ldy + n] = acc[i][j][r];
-                }
-            }
-        }
-    }
-}
-
-}  // namespace
-
-namespace {
-
-// 8-wavefront variant: wavefront (wm, wn) = (wave / 4, wave % 4) owns a
-// 128 x (NT / 4) part of the 256 x NT tile (4 x NT/128 blocks of 32x32x16
-// MFMAs), so two wavefronts share each SIMD.  NT = 256 for whole tiles.
+// them per row of tiles).  Wavefront (wm, wn) = (wave / 4, wave % 4) owns a
+// 128 x (NT / 4) part of the 256 x NT tile (8 x NT/64 blocks of 16x16x32
+// MFMAs), so two wavefronts share each SIMD.  NT = 256 for whole tiles; when
+// the last round would fill only part of the GPU and four workgroups per tile
+// do not fit in it, its tiles (those from n_full on) are split in two K
+// halves -- stages [0, s_split) and [s_split, S) -- added into Y.
 // NT = 128 runs the tiles of a last, partial round as quarters: workgroup
 // n_full + q takes N half (q / 2) % 2 and K half q % 2 of tile n_full + q / 4
 // and adds its partial tile into Y (zeroed there beforehand), so that round
@@ -707,14 +538,13 @@ hipError_t launch(const void* W, int64_t N, int64_t K, const void* X, int64_t M,
     const int64_t tiles = gn * gm;
     if (tiles > 0x3fffffff) return hipErrorInvalidValue;
     // one workgroup per CU (the LDS holds one).  A last round that would
-    // fill only part of the GPU runs its tiles as K halves (two workgroups
-    // per tile) or, for the 8-wavefront kernel when four per tile still fit
-    // in one round, as N and K quarters.
+    // fill only part of the GPU runs its tiles as N and K quarters when four
+    // workgroups per tile fit in one round, else as K halves.
     const int cus = gqk_cu_count();
     const int64_t tail = tiles % cus;
     const int S = (int)((K + BK - 1) / BK);
     const bool part = tiles > cus && tail > 0 && S >= 4;
-    const bool quarters = TYPE != T_Q6_K && part && 4 * tail <= cus;
+    const bool quarters = part && 4 * tail <= cus;
     const bool halves = !quarters && part && tail <= cus / 2;
     const int n_full = (int)(part && (quarters || halves) ? tiles - tail : tiles);
     if (n_full < tiles) {
@@ -723,25 +553,13 @@ hipError_t launch(const void* W, int64_t N, int64_t K, const void* X, int64_t M,
         if (e0 != hipSuccess) return e0;
     }
     // LDS above the default per-workgroup size (gfx950 allows 160 KB)
-    // eight wavefronts (two per SIMD) where the format's registers allow
-    // it; Q6_K's larger stage registers keep the four-wavefront kernel
-    if constexpr (TYPE != T_Q6_K) {
-        const int64_t grid = halves ? n_full + 2 * tail : quarters ? n_full + 4 * tail : tiles;
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul8<TYPE>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS8_BYTES);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_matmul8<TYPE>, dim3((unsigned)grid), dim3(512), LDS8_BYTES, s,
-                           static_cast<const uint8_t*>(W), N, K, static_cast<const uint16_t*>(X), M, ldx, Y, ldy,
-                           (int)gn, n_full, S / 2, quarters ? 1 : 0);
-    } else {
-        const int64_t grid = halves ? n_full + 2 * tail : tiles;
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul<TYPE>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_matmul<TYPE>, dim3((unsigned)grid), dim3(256), LDS_BYTES, s,
-                           static_cast<const uint8_t*>(W), N, K, static_cast<const uint16_t*>(X), M, ldx, Y, ldy,
-                           (int)gn, n_full, S / 2);
-    }
+    const int64_t grid = halves ? n_full + 2 * tail : quarters ? n_full + 4 * tail : tiles;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_matmul8<TYPE>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS8_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_matmul8<TYPE>, dim3((unsigned)grid), dim3(512), LDS8_BYTES, s,
+                       static_cast<const uint8_t*>(W), N, K, static_cast<const uint16_t*>(X), M, ldx, Y, ldy,
+                       (int)gn, n_full, S / 2, quarters ? 1 : 0);
     return hipGetLastError();
 }
 
