@@ -29,13 +29,33 @@ __device__ __forceinline__ float key_value(uint32_t k) {
     return __builtin_bit_cast(float, b);
 }
 
+// One step of the wave maximum: each lane takes the larger of its key and
+// the key that the DPP pattern CTRL brings from another lane (rows outside
+// ROWS, and lanes whose source lies outside their row, keep their own).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void max_step(uint32_t& hi, uint32_t& lo) {
+    const uint32_t th = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROWS, 0xF, false);
+    const uint32_t tl = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROWS, 0xF, false);
+    const bool gt = th > hi || (th == hi && tl > lo);
+    hi = gt ? th : hi;
+    lo = gt ? tl : lo;
+}
+
+// Largest 64-bit key of the wave, in every lane.  Cross-lane moves by DPP
+// instead of LDS permutes: row shifts right by 1, 2, 4, 8 leave each 16-lane
+// row's maximum in its lane 15; row_bcast15 and row_bcast31 carry those into
+// lane 63, which is then read as a scalar.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint64_t o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+    uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+    max_step<0x111, 0xF>(hi, lo);  // row_shr:1
+    max_step<0x112, 0xF>(hi, lo);  // row_shr:2
+    max_step<0x114, 0xF>(hi, lo);  // row_shr:4
+    max_step<0x118, 0xF>(hi, lo);  // row_shr:8
+    max_step<0x142, 0xA>(hi, lo);  // row_bcast15 into rows 1 and 3
+    max_step<0x143, 0xC>(hi, lo);  // row_bcast31 into rows 2 and 3
+    const uint32_t h = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
+    const uint32_t l = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+    return ((uint64_t)h << 32) | l;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
