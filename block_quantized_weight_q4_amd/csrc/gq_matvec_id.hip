@@ -315,6 +315,9 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
 // ------------------------------------------------------------- combine ----
 // y[t][n] = sum_j route_w[t][j] * slot[t][j][n] over the valid slots, j in
 // increasing order (slot_e: each slot's expert from the table, -1 if invalid).
+// The slots are read eight at a time, every load issued before the first sum
+// (an invalid slot's row is read and then skipped), so that a token's slots
+// cost one round trip per eight instead of one each.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ slot_out, const int* __restrict__ slot_e,
                                                  const float* __restrict__ route_w, int top_k, int64_t N,
                                                  float* __restrict__ y) {
@@ -322,9 +325,19 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ slot_
     const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (n >= N) return;
     float acc = 0.f;
-    for (int j = 0; j < top_k; ++j) {
-        if (slot_e[t * top_k + j] < 0) continue;
-        acc = __builtin_fmaf(route_w[t * top_k + j], slot_out[((int64_t)t * top_k + j) * N + n], acc);
+    for (int j0 = 0; j0 < top_k; j0 += 8) {
+        float v[8], w[8];
+        bool ok[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u < top_k ? j0 + u : top_k - 1;
+            ok[u] = j0 + u < top_k && slot_e[t * top_k + j] >= 0;
+            w[u] = route_w[t * top_k + j];
+            v[u] = slot_out[((int64_t)t * top_k + j) * N + n];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (ok[u]) acc = __builtin_fmaf(w[u], v[u], acc);
     }
     y[(int64_t)t * N + n] = acc;
 }
