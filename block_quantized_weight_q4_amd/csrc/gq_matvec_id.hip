@@ -81,7 +81,10 @@ WsLayout layout(int n_experts, int n_tokens, int top_k, int64_t N) {
 // a scan of ceil(count / CH) over the experts; with more than
 // MAX_EXPERTS_LDS experts, the group heads -- rank % CH == 0 -- with a smaller
 // expert id, counted directly).  out (if given): the [S][N] outputs whose rows
-// of invalid slots are zeroed (fp32, or bf16 when out_bf16).
+// of invalid slots are zeroed (fp32, or bf16 when out_bf16).  The barriers
+// order LDS traffic only: no thread reads what another wrote to global memory
+// before the kernel ends, and a full barrier would wait for every store to be
+// acknowledged (together about 3 of the router kernel's 8 us).
 constexpr int MAX_EXPERTS_LDS = 1024;
 
 template <int NT>
@@ -109,12 +112,13 @@ __device__ __forceinline__ void plan_body(const int32_t* ids, int S, int n_exper
         key[s] = s >= S ? -2 : ((e >= 0 && e < n_experts) ? e : -1);  // -2: padding
         head[s] = 0x7fffffff;
     }
-    __syncthreads();
+    lds_barrier();
     int bad = 0;
     for (int s = tid; s < S; s += NT) {
         const int e = key[s];
         slot_e[s] = e;
         int r = 0;
+#pragma unroll 4
         for (int j4 = 0; 4 * j4 < s; ++j4) {
             const int4 k = key4[j4];
             const int j = 4 * j4;
@@ -128,7 +132,7 @@ __device__ __forceinline__ void plan_body(const int32_t* ids, int S, int n_exper
         }
     }
     if (bad) atomicAdd(&n_bad, bad);
-    __syncthreads();
+    lds_barrier();
     if (small_e) {
         // exclusive scan of ceil(cnt / CH) over the experts by wavefront 0:
         // each lane a contiguous run of experts, then a shuffle scan of the
@@ -150,8 +154,9 @@ __device__ __forceinline__ void plan_body(const int32_t* ids, int S, int n_exper
                 cnt[e] = run | (c << 16);  // groups before e (low half), slot count (high half)
                 run += (c + CH - 1) / CH;
             }
+            if (tid == 63) n_grp = incl;  // the group count: the scan's total
         }
-        __syncthreads();
+        lds_barrier();
     }
     int heads = 0;
     for (int s = tid; s < S; s += NT) {
@@ -179,8 +184,11 @@ __device__ __forceinline__ void plan_body(const int32_t* ids, int S, int n_exper
             ++heads;
         }
     }
-    if (heads) atomicAdd(&n_grp, heads);
-    __syncthreads();
+    // (an LDS atomic that every lane of a wavefront takes part in costs a
+    // scalar loop over the lanes, about 2 us for 64: the scan counts the
+    // groups when the experts fit in LDS)
+    if (!small_e && heads) atomicAdd(&n_grp, heads);
+    lds_barrier();
     if (tid == 0) {
         hdr[0] = n_bad;
         hdr[1] = n_grp;
@@ -225,7 +233,7 @@ __global__ __launch_bounds__(64 * RW) void k_route_plan(const float* __restrict_
             lids[t * top_k + lane] = id;
         }
     }
-    __syncthreads();
+    lds_barrier();
     plan_body<64 * RW>(lids, n_tokens * top_k, n_experts, hdr, slot_e, plan, nullptr, 0, 0);
 }
 
