@@ -212,6 +212,8 @@ struct WF<T_Q4_0> {
     // input index of the stage's 8-input chunk c (c = 0..7): contiguous
     __device__ static uint32_t xin(int s, int c) { return (uint32_t)s * 64u + 8u * (uint32_t)c; }
     static constexpr int QK = 32, BB = 18;
+    // (3 loads, the last one's address chosen by full, removes the 8-byte
+    // spill but measured 1.3% slower)
     static constexpr int NLOADS = 4;
     static constexpr int IL = -1;  // 0 / 2 / 3: 6.5% / 6.5% / 4.5% slower
     struct Regs {
@@ -305,16 +307,17 @@ struct WF<T_Q6_K> {
     }
     // slices 2 part, 2 part + 1 use ql / qh bytes 16 part..16 part + 15 of
     // the stage's 32 (into l0 / h0), the scales and d
-    static constexpr int NLOADS = 5;
-    static constexpr int IL = 0;  // 3.8% faster than -1 (2: 2.8%)
+    static constexpr int NLOADS = 4;  // one scale load instead of two: 0.986-0.988 (A-B-B-A, twice)
+    static constexpr int IL = 0;      // 3.8% faster than -1 (2: 2.8%)
     __device__ static void load_part(Rsrc wr, uint32_t woff, int s, bool ok, bool, int part, Regs& r) {
         const uint32_t c4 = (uint32_t)(s & 3), h = c4 >> 1, p = c4 & 1u;
         const uint32_t bo = ok ? woff + (uint32_t)(s >> 2) * BB : 0x80000000u;
         r.l0 = bld16(wr, bo + 64 * h + 32 * p + 16 * part);
         r.h0 = bld16(wr, bo + 128 + 32 * h + 16 * part);
-        const uint32_t sa = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 192 + 8 * h + 2 * p), 0, 0);
-        const uint32_t sb = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 196 + 8 * h + 2 * p), 0, 0);
-        r.sc = sa | (sb << 16);
+        // the 8 scale bytes of half h in one load; the stage's four are
+        // bytes 2p, 2p + 1 (quarter p) and 4 + 2p, 5 + 2p (quarter p + 2)
+        const auto sv = __builtin_amdgcn_raw_buffer_load_b64(wr, (int)(bo + 192 + 8 * h), 0, 0);
+        r.sc = __builtin_amdgcn_perm(sv[1], sv[0], p ? 0x07060302u : 0x05040100u);
         r.d = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wr, (int)(bo + 208), 0, 0);
     }
     __device__ static void expand_part(const Regs& r, const Scl& sc, int s, int j, u32x4& lo, u32x4& hi) {
