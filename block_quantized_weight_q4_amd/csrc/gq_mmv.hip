@@ -447,9 +447,16 @@ struct MF<T_Q4_0> {
 // ql[64 h + 32 (q4 & 1) + l], high 2 bits = bits 2 q4, 2 q4 + 1 of
 // qh[32 h + l]; sub-block (16 weights) 8 h + 2 q4 + l / 16.  Group g loads
 // 16-byte piece g of ql[0..63], ql[64..127] and qh; after transpose4 its dword
-// j of each holds bytes 16 j + 4 g .. 16 j + 4 g + 3, so for sub-block
-// (h, q4, a = l / 16) its k-slots i = 0..3 are l = 16 a + 4 g + i: ql dword
-// 2 (q4 & 1) + a of half h, qh dword 2 h + a.  w = d sc (q - 32): the
+// j of each holds bytes 16 j + 4 p(g) .. 16 j + 4 p(g) + 3, so for sub-block
+// (h, q4, a = l / 16) its k-slots i = 0..3 are l = 16 a + 4 p(g) + i: ql
+// dword 2 (q4 & 1) + a of half h, qh dword 2 h + a.  p(g) = g for fp32
+// activations.  bf16 activations are loaded 16 bytes at a time, group g the
+// inputs 8 g .. 8 g + 7 of a sub-block pair, then v_permlane32_swap gives
+// group g the inputs 4 p(g) .. 4 p(g) + 3 of each sub-block of the pair with
+// p = (0, 2, 1, 3) (half the load instructions of 8-byte loads, which limited
+// this path); the weight pieces' dwords 1 and 2 are exchanged before the
+// transpose to match (the product sums over each sub-block's k, so any order
+// common to both operands gives the same sums).  w = d sc (q - 32): the
 // operand is 4 (q - 32), the byte 4 q with its sign bit flipped, read
 // sign-extended (c = 4).
 template <>
@@ -459,6 +466,8 @@ struct MF<T_Q6_K> {
         u32x4 l0, l1, qh, sc;
         uint32_t d;
     };
+    // fp32: sub-block sb's four inputs per lane; bf16: sub-block pair pp's
+    // eight inputs 8 g.. per lane as loaded
     template <int XT>
     struct X {
         XA4<XT> a[16];  // sub-block index 8 h + 2 q4 + a
@@ -472,15 +481,44 @@ struct MF<T_Q6_K> {
     }
     template <int XT>
     __device__ static void load_x(Rsrc xs, uint32_t xo, uint32_t k0, int g, X<XT>& x) {
-        constexpr uint32_t ESZ = XT == 0 ? 4 : 2;
-        const uint32_t base = xo + ESZ * (k0 + 4 * g);
+        if constexpr (XT == 0) {
+            const uint32_t base = xo + 4 * (k0 + 4 * g);
 #pragma unroll
-        for (int sb = 0; sb < 16; ++sb) x.a[sb].load4(xs, base + ESZ * 16 * sb);
+            for (int sb = 0; sb < 16; ++sb) x.a[sb].load4(xs, base + 4 * 16 * sb);
+        } else {
+            const uint32_t base = xo + 2 * (k0 + 8 * g);
+#pragma unroll
+            for (int pp = 0; pp < 8; ++pp) {
+                const u32x4 v = bld16(xs, base + 2 * 32 * pp);
+                x.a[2 * pp].v = u32x2{v.x, v.y};
+                x.a[2 * pp + 1].v = u32x2{v.z, v.w};
+            }
+        }
     }
     template <int XT, int R>
-    __device__ static void compute(W (&w)[R], const X<XT>& x, int, f32x4 (&y)[R]) {
+    __device__ static void compute(W (&w)[R], const X<XT>& xin, int, f32x4 (&y)[R]) {
+        X<XT> x = xin;
+        if constexpr (XT == 1) {
+            // groups 0, 1 keep inputs 0..3 of their eight and take 0..3 of
+            // groups 2, 3 (the pair's second sub-block); groups 2, 3 keep
+            // 4..7 and take 4..7 of groups 0, 1 (the first sub-block)
+#pragma unroll
+            for (int pp = 0; pp < 8; ++pp) {
+                uint32_t a0 = x.a[2 * pp].v.x, a1 = x.a[2 * pp].v.y;
+                uint32_t b0 = x.a[2 * pp + 1].v.x, b1 = x.a[2 * pp + 1].v.y;
+                swap32(a0, b0);
+                swap32(a1, b1);
+                x.a[2 * pp].v = u32x2{a0, a1};
+                x.a[2 * pp + 1].v = u32x2{b0, b1};
+            }
+        }
 #pragma unroll
         for (int t = 0; t < R; ++t) {
+            if constexpr (XT == 1) {
+                w[t].l0 = u32x4{w[t].l0.x, w[t].l0.z, w[t].l0.y, w[t].l0.w};
+                w[t].l1 = u32x4{w[t].l1.x, w[t].l1.z, w[t].l1.y, w[t].l1.w};
+                w[t].qh = u32x4{w[t].qh.x, w[t].qh.z, w[t].qh.y, w[t].qh.w};
+            }
             transpose4(w[t].l0);
             transpose4(w[t].l1);
             transpose4(w[t].qh);
