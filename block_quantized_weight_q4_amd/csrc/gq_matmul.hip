@@ -23,7 +23,8 @@
 // Pipeline.  LDS holds two stage buffers.  While the MFMAs of stage s read
 // buffer s & 1, the wavefronts fill the other buffer with stage s+1: its W
 // rows expanded to bf16 (the format's fp32 weight, one rounding to nearest
-// even) in slices placed between the k steps, from global loads issued two
+// even) in slices placed among or after a k step's MFMAs (per format:
+// WF<>::IL), from global loads issued two
 // stages ahead into two alternating register sets, and its X rows copied by
 // the global-to-LDS form of the buffer load, issued at the start of stage s
 // and waited for before its end (no registers and no LDS stores for X).  One
