@@ -1000,6 +1000,13 @@ def bench_context(torch, gq, dev, stream, t_):
         "tokens_per_s_equiv_30_layers": round(m.T / (30 * ms * 1e-3), 1)}
     del cp4
     torch.cuda.empty_cache()
+    # the same fused layer for a 64-token block (groups of up to 8 slots:
+    # about 127 groups over 125 distinct experts)
+    m64 = WL.MoeLayer(T=64)
+    ms64 = measure(torch, gq, dev, stream, t_, "moe:64")
+    res["moe_q4_0_128x_h2816_f704_t64_top8_fused_glu"] = {
+        "launches": "as the 8-token fused layer", "us_per_layer": round(ms64 * 1e3, 2),
+        "tokens_per_s_equiv_30_layers": round(m64.T / (30 * ms64 * 1e-3), 1)}
     return res
 
 
