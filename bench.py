@@ -383,13 +383,15 @@ def stats_summary(d: str, out: str):
     # per (kernel, grid) averages from the trace: one kernel serves several shapes
     per = {}
     for r in csv.DictReader(open(trace[0])):
-        k = (r["Kernel_Name"][:80], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        gy = int(r.get("Grid_Size_Y") or 1)
+        grid = r["Grid_Size_X"] if gy == 1 else "%sx%d" % (r["Grid_Size_X"], gy)
+        k = (r["Kernel_Name"][:80], grid, int(r["Workgroup_Size_X"]))
         per.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    lines += ["", "per launch shape (grid = work-items):",
-              "%-80s %9s %5s %7s %10s %10s" % ("kernel", "grid", "wg", "calls", "avg_us", "median_us")]
+    lines += ["", "per launch shape (grid = work-items, x or x by y):",
+              "%-80s %11s %5s %7s %10s %10s" % ("kernel", "grid", "wg", "calls", "avg_us", "median_us")]
     for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         v.sort()
-        lines.append("%-80s %9d %5d %7d %10.3f %10.3f" % (k[0], k[1], k[2], len(v), sum(v) / len(v), v[len(v) // 2]))
+        lines.append("%-80s %11s %5d %7d %10.3f %10.3f" % (k[0], k[1], k[2], len(v), sum(v) / len(v), v[len(v) // 2]))
     with open(out, "a") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
