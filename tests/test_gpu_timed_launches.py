@@ -72,12 +72,12 @@ def test_timed_glu_launch(gq, orc, G):
     assert np.all(err <= bound), float(np.max(err / np.maximum(bound, 1e-300)))
 
 
-def test_timed_moe_layer(gq, orc):
-    """The routed-expert workload exactly as timed: device routing of the
-    seeded logits, gate and up per token (fp32 x), the weighted down
-    projection of seeded per-slot h (fp32) and of the bf16 h the routed gated
-    unit writes."""
-    m = workloads.MOE
+@pytest.mark.parametrize("m", [workloads.MOE, workloads.MoeLayer(T=64)], ids=["tokens8", "tokens64"])
+def test_timed_moe_layer(gq, orc, m):
+    """The routed-expert workload exactly as timed (8 tokens, and the fused
+    layer's 64-token block): device routing of the seeded logits, gate and up
+    per token (fp32 x), the weighted down projection of seeded per-slot h
+    (fp32) and of the bf16 h the routed gated unit writes."""
     ex = m.experts()
     logits = m.logits()
     ids_t = torch.empty((m.T, m.k), dtype=torch.int32, device="cuda")
