@@ -15,6 +15,7 @@ import torch
 
 from block_quantized_weight_q4_amd import synth, workloads
 from tests.test_gpu_dequant_matvec import _name_the_case, check_bound, dev, gq  # noqa: F401
+from tests.test_gpu_matvec_id_glu import check as glu_check, glu_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -113,7 +114,9 @@ def test_timed_moe_layer(gq, orc, m):
     torch.cuda.synchronize()
     hbits = hb.view(torch.int16).cpu().numpy().view(np.uint16)
     hf = synth.bf16_to_f32(hbits)
-    assert np.all(np.isfinite(hf))
+    # h against the oracle's gated unit, with the routed gated unit's bound
+    href, hbound = glu_ref(orc, m.t, ex["gate"], ex["up"], m.E, m.F, m.H, ids, x, "silu", "bf16")
+    glu_check(hf, href, hbound, "routed gated unit h (bf16)")
     # the down projection as timed: it reuses the group table the gated call
     # left in ws; the result equals a call that builds its own, bit for bit
     y = torch.full((m.T, m.H), float("nan"), device="cuda")
