@@ -140,8 +140,8 @@ def pmc_pass():
 
 
 def pmc_moe_pass(meta_path: str):
-    """The fused MoE layer (router + group table, gated unit, weighted down
-    product on that table) on one copy of the experts, 3 times at 8 tokens and
+    """The fused MoE layer (router and gated unit, weighted down product on
+    the group table they leave) on one copy of the experts, 3 times at 8 tokens and
     3 times at 64 tokens (top 8 of 128), then the copy kernel of pmc_pass.
     meta_path gets, per layer in launch order, the token count, the distinct
     experts the router chose, the group count of the table and the bytes of
@@ -162,14 +162,16 @@ def pmc_moe_pass(meta_path: str):
         yd = torch.empty(T, m.H, device=dev)
         ws = torch.zeros(gq.gq_matvec_id_workspace(m.E, T, m.k, m.H), dtype=torch.uint8, device=dev)
         for _ in range(3):
-            gq.gq_route_topk_plan(lg, m.k, ids, rw, ws)
-            gq.gq_matvec_id_glu(m.t, ex["gate"], ex["up"], m.E, m.F, m.H, (T, m.k), x, "silu", hb, ws)
+            gq.gq_route_matvec_id_glu(m.t, ex["gate"], ex["up"], m.E, m.F, m.H, lg, m.k, ids, rw, x, "silu", hb, ws)
             gq.gq_matvec_id(m.t, ex["down"], m.E, m.H, m.F, (T, m.k), hb, True, yd, ws, rw)
             torch.cuda.synchronize()
             hdr = ws[:8].view(torch.int32).cpu().numpy()
-            distinct = int(np.unique(ids.cpu().numpy()).size)
-            meta.append({"tokens": T, "top_k": m.k, "experts": m.E, "distinct_experts": distinct,
-                         "groups": int(hdr[1]), "invalid_ids": int(hdr[0]),
+            _, counts = np.unique(ids.cpu().numpy(), return_counts=True)
+            # groups of at most 8 slots per expert (the table of the one-launch
+            # form is indexed by slot, so its header holds the slot count)
+            groups = int(sum((c + 7) // 8 for c in counts))
+            meta.append({"tokens": T, "top_k": m.k, "experts": m.E, "distinct_experts": int(counts.size),
+                         "groups": groups, "invalid_ids": int(hdr[0]),
                          "expert_matrix_bytes": int(ex["down"].numel() // m.E)})
     src = torch.empty(COPY_BYTES // 4, device=dev).normal_()
     dst = torch.empty_like(src)
@@ -200,21 +202,25 @@ def moe_traffic_summary(fetch_dir: str, write_dir: str, meta_path: str):
               if "vectorized_elementwise_kernel" in r["Kernel_Name"] and "add" in r["Kernel_Name"].lower()]
         assert len(cp) == 1, cp
         factor = (COPY_BYTES / 1024.0) / cp[0]
+        # a layer starts with the routing launch: the routed gated unit (8
+        # tokens) or the router with its table (64 tokens)
         layers, cur = [], None
         for r in rows:
             name = r["Kernel_Name"]
-            if "k_route_plan" in name:
+            if "k_route_plan" in name or "k_experts_routed" in name:
                 cur = []
                 layers.append(cur)
             if cur is not None and ("k_route_plan" in name or "k_experts" in name):
                 cur.append(float(r["Counter_Value"]) * 1024.0 * factor)
-        assert len(layers) == len(meta) and all(len(l) == 3 for l in layers), (len(layers), [len(l) for l in layers])
+        assert len(layers) == len(meta) and all(len(l) in (2, 3) for l in layers), (
+            len(layers), [len(l) for l in layers])
         per_ctr[ctr] = (layers, factor)
     out = ["# HBM traffic of the fused MoE layer (128 Q4_0 experts, hidden 2816, FFN 704, top 8) at 8 and 64 tokens",
            "",
-           "kernels: k_route_plan (router + group table), k_experts GLU form (gate|up + SiLU, bf16 h),",
-           "k_experts weighted down product on the same table; one copy of the experts, so every layer",
-           "reads its experts from HBM or the last-level cache, not from L2 (4 MB per XCD)",
+           "kernels: 8 tokens: k_experts_routed (routing + gate|up + SiLU, bf16 h), then the weighted down",
+           "product k_experts on the table it leaves; 64 tokens: k_route_plan (router + group table), the",
+           "k_experts GLU form, the weighted down product on that table; one copy of the experts, so every",
+           "layer reads its experts from HBM or the last-level cache, not from L2 (4 MB per XCD)",
            "source_sha256: %s" % source_hash(MOE_SOURCES),
            "commands (from the repository root, on the GPU host):",
            "  timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -- python3 bench.py "
@@ -236,7 +242,8 @@ def moe_traffic_summary(fetch_dir: str, write_dir: str, meta_path: str):
         out.append("%-7d %9d %7d %14.0f %14d %14d %9.4f %9.4f" % (m["tokens"], m["distinct_experts"], m["groups"],
                                                                   fetch, dist_b, grp_b, fetch / dist_b,
                                                                   fetch / grp_b))
-    out += ["", "read_bytes: FETCH_SIZE of the layer's three dispatches (weights, activations, logits, the table);",
+    out += ["", "read_bytes: FETCH_SIZE of the layer's routing and product dispatches (weights, activations, logits,",
+            "the table);",
             "written bytes per layer (WRITE_SIZE): " + ", ".join(
                 "%.0f" % sum(l) for l in per_ctr["WRITE_SIZE"][0])]
     with open(MOE_TRAFFIC_FILE, "w") as f:
@@ -742,9 +749,12 @@ def measure(torch, gq, dev, stream, t_, workload: str) -> float:
                     gq.gq_matvec(L.t, c[L.name], L.N, L.K, xs[L.name], ys[L.name], stream)
 
         return float(np.median(Timer(torch, run, stream).replays(2 * MIN_REPS))) / nc
-    if workload in ("moe", "moe:64"):
-        # the fused MoE layer at 8 tokens ("moe", the context workload) or 64
-        m = WL.MOE if workload == "moe" else WL.MoeLayer(T=64)
+    if workload in ("moe", "moe:64", "moe:split"):
+        # the fused MoE layer at 8 tokens ("moe", the context workload) or 64;
+        # "moe:split": at 8 tokens with the router and its table in a launch
+        # of their own before the gated unit
+        m = WL.MoeLayer(T=64) if workload == "moe:64" else WL.MOE
+        split = workload == "moe:split"
         ex = m.experts()
         nb = sum(v.nbytes for v in ex.values())
         cps = [{k: t_(v) for k, v in ex.items()} for _ in range(n_copies(nb))]
@@ -757,8 +767,13 @@ def measure(torch, gq, dev, stream, t_, workload: str) -> float:
 
         def run():
             for c in cps:
-                gq.gq_route_topk_plan(lg, m.k, ids, rw, ws, stream)
-                gq.gq_matvec_id_glu(m.t, c["gate"], c["up"], m.E, m.F, m.H, (m.T, m.k), x4, "silu", hb, ws, stream)
+                if split:
+                    gq.gq_route_topk_plan(lg, m.k, ids, rw, ws, stream)
+                    gq.gq_matvec_id_glu(m.t, c["gate"], c["up"], m.E, m.F, m.H, (m.T, m.k), x4, "silu", hb, ws,
+                                        stream)
+                else:
+                    gq.gq_route_matvec_id_glu(m.t, c["gate"], c["up"], m.E, m.F, m.H, lg, m.k, ids, rw, x4, "silu",
+                                              hb, ws, stream)
                 gq.gq_matvec_id(m.t, c["down"], m.E, m.H, m.F, (m.T, m.k), hb, True, yd, ws, rw, stream)
 
         return float(np.median(Timer(torch, run, stream).replays(2 * MIN_REPS))) / len(cps)
@@ -770,7 +785,8 @@ def measure(torch, gq, dev, stream, t_, workload: str) -> float:
         Y5 = torch.empty(L.M, L.N, device=dev)
         return float(np.median(Timer(torch, lambda: gq.gq_matmul(L.t, W5, L.N, L.K, X5, Y5, stream),
                                      stream).replays(30, warm=60)))
-    raise SystemExit("unknown workload %r (headline, moe, moe:64, prefill, prefill:q6_k, prefill:q4_0)" % workload)
+    raise SystemExit("unknown workload %r (headline, moe, moe:64, moe:split, prefill, prefill:q6_k, prefill:q4_0)"
+                     % workload)
 
 
 def abba(lib_a: str, lib_b: str, rounds: int, workload: str):
@@ -997,6 +1013,21 @@ def bench_context(torch, gq, dev, stream, t_):
     ms = float(np.median(Timer(torch, p5, stream).replays(MIN_REPS))) / len(cp4)
     res["moe_q4_0_128x_h2816_f704_t8_top8_fused_glu"] = {
         "launches": "route_topk + group table, gate|up + SiLU (bf16 h), down (weighted), both on that table",
+        "us_per_layer": round(ms * 1e3, 2), "distinct_experts": distinct, "packed_bytes_read": read_bytes,
+        "GBps": round(read_bytes / (ms * 1e-3) / 1e9, 1),
+        "tokens_per_s_equiv_30_layers": round(m.T / (30 * ms * 1e-3), 1)}
+
+    # the routing inside the gated unit's launch (every workgroup routes the
+    # 8 tokens itself): three launches per layer
+    def p6():
+        for c in cp4:
+            gq.gq_route_matvec_id_glu(m.t, c["gate"], c["up"], m.E, m.F, m.H, lg_t, m.k, ids_t, rw_t, x4, "silu",
+                                      hb, ws[0], stream)
+            gq.gq_matvec_id(m.t, c["down"], m.E, m.H, m.F, (m.T, m.k), hb, True, yd, ws[0], rw_t, stream)
+
+    ms = float(np.median(Timer(torch, p6, stream).replays(MIN_REPS))) / len(cp4)
+    res["moe_q4_0_128x_h2816_f704_t8_top8_fused_routed_glu"] = {
+        "launches": "route_topk inside gate|up + SiLU (bf16 h), down (weighted) on the table it leaves",
         "us_per_layer": round(ms * 1e3, 2), "distinct_experts": distinct, "packed_bytes_read": read_bytes,
         "GBps": round(read_bytes / (ms * 1e-3) / 1e9, 1),
         "tokens_per_s_equiv_30_layers": round(m.T / (30 * ms * 1e-3), 1)}

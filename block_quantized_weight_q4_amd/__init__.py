@@ -10,7 +10,7 @@ The binding is loaded on first use, so ``block_quantized_weight_q4_amd.synth``
 __all__ = [
     "gq_abi_version", "gq_block_info", "gq_dequant", "gq_matvec", "gq_matvec_id",
     "gq_matvec_id_workspace", "gq_matvec_id_check", "gq_matmul", "gq_route_topk", "gq_matvec_glu",
-    "gq_matvec_id_glu", "gq_matvec_id_noalloc", "gq_route_topk_plan", "GqError", "TYPES", "lib_path",
+    "gq_matvec_id_glu", "gq_matvec_id_noalloc", "gq_route_topk_plan", "gq_route_matvec_id_glu", "GqError", "TYPES", "lib_path",
 ]
 
 

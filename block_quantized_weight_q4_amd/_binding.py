@@ -45,13 +45,16 @@ _lib.gq_matmul.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_int, I64, I64,
 _lib.gq_route_topk.argtypes = [P, I32, I32, I32, P, P, P]
 if hasattr(_lib, "gq_route_topk_plan"):
     _lib.gq_route_topk_plan.argtypes = [P, I32, I32, I32, P, P, P, SZ, P]
+if hasattr(_lib, "gq_route_matvec_id_glu"):
+    _lib.gq_route_matvec_id_glu.argtypes = [ctypes.c_int, P, P, I32, I64, I64, P, I32, I32, P, P, P, ctypes.c_int,
+                                            ctypes.c_int, P, ctypes.c_int, P, SZ, P]
 _lib.gq_matvec_glu.argtypes = [ctypes.c_int, P, P, I64, I64, P, ctypes.c_int, I32, ctypes.c_int, P, ctypes.c_int, P]
 _lib.gq_matvec_id_glu.argtypes = [ctypes.c_int, P, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, ctypes.c_int, P,
                                   ctypes.c_int, P, SZ, P]
 ACTS = {"silu": 0, "gelu_tanh": 1}
 for _f in ("gq_block_info", "gq_dequant", "gq_matvec", "gq_matvec_id_workspace", "gq_matvec_id", "gq_matvec_id_noalloc",
            "gq_matvec_id_check", "gq_matmul", "gq_route_topk", "gq_route_topk_plan", "gq_matvec_glu",
-           "gq_matvec_id_glu"):
+           "gq_matvec_id_glu", "gq_route_matvec_id_glu"):
     if hasattr(_lib, _f):
         getattr(_lib, _f).restype = ctypes.c_int
 
@@ -371,6 +374,39 @@ def gq_route_topk_plan(logits: torch.Tensor, top_k: int, ids: torch.Tensor, weig
     _check("gq_route_topk_plan", _lib.gq_route_topk_plan(_ptr(logits), n_tokens, n_experts, top_k, _ptr(ids),
                                                          _ptr(weights), _ptr(ws), ws.numel(), _stream(stream)))
     return ids, weights
+
+
+def gq_route_matvec_id_glu(t, experts_gate: torch.Tensor, experts_up: torch.Tensor, n_experts: int, N: int, K: int,
+                           logits: torch.Tensor, top_k: int, ids: torch.Tensor, weights: torch.Tensor, x: torch.Tensor,
+                           act: str, h: torch.Tensor, ws: torch.Tensor, stream=None) -> torch.Tensor:
+    """gq_route_topk_plan then gq_matvec_id_glu on the table it leaves (one
+    launch where the sizes allow): ids, weights and h as those two calls write
+    them; later products may take ids as a (n_tokens, top_k) tuple."""
+    _tensor("logits", logits, _F32)
+    _tensor("ids", ids, _I32)
+    _tensor("weights", weights, _F32)
+    _tensor("x", x, _ACT)
+    _tensor("h", h, _ACT)
+    _need(logits.dim() == 2 and logits.shape[1] == n_experts, "logits must be [n_tokens][n_experts]")
+    n_tokens = logits.shape[0]
+    _need(ids.numel() == n_tokens * top_k and weights.numel() == n_tokens * top_k,
+          "ids / weights must hold n_tokens * top_k elements")
+    _need(act in ACTS, "act must be one of %s" % sorted(ACTS))
+    rows = max(n_experts, 0) * N if n_tokens and N else 0
+    _weights("experts_gate", experts_gate, t, rows, K)
+    _weights("experts_up", experts_up, t, rows, K)
+    _workspace(ws)
+    for name, v in (("logits", logits), ("ids", ids), ("weights", weights), ("x", x), ("h", h)):
+        _contig(name, v)
+    _need(x.numel() == n_tokens * K, "x must hold n_tokens x K = %d x %d elements" % (n_tokens, K))
+    _need(h.numel() >= n_tokens * top_k * N, "h holds %d elements, fewer than n_tokens * top_k * N" % h.numel())
+    _on_gpu(experts_gate=experts_gate, experts_up=experts_up, logits=logits, ids=ids, weights=weights, x=x, h=h, ws=ws)
+    _check("gq_route_matvec_id_glu",
+           _lib.gq_route_matvec_id_glu(_type(t), _ptr(experts_gate), _ptr(experts_up), n_experts, N, K, _ptr(logits),
+                                       n_tokens, top_k, _ptr(ids), _ptr(weights), _ptr(x), _DTYPES[x.dtype], ACTS[act],
+                                       _ptr(h), _DTYPES[h.dtype], _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream)))
+    return h
 
 
 # raw handle for the tests that check the exported symbols

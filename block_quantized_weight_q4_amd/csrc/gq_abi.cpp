@@ -235,6 +235,37 @@ gq_status gq_route_topk_plan(const float* logits, int32_t n_tokens, int32_t n_ex
     }
 }
 
+gq_status gq_route_matvec_id_glu(gq_type t, const void* experts_gate, const void* experts_up, int32_t n_experts,
+                                 int64_t N, int64_t K, const float* logits, int32_t n_tokens, int32_t top_k,
+                                 int32_t* ids, float* weights, const void* x, gq_dtype x_dtype, gq_act act, void* h,
+                                 gq_dtype h_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!known_type(t)) return GQ_ERR_TYPE;
+    if (x_dtype != GQ_F32 && x_dtype != GQ_BF16) return GQ_ERR_DTYPE;
+    if (h_dtype != GQ_F32 && h_dtype != GQ_BF16) return GQ_ERR_DTYPE;
+    if (n_experts < 1 || n_tokens < 0 || top_k < 1 || top_k > n_experts || N < 0 || K < 0 ||
+        K % qk_of(t) != 0 || (int64_t)n_tokens * top_k > 1024)
+        return GQ_ERR_SHAPE;
+    if ((int64_t)n_tokens * n_experts > MAX_ELEMS) return GQ_ERR_SHAPE;
+    if (N > MAX_ELEMS || K > MAX_K_DECODE || (K > 0 && N > MAX_ELEMS / K) ||
+        (K > 0 && N > 0 && (int64_t)n_experts > MAX_ELEMS / (N * K)))
+        return GQ_ERR_SHAPE;
+    if (n_experts > 4096 || top_k > 64) return GQ_ERR_UNSUPPORTED;
+    if (act != GQ_ACT_SILU && act != GQ_ACT_GELU_TANH) return GQ_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return GQ_OK;
+    if (!logits || !ids || !weights || !ws || (N > 0 && !h) || (N > 0 && K > 0 && (!experts_gate || !experts_up || !x)))
+        return GQ_ERR_NULL;
+    if (!aligned16(logits) || !aligned16(ids) || !aligned16(weights) || !aligned16(ws) || (N > 0 && !aligned16(h)) ||
+        (N > 0 && K > 0 && (!aligned16(experts_gate) || !aligned16(experts_up) || !aligned16(x))))
+        return GQ_ERR_ALIGN;
+    if (ws_bytes < gqk_matvec_id_ws_bytes(n_experts, n_tokens, top_k, N)) return GQ_ERR_WORKSPACE;
+    try {
+        return from_hip(gqk_route_matvec_id_glu(t, experts_gate, experts_up, n_experts, N, K, logits, n_tokens, top_k,
+                                                ids, weights, x, x_dtype, act, h, h_dtype, ws, stream));
+    } catch (...) {
+        return GQ_ERR_LAUNCH;
+    }
+}
+
 gq_status gq_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t top_k, int32_t* ids,
                         float* weights, hipStream_t stream) {
     if (n_tokens < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts) return GQ_ERR_SHAPE;

@@ -45,6 +45,13 @@ hipError_t gqk_matmul(int type, const void* W, int64_t N, int64_t K, const void*
 
 hipError_t gqk_route_topk(const float* logits, int n_tokens, int n_experts, int top_k, int32_t* ids, float* w,
                           hipStream_t s);
+// Routing and the routed gated unit (gq_matvec_id.hip): ids, weights, h and
+// the group table in ws, as gqk_route_topk_plan then gqk_matvec_id_glu with
+// no ids.
+hipError_t gqk_route_matvec_id_glu(int type, const void* experts_gate, const void* experts_up, int n_experts,
+                                   int64_t N, int64_t K, const float* logits, int n_tokens, int top_k, int32_t* ids,
+                                   float* w, const void* x, int x_dtype, int act, void* h, int h_dtype, void* ws,
+                                   hipStream_t s);
 // Routing plus the routed products' group table in ws (gq_matvec_id.hip).
 hipError_t gqk_route_topk_plan(const float* logits, int n_tokens, int n_experts, int top_k, int32_t* ids, float* w,
                                void* ws, hipStream_t s);

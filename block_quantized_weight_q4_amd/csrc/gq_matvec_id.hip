@@ -263,24 +263,15 @@ __host__ __device__ inline int tile_for(int64_t units, int nb, int LPR) {
 // workgroup covers 2 SR rows, wavefronts 0, 1 computing the gate rows and
 // wavefronts 2, 3 the same rows of the up matrix (on the activations they
 // stage together), and out[slot][n] = act(gate) * up, fp32 or bf16 (out_bf16).
+// Row tile blockIdx.x of the product of one group: entry en (expert e, nb >= 1
+// slots; en may point to global or LDS memory).
 template <int TYPE, int XT, int D, bool RING, bool GLU>
-__global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict__ experts,
-                                                      const uint8_t* __restrict__ experts_up, int64_t expert_bytes,
-                                                      int64_t N, int64_t K, const uint8_t* __restrict__ x,
-                                                      int x_per_slot, int top_k, int n_experts, int S,
-                                                      const int* __restrict__ ws_hdr, const Entry* __restrict__ plan,
-                                                      void* __restrict__ out, int out_bf16, int act, int LPR) {
-    extern __shared__ __align__(16) uint8_t lds[];
-    const int tid = threadIdx.x, g = blockIdx.y;
-    // the group count and this workgroup's entry, loaded together (the grid
-    // has one row per table entry, so plan[g] exists even when unused)
-    const int n_groups = ws_hdr[1];
-    const Entry* en = plan + g;
-    // fields clamped to their ranges: a workspace that holds no table (a
-    // caller's mistake when ids are not given) then gives wrong numbers but
-    // no access outside the experts, the activations or the outputs
-    const int nb = min(max(en->nb, 0), CH), e = min(max(en->e, 0), n_experts - 1);
-    if (g >= n_groups) return;
+__device__ __forceinline__ void experts_tile(const uint8_t* __restrict__ experts,
+                                             const uint8_t* __restrict__ experts_up, int64_t expert_bytes, int64_t N,
+                                             int64_t K, const uint8_t* __restrict__ x, int x_per_slot, int top_k,
+                                             int S, const Entry* en, int nb, int e, void* __restrict__ out,
+                                             int out_bf16, int act, int LPR, uint8_t* lds) {
+    const int tid = threadIdx.x;
     const int tile_units = tile_for<Fmt<TYPE>>(K / Fmt<TYPE>::UW, nb, LPR);
     const int64_t rpw = (int64_t)(GLU ? 2 : NTHREADS >> 6) * (64 / LPR);
     const int64_t rowA = (int64_t)blockIdx.x * rpw;
@@ -322,6 +313,164 @@ __global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict_
             else static_cast<float*>(out)[o] = v;
         }
     }
+}
+
+template <int TYPE, int XT, int D, bool RING, bool GLU>
+__global__ __launch_bounds__(NTHREADS) void k_experts(const uint8_t* __restrict__ experts,
+                                                      const uint8_t* __restrict__ experts_up, int64_t expert_bytes,
+                                                      int64_t N, int64_t K, const uint8_t* __restrict__ x,
+                                                      int x_per_slot, int top_k, int n_experts, int S,
+                                                      const int* __restrict__ ws_hdr, const Entry* __restrict__ plan,
+                                                      void* __restrict__ out, int out_bf16, int act, int LPR) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int g = blockIdx.y;
+    // the group count and this workgroup's entry, loaded together (the grid
+    // has one row per table entry, so plan[g] exists even when unused)
+    const int n_groups = ws_hdr[1];
+    const Entry* en = plan + g;
+    // fields clamped to their ranges: a workspace that holds no table (a
+    // caller's mistake when ids are not given) then gives wrong numbers but
+    // no access outside the experts, the activations or the outputs.  An
+    // entry of no slots is a slot that heads no group in a table indexed by
+    // slot (k_experts_routed's).
+    const int nb = min(max(en->nb, 0), CH), e = min(max(en->e, 0), n_experts - 1);
+    if (g >= n_groups || nb == 0) return;
+    experts_tile<TYPE, XT, D, RING, GLU>(experts, experts_up, expert_bytes, N, K, x, x_per_slot, top_k, S, en, nb, e,
+                                         out, out_bf16, act, LPR, lds);
+}
+
+// The gated unit with the routing in the same launch, for at most 8 tokens,
+// 64 slots and 128 experts.  Row blockIdx.y of the grid stands for slot
+// s = t * top_k + j, and each workgroup finds the group that s heads, if any,
+// without a table: the expert e of s is the key of rank j among token t's
+// (the 64-bit keys of gq_route_topk: the logit's order-preserving image above
+// the complemented id), found bit by bit from the top -- the largest v with
+// more than j keys >= v -- by wavefront ballots; the slots of e are then, for
+// each token u, slot u * top_k + r when the rank r of e's key among token u's
+// keys is below top_k.  s heads a group when its rank among the slots of e
+// (slot order) is a multiple of CH, and the group is s and the next slots of
+// e, at most CH: the groups k_plan forms, each computed in the same order, so
+// h is identical to routing and a k_experts launch.  Workgroups of the other
+// slots exit.  For the later products of the layer, the workgroups of row
+// tile 0 leave a table indexed by slot in the workspace (entry s: the group
+// that s heads, or no slots), the slots' experts, the header (no invalid ids,
+// S entries), and slot s's id and weight, which they take from the router's
+// own step (gq_route_topk's top_k rounds and softmax) so that both are
+// bit-identical to gq_route_topk's.
+constexpr int ROUTE_NI = 2;    // keys per lane: up to 128 experts
+constexpr int ROUTE_TMAX = 8;  // tokens
+
+// (the load is unconditional, from a clamped index, so that the loads of all
+// the keys are issued before the first wait)
+__device__ __forceinline__ uint64_t route_key(const float* __restrict__ l, int ex, int n_experts, bool valid) {
+    const float v = l[ex < n_experts ? ex : n_experts - 1];
+    const uint64_t keep = 0ull - (uint64_t)(valid && ex < n_experts);  // all ones or zero
+    return (((uint64_t)gqr::order_key(v) << 32) | (uint32_t)~(uint32_t)ex) & keep;
+}
+
+// number of the wavefront's keys (ROUTE_NI per lane) >= v, or > v (GT)
+template <bool GT>
+__device__ __forceinline__ int keys_above(const uint64_t (&k)[ROUTE_NI], uint64_t v) {
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < ROUTE_NI; ++i) c += __popcll(__ballot(GT ? k[i] > v : k[i] >= v));
+    return c;
+}
+
+template <int TYPE, int XT, int D, bool RING>
+__global__ __launch_bounds__(NTHREADS) void k_experts_routed(
+    const uint8_t* __restrict__ gate, const uint8_t* __restrict__ up, int64_t expert_bytes, int64_t N, int64_t K,
+    const uint8_t* __restrict__ x, const float* __restrict__ logits, int n_tokens, int top_k, int n_experts,
+    int32_t* __restrict__ ids, float* __restrict__ weights, int* __restrict__ hdr, int* __restrict__ slot_e,
+    Entry* __restrict__ plan, void* __restrict__ out, int out_bf16, int act, int LPR) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ Entry le;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int S = n_tokens * top_k, s = blockIdx.y, t = s / top_k, j = s - t * top_k;
+    const bool writer = blockIdx.x == 0;
+    // every token's keys, token t's apart; the empty asm statements take
+    // every loaded value before the first use, so that all the loads are in
+    // flight together (left to itself the compiler issues the later tokens'
+    // loads one round trip after the search)
+    uint64_t key[ROUTE_TMAX][ROUTE_NI], kt[ROUTE_NI];
+#pragma unroll
+    for (int u = 0; u < ROUTE_TMAX; ++u)
+#pragma unroll
+        for (int i = 0; i < ROUTE_NI; ++i)
+            key[u][i] = route_key(logits + (int64_t)min(u, n_tokens - 1) * n_experts, lane + 64 * i, n_experts,
+                                  u < n_tokens);
+#pragma unroll
+    for (int i = 0; i < ROUTE_NI; ++i)
+        kt[i] = route_key(logits + (int64_t)t * n_experts, lane + 64 * i, n_experts, true);
+#pragma unroll
+    for (int u = 0; u < ROUTE_TMAX; ++u)
+#pragma unroll
+        for (int i = 0; i < ROUTE_NI; ++i) asm volatile("" : : "v"(key[u][i]));
+    // the key of rank j: its high half bit by bit, then the id bits (every
+    // real key's low half is ~id with id < 128, so its 25 upper bits are set)
+    uint64_t v = 0;
+    for (int b = 63; b >= 32; --b) {
+        const uint64_t c = v | (1ull << b);
+        if (keys_above<false>(kt, c) > j) v = c;
+    }
+    v |= 0xFFFFFF80ull;
+    for (int b = 6; b >= 0; --b) {
+        const uint64_t c = v | (1ull << b);
+        if (keys_above<false>(kt, c) > j) v = c;
+    }
+    const int e = min(max((int)~(uint32_t)v, 0), n_experts - 1);  // (in range by construction)
+    // the slots of e: token u holds e at rank r < top_k as slot u * top_k + r
+    uint64_t same = 0;
+#pragma unroll
+    for (int u = 0; u < ROUTE_TMAX; ++u) {
+        const uint64_t kh = ROUTE_NI == 1 || e < 64 ? key[u][0] : key[u][ROUTE_NI - 1];
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(kh >> 32), e & 63);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)kh, e & 63);
+        const int r = keys_above<true>(key[u], ((uint64_t)hi << 32) | lo);
+        if (u < n_tokens && r < top_k) same |= 1ull << (u * top_k + r);
+    }
+    const uint64_t below = same & ((1ull << s) - 1ull);  // s < S <= 64
+    const uint64_t from = same & ~below;                 // s and the later slots of e
+    const int nb = __popcll(below) % CH ? 0 : min(CH, __popcll(from));
+    int sel = s;  // lane i < nb: the i-th slot of the group
+    uint64_t m = from;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int b = __ffsll((unsigned long long)m) - 1;
+        if (lane == i && i < nb) sel = b;
+        m &= m - 1ull;
+    }
+    if (writer && wave == 0) {
+        int id;
+        float w;
+        gqr::route_token<ROUTE_NI>(logits + (int64_t)t * n_experts, n_experts, top_k, lane, id, w);
+        if (lane == j) {
+            ids[s] = id;
+            weights[s] = w;
+        }
+        if (lane < CH) plan[s].sel[lane] = sel;
+        if (lane == 0) {
+            plan[s].e = e;
+            plan[s].nb = nb;
+            slot_e[s] = e;
+            if (s == 0) {
+                hdr[0] = 0;
+                hdr[1] = S;
+            }
+        }
+    }
+    if (nb == 0) return;
+    if (wave == 0) {
+        if (lane < CH) le.sel[lane] = sel;
+        if (lane == 0) {
+            le.e = e;
+            le.nb = nb;
+        }
+    }
+    lds_barrier();
+    experts_tile<TYPE, XT, D, RING, true>(gate, up, expert_bytes, N, K, x, 0, top_k, S, &le, nb, e, out, out_bf16,
+                                          act, LPR, lds);
 }
 
 // ------------------------------------------------------------- combine ----
@@ -369,6 +518,12 @@ struct Job {
     void* out;
     int out_bf16, act;
     bool zero_bad;  // invalid slots' output rows are the caller's (zero them)
+    // the gated unit routing its tokens itself (k_experts_routed): logits in,
+    // ids and weights out
+    const float* logits = nullptr;
+    int n_tokens = 0;
+    int32_t* ids_out = nullptr;
+    float* w_out = nullptr;
 };
 
 template <int TYPE, int XT, int D, bool RING = false>
@@ -379,6 +534,13 @@ hipError_t launch_experts_d(const Plan& p, const WsLayout& L, const Job& j, hipS
     const int64_t rpw = (int64_t)(glu ? 2 : NTHREADS >> 6) * (64 / p.LPR);
     const int64_t gy = (j.N + rpw - 1) / rpw;
     if (L.Gmax > 65535 || gy > 0x7fffffff) return hipErrorInvalidValue;
+    if (j.logits) {
+        hipLaunchKernelGGL((k_experts_routed<TYPE, XT, D, RING>), dim3((unsigned)gy, (unsigned)L.S), dim3(NTHREADS),
+                           p.lds, s, j.experts, j.up, expert_bytes, j.N, j.K, j.x, j.logits, j.n_tokens, j.top_k,
+                           j.n_experts, j.ids_out, j.w_out, j.ws_hdr, j.slot_e, j.plan, j.out, j.out_bf16, j.act,
+                           p.LPR);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)gy, (unsigned)L.Gmax);
     if (glu)
         hipLaunchKernelGGL((k_experts<TYPE, XT, D, RING, true>), grid, dim3(NTHREADS), p.lds, s, j.experts, j.up,
@@ -509,6 +671,34 @@ hipError_t gqk_matvec_id_glu(int type, const void* experts_gate, const void* exp
                 static_cast<const uint8_t*>(x), 0, top_k, n_experts, ids, reinterpret_cast<int*>(w),
                 reinterpret_cast<int*>(w + L.off_slot), reinterpret_cast<Entry*>(w + L.off_plan), h,
                 h_dtype == DT_BF16 ? 1 : 0, act, true};
+    return launch_type(type, L, j, x_dtype, s);
+}
+
+hipError_t gqk_route_matvec_id_glu(int type, const void* experts_gate, const void* experts_up, int n_experts,
+                                   int64_t N, int64_t K, const float* logits, int n_tokens, int top_k, int32_t* ids,
+                                   float* w, const void* x, int x_dtype, int act, void* h, int h_dtype, void* ws,
+                                   hipStream_t s) {
+    const WsLayout L = layout(n_experts, n_tokens, top_k, N);
+    if (L.S > MAX_SLOTS) return hipErrorInvalidValue;
+    // the one-launch form needs the slots in one wavefront's lanes, the
+    // logits in ROUTE_NI per lane, and a table slot for every slot (the later
+    // products' grids have Gmax rows); otherwise the router with the table,
+    // then the gated unit on it
+    if (n_tokens > ROUTE_TMAX || L.S > 64 || n_experts > 64 * ROUTE_NI || L.S > L.Gmax || N == 0 || K == 0) {
+        const hipError_t e = gqk_route_topk_plan(logits, n_tokens, n_experts, top_k, ids, w, ws, s);
+        if (e != hipSuccess || N == 0) return e;
+        return gqk_matvec_id_glu(type, experts_gate, experts_up, n_experts, N, K, nullptr, n_tokens, top_k, x,
+                                 x_dtype, act, h, h_dtype, ws, s);
+    }
+    uint8_t* b = static_cast<uint8_t*>(ws);
+    Job j{static_cast<const uint8_t*>(experts_gate), static_cast<const uint8_t*>(experts_up), N, K,
+          static_cast<const uint8_t*>(x), 0, top_k, n_experts, nullptr, reinterpret_cast<int*>(b),
+          reinterpret_cast<int*>(b + L.off_slot), reinterpret_cast<Entry*>(b + L.off_plan), h,
+          h_dtype == DT_BF16 ? 1 : 0, act, true};
+    j.logits = logits;
+    j.n_tokens = n_tokens;
+    j.ids_out = ids;
+    j.w_out = w;
     return launch_type(type, L, j, x_dtype, s);
 }
 

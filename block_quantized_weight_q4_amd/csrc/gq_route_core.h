@@ -71,11 +71,15 @@ __device__ __forceinline__ void route_token(const float* __restrict__ l, int n_e
                                             int& id, float& weight) {
     // key 0 marks an empty or already chosen position: every real key is
     // larger, since its low half (the complemented id) is never zero.
+    // (each load is unconditional, from a clamped index, and masked
+    // afterwards: as a conditional load each would wait for the one before)
     uint64_t key[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int e = lane + 64 * i;
-        key[i] = e < n_experts ? ((uint64_t)order_key(l[e]) << 32) | (uint32_t)~(uint32_t)e : 0ull;
+        const float v = l[e < n_experts ? e : n_experts - 1];
+        const uint64_t keep = 0ull - (uint64_t)(e < n_experts);
+        key[i] = (((uint64_t)order_key(v) << 32) | (uint32_t)~(uint32_t)e) & keep;
     }
     int my_id = 0;
     float my_logit = 0.f;

@@ -182,8 +182,8 @@ gq_status gq_matvec_id_workspace(int32_t n_experts, int32_t n_tokens, int32_t to
  * ws: device workspace of at least gq_matvec_id_workspace bytes; its contents
  * need no initialisation.  Each call given ids leaves in ws the table of
  * groups it built from them.  ids may be NULL: the call then uses the table
- * already in ws -- left by gq_route_topk_plan or by the previous routed call
- * (gq_matvec_id or gq_matvec_id_glu) made with the same ws, n_experts,
+ * already in ws -- left by gq_route_topk_plan, gq_route_matvec_id_glu or the
+ * previous routed call (gq_matvec_id or gq_matvec_id_glu) made with the same ws, n_experts,
  * n_tokens, top_k and ids -- and builds none, so that the products of one
  * layer share one table; ws must still be large enough for this call's N.
  * (Table fields are clamped to their ranges, so a workspace that holds no
@@ -279,6 +279,28 @@ gq_status gq_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts
  * table alone).  n_tokens * top_k <= 1024; other limits as gq_route_topk. */
 gq_status gq_route_topk_plan(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t top_k,
                              int32_t* ids, float* weights, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* gq_route_topk_plan followed by gq_matvec_id_glu with ids == NULL, in one
+ * launch where it fits: the router of a routed feed-forward block (kernel
+ * table row "topk" of "GGUF in transformers", section "Reusing ggml's Metal
+ * kernels") and its gated unit (the routed 4-bit experts of the Architecture
+ * section of the Gemma 4 26B-A4B Show HN page).  logits: fp32
+ * [n_tokens][n_experts]; ids, weights: [n_tokens][top_k] as gq_route_topk
+ * writes them (bit-identical); h: [n_tokens][top_k][N] as gq_matvec_id_glu
+ * computes it from those ids (bit-identical); ws: at least
+ * gq_matvec_id_workspace(n_experts, n_tokens, top_k, N') bytes, N' the
+ * largest N of this call and the products that follow, which may then be
+ * called with ids == NULL (a down projection by gq_matvec_id with
+ * x_per_slot == 1 and route_w = weights).  The one-launch form needs
+ * n_tokens * top_k <= 64, n_experts <= 128 and n_tokens * top_k <= n_experts
+ * (one top-8 step of up to 8 tokens over 128 experts); every workgroup of it
+ * routes all the tokens itself.  Other sizes take the two launches.  Limits,
+ * x_dtype, h_dtype and act as gq_route_topk and gq_matvec_id_glu; N == 0
+ * routes only; n_tokens == 0 is a no-op. */
+gq_status gq_route_matvec_id_glu(gq_type t, const void* experts_gate, const void* experts_up, int32_t n_experts,
+                                 int64_t N, int64_t K, const float* logits, int32_t n_tokens, int32_t top_k,
+                                 int32_t* ids, float* weights, const void* x, gq_dtype x_dtype, gq_act act, void* h,
+                                 gq_dtype h_dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Prefill product Y[m][n] = sum_k X[m][k] * w[n][k] for 0 <= m < M, 0 <= n < N.
  * X: [M][ldx] of x_dtype (row stride ldx >= K elements); Y: [M][ldy] fp32

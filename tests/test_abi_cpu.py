@@ -37,6 +37,8 @@ def lib(gq_lib_path):
     L.gq_matvec_glu.argtypes = [ctypes.c_int, P, P, I64, I64, P, ctypes.c_int, I32, ctypes.c_int, P, ctypes.c_int, P]
     L.gq_matvec_id_glu.argtypes = [ctypes.c_int, P, P, I32, I64, I64, P, I32, I32, P, ctypes.c_int, ctypes.c_int, P,
                                    ctypes.c_int, P, SZ, P]
+    L.gq_route_matvec_id_glu.argtypes = [ctypes.c_int, P, P, I32, I64, I64, P, I32, I32, P, P, P, ctypes.c_int,
+                                         ctypes.c_int, P, ctypes.c_int, P, SZ, P]
     return L
 
 
@@ -48,7 +50,7 @@ def declared_functions() -> list[str]:
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -295,3 +297,36 @@ def test_route_topk_plan_validation(lib):
         assert call(**{"a%d" % i: MIS}) == GQ_ERR_ALIGN, i
     assert call(a7=need - 1) == GQ_ERR_WORKSPACE
     assert call(a1=0, a0=None, a4=None, a5=None, a6=None) == GQ_OK  # no tokens: no-op
+
+
+def test_route_matvec_id_glu_validation(lib):
+    """Routing and the routed gated unit in one call: the union of the router's
+    and the gated unit's checks, all on the host."""
+    f = lib.gq_route_matvec_id_glu
+    need = ctypes.c_size_t()
+    assert lib.gq_matvec_id_workspace(128, 8, 8, 704, ctypes.byref(need)) == GQ_OK
+    # (type, gate, up, n_experts, N, K, logits, n_tokens, top_k, ids, weights, x, x_dtype, act, h, h_dtype, ws,
+    #  ws_bytes, stream)
+    ok = [1, A, A, 128, 704, 2816, A, 8, 8, A, A, A, 0, 0, A, 1, A, need.value, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a0=9) == GQ_ERR_TYPE
+    assert call(a12=2) == GQ_ERR_DTYPE  # fp16 activations
+    assert call(a15=2) == GQ_ERR_DTYPE  # fp16 output
+    assert call(a5=100) == GQ_ERR_SHAPE  # K not whole blocks
+    assert call(a3=0) == GQ_ERR_SHAPE
+    assert call(a8=0) == GQ_ERR_SHAPE
+    assert call(a8=129) == GQ_ERR_SHAPE  # top_k > n_experts
+    assert call(a7=129) == GQ_ERR_SHAPE  # 129 * 8 slots > 1024
+    assert call(a3=5000, a7=1) == GQ_ERR_UNSUPPORTED  # more experts than the router takes
+    assert call(a13=2) == GQ_ERR_UNSUPPORTED  # unknown activation
+    for i in (1, 2, 6, 9, 10, 11, 14, 16):
+        assert call(**{"a%d" % i: None}) == GQ_ERR_NULL, i
+        assert call(**{"a%d" % i: MIS}) == GQ_ERR_ALIGN, i
+    assert call(a17=need.value - 1) == GQ_ERR_WORKSPACE
+    assert call(a7=0, a1=None, a2=None, a6=None, a9=None, a10=None, a11=None, a14=None, a16=None) == GQ_OK

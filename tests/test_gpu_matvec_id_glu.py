@@ -289,3 +289,86 @@ def test_route_topk_plan_feeds_the_layer(gq, orc, T):
     yref, sa = orc.matvec_id("q4_0", gate.cpu().numpy(), E, F, H, ids, x.cpu().numpy(), False)
     err = np.abs(yg.cpu().numpy().astype(np.float64) - yref)
     assert np.all(err <= 1e-3 * sa)
+
+
+# (type, n_experts, hidden K, expert rows N, tokens, top_k, x dtype, h dtype, skew): the one-launch form at the
+# MoE layer's shape, one token, experts taking more than 8 slots (two groups each), every format; then sizes
+# that take the two launches (512 slots; more slots than experts)
+ROUTED_GLU_CASES = [
+    ("q4_0", 128, 2816, 704, 8, 8, "f32", "bf16", False),
+    ("q4_0", 128, 2816, 704, 1, 8, "f32", "f32", False),
+    ("q4_k", 64, 512, 256, 16, 4, "bf16", "bf16", True),
+    ("q6_k", 64, 512, 256, 16, 4, "f32", "f32", True),
+    ("q5_k", 100, 768, 256, 6, 6, "bf16", "f32", False),
+    ("q4_0", 40, 256, 96, 5, 8, "f32", "bf16", True),
+    ("q4_0", 128, 2816, 704, 64, 8, "f32", "bf16", False),
+    ("q4_k", 16, 512, 256, 8, 4, "f32", "f32", False),
+    ("q4_0", 64, 256, 64, 8, 8, "f32", "f32", "ties"),
+]
+
+
+@pytest.mark.parametrize("case", ROUTED_GLU_CASES, ids=lambda c: "%s_E%d_T%dk%d_%s%s" % (
+    c[0], c[1], c[4], c[5], c[7], "_" + (c[8] if isinstance(c[8], str) else "skew") if c[8] else ""))
+def test_route_matvec_id_glu_matches_routing_then_glu(gq, orc, case):
+    """gq_route_matvec_id_glu: ids and weights bit-identical to gq_route_topk's
+    and the oracle's ids; h bit-identical to gq_route_topk_plan then the
+    tableless gq_matvec_id_glu, and within the oracle's bound; the table it
+    leaves in ws gives the weighted down projection and an unweighted routed
+    product bit for bit what the router's table gives them."""
+    t, E, K, N, T, k, xdt, hdt, skew = case
+    g = synth.rng(0x6751000B, E * 1000 + T * 10 + k)
+    logits_np = synth.router_logits(g, T, E)
+    if skew == "ties":  # logits on a coarse grid, with signed zeros: many equal logits (lower id first)
+        logits_np = np.round(logits_np * 2.0).astype(np.float32) / np.float32(2.0)
+        logits_np[logits_np == 0] = np.where(np.arange(int((logits_np == 0).sum())) % 2, -0.0, 0.0)
+    elif skew:  # experts 3 and 5 chosen by every token: 2 groups each for 16 tokens
+        logits_np[:, 3] += 50.0
+        logits_np[:, 5] += 40.0
+    logits = dev(logits_np)
+    hdtype = torch.float32 if hdt == "f32" else torch.bfloat16
+    x, x_t = make_x(g, (T, K), xdt)
+    gate = synth.weight(t, synth.rng(0x6751000B, 1), E * N, K)
+    up = synth.weight(t, synth.rng(0x6751000B, 2), E * N, K)
+    down = synth.weight(t, synth.rng(0x6751000B, 3), E * K, N)
+    gate_t, up_t, down_t = dev(gate), dev(up), dev(down)
+    ws_n = max(N, K)
+
+    def fresh():
+        ws = torch.empty(gq.gq_matvec_id_workspace(E, T, k, ws_n), dtype=torch.uint8, device="cuda")
+        ws.fill_(0xCD)  # contents need no initialisation
+        return (ws, torch.full((T, k), -7, dtype=torch.int32, device="cuda"),
+                torch.full((T, k), float("nan"), device="cuda"),
+                torch.full((T, k, N), float("nan"), device="cuda", dtype=hdtype))
+
+    ws_a, ids_a, rw_a, h_a = fresh()  # one call
+    gq.gq_route_matvec_id_glu(t, gate_t, up_t, E, N, K, logits, k, ids_a, rw_a, x_t, "silu", h_a, ws_a)
+    ws_b, ids_b, rw_b, h_b = fresh()  # the router with its table, then the tableless gated unit
+    gq.gq_route_topk_plan(logits, k, ids_b, rw_b, ws_b)
+    gq.gq_matvec_id_glu(t, gate_t, up_t, E, N, K, (T, k), x_t, "silu", h_b, ws_b)
+    ids_r = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    rw_r = torch.empty((T, k), device="cuda")
+    gq.gq_route_topk(logits, k, ids_r, rw_r)
+    outs = {}
+    for name, ws, rw, h in (("a", ws_a, rw_a, h_a), ("b", ws_b, rw_b, h_b)):
+        y = torch.full((T, K), float("nan"), device="cuda")
+        gq.gq_matvec_id(t, down_t, E, K, N, (T, k), h, True, y, ws, rw)
+        yg = torch.full((T, k, N), float("nan"), device="cuda")
+        gq.gq_matvec_id(t, gate_t, E, N, K, (T, k), x_t, False, yg, ws)
+        outs[name] = (y, yg)
+    torch.cuda.synchronize()
+    ids = ids_a.cpu().numpy()
+    ids_o, _ = orc.route_topk(logits_np, k)
+    assert np.array_equal(ids, ids_o)
+    assert torch.equal(ids_a, ids_r) and torch.equal(ids_a, ids_b)
+    assert torch.equal(rw_a.view(torch.int32), rw_r.view(torch.int32))
+    assert torch.equal(rw_a.view(torch.int32), rw_b.view(torch.int32))
+    hv = h_a.view(torch.int16) if hdt == "bf16" else h_a.view(torch.int32)
+    assert torch.equal(hv, h_b.view(torch.int16) if hdt == "bf16" else h_b.view(torch.int32))
+    for i in range(2):
+        assert torch.equal(outs["a"][i].view(torch.int32), outs["b"][i].view(torch.int32)), ("y", "yg")[i]
+    assert gq.gq_matvec_id_check(ws_a) == 0
+    if skew is True:  # every token chose both (more than 8 slots each when T > 8)
+        assert (ids == 3).sum() == T and (ids == 5).sum() == T
+    ref, bound = glu_ref(orc, t, gate, up, E, N, K, ids, x, "silu", hdt)
+    r = check(h_a.float().cpu().numpy(), ref, bound, "routed gated unit")
+    print("routed gated unit worst err/bound %.4f" % r)

@@ -103,15 +103,16 @@ def test_timed_moe_layer(gq, orc, m):
     torch.cuda.synchronize()
     yref, sa = orc.matvec_id(m.t, ex["down"], m.E, m.H, m.F, ids, h, True, rw)
     check_bound(y.cpu().numpy(), yref, sa, "down (seeded h)")
-    # routing with the table -> routed gated unit -> bf16 h -> weighted down,
-    # as in the fused timed layer (both products on the routed table)
-    gq.gq_route_topk_plan(dev(logits), m.k, ids_t, rw_t, ws)
+    # routing and the routed gated unit -> bf16 h -> weighted down, as in the
+    # fused timed layer (the down product on the table the first call left)
+    ids_t.fill_(-7)
+    rw_t.fill_(float("nan"))
+    hb = torch.full((m.T, m.k, m.F), float("nan"), device="cuda", dtype=torch.bfloat16)
+    gq.gq_route_matvec_id_glu(m.t, dev(ex["gate"]), dev(ex["up"]), m.E, m.F, m.H, dev(logits), m.k, ids_t, rw_t,
+                              dev(x), "silu", hb, ws)
     torch.cuda.synchronize()
     assert np.array_equal(ids_t.cpu().numpy(), ids)
     assert np.array_equal(rw_t.cpu().numpy().view(np.uint32), rw.view(np.uint32))
-    hb = torch.full((m.T, m.k, m.F), float("nan"), device="cuda", dtype=torch.bfloat16)
-    gq.gq_matvec_id_glu(m.t, dev(ex["gate"]), dev(ex["up"]), m.E, m.F, m.H, (m.T, m.k), dev(x), "silu", hb, ws)
-    torch.cuda.synchronize()
     hbits = hb.view(torch.int16).cpu().numpy().view(np.uint16)
     hf = synth.bf16_to_f32(hbits)
     # h against the oracle's gated unit, with the routed gated unit's bound
