@@ -389,59 +389,100 @@ __global__ __launch_bounds__(NTHREADS) void k_experts_routed(
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int S = n_tokens * top_k, s = blockIdx.y, t = s / top_k, j = s - t * top_k;
     const bool writer = blockIdx.x == 0;
-    // every token's keys, token t's apart; the empty asm statements take
-    // every loaded value before the first use, so that all the loads are in
-    // flight together (left to itself the compiler issues the later tokens'
-    // loads one round trip after the search)
-    uint64_t key[ROUTE_TMAX][ROUTE_NI], kt[ROUTE_NI];
+    // wavefront 0 finds the group (the others wait at the barrier, leaving
+    // their SIMDs' issue slots to the other workgroups there); in row tile 0
+    // wavefront 1 meanwhile routes token t for slot s's id and weight
+    if (wave == 0) {
+        // every token's keys, token t's apart; the empty asm statements take
+        // every loaded value before the first use, so that all the loads are
+        // in flight together (left to itself the compiler issues the later
+        // tokens' loads one round trip after the search)
+        uint64_t key[ROUTE_TMAX][ROUTE_NI], kt[ROUTE_NI];
 #pragma unroll
-    for (int u = 0; u < ROUTE_TMAX; ++u)
+        for (int u = 0; u < ROUTE_TMAX; ++u)
+#pragma unroll
+            for (int i = 0; i < ROUTE_NI; ++i)
+                key[u][i] = route_key(logits + (int64_t)min(u, n_tokens - 1) * n_experts, lane + 64 * i, n_experts,
+                                      u < n_tokens);
 #pragma unroll
         for (int i = 0; i < ROUTE_NI; ++i)
-            key[u][i] = route_key(logits + (int64_t)min(u, n_tokens - 1) * n_experts, lane + 64 * i, n_experts,
-                                  u < n_tokens);
+            kt[i] = route_key(logits + (int64_t)t * n_experts, lane + 64 * i, n_experts, true);
 #pragma unroll
-    for (int i = 0; i < ROUTE_NI; ++i)
-        kt[i] = route_key(logits + (int64_t)t * n_experts, lane + 64 * i, n_experts, true);
+        for (int u = 0; u < ROUTE_TMAX; ++u)
 #pragma unroll
-    for (int u = 0; u < ROUTE_TMAX; ++u)
+            for (int i = 0; i < ROUTE_NI; ++i) asm volatile("" : : "v"(key[u][i]));
+        // the key of rank j: its high half bit by bit (32-bit compares), then
+        // the id bits among the keys of that high half (every real key's low
+        // half is ~id with id < 128, so its 25 upper bits are set)
+        uint32_t kh[ROUTE_NI], kl[ROUTE_NI];
 #pragma unroll
-        for (int i = 0; i < ROUTE_NI; ++i) asm volatile("" : : "v"(key[u][i]));
-    // the key of rank j: its high half bit by bit, then the id bits (every
-    // real key's low half is ~id with id < 128, so its 25 upper bits are set)
-    uint64_t v = 0;
-    for (int b = 63; b >= 32; --b) {
-        const uint64_t c = v | (1ull << b);
-        if (keys_above<false>(kt, c) > j) v = c;
-    }
-    v |= 0xFFFFFF80ull;
-    for (int b = 6; b >= 0; --b) {
-        const uint64_t c = v | (1ull << b);
-        if (keys_above<false>(kt, c) > j) v = c;
-    }
-    const int e = min(max((int)~(uint32_t)v, 0), n_experts - 1);  // (in range by construction)
-    // the slots of e: token u holds e at rank r < top_k as slot u * top_k + r
-    uint64_t same = 0;
+        for (int i = 0; i < ROUTE_NI; ++i) {
+            kh[i] = (uint32_t)(kt[i] >> 32);
+            kl[i] = (uint32_t)kt[i];
+        }
+        uint32_t vh = 0;
+        for (int b = 31; b >= 0; --b) {
+            const uint32_t c = vh | (1u << b);
+            int n = 0;
 #pragma unroll
-    for (int u = 0; u < ROUTE_TMAX; ++u) {
-        const uint64_t kh = ROUTE_NI == 1 || e < 64 ? key[u][0] : key[u][ROUTE_NI - 1];
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(kh >> 32), e & 63);
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)kh, e & 63);
-        const int r = keys_above<true>(key[u], ((uint64_t)hi << 32) | lo);
-        if (u < n_tokens && r < top_k) same |= 1ull << (u * top_k + r);
-    }
-    const uint64_t below = same & ((1ull << s) - 1ull);  // s < S <= 64
-    const uint64_t from = same & ~below;                 // s and the later slots of e
-    const int nb = __popcll(below) % CH ? 0 : min(CH, __popcll(from));
-    int sel = s;  // lane i < nb: the i-th slot of the group
-    uint64_t m = from;
+            for (int i = 0; i < ROUTE_NI; ++i) n += __popcll(__ballot(kh[i] >= c));
+            if (n > j) vh = c;
+        }
+        int above = 0;
+        uint64_t eq[ROUTE_NI];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int b = __ffsll((unsigned long long)m) - 1;
-        if (lane == i && i < nb) sel = b;
-        m &= m - 1ull;
-    }
-    if (writer && wave == 0) {
+        for (int i = 0; i < ROUTE_NI; ++i) {
+            above += __popcll(__ballot(kh[i] > vh));
+            eq[i] = __ballot(kh[i] == vh);
+        }
+        uint32_t vl = 0xFFFFFF80u;
+        for (int b = 6; b >= 0; --b) {
+            const uint32_t c = vl | (1u << b);
+            int n = above;
+#pragma unroll
+            for (int i = 0; i < ROUTE_NI; ++i) n += __popcll(__ballot(kl[i] >= c) & eq[i]);
+            if (n > j) vl = c;
+        }
+        const int e = min(max((int)~vl, 0), n_experts - 1);  // (in range by construction)
+        // the slots of e: token u holds e at rank r < top_k as slot u * top_k + r
+        uint64_t same = 0;
+#pragma unroll
+        for (int u = 0; u < ROUTE_TMAX; ++u) {
+            const uint64_t kx = ROUTE_NI == 1 || e < 64 ? key[u][0] : key[u][ROUTE_NI - 1];
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(kx >> 32), e & 63);
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)kx, e & 63);
+            const int r = keys_above<true>(key[u], ((uint64_t)hi << 32) | lo);
+            if (u < n_tokens && r < top_k) same |= 1ull << (u * top_k + r);
+        }
+        const uint64_t below = same & ((1ull << s) - 1ull);  // s < S <= 64
+        const uint64_t from = same & ~below;                 // s and the later slots of e
+        const int nb = __popcll(below) % CH ? 0 : min(CH, __popcll(from));
+        int sel = s;  // lane i < nb: the i-th slot of the group
+        uint64_t m = from;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int b = __ffsll((unsigned long long)m) - 1;
+            if (lane == i && i < nb) sel = b;
+            m &= m - 1ull;
+        }
+        if (lane < CH) le.sel[lane] = sel;
+        if (lane == 0) {
+            le.e = e;
+            le.nb = nb;
+        }
+        if (writer) {
+            if (lane < CH) plan[s].sel[lane] = sel;
+            if (lane == 0) {
+                plan[s].e = e;
+                plan[s].nb = nb;
+                slot_e[s] = e;
+                if (s == 0) {
+                    hdr[0] = 0;
+                    hdr[1] = S;
+                }
+            }
+        }
+    } else if (wave == 1 && writer) {
         int id;
         float w;
         gqr::route_token<ROUTE_NI>(logits + (int64_t)t * n_experts, n_experts, top_k, lane, id, w);
@@ -449,26 +490,10 @@ __global__ __launch_bounds__(NTHREADS) void k_experts_routed(
             ids[s] = id;
             weights[s] = w;
         }
-        if (lane < CH) plan[s].sel[lane] = sel;
-        if (lane == 0) {
-            plan[s].e = e;
-            plan[s].nb = nb;
-            slot_e[s] = e;
-            if (s == 0) {
-                hdr[0] = 0;
-                hdr[1] = S;
-            }
-        }
-    }
-    if (nb == 0) return;
-    if (wave == 0) {
-        if (lane < CH) le.sel[lane] = sel;
-        if (lane == 0) {
-            le.e = e;
-            le.nb = nb;
-        }
     }
     lds_barrier();
+    const int nb = __builtin_amdgcn_readfirstlane(le.nb), e = __builtin_amdgcn_readfirstlane(le.e);
+    if (nb == 0) return;
     experts_tile<TYPE, XT, D, RING, true>(gate, up, expert_bytes, N, K, x, 0, top_k, S, &le, nb, e, out, out_bf16,
                                           act, LPR, lds);
 }
